@@ -1,0 +1,290 @@
+"""Paged KV pool: cache-write replay, dequantization and block-table gather (fp64, CPU).
+
+TEST INFRASTRUCTURE. Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline
+leg may import this package.
+
+What the pages fix:
+  * KV lives in fixed physical blocks of 16 tokens, reached through a per-sequence
+    logical->physical block table (inferensys glossary "vLLM", PagedAttention entry;
+    xonoai.com field report on vLLM v0.7.2, "Deconstructing the v0.7.2 Architecture",
+    and its launch flag --block-size 16).
+  * FP8 E4M3 KV quantization with a fp32 scale (xonoai.com report, same section).
+  * 4-bit outlier-aware quantization (dailyaiworld.com, "vLLM 0.7 Ships Unified KV
+    Cache Compression", "Technical Breakdown: Dynamic Quantization with Outlier
+    Retention", steps 1-3): per-channel magnitude norms, channels at or above a 3.2 sigma
+    threshold kept in an fp16 outlier buffer, the remaining channels normalized and
+    quantized to FP4.
+
+Readings where the pages are silent (each listed in the design notes):
+  * FP8: code = E4M3(fp32(x / s_h)); the quotient is the correctly rounded fp32 one and
+    that fp32 value is rounded to E4M3 (nearest, ties even, saturating). s_h is the
+    per-(layer, kv-head) fp32 scale fp32(absmax_h / 448), absmax over every value of that
+    head the run writes, K and V separately. s = 0 gives +0 codes.
+  * FP4 calibration granularity: per (physical block, kv-head, K|V), on the tokens the
+    first write into that block carries; later writes reuse the stored channel set.
+    The per-channel norm is the RMS over those tokens; mu and sigma are the mean and
+    population standard deviation of the D norms; outliers are the channels with
+    norm >= mu + 3.2 sigma, ascending; sigma = 0 means no outliers.
+  * FP4 scale: one fp32 scale per (token, kv-head, K|V), fp32(inlier absmax / 6); inlier
+    codes are E2M1(fp32(x / s_t)); outlier positions hold code +0; s_t = 0 gives +0 codes;
+    two codes per byte, even channel in the low nibble; outliers are stored as fp16(x).
+
+Pool layout (the boundary's layout, row-major, one array per field):
+  f16 / bf16 : k, v          uint16 [NB, Hkv, 16, D]
+  fp8        : k, v          uint8  [NB, Hkv, 16, D]        (+ per-head fp32 scales)
+  fp4        : k, v          uint8  [NB, Hkv, 16, D/2]
+               *_tok_scale   fp32   [NB, Hkv, 16]
+               *_out_idx     uint8  [NB, Hkv, 16]  byte 0 = count (0xFF = not yet
+                                    calibrated), then the ascending channel indices,
+                                    then 0xFF in the unused bytes
+               *_out_val     uint16 [NB, Hkv, CAP, 16]  fp16 bits, slot j = j-th outlier
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from .formats import (
+    E4M3_MAX,
+    E2M1_MAX,
+    act_decode,
+    e2m1_decode,
+    e2m1_encode,
+    e4m3_decode,
+    e4m3_encode,
+    f16_decode,
+    f16_encode,
+    f32_quotient,
+    f32_round,
+)
+
+BLOCK_TOKENS = 16
+OUTLIER_SIGMAS = 3.2
+UNCALIBRATED = 0xFF
+
+
+def outlier_capacity(head_dim: int) -> int:
+    """Most channels that can reach mu + 3.2 sigma among head_dim norms.
+
+    If k channels satisfy r_c - mu >= 3.2 sigma, the other head_dim - k deviations sum to
+    at most -3.2 k sigma, so (Cauchy-Schwarz) D sigma^2 >= 10.24 k sigma^2 (1 + k/(D-k)),
+    i.e. k <= D / (1 + 3.2^2). 11 for D = 128, 5 for D = 64."""
+    return int(np.floor(head_dim / (1.0 + OUTLIER_SIGMAS ** 2)))
+
+
+@dataclass
+class Pool:
+    kind: str  # "f16" | "bf16" | "fp8" | "fp4"
+    num_blocks: int
+    num_kv_heads: int
+    head_dim: int
+    arrays: dict = field(default_factory=dict)
+
+    @staticmethod
+    def shapes(kind, nb, hkv, d):
+        if kind in ("f16", "bf16"):
+            return {"k": ((nb, hkv, 16, d), np.uint16), "v": ((nb, hkv, 16, d), np.uint16)}
+        if kind == "fp8":
+            return {"k": ((nb, hkv, 16, d), np.uint8), "v": ((nb, hkv, 16, d), np.uint8)}
+        if kind == "fp4":
+            cap = outlier_capacity(d)
+            out = {}
+            for kv in ("k", "v"):
+                out[kv] = ((nb, hkv, 16, d // 2), np.uint8)
+                out[kv + "_tok_scale"] = ((nb, hkv, 16), np.float32)
+                out[kv + "_out_idx"] = ((nb, hkv, 16), np.uint8)
+                out[kv + "_out_val"] = ((nb, hkv, cap, 16), np.uint16)
+            return out
+        raise ValueError(kind)
+
+    @classmethod
+    def filled(cls, kind, nb, hkv, d, sentinel=0xA5):
+        """A pool whose every byte is `sentinel`, except that FP4 calibration records
+        start as 'not calibrated' (all 0xFF), which the caller must arrange."""
+        p = cls(kind, nb, hkv, d)
+        for name, (shape, dt) in cls.shapes(kind, nb, hkv, d).items():
+            n = int(np.prod(shape)) * np.dtype(dt).itemsize
+            fill = UNCALIBRATED if name.endswith("_out_idx") else sentinel
+            p.arrays[name] = np.full(n, fill, dtype=np.uint8).view(dt).reshape(shape)
+        return p
+
+
+# ----------------------------------------------------------------------------------
+# scales
+# ----------------------------------------------------------------------------------
+
+
+def fp8_head_scale(rows_bits: np.ndarray, act: str) -> np.ndarray:
+    """Per-kv-head fp32 scale fp32(absmax_h / 448) over rows [T, Hkv, D]."""
+    x = act_decode(rows_bits, act)
+    absmax = np.abs(x).max(axis=(0, 2))
+    return f32_quotient(absmax, E4M3_MAX).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------------
+# FP4 pieces
+# ----------------------------------------------------------------------------------
+
+
+def fp4_calibrate(x: np.ndarray) -> np.ndarray:
+    """Outlier channel set of one (block, head) from its tokens x [n, D] (fp64).
+
+    Per-channel RMS norm over the n tokens, then every channel whose norm is at least
+    mean + 3.2 * population-std of the D norms; ascending. sigma = 0 -> none."""
+    r = np.sqrt(np.mean(x * x, axis=0))
+    mu = np.mean(r)
+    sigma = np.sqrt(np.mean((r - mu) ** 2))
+    if sigma == 0.0:
+        return np.zeros(0, dtype=np.int64)
+    return np.nonzero(r >= mu + OUTLIER_SIGMAS * sigma)[0].astype(np.int64)
+
+
+def fp4_calibration_margin(x: np.ndarray) -> float:
+    """Smallest |r_c - threshold| / threshold of the calibration above (inf if sigma=0);
+    used to flag near-ties where fp32 and fp64 statistics may disagree."""
+    r = np.sqrt(np.mean(x * x, axis=0))
+    mu = np.mean(r)
+    sigma = np.sqrt(np.mean((r - mu) ** 2))
+    if sigma == 0.0:
+        return np.inf
+    thr = mu + OUTLIER_SIGMAS * sigma
+    return float(np.min(np.abs(r - thr)) / thr)
+
+
+def fp4_encode_row(x: np.ndarray, outliers: np.ndarray):
+    """One token row x [D] (fp64 of the input values) with its block's outlier set.
+
+    Returns (packed codes [D/2] uint8, fp32 scale, fp16 outlier bits [len(outliers)])."""
+    d = x.shape[0]
+    inlier = np.ones(d, dtype=bool)
+    inlier[outliers] = False
+    a = np.abs(x[inlier]).max() if inlier.any() else 0.0
+    s = float(f32_quotient(a, E2M1_MAX))
+    codes = np.zeros(d, dtype=np.uint8)
+    if s != 0.0:
+        codes[inlier] = e2m1_encode(f32_quotient(x[inlier], s))
+    packed = (codes[0::2] | (codes[1::2] << np.uint8(4))).astype(np.uint8)
+    return packed, np.float32(s), f16_encode(x[outliers])
+
+
+# ----------------------------------------------------------------------------------
+# the write
+# ----------------------------------------------------------------------------------
+
+
+def cache_write(pool: Pool, k_rows, v_rows, act: str, slots, k_scale=None, v_scale=None,
+                only_blocks=None):
+    """Replay one cache-write call: row i of k_rows/v_rows [T, Hkv, D] (raw 16-bit bits)
+    goes to slot slots[i] = physical_block * 16 + offset; negative slots are skipped.
+
+    Slots within one call must be distinct. If only_blocks is given, only writes into
+    those physical blocks are replayed (each block's contents depend only on the calls
+    that write into it, so sampled replays are exact)."""
+    slots = np.asarray(slots, dtype=np.int64)
+    live = np.nonzero(slots >= 0)[0]
+    assert len(np.unique(slots[live])) == len(live), "slots within one call must be distinct"
+    if only_blocks is not None:
+        keep = np.isin(slots[live] // BLOCK_TOKENS, np.asarray(list(only_blocks)))
+        live = live[keep]
+    blk = slots[live] // BLOCK_TOKENS
+    off = slots[live] % BLOCK_TOKENS
+    assert (blk < pool.num_blocks).all()
+    A = pool.arrays
+    if pool.kind in ("f16", "bf16"):
+        assert pool.kind == act, "a 16-bit pool stores the activation dtype unchanged"
+        A["k"][blk, :, off, :] = np.asarray(k_rows)[live]
+        A["v"][blk, :, off, :] = np.asarray(v_rows)[live]
+        return
+    if pool.kind == "fp8":
+        for name, rows, sc in (("k", k_rows, k_scale), ("v", v_rows, v_scale)):
+            x = act_decode(np.asarray(rows)[live], act)  # [n, Hkv, D]
+            s = np.asarray(sc, dtype=np.float32).astype(np.float64)[None, :, None]
+            q = f32_quotient(x, s)
+            codes = e4m3_encode(np.where(s == 0.0, 0.0, q))
+            A[name][blk, :, off, :] = codes
+        return
+    if pool.kind == "fp4":
+        hkv = pool.num_kv_heads
+        for name, rows in (("k", k_rows), ("v", v_rows)):
+            x_all = act_decode(np.asarray(rows)[live], act)  # [n, Hkv, D]
+            idx_arr, val_arr = A[name + "_out_idx"], A[name + "_out_val"]
+            # step 1-2: calibrate blocks this call opens, on this call's tokens
+            for b in np.unique(blk):
+                rows_in_b = np.nonzero(blk == b)[0]
+                for h in range(hkv):
+                    if idx_arr[b, h, 0] != UNCALIBRATED:
+                        continue
+                    o = fp4_calibrate(x_all[rows_in_b, h, :])
+                    rec = np.full(16, UNCALIBRATED, dtype=np.uint8)
+                    rec[0] = len(o)
+                    rec[1:1 + len(o)] = o
+                    idx_arr[b, h, :] = rec
+            # step 3: encode every row with its block's channel set
+            for i in range(len(live)):
+                for h in range(hkv):
+                    rec = idx_arr[blk[i], h]
+                    o = rec[1:1 + rec[0]].astype(np.int64)
+                    packed, s, ov = fp4_encode_row(x_all[i, h, :], o)
+                    A[name][blk[i], h, off[i], :] = packed
+                    A[name + "_tok_scale"][blk[i], h, off[i]] = s
+                    val_arr[blk[i], h, :len(o), off[i]] = ov
+        return
+    raise ValueError(pool.kind)
+
+
+# ----------------------------------------------------------------------------------
+# dequantization and gather
+# ----------------------------------------------------------------------------------
+
+
+def dequant_slot_rows(pool: Pool, blk, off, k_scale=None, v_scale=None):
+    """Dequantized K and V rows [n, Hkv, D] (fp64, exact) at (blk[i], off[i])."""
+    A = pool.arrays
+    blk = np.asarray(blk, dtype=np.int64)
+    off = np.asarray(off, dtype=np.int64)
+    out = []
+    for name, sc in (("k", k_scale), ("v", v_scale)):
+        if pool.kind == "bf16":
+            out.append(act_decode(A[name][blk, :, off, :], "bf16"))
+        elif pool.kind == "f16":
+            out.append(f16_decode(A[name][blk, :, off, :]))
+        elif pool.kind == "fp8":
+            s = np.asarray(sc, dtype=np.float32).astype(np.float64)[None, :, None]
+            out.append(e4m3_decode(A[name][blk, :, off, :]) * s)
+        elif pool.kind == "fp4":
+            packed = A[name][blk, :, off, :]  # [n, Hkv, D/2]
+            n, hkv, half = packed.shape
+            codes = np.empty((n, hkv, 2 * half), dtype=np.uint8)
+            codes[..., 0::2] = packed & 0xF
+            codes[..., 1::2] = packed >> 4
+            s = A[name + "_tok_scale"][blk, :, off].astype(np.float64)[..., None]
+            x = e2m1_decode(codes) * s
+            rec = A[name + "_out_idx"][blk]  # [n, Hkv, 16]
+            vals = A[name + "_out_val"][blk]  # [n, Hkv, CAP, 16]
+            for i in range(n):
+                for h in range(hkv):
+                    cnt = int(rec[i, h, 0])
+                    assert cnt != UNCALIBRATED, "read of a block that was never written"
+                    for j in range(cnt):
+                        x[i, h, rec[i, h, 1 + j]] = f16_decode(vals[i, h, j, off[i]])
+            out.append(x)
+        else:
+            raise ValueError(pool.kind)
+    return out[0], out[1]
+
+
+def gather_sequence(pool: Pool, block_table_row, context_len, k_scale=None, v_scale=None):
+    """K̂, V̂ [L, Hkv, D] of one sequence: token t lives at
+    (block_table_row[t // 16], t % 16)."""
+    t = np.arange(int(context_len))
+    blk = np.asarray(block_table_row, dtype=np.int64)[t // BLOCK_TOKENS]
+    assert (blk >= 0).all() and (blk < pool.num_blocks).all()
+    return dequant_slot_rows(pool, blk, t % BLOCK_TOKENS, k_scale, v_scale)
+
+
+__all__ = [
+    "BLOCK_TOKENS", "OUTLIER_SIGMAS", "UNCALIBRATED", "Pool", "outlier_capacity",
+    "fp8_head_scale", "fp4_calibrate", "fp4_calibration_margin", "fp4_encode_row",
+    "cache_write", "dequant_slot_rows", "gather_sequence", "f32_round",
+]

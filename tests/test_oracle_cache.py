@@ -1,0 +1,226 @@
+"""Pins of the oracle's cache write, FP4 outlier calibration and dequantization (CPU).
+
+Closed forms and invariants the pages and the mathematics fix: slot placement with
+sentinel bytes, the k-equal-channels threshold closed form (which also shows the outlier
+capacity is tight), the planted x20 channel, sigma = 0, per-token scale and per-head
+scale invariants (the absmax element lands on the largest code), and dequantization
+error bounds."""
+import numpy as np
+import pytest
+
+from oracle import cache as C
+from oracle import formats as F
+
+
+def _bf16_bits(x):
+    """fp32 -> bf16 bits, round to nearest even (test-side input preparation)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = u + 0x7FFF + ((u >> 16) & 1)
+    return (u >> 16).astype(np.uint16)
+
+
+def test_outlier_capacity_closed_form():
+    assert C.outlier_capacity(128) == 11
+    assert C.outlier_capacity(64) == 5
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_k_equal_channels_threshold_is_tight(d):
+    # k channels with norm a, D-k with norm 0: flagged iff D - k >= 10.24 k, i.e. k <= cap
+    cap = C.outlier_capacity(d)
+    for k in range(1, cap + 3):
+        x = np.zeros((3, d))
+        x[:, :k] = 2.0
+        o = C.fp4_calibrate(x)
+        if k <= cap:
+            assert o.tolist() == list(range(k)), k
+        else:
+            assert len(o) == 0, k
+
+
+def test_planted_channel_closed_form():
+    # 127 channels of RMS 1 and one of RMS 20: mu = 147/128, sigma^2 = 527/128 - mu^2
+    x = np.ones((16, 128))
+    x[:, 77] = 20.0
+    x[::2] *= -1  # signs do not change RMS
+    mu = 147 / 128
+    sigma = np.sqrt(527 / 128 - mu ** 2)
+    assert 1.0 < mu + 3.2 * sigma < 20.0
+    assert C.fp4_calibrate(x).tolist() == [77]
+
+
+def test_sigma_zero_gives_no_outliers():
+    assert len(C.fp4_calibrate(np.full((4, 128), 0.75))) == 0
+    assert len(C.fp4_calibrate(np.zeros((1, 64)))) == 0
+
+
+def test_single_token_rms_is_abs():
+    x = np.zeros((1, 128))
+    x[0, 5] = -9.0
+    x[0, 6:] = 0.1
+    assert C.fp4_calibrate(x).tolist() == [5]
+
+
+def test_cantelli_bound_holds_on_heavy_tails():
+    rng = np.random.default_rng(0)
+    for _ in range(300):
+        x = rng.standard_cauchy((rng.integers(1, 17), 128)) * rng.uniform(0.1, 10)
+        assert len(C.fp4_calibrate(x)) <= 11
+
+
+def test_fp4_row_invariants():
+    rng = np.random.default_rng(1)
+    for _ in range(200):
+        x = F.bf16_decode(_bf16_bits(rng.standard_normal(128) * rng.uniform(0.01, 50)))
+        o = np.sort(rng.choice(128, size=rng.integers(0, 4), replace=False))
+        packed, s, ov = C.fp4_encode_row(x, o)
+        codes = np.empty(128, dtype=np.uint8)
+        codes[0::2], codes[1::2] = packed & 0xF, packed >> 4
+        inl = np.setdiff1d(np.arange(128), o)
+        amax = inl[np.argmax(np.abs(x[inl]))]
+        # the inlier absmax lands on +-6, outlier positions hold +0
+        assert codes[amax] & 7 == 7
+        assert np.all(codes[o] == 0)
+        assert np.float32(s) == np.float32(np.abs(x[inl]).max()) / np.float32(6.0)
+        assert np.array_equal(F.f16_decode(ov), x[o])  # bf16 values are exact in fp16 here
+        # dequant error: at most half the E2M1 spacing at the scaled value (plus the
+        # fp32 rounding of the quotient)
+        v = x[inl] / float(s)
+        deq = F.e2m1_decode(codes[inl]) * float(s)
+        half = np.where(np.abs(v) < 2, 0.25, np.where(np.abs(v) < 4, 0.5, 1.0))
+        assert np.all(np.abs(deq - x[inl]) <= (half + 1e-6) * float(s))
+
+
+def test_fp4_zero_row():
+    packed, s, ov = C.fp4_encode_row(np.zeros(128), np.zeros(0, dtype=np.int64))
+    assert s == 0 and np.all(packed == 0)
+    x = np.zeros(128)
+    x[3] = -0.0
+    packed, s, _ = C.fp4_encode_row(x, np.zeros(0, dtype=np.int64))
+    assert np.all(packed == 0)  # s = 0 gives +0 codes
+
+
+def test_fp8_head_scale_invariant():
+    rng = np.random.default_rng(2)
+    rows = _bf16_bits(rng.standard_normal((50, 4, 64)) * np.array([1, 3, 0.01, 100])[None, :, None])
+    s = C.fp8_head_scale(rows, "bf16")
+    x = F.bf16_decode(rows)
+    for h in range(4):
+        a = np.abs(x[:, h, :]).max()
+        assert s[h] == np.float32(a) / np.float32(448.0)
+        code = F.e4m3_encode(F.f32_quotient(np.array([a, -a]), s[h]))
+        assert code.tolist() == [0x7E, 0xFE]
+
+
+def _write_and_read(kind, act, rows_k, rows_v, slots, nb=8, **kw):
+    hkv, d = rows_k.shape[1], rows_k.shape[2]
+    pool = C.Pool.filled(kind, nb, hkv, d)
+    before = {n: a.copy() for n, a in pool.arrays.items()}
+    C.cache_write(pool, rows_k, rows_v, act, slots, **kw)
+    return pool, before
+
+
+def test_slot_placement_and_sentinels_copy_path():
+    rng = np.random.default_rng(3)
+    T, hkv, d = 11, 2, 64
+    k = rng.integers(0, 2 ** 16, (T, hkv, d), dtype=np.uint16)
+    v = rng.integers(0, 2 ** 16, (T, hkv, d), dtype=np.uint16)
+    slots = rng.choice(8 * 16, T, replace=False).astype(np.int64)
+    slots[4] = -1  # skipped
+    pool, before = _write_and_read("f16", "f16", k, v, slots)
+    written = np.zeros((8, hkv, 16), dtype=bool)
+    for i, s in enumerate(slots):
+        if s < 0:
+            continue
+        b, o = divmod(int(s), 16)
+        assert np.array_equal(pool.arrays["k"][b, :, o, :], k[i])
+        assert np.array_equal(pool.arrays["v"][b, :, o, :], v[i])
+        written[b, :, o] = True
+    for n in ("k", "v"):
+        assert np.array_equal(pool.arrays[n][~written], before[n][~written])  # sentinels
+
+
+def test_distinct_slots_required():
+    k = np.zeros((2, 1, 64), dtype=np.uint16)
+    with pytest.raises(AssertionError):
+        _write_and_read("f16", "f16", k, k, np.array([5, 5]))
+
+
+def test_fp8_write_dequant_error_bound():
+    rng = np.random.default_rng(4)
+    T, hkv, d = 40, 2, 128
+    k = _bf16_bits(rng.standard_normal((T, hkv, d)))
+    v = _bf16_bits(rng.standard_normal((T, hkv, d)) * 3)
+    ks, vs = C.fp8_head_scale(k, "bf16"), C.fp8_head_scale(v, "bf16")
+    slots = rng.permutation(8 * 16)[:T].astype(np.int64)
+    pool, before = _write_and_read("fp8", "bf16", k, v, slots, k_scale=ks, v_scale=vs)
+    kd, vd = C.dequant_slot_rows(pool, slots // 16, slots % 16, ks, vs)
+    for x_bits, deq, s in ((k, kd, ks), (v, vd, vs)):
+        x = F.bf16_decode(x_bits)
+        a = np.abs(x / s[None, :, None])
+        e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+        # half the E4M3 spacing at x/s, plus the fp32 rounding of the quotient x/s
+        # (the code is E4M3 of the fp32 quotient, so a quotient that rounds onto a tie
+        # may land a full half-spacing plus one fp32 ulp away)
+        bound = (2.0 ** (e - 4) + a * 2.0 ** -23) * s[None, :, None]
+        assert np.all(np.abs(deq - x) <= bound)
+    # zero scale gives +0 codes
+    pool, _ = _write_and_read("fp8", "bf16", k, v, slots, k_scale=np.zeros(hkv, np.float32),
+                              v_scale=vs)
+    assert np.all(pool.arrays["k"][slots // 16, :, slots % 16, :] == 0)
+
+
+def test_fp4_calibrates_once_per_block_and_reuses():
+    rng = np.random.default_rng(5)
+    d, hkv = 128, 1
+    x1 = rng.standard_normal((4, hkv, d))
+    x1[:, 0, 9] *= 20
+    x2 = rng.standard_normal((4, hkv, d))
+    x2[:, 0, 50] *= 20  # a different channel would be flagged if recalibrated
+    k1, k2 = _bf16_bits(x1), _bf16_bits(x2)
+    pool = C.Pool.filled("fp4", 4, hkv, d)
+    C.cache_write(pool, k1, k1, "bf16", np.array([32, 33, 34, 35]))  # block 2, offsets 0-3
+    rec = pool.arrays["k_out_idx"][2, 0]
+    assert rec[0] == 1 and rec[1] == 9 and np.all(rec[2:] == 0xFF)
+    C.cache_write(pool, k2, k2, "bf16", np.array([36, 37, 38, 39]))
+    assert np.array_equal(pool.arrays["k_out_idx"][2, 0], rec)  # reused, not recomputed
+    kd, _ = C.dequant_slot_rows(pool, np.full(8, 2), np.arange(8))
+    xall = F.bf16_decode(np.concatenate([k1, k2]))
+    # the outlier channel comes back exactly (fp16 holds bf16 values exactly)
+    assert np.array_equal(kd[:, 0, 9], xall[:, 0, 9])
+    # untouched offsets and the unused outlier slots keep their sentinel bytes
+    assert np.all(pool.arrays["k"][2, 0, 8:].view(np.uint8) == 0xA5)
+    assert np.all(pool.arrays["k_out_val"][2, 0, 1:].view(np.uint8) == 0xA5)
+    assert np.all(pool.arrays["k_out_idx"][[0, 1, 3]] == 0xFF)
+
+
+def test_fp4_calibration_uses_only_the_calls_tokens_in_the_block():
+    d = 128
+    x = np.ones((3, 1, d))
+    x[0, 0, 10] = 30.0  # token in block 0
+    x[1, 0, 20] = 30.0  # token in block 1
+    x[2, 0, 21] = 30.0  # token in block 1
+    bits = _bf16_bits(x)
+    pool = C.Pool.filled("fp4", 2, 1, d)
+    C.cache_write(pool, bits, bits, "bf16", np.array([3, 16, 17]))
+    assert pool.arrays["k_out_idx"][0, 0, :2].tolist() == [1, 10]
+    assert pool.arrays["k_out_idx"][1, 0, :3].tolist() == [2, 20, 21]
+
+
+def test_fp8_code_is_e4m3_of_the_fp32_quotient():
+    # The reading: the quantizer divides in fp32 (correctly rounded) and rounds that fp32
+    # value to E4M3. Here x = 3.046875 (a bf16 value) and s = fp32 bits 0x3C149249: the
+    # exact quotient is slightly above the tie 336 (between 320 and 352), but its fp32
+    # rounding is exactly 336.0, so the code is the even neighbour 320 (0x7A), not 352.
+    from fractions import Fraction
+    s = np.array([0x3C149249], dtype=np.uint32).view(np.float32)[0]
+    x = 3.046875
+    assert Fraction(x) / Fraction(float(s)) > 336
+    q = F.f32_quotient(x, s)
+    assert q == 336.0
+    assert int(F.e4m3_encode(q)) == 0x7A
+    pool = C.Pool.filled("fp8", 1, 1, 64)
+    row = np.zeros((1, 1, 64), dtype=np.uint16)
+    row[0, 0, 0] = _bf16_bits(np.array([x]))[0]
+    C.cache_write(pool, row, row, "bf16", np.array([0]), k_scale=np.array([s]), v_scale=np.array([s]))
+    assert pool.arrays["k"][0, 0, 0, 0] == 0x7A
