@@ -1,0 +1,226 @@
+/*
+ * pa.h - C ABI of the paged, quantized KV-cache library for AMD Instinct MI355X (gfx950).
+ *
+ * Two operations make up the hot path of paged decode over a low-precision KV cache:
+ *
+ *   cache write  - scatter each new token's K/V row into its slot of a fixed 16-token
+ *                  physical block, quantizing on the fly (dailyaiworld.com, "vLLM 0.7 Ships
+ *                  Unified KV Cache Compression": the engine diagram and the section "The KV
+ *                  Cache Memory Crisis in Enterprise Agent Deployments"; xonoai.com field
+ *                  report on vLLM v0.7.2, "Deconstructing the v0.7.2 Architecture").
+ *   paged decode - gather a sequence's blocks through its block table, dequantize, and run
+ *                  softmax attention for one new query token, optionally split into
+ *                  context partitions that a log-sum-exp merge recombines (inferensys
+ *                  glossary "vLLM", PagedAttention entry; dailyaiworld.com, "Technical
+ *                  Breakdown: Dynamic Quantization with Outlier Retention", step 4).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are device pointers unless stated otherwise. The caller owns all memory;
+ *     the library allocates nothing and keeps no mutable global state, so calls from
+ *     several host threads or streams are safe if their buffers do not overlap.
+ *   - Arguments are validated on the host before anything is launched; a failed check
+ *     returns a negative pa_status and launches nothing. Work is queued asynchronously
+ *     on `stream` (a hipStream_t; NULL = the default stream). Device-side faults surface
+ *     at the caller's next synchronization.
+ *   - Device-side checks (a block id outside [0, num_blocks), a slot outside
+ *     [0, num_blocks * 16), a context length outside [1, max_blocks_per_seq * 16), a read
+ *     of an FP4 block that was never written) skip the offending access and OR a bit into
+ *     the optional `dev_err` word (an int32 in device memory the caller zeroes; NULL = no
+ *     reporting). Bits: PA_DEVERR_*.
+ *   - All arrays are dense, row-major, in the shapes written below, 16-byte aligned.
+ *   - Query head h reads kv head h / (num_q_heads / num_kv_heads) (grouped-query attention
+ *     with contiguous groups); num_q_heads / num_kv_heads must be 1..16.
+ *   - head_dim is 64 or 128; block_size is 16 (the block size the pages use: xonoai.com
+ *     report, "Deconstructing the v0.7.2 Architecture", and its --block-size 16 flag).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_BLOCK_SIZE 16
+
+/* KV cache storage formats (the --kv-cache-dtype choices on the pages, plus 16-bit). */
+typedef enum {
+  PA_KV_F16 = 0,            /* fp16 copy, no quantization                              */
+  PA_KV_BF16 = 1,           /* bf16 copy, no quantization                              */
+  PA_KV_FP8_E4M3 = 2,       /* OCP E4M3FN codes, one fp32 scale per kv head (K and V)  */
+  PA_KV_FP4_E2M1_OUTL = 3   /* E2M1 codes + per-token fp32 scale + fp16 outlier buffer */
+} pa_kv_dtype;
+
+/* Activation (query and new K/V row) dtypes. */
+typedef enum { PA_ACT_F16 = 0, PA_ACT_BF16 = 1 } pa_act_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL                                 */
+  PA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent                     */
+  PA_ERR_DTYPE = -3,       /* unknown dtype or an unsupported kv/activation combination  */
+  PA_ERR_BLOCK_SIZE = -4,  /* block_size != 16                                          */
+  PA_ERR_CONTEXT = -5,     /* max_blocks_per_seq out of range                           */
+  PA_ERR_PARTITION = -6,   /* partition_size not 0 and not a positive multiple of 16    */
+  PA_ERR_LAUNCH = -7,      /* the HIP runtime refused a launch                          */
+  PA_ERR_ALIGN = -8        /* a pointer is not 16-byte aligned                          */
+} pa_status;
+
+#define PA_DEVERR_BAD_BLOCK 1        /* block table entry outside [0, num_blocks)        */
+#define PA_DEVERR_BAD_SLOT 2         /* slot_mapping entry outside [0, num_blocks * 16)   */
+#define PA_DEVERR_BAD_CONTEXT 4      /* context_lens entry outside [1, MB * 16]           */
+#define PA_DEVERR_UNCALIBRATED 8     /* decode read an FP4 block whose record is unset    */
+
+/*
+ * The paged KV pool (passed by host pointer; the arrays it points to are device memory).
+ *
+ *   PA_KV_F16 / PA_KV_BF16 : k, v   [num_blocks, num_kv_heads, 16, head_dim] 16-bit values
+ *   PA_KV_FP8_E4M3         : k, v   [num_blocks, num_kv_heads, 16, head_dim] uint8 codes
+ *                            k_scale, v_scale [num_kv_heads] fp32 (inputs, read-only):
+ *                            the stored value is code * scale (per layer and kv head;
+ *                            see pa_fp8_head_scales).
+ *   PA_KV_FP4_E2M1_OUTL    : k, v   [num_blocks, num_kv_heads, 16, head_dim / 2] uint8,
+ *                                   two E2M1 codes per byte, even channel in the low nibble
+ *                            *_tok_scale [num_blocks, num_kv_heads, 16] fp32, per token
+ *                            *_out_idx   [num_blocks, num_kv_heads, 16] uint8 record per
+ *                                        (block, kv head): byte 0 = outlier count, or 0xFF
+ *                                        while the block has never been written; bytes
+ *                                        1..count = ascending channel indices; the other
+ *                                        bytes 0xFF. The caller fills a block's record with
+ *                                        0xFF before the block is first written (see
+ *                                        pa_reset_blocks).
+ *                            *_out_val   [num_blocks, num_kv_heads, CAP, 16] fp16 bits:
+ *                                        slot j holds the j-th outlier channel's value for
+ *                                        each token offset; CAP = pa_outlier_capacity(D).
+ *   Fields a format does not use are ignored (may be NULL).
+ */
+typedef struct pa_kv_pool {
+  int32_t dtype;          /* pa_kv_dtype */
+  int32_t num_blocks;
+  int32_t block_size;     /* must be 16 */
+  int32_t num_kv_heads;
+  int32_t head_dim;       /* 64 or 128 */
+  int32_t reserved;
+  void* k;
+  void* v;
+  float* k_tok_scale;
+  float* v_tok_scale;
+  uint8_t* k_out_idx;
+  uint8_t* v_out_idx;
+  uint16_t* k_out_val;
+  uint16_t* v_out_val;
+  const float* k_scale;
+  const float* v_scale;
+} pa_kv_pool;
+
+/*
+ * Host-only. Byte sizes of the pool arrays for a format, in the order
+ * {k, v, k_tok_scale, v_tok_scale, k_out_idx, v_out_idx, k_out_val, v_out_val}
+ * (0 for arrays the format does not use). Returns PA_OK or an error status.
+ */
+int pa_pool_layout(int32_t dtype, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                   size_t bytes_out[8]);
+
+/*
+ * Host-only. Outlier slots per (block, kv head) of the FP4 format: the largest number of
+ * channels whose per-channel RMS can reach mean + 3.2 sigma of head_dim values,
+ * floor(head_dim / (1 + 3.2^2)) = 11 for 128, 5 for 64 (the threshold is the pages':
+ * dailyaiworld.com, "Technical Breakdown: Dynamic Quantization with Outlier Retention",
+ * step 2). Returns -PA_ERR_SHAPE-style negative status for an unsupported head_dim.
+ */
+int pa_outlier_capacity(int32_t head_dim);
+
+/*
+ * Cache write ("reshape and cache"). Row i of k_new / v_new [num_tokens, num_kv_heads,
+ * head_dim] (activation dtype `act`) is stored at slot_mapping[i] = block * 16 + offset
+ * (int64; negative = skip the row). Slots within one call must be distinct.
+ *   F16 / BF16 : bit copy; the pool dtype must equal `act`.
+ *   FP8        : code = E4M3(fp32(x / scale_h)), the correctly rounded fp32 quotient
+ *                rounded to the nearest E4M3FN value, ties to even, saturating at +-448,
+ *                sign of zero kept; scale 0 stores +0.
+ *   FP4        : dailyaiworld.com, "Technical Breakdown: Dynamic Quantization with
+ *                Outlier Retention", steps 1-3. A block whose record is 0xFF is calibrated
+ *                by this call, separately per kv head and for K and V, on the rows of this
+ *                call that land in it: per-channel RMS r_c over those rows, mean mu and
+ *                population std sigma of the head_dim values r_c, outliers = channels with
+ *                r_c >= mu + 3.2 sigma (none if sigma = 0), stored ascending in the record.
+ *                Later writes reuse the record. Every row then stores fp16(x_c) for its
+ *                block's outlier channels, code +0 at those channels, a scale
+ *                s = fp32(max inlier |x_c| / 6) and codes E2M1(fp32(x_c / s)) (nearest,
+ *                ties to even, saturating at +-6; s = 0 stores +0 codes).
+ * Asynchronous on `stream`. Returns PA_OK or an error status (nothing launched on error).
+ */
+int pa_cache_write(const pa_kv_pool* pool, const void* k_new, const void* v_new, int32_t act,
+                   int32_t num_tokens, const int64_t* slot_mapping, int32_t* dev_err,
+                   void* stream);
+
+/*
+ * Per-kv-head FP8 scale of a tensor x [num_rows, num_kv_heads, head_dim] (activation dtype
+ * `act`): scale_out[h] = fp32(max |x[:, h, :]| / 448), the per-(layer, kv head) fp32 scale
+ * that maps each head's largest magnitude onto the largest E4M3FN value (xonoai.com
+ * report, "Deconstructing the v0.7.2 Architecture" and "Field Observations", on FP8
+ * calibration). scale_out [num_kv_heads] fp32 is overwritten. Call once for K and once
+ * for V. Asynchronous on `stream`.
+ */
+int pa_fp8_head_scales(const void* x, int32_t act, int64_t num_rows, int32_t num_kv_heads,
+                       int32_t head_dim, float* scale_out, void* stream);
+
+/*
+ * Mark the listed physical blocks as never written (FP4 records set to 0xFF), so the next
+ * write into each one calibrates it afresh: the engine calls this when it hands a freed
+ * block to a new sequence (inferensys glossary "vLLM", continuous batching entry: finished
+ * sequences release their blocks to the pool). block_ids [n] int32, device memory.
+ * No-op (PA_OK) for formats without records.
+ */
+int pa_reset_blocks(const pa_kv_pool* pool, const int32_t* block_ids, int32_t n, void* stream);
+
+/*
+ * Paged decode for one query token per sequence.
+ *   q             [num_seqs, num_q_heads, head_dim], dtype q_dtype
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32; entries past a sequence's last
+ *                 block are never read
+ *   context_lens  [num_seqs] int32, tokens to attend (including the token just written)
+ *   sm_scale      softmax scale (1 / sqrt(head_dim) for the usual attention)
+ *   partition_size 0: one pass per sequence; writes out [num_seqs, num_q_heads, head_dim]
+ *                 fp32. Otherwise a positive multiple of 16: partition p of a sequence
+ *                 covers tokens [p * ps, min((p + 1) * ps, L)); each partition with
+ *                 p < ceil(L / ps) writes part_out[s, h, p, :] (its normalized output, fp32)
+ *                 and part_lse[s, h, p] (natural-log log-sum-exp of its scaled logits);
+ *                 part_out [num_seqs, num_q_heads, max_partitions, head_dim] and part_lse
+ *                 [num_seqs, num_q_heads, max_partitions] with max_partitions =
+ *                 ceil(max_blocks_per_seq * 16 / ps). Combine them with pa_merge.
+ * The result is softmax attention over the dequantized cache, exactly as stored (the FP4
+ * outlier terms are added to the compressed ones; dailyaiworld.com, "Technical
+ * Breakdown", step 4). Asynchronous on `stream`.
+ */
+int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+              const pa_kv_pool* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, float sm_scale, int32_t partition_size, float* out,
+              float* part_out, float* part_lse, int32_t* dev_err, void* stream);
+
+/*
+ * Log-sum-exp merge of pa_decode partitions: for each (s, h), over p < ceil(L_s / ps),
+ * M = max lse_p, w_p = exp(lse_p - M), out = sum w_p o_p / sum w_p and, if lse_out is
+ * not NULL, lse_out[s, h] = M + ln sum w_p. Shapes as in pa_decode; out [num_seqs,
+ * num_q_heads, head_dim] fp32, lse_out [num_seqs, num_q_heads] fp32. Asynchronous.
+ */
+int pa_merge(const float* part_out, const float* part_lse, const int32_t* context_lens,
+             int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_partitions,
+             int32_t partition_size, float* out, float* lse_out, void* stream);
+
+/* Host-only: a static, human-readable name for a pa_status value. */
+const char* pa_status_string(int status);
+
+/*
+ * Copy the device error word to host memory (*host_out) and wait for it on `stream`.
+ * dev_err is the device pointer passed to the other calls.
+ */
+int pa_read_device_error(const int32_t* dev_err, int32_t* host_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -116,9 +116,12 @@ class Pool:
 
 
 def fp8_head_scale(rows_bits: np.ndarray, act: str) -> np.ndarray:
-    """Per-kv-head fp32 scale fp32(absmax_h / 448) over rows [T, Hkv, D]."""
-    x = act_decode(rows_bits, act)
-    absmax = np.abs(x).max(axis=(0, 2))
+    """Per-kv-head fp32 scale fp32(absmax_h / 448) over rows [T, Hkv, D] (the rows are
+    visited in slices only to bound memory; a maximum does not depend on order)."""
+    absmax = np.zeros(rows_bits.shape[1])
+    for lo in range(0, rows_bits.shape[0], 1 << 16):
+        x = act_decode(rows_bits[lo:lo + (1 << 16)], act)
+        absmax = np.maximum(absmax, np.abs(x).max(axis=(0, 2)))
     return f32_quotient(absmax, E4M3_MAX).astype(np.float32)
 
 
@@ -174,13 +177,15 @@ def fp4_encode_row(x: np.ndarray, outliers: np.ndarray):
 
 
 def cache_write(pool: Pool, k_rows, v_rows, act: str, slots, k_scale=None, v_scale=None,
-                only_blocks=None):
+                only_blocks=None, calib_log=None):
     """Replay one cache-write call: row i of k_rows/v_rows [T, Hkv, D] (raw 16-bit bits)
     goes to slot slots[i] = physical_block * 16 + offset; negative slots are skipped.
 
     Slots within one call must be distinct. If only_blocks is given, only writes into
     those physical blocks are replayed (each block's contents depend only on the calls
-    that write into it, so sampled replays are exact)."""
+    that write into it, so sampled replays are exact). If calib_log is a list, every FP4
+    calibration appends (name, block, head, margin) with margin as in
+    fp4_calibration_margin."""
     slots = np.asarray(slots, dtype=np.int64)
     live = np.nonzero(slots >= 0)[0]
     assert len(np.unique(slots[live])) == len(live), "slots within one call must be distinct"
@@ -216,6 +221,9 @@ def cache_write(pool: Pool, k_rows, v_rows, act: str, slots, k_scale=None, v_sca
                     if idx_arr[b, h, 0] != UNCALIBRATED:
                         continue
                     o = fp4_calibrate(x_all[rows_in_b, h, :])
+                    if calib_log is not None:
+                        calib_log.append((name, int(b), h,
+                                          fp4_calibration_margin(x_all[rows_in_b, h, :])))
                     rec = np.full(16, UNCALIBRATED, dtype=np.uint8)
                     rec[0] = len(o)
                     rec[1:1 + len(o)] = o

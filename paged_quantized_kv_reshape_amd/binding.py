@@ -1,0 +1,197 @@
+"""Thin ctypes binding of libpa (include/pa.h), with the C entry points' names.
+
+Argument marshalling only: torch tensors supply device memory and the current HIP stream,
+and every step of the hot path runs in libpa's gfx950 kernels. There is no fallback: if
+libpa.so is missing or a call is rejected, this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+_lib = None
+
+KV_DTYPES = {"f16": 0, "bf16": 1, "fp8": 2, "fp4": 3}
+ACT_DTYPES = {torch.float16: 0, torch.bfloat16: 1}
+BLOCK_SIZE = 16
+DEVERR_BITS = {1: "bad block id", 2: "bad slot", 4: "bad context length",
+               8: "read of an uncalibrated FP4 block"}
+
+
+class PAError(RuntimeError):
+    """A libpa call returned a non-zero pa_status."""
+
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {lib().pa_status_string(status).decode()} (status {status})")
+        self.status = status
+
+
+class pa_kv_pool(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("k_tok_scale", ctypes.c_void_p), ("v_tok_scale", ctypes.c_void_p),
+        ("k_out_idx", ctypes.c_void_p), ("v_out_idx", ctypes.c_void_p),
+        ("k_out_val", ctypes.c_void_p), ("v_out_val", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+    ]
+
+
+def lib():
+    """Load libpa.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"libpa.so not found at {_LIB_PATH}; build it with "
+                               "`python -m paged_quantized_kv_reshape_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        pool_p = ctypes.POINTER(pa_kv_pool)
+        sig = {
+            "pa_pool_layout": (ctypes.c_int, [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]),
+            "pa_outlier_capacity": (ctypes.c_int, [i32]),
+            "pa_cache_write": (ctypes.c_int, [pool_p, vp, vp, i32, i32, vp, vp, vp]),
+            "pa_fp8_head_scales": (ctypes.c_int, [vp, i32, i64, i32, i32, vp, vp]),
+            "pa_reset_blocks": (ctypes.c_int, [pool_p, vp, i32, vp]),
+            "pa_decode": (ctypes.c_int, [vp, i32, i32, i32, pool_p, vp, i32, vp, f32, i32, vp, vp,
+                                         vp, vp, vp]),
+            "pa_merge": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]),
+            "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "pa_read_device_error": (ctypes.c_int, [vp, vp, vp]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(fn, status):
+    if status != 0:
+        raise PAError(fn, status)
+
+
+def pa_pool_layout(kv_dtype: str, num_blocks: int, num_kv_heads: int, head_dim: int):
+    out = (ctypes.c_size_t * 8)()
+    _check("pa_pool_layout", lib().pa_pool_layout(KV_DTYPES[kv_dtype], num_blocks, num_kv_heads,
+                                                  head_dim, out))
+    return list(out)
+
+
+def pa_outlier_capacity(head_dim: int) -> int:
+    c = lib().pa_outlier_capacity(head_dim)
+    if c < 0:
+        raise PAError("pa_outlier_capacity", c)
+    return c
+
+
+class KVPool:
+    """Device arrays of one paged pool (caller-owned memory, as the ABI requires).
+
+    `fill` is the byte every array starts with (FP4 outlier records always start as 0xFF,
+    i.e. never written). FP8 pools need k_scale / v_scale [Hkv] fp32 device tensors."""
+
+    NAMES = ["k", "v", "k_tok_scale", "v_tok_scale", "k_out_idx", "v_out_idx", "k_out_val",
+             "v_out_val"]
+
+    def __init__(self, kv_dtype, num_blocks, num_kv_heads, head_dim, device="cuda", fill=0,
+                 k_scale=None, v_scale=None):
+        self.kv_dtype, self.num_blocks = kv_dtype, num_blocks
+        self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
+        sizes = pa_pool_layout(kv_dtype, num_blocks, num_kv_heads, head_dim)
+        self.bytes = {}
+        for name, n in zip(self.NAMES, sizes):
+            if n:
+                f = 0xFF if name.endswith("_out_idx") else fill
+                self.bytes[name] = torch.full((n,), f, dtype=torch.uint8, device=device)
+        self.k_scale, self.v_scale = k_scale, v_scale
+        if kv_dtype == "fp8" and (k_scale is None or v_scale is None):
+            raise ValueError("an fp8 pool needs k_scale and v_scale")
+
+    def struct(self) -> pa_kv_pool:
+        s = pa_kv_pool()
+        s.dtype = KV_DTYPES[self.kv_dtype]
+        s.num_blocks, s.block_size = self.num_blocks, BLOCK_SIZE
+        s.num_kv_heads, s.head_dim = self.num_kv_heads, self.head_dim
+        for name in self.NAMES:
+            setattr(s, name, _ptr(self.bytes.get(name)))
+        s.k_scale, s.v_scale = _ptr(self.k_scale), _ptr(self.v_scale)
+        return s
+
+    def numpy(self) -> dict:
+        """Host copies of the raw pool bytes, keyed like the arrays of the ABI."""
+        return {n: t.cpu().numpy() for n, t in self.bytes.items()}
+
+
+def pa_cache_write(pool: KVPool, k_new, v_new, slot_mapping, dev_err=None):
+    assert k_new.dtype in ACT_DTYPES and v_new.dtype == k_new.dtype
+    assert slot_mapping.dtype == torch.int64
+    T = k_new.shape[0]
+    s = pool.struct()
+    _check("pa_cache_write", lib().pa_cache_write(
+        ctypes.byref(s), _ptr(k_new), _ptr(v_new), ACT_DTYPES[k_new.dtype], T,
+        _ptr(slot_mapping), _ptr(dev_err), _stream()))
+
+
+def pa_fp8_head_scales(x, scale_out):
+    """x [rows, Hkv, D] fp16/bf16 -> scale_out [Hkv] fp32 (overwritten)."""
+    assert x.dtype in ACT_DTYPES and scale_out.dtype == torch.float32
+    _check("pa_fp8_head_scales", lib().pa_fp8_head_scales(
+        _ptr(x), ACT_DTYPES[x.dtype], x.shape[0], x.shape[1], x.shape[2], _ptr(scale_out),
+        _stream()))
+
+
+def pa_reset_blocks(pool: KVPool, block_ids):
+    assert block_ids.dtype == torch.int32
+    s = pool.struct()
+    _check("pa_reset_blocks", lib().pa_reset_blocks(ctypes.byref(s), _ptr(block_ids),
+                                                    block_ids.numel(), _stream()))
+
+
+def max_partitions(max_blocks_per_seq: int, partition_size: int) -> int:
+    return -(-max_blocks_per_seq * BLOCK_SIZE // partition_size) if partition_size else 1
+
+
+def pa_decode(q, pool: KVPool, block_tables, context_lens, sm_scale, partition_size=0, out=None,
+              part_out=None, part_lse=None, dev_err=None):
+    """q [S, Hq, D]; block_tables [S, MB] int32; context_lens [S] int32. With
+    partition_size = 0 fills out [S, Hq, D] fp32; otherwise part_out / part_lse."""
+    assert q.dtype in ACT_DTYPES and block_tables.dtype == torch.int32
+    assert context_lens.dtype == torch.int32
+    S, Hq, _ = q.shape
+    s = pool.struct()
+    _check("pa_decode", lib().pa_decode(
+        _ptr(q), ACT_DTYPES[q.dtype], S, Hq, ctypes.byref(s), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), float(sm_scale), partition_size, _ptr(out),
+        _ptr(part_out), _ptr(part_lse), _ptr(dev_err), _stream()))
+
+
+def pa_merge(part_out, part_lse, context_lens, partition_size, out, lse_out=None):
+    S, Hq, P, D = part_out.shape
+    _check("pa_merge", lib().pa_merge(
+        _ptr(part_out), _ptr(part_lse), _ptr(context_lens), S, Hq, D, P, partition_size,
+        _ptr(out), _ptr(lse_out), _stream()))
+
+
+def pa_read_device_error(dev_err) -> int:
+    host = ctypes.c_int32(0)
+    _check("pa_read_device_error", lib().pa_read_device_error(_ptr(dev_err), ctypes.byref(host),
+                                                              _stream()))
+    return host.value
+
+
+def describe_device_error(bits: int) -> str:
+    return ", ".join(v for k, v in DEVERR_BITS.items() if bits & k) or "none"

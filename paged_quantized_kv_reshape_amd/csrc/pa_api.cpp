@@ -1,0 +1,238 @@
+// pa_api.cpp - the C ABI of libpa (declared in include/pa.h): host-side argument checks,
+// launch geometry, status strings. Every check runs before any HIP call, so a rejected
+// call has no effect on the device.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/pa.h"
+#include "pa_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxGridYZ = 65535;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_pool(const pa_kv_pool* p) {
+  if (!p) return PA_ERR_NULL;
+  if (p->dtype < PA_KV_F16 || p->dtype > PA_KV_FP4_E2M1_OUTL) return PA_ERR_DTYPE;
+  if (p->block_size != PA_BLOCK_SIZE) return PA_ERR_BLOCK_SIZE;
+  if (p->num_blocks < 1 || p->num_kv_heads < 1 || p->num_kv_heads > kMaxGridYZ)
+    return PA_ERR_SHAPE;
+  if (p->head_dim != 64 && p->head_dim != 128) return PA_ERR_SHAPE;
+  if ((int64_t)p->num_blocks * PA_BLOCK_SIZE > INT64_C(0x3FFFFFFFFFFFFFFF)) return PA_ERR_SHAPE;
+  if (!p->k || !p->v) return PA_ERR_NULL;
+  if (!aligned(p->k, 16) || !aligned(p->v, 16)) return PA_ERR_ALIGN;
+  if (p->dtype == PA_KV_FP8_E4M3) {
+    if (!p->k_scale || !p->v_scale) return PA_ERR_NULL;
+    if (!aligned(p->k_scale, 4) || !aligned(p->v_scale, 4)) return PA_ERR_ALIGN;
+  }
+  if (p->dtype == PA_KV_FP4_E2M1_OUTL) {
+    if (p->head_dim != 128) return PA_ERR_SHAPE;  // 4-bit format: head_dim 128 only
+    if (!p->k_tok_scale || !p->v_tok_scale || !p->k_out_idx || !p->v_out_idx ||
+        !p->k_out_val || !p->v_out_val)
+      return PA_ERR_NULL;
+    if (!aligned(p->k_tok_scale, 16) || !aligned(p->v_tok_scale, 16) ||
+        !aligned(p->k_out_idx, 16) || !aligned(p->v_out_idx, 16) || !aligned(p->k_out_val, 8) ||
+        !aligned(p->v_out_val, 8))
+      return PA_ERR_ALIGN;
+  }
+  return PA_OK;
+}
+
+bool act_ok(int32_t act) { return act == PA_ACT_F16 || act == PA_ACT_BF16; }
+
+// A 16-bit pool stores the activation dtype itself.
+bool act_matches_pool(int32_t act, int32_t kv) {
+  if (kv == PA_KV_F16) return act == PA_ACT_F16;
+  if (kv == PA_KV_BF16) return act == PA_ACT_BF16;
+  return true;
+}
+
+int env_int(const char* name, int fallback) {
+  const char* s = getenv(name);
+  if (!s || !*s) return fallback;
+  return atoi(s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: a size is out of range or inconsistent";
+    case PA_ERR_DTYPE: return "PA_ERR_DTYPE: unknown or unsupported dtype combination";
+    case PA_ERR_BLOCK_SIZE: return "PA_ERR_BLOCK_SIZE: block_size must be 16";
+    case PA_ERR_CONTEXT: return "PA_ERR_CONTEXT: max_blocks_per_seq out of range";
+    case PA_ERR_PARTITION: return "PA_ERR_PARTITION: partition_size must be 0 or a positive multiple of 16";
+    case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: the HIP runtime refused a launch";
+    case PA_ERR_ALIGN: return "PA_ERR_ALIGN: a pointer is not suitably aligned";
+    default: return "unknown pa_status";
+  }
+}
+
+int pa_outlier_capacity(int32_t head_dim) {
+  const int c = pa::outlier_capacity(head_dim);
+  return c < 0 ? PA_ERR_SHAPE : c;
+}
+
+int pa_pool_layout(int32_t dtype, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                   size_t bytes_out[8]) {
+  if (!bytes_out) return PA_ERR_NULL;
+  if (dtype < PA_KV_F16 || dtype > PA_KV_FP4_E2M1_OUTL) return PA_ERR_DTYPE;
+  if (num_blocks < 1 || num_kv_heads < 1 || (head_dim != 64 && head_dim != 128))
+    return PA_ERR_SHAPE;
+  if (dtype == PA_KV_FP4_E2M1_OUTL && head_dim != 128) return PA_ERR_SHAPE;
+  for (int i = 0; i < 8; ++i) bytes_out[i] = 0;
+  const size_t bh = (size_t)num_blocks * num_kv_heads;
+  const size_t rows = bh * PA_BLOCK_SIZE;
+  switch (dtype) {
+    case PA_KV_F16:
+    case PA_KV_BF16: bytes_out[0] = bytes_out[1] = rows * head_dim * 2; break;
+    case PA_KV_FP8_E4M3: bytes_out[0] = bytes_out[1] = rows * head_dim; break;
+    default:
+      bytes_out[0] = bytes_out[1] = rows * head_dim / 2;
+      bytes_out[2] = bytes_out[3] = rows * sizeof(float);
+      bytes_out[4] = bytes_out[5] = bh * 16;
+      bytes_out[6] = bytes_out[7] =
+          bh * (size_t)pa::outlier_capacity(head_dim) * PA_BLOCK_SIZE * sizeof(uint16_t);
+  }
+  return PA_OK;
+}
+
+int pa_cache_write(const pa_kv_pool* pool, const void* k_new, const void* v_new, int32_t act,
+                   int32_t num_tokens, const int64_t* slot_mapping, int32_t* dev_err,
+                   void* stream) {
+  int st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (!act_ok(act) || !act_matches_pool(act, pool->dtype)) return PA_ERR_DTYPE;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slot_mapping, 8) ||
+      !aligned(dev_err, 4))
+    return PA_ERR_ALIGN;
+  return pa::launch_write(*pool, k_new, v_new, act == PA_ACT_BF16, num_tokens, slot_mapping,
+                          dev_err, (hipStream_t)stream);
+}
+
+int pa_fp8_head_scales(const void* x, int32_t act, int64_t num_rows, int32_t num_kv_heads,
+                       int32_t head_dim, float* scale_out, void* stream) {
+  if (!act_ok(act)) return PA_ERR_DTYPE;
+  if (num_rows < 0 || num_kv_heads < 1 || num_kv_heads > 256 ||
+      (head_dim != 64 && head_dim != 128))
+    return PA_ERR_SHAPE;
+  if (!scale_out || (num_rows > 0 && !x)) return PA_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(scale_out, 4)) return PA_ERR_ALIGN;
+  return pa::launch_fp8_scales(x, act == PA_ACT_BF16, num_rows, num_kv_heads, head_dim, scale_out,
+                               (hipStream_t)stream);
+}
+
+int pa_reset_blocks(const pa_kv_pool* pool, const int32_t* block_ids, int32_t n, void* stream) {
+  int st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (n < 0) return PA_ERR_SHAPE;
+  if (pool->dtype != PA_KV_FP4_E2M1_OUTL || n == 0) return PA_OK;
+  if (!block_ids) return PA_ERR_NULL;
+  if (!aligned(block_ids, 4)) return PA_ERR_ALIGN;
+  return pa::launch_reset(*pool, block_ids, n, (hipStream_t)stream);
+}
+
+int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+              const pa_kv_pool* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, float sm_scale, int32_t partition_size, float* out,
+              float* part_out, float* part_lse, int32_t* dev_err, void* stream) {
+  int st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (!act_ok(q_dtype) || !act_matches_pool(q_dtype, pool->dtype)) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_q_heads < 1) return PA_ERR_SHAPE;
+  if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_SHAPE;
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (group > 16) return PA_ERR_SHAPE;
+  if (max_blocks_per_seq < 1 || (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE > INT32_MAX)
+    return PA_ERR_CONTEXT;
+  if (partition_size < 0 || partition_size % PA_BLOCK_SIZE != 0) return PA_ERR_PARTITION;
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !block_tables || !context_lens) return PA_ERR_NULL;
+  const int64_t cap_tokens = (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE;
+  const int max_part =
+      partition_size > 0 ? (int)((cap_tokens + partition_size - 1) / partition_size) : 1;
+  if (partition_size == 0) {
+    if (!out) return PA_ERR_NULL;
+    if (!aligned(out, 16)) return PA_ERR_ALIGN;
+  } else {
+    if (!part_out || !part_lse) return PA_ERR_NULL;
+    if (!aligned(part_out, 16) || !aligned(part_lse, 4)) return PA_ERR_ALIGN;
+  }
+  if (!aligned(q, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
+      !aligned(dev_err, 4))
+    return PA_ERR_ALIGN;
+
+  pa::DecodeArgs a;
+  a.q = q;
+  a.k = pool->k;
+  a.v = pool->v;
+  a.k_tok_scale = pool->k_tok_scale;
+  a.v_tok_scale = pool->v_tok_scale;
+  a.k_out_idx = pool->k_out_idx;
+  a.v_out_idx = pool->v_out_idx;
+  a.k_out_val = pool->k_out_val;
+  a.v_out_val = pool->v_out_val;
+  a.k_scale = pool->k_scale;
+  a.v_scale = pool->v_scale;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.part_out = part_out;
+  a.part_lse = part_lse;
+  a.err = dev_err;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.group = group;
+  a.num_blocks = pool->num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.partition_size = partition_size;
+  a.max_partitions = max_part;
+  a.cap = pa::outlier_capacity(pool->head_dim);
+  a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+
+  // Waves per workgroup: enough to split a partition's blocks a few ways, at most 4.
+  const int64_t span = partition_size > 0 ? partition_size : cap_tokens;
+  const int64_t blocks = (span + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
+  int waves = blocks >= 64 ? 4 : blocks >= 16 ? 2 : 1;
+  const int forced = env_int("PA_DECODE_WAVES", 0);
+  if (forced == 1 || forced == 2 || forced == 4 || forced == 8) waves = forced;
+  return pa::launch_decode(a, pool->dtype, q_dtype == PA_ACT_BF16, pool->head_dim, waves,
+                           (hipStream_t)stream);
+}
+
+int pa_merge(const float* part_out, const float* part_lse, const int32_t* context_lens,
+             int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_partitions,
+             int32_t partition_size, float* out, float* lse_out, void* stream) {
+  if (num_seqs < 0 || num_q_heads < 1 || (head_dim != 64 && head_dim != 128) ||
+      max_partitions < 1)
+    return PA_ERR_SHAPE;
+  if (partition_size <= 0 || partition_size % PA_BLOCK_SIZE != 0) return PA_ERR_PARTITION;
+  if (num_seqs == 0) return PA_OK;
+  if (!part_out || !part_lse || !context_lens || !out) return PA_ERR_NULL;
+  if (!aligned(part_out, 16) || !aligned(part_lse, 4) || !aligned(context_lens, 4) ||
+      !aligned(out, 16) || !aligned(lse_out, 4))
+    return PA_ERR_ALIGN;
+  return pa::launch_merge(part_out, part_lse, context_lens, num_seqs, num_q_heads, head_dim,
+                          max_partitions, partition_size, out, lse_out, (hipStream_t)stream);
+}
+
+int pa_read_device_error(const int32_t* dev_err, int32_t* host_out, void* stream) {
+  if (!dev_err || !host_out) return PA_ERR_NULL;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipMemcpyAsync(host_out, dev_err, sizeof(int32_t), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return hipStreamSynchronize(st) == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,525 @@
+// pa_decode.hip - paged decode attention for gfx950 (MI355X).
+//
+// One query token per sequence attends to the K/V of its context, which sits in fixed
+// 16-token physical blocks reached through the sequence's block table (inferensys
+// glossary "vLLM", PagedAttention entry; xonoai.com field report on vLLM v0.7.2,
+// "Deconstructing the v0.7.2 Architecture"). The cache is read as stored: 16-bit values,
+// FP8 E4M3 codes times a per-head scale, or E2M1 codes times a per-token scale with the
+// block's fp16 outlier channels added back in (dailyaiworld.com, "vLLM 0.7 Ships Unified
+// KV Cache Compression", "Technical Breakdown: Dynamic Quantization with Outlier
+// Retention", step 4). Long contexts split into partitions that run as independent
+// workgroups and are recombined by a log-sum-exp merge (split-KV "Flash-Decoding", the
+// same page and its cited sources).
+//
+// Work decomposition
+//   grid (partition, kv head, sequence); a workgroup of W waves covers one partition and
+//   wave w takes the partition's blocks w, w + W, w + 2W, ...; the waves' (max, sum, acc)
+//   states are merged in LDS at the end. All query heads of a kv head (the GQA group,
+//   G <= 16) are processed together by every wave, so each K/V tile is read exactly once.
+//
+// Per 16-token block, one wave (lane l: c = l % 16, kg = l / 16):
+//   S^T = K Q^T   MFMA 16x16x32 (rows = the block's 16 tokens, columns = query heads):
+//                 lane (c, kg) loads token c's channels [D/4 kg, D/4 (kg+1)) with 16-byte
+//                 loads and holds, after the MFMA, the logits of head c for tokens
+//                 4 kg .. 4 kg + 3;
+//   softmax       running max m and sum l per head, base 2 (log2 e folded into the
+//                 scale); the max over the 4 lanes of a head is a 2-step butterfly; the
+//                 accumulator is rescaled only when some head's max grows by more than
+//                 kRescale (then every probability stays below 2^kRescale);
+//   O^T += V^T P^T MFMA 16x16x16 per 16 output channels (rows = channels, k = tokens):
+//                 the probabilities are already in the B-operand layout (head c, tokens
+//                 4 kg..4 kg+3); lane (c, kg) loads channels [NT c, NT (c+1)) of tokens
+//                 4 kg..4 kg+3 and transposes them in registers (v_perm) so one register
+//                 pair holds one channel of four tokens. P enters as a hi + lo pair of
+//                 16-bit values (about 16 significant bits), so PV loses nothing to
+//                 16-bit rounding of P. After the block loop lane (c, kg) holds head c's
+//                 output channels [D/4 kg, D/4 (kg+1)).
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+enum { KV_F16 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_FP4 = 3 };
+
+constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
+constexpr int kPrefetch = 2;      // blocks in flight per wave beyond the one in use
+
+template <int KV, int D>
+struct Geo {
+  static constexpr int KS = D / 32;  // QK MFMA steps (k = 32 channels each)
+  static constexpr int NT = D / 16;  // PV MFMA tiles (16 output channels each)
+  static constexpr int DL = D / 4;   // channels per lane in K fragments and outputs
+  static constexpr int EBITS = KV == KV_FP8 ? 8 : KV == KV_FP4 ? 4 : 16;
+  static constexpr int ROWB = D * EBITS / 8;       // bytes of one token row
+  static constexpr int TILEB = kBlock * ROWB;      // bytes of one (block, head) tile
+  static constexpr int KW = DL * EBITS / 32;       // K words per lane
+  static constexpr int VW = NT * EBITS / 32;       // V words per lane per token
+  static constexpr int KLANEB = DL * EBITS / 8;    // K bytes per lane
+  static constexpr int VLANEB = NT * EBITS / 8;    // V bytes per lane per token
+};
+
+template <int N>
+__device__ __forceinline__ void load_words(uint32_t (&w)[N], const uint8_t* p) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const uint4 x = reinterpret_cast<const uint4*>(p)[i];
+      w[4 * i] = x.x;
+      w[4 * i + 1] = x.y;
+      w[4 * i + 2] = x.z;
+      w[4 * i + 3] = x.w;
+    }
+  } else if constexpr (N == 2) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    w[0] = x.x;
+    w[1] = x.y;
+  } else {
+    static_assert(N == 1, "word count");
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+
+// Hardware conversions (scale 1.0, so exact: every E4M3 and E2M1 value is a bf16 and an
+// fp16 value). SEL picks the 16-bit half (FP8) or the byte (FP4) of the source word.
+template <bool BF, int SEL>
+__device__ __forceinline__ uint32_t cvt_fp8x2(uint32_t w) {
+  if constexpr (BF)
+    return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, SEL != 0));
+  else
+    return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, SEL != 0));
+}
+template <bool BF, int SEL>
+__device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t w) {
+  if constexpr (BF)
+    return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
+  else
+    return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL));
+}
+
+template <int KV, int D>
+struct Tile {
+  using G_ = Geo<KV, D>;
+  uint32_t k[G_::KW];
+  uint32_t v[4][G_::VW];
+  float4 sk, sv;  // FP4 per-token scales of tokens 4 kg .. 4 kg + 3
+  uint4 rk, rv;   // FP4 outlier records
+  int64_t tile;   // b * Hkv + kv head
+  int jb;         // logical block index in the sequence
+  bool ok;        // block id in range
+};
+
+// 16-bit K fragment for step t: 8 values of channels D/4 kg + 8 t + (0..7).
+template <int KV, int D, bool QBF>
+__device__ __forceinline__ uint4 k_fragment(const Tile<KV, D>& T, int t) {
+  if constexpr (KV == KV_F16 || KV == KV_BF16) {
+    return make_uint4(T.k[4 * t], T.k[4 * t + 1], T.k[4 * t + 2], T.k[4 * t + 3]);
+  } else if constexpr (KV == KV_FP8) {
+    const uint32_t a = T.k[2 * t], b = T.k[2 * t + 1];
+    return make_uint4(cvt_fp8x2<QBF, 0>(a), cvt_fp8x2<QBF, 1>(a), cvt_fp8x2<QBF, 0>(b),
+                      cvt_fp8x2<QBF, 1>(b));
+  } else {
+    const uint32_t a = T.k[t];
+    return make_uint4(cvt_fp4x2<QBF, 0>(a), cvt_fp4x2<QBF, 1>(a), cvt_fp4x2<QBF, 2>(a),
+                      cvt_fp4x2<QBF, 3>(a));
+  }
+}
+
+// V^T fragments: vf[n] = channel NT c + n of tokens 4 kg .. 4 kg + 3 as four 16-bit values
+// (tokens 0,1 in the low word, 2,3 in the high word).
+template <int KV, int D, bool PVB>
+__device__ __forceinline__ void v_fragments(const Tile<KV, D>& T, uint2 (&vf)[Geo<KV, D>::NT]) {
+  constexpr int NT = Geo<KV, D>::NT;
+  if constexpr (KV == KV_F16 || KV == KV_BF16 || KV == KV_FP4) {
+    // pairs[r][i] = 16-bit channels (2i, 2i+1) of token r
+    uint32_t pairs[4][NT / 2];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (KV == KV_FP4) {
+        const uint32_t w = T.v[r][0];
+        pairs[r][0] = cvt_fp4x2<true, 0>(w);
+        pairs[r][1] = cvt_fp4x2<true, 1>(w);
+        if constexpr (NT / 2 > 2) {
+          pairs[r][2] = cvt_fp4x2<true, 2>(w);
+          pairs[r][3] = cvt_fp4x2<true, 3>(w);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NT / 2; ++i) pairs[r][i] = T.v[r][i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NT / 2; ++i) {
+      vf[2 * i].x = __builtin_amdgcn_perm(pairs[1][i], pairs[0][i], 0x05040100u);
+      vf[2 * i].y = __builtin_amdgcn_perm(pairs[3][i], pairs[2][i], 0x05040100u);
+      vf[2 * i + 1].x = __builtin_amdgcn_perm(pairs[1][i], pairs[0][i], 0x07060302u);
+      vf[2 * i + 1].y = __builtin_amdgcn_perm(pairs[3][i], pairs[2][i], 0x07060302u);
+    }
+  } else {
+    // FP8: 4x4 byte transposes, then one conversion per token pair.
+#pragma unroll
+    for (int wi = 0; wi < Geo<KV, D>::VW; ++wi) {
+      const uint32_t x0 = T.v[0][wi], x1 = T.v[1][wi], x2 = T.v[2][wi], x3 = T.v[3][wi];
+      const uint32_t u0 = __builtin_amdgcn_perm(x1, x0, 0x05010400u);  // x0b0 x1b0 x0b1 x1b1
+      const uint32_t u1 = __builtin_amdgcn_perm(x1, x0, 0x07030602u);  // x0b2 x1b2 x0b3 x1b3
+      const uint32_t w0 = __builtin_amdgcn_perm(x3, x2, 0x05010400u);
+      const uint32_t w1 = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
+      const uint32_t t[4] = {
+          __builtin_amdgcn_perm(w0, u0, 0x05040100u),  // channel 0 of tokens 0..3
+          __builtin_amdgcn_perm(w0, u0, 0x07060302u),  // channel 1
+          __builtin_amdgcn_perm(w1, u1, 0x05040100u),  // channel 2
+          __builtin_amdgcn_perm(w1, u1, 0x07060302u)}; // channel 3
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        vf[4 * wi + c].x = cvt_fp8x2<PVB, 0>(t[c]);
+        vf[4 * wi + c].y = cvt_fp8x2<PVB, 1>(t[c]);
+      }
+    }
+  }
+}
+
+template <int KV, int D, bool QBF>
+__global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
+  using G_ = Geo<KV, D>;
+  constexpr int KS = G_::KS, NT = G_::NT, DL = G_::DL;
+  constexpr bool PVB = QBF || KV == KV_FP4;  // PV MFMA in bf16 (else fp16)
+  extern __shared__ float smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int W = blockDim.x >> 6;
+  const int c = lane & 15;  // MFMA column: query head (QK, PV); K row token; V channel group
+  const int kg = lane >> 4;
+  const int p = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+  const int G = a.group;
+  const int Hq = a.num_q_heads;
+
+  const int L = a.context_lens[s];
+  const int cap_tokens = a.max_blocks * kBlock;
+  const bool split = a.partition_size > 0;
+  if (L < 1 || L > cap_tokens) {
+    if (threadIdx.x == 0 && p == 0 && kvh == 0 && a.err) atomicOr(a.err, PA_DEVERR_BAD_CONTEXT);
+    if (!split && p == 0) {
+      for (int i = threadIdx.x; i < G * D; i += blockDim.x)
+        a.out[((int64_t)s * Hq + kvh * G) * D + i] = 0.0f;
+    }
+    return;
+  }
+  const int start = split ? p * a.partition_size : 0;
+  if (start >= L) return;  // empty partition: not written, the merge skips it
+  const int end = split ? min(start + a.partition_size, L) : L;
+  const int jb0 = start / kBlock;
+  const int nblk = (end + kBlock - 1) / kBlock - jb0;
+  const int my_n = wave < nblk ? (nblk - wave + W - 1) / W : 0;
+
+  // ---- query fragments (B operand of S^T = K Q^T), zero for padded heads ----
+  uint4 qf[KS];
+  {
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
+                          (((int64_t)s * Hq + kvh * G + c) * D + DL * kg) * 2;
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+      qf[t] = c < G ? reinterpret_cast<const uint4*>(qrow)[t] : make_uint4(0, 0, 0, 0);
+  }
+  float* q_lds = smem;  // FP4 only: q in fp32, [16][D]
+  if constexpr (KV == KV_FP4) {
+    if (wave == 0) {
+#pragma unroll
+      for (int t = 0; t < KS; ++t) {
+        const uint32_t w[4] = {qf[t].x, qf[t].y, qf[t].z, qf[t].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t b16 = (w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+          q_lds[c * D + DL * kg + 8 * t + e] = act_to_f32<QBF>(b16);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- scale of the logits (base 2) ----
+  float cz = a.sm_scale_log2;
+  if constexpr (KV == KV_FP8) cz *= a.k_scale[kvh];
+
+  // ---- block ids: 64 of this wave's blocks per register, two registers ahead ----
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks + jb0 + wave;
+  auto load_ids = [&](int chunk) -> int {
+    const int x = chunk * 64 + lane;
+    return x < my_n ? bt[(int64_t)x * W] : 0;
+  };
+  int ids_a = load_ids(0), ids_b = load_ids(1);
+
+  const uint8_t* kpool = reinterpret_cast<const uint8_t*>(a.k);
+  const uint8_t* vpool = reinterpret_cast<const uint8_t*>(a.v);
+  const int k_lane_off = c * G_::ROWB + kg * G_::KLANEB;
+  const int v_lane_off = 4 * kg * G_::ROWB + c * G_::VLANEB;
+
+  auto load_tile = [&](Tile<KV, D>& T, int x) {
+    if (x > 0 && (x & 63) == 0) {
+      ids_a = ids_b;
+      ids_b = load_ids((x >> 6) + 1);
+    }
+    int b = __builtin_amdgcn_readlane(ids_a, x & 63);
+    T.jb = jb0 + wave + x * W;
+    T.ok = (unsigned)b < (unsigned)a.num_blocks;
+    if (!T.ok) {
+      if (lane == 0 && a.err) atomicOr(a.err, PA_DEVERR_BAD_BLOCK);
+      b = 0;
+    }
+    T.tile = (int64_t)b * a.num_kv_heads + kvh;
+    load_words(T.k, kpool + T.tile * G_::TILEB + k_lane_off);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      load_words(T.v[r], vpool + T.tile * G_::TILEB + v_lane_off + r * G_::ROWB);
+    if constexpr (KV == KV_FP4) {
+      T.sk = reinterpret_cast<const float4*>(a.k_tok_scale + T.tile * kBlock)[kg];
+      T.sv = reinterpret_cast<const float4*>(a.v_tok_scale + T.tile * kBlock)[kg];
+      T.rk = *reinterpret_cast<const uint4*>(a.k_out_idx + T.tile * 16);
+      T.rv = *reinterpret_cast<const uint4*>(a.v_out_idx + T.tile * 16);
+    }
+  };
+
+  // ---- online softmax state ----
+  float m = -INFINITY;  // running max (base-2 logits) of head c, same in its 4 lanes
+  float l = 0.0f;       // this lane's part of the running sum
+  f32x4 acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](Tile<KV, D>& T) {
+    const int tok0 = T.jb * kBlock + 4 * kg;
+    bool valid[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) valid[r] = T.ok && (tok0 + r < end);
+    const bool partial = !T.ok || (T.jb * kBlock + kBlock > end);  // wave-uniform
+    if (partial) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int i = 0; i < G_::VW; ++i) T.v[r][i] = valid[r] ? T.v[r][i] : 0u;
+    }
+
+    // logits S^T[token 4 kg + r][head c]
+    f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < KS; ++t) sacc = mfma_k32(k_fragment<KV, D, QBF>(T, t), qf[t], sacc, QBF);
+    float z[4];
+    if constexpr (KV == KV_FP4) {
+      const float sk[4] = {T.sk.x, T.sk.y, T.sk.z, T.sk.w};
+      float ok[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      int nk = (int)(T.rk.x & 0xFFu);
+      if (nk == 0xFF) {
+        if (T.ok && lane == 0 && a.err) atomicOr(a.err, PA_DEVERR_UNCALIBRATED);
+        nk = 0;
+      }
+      if (nk > a.cap) nk = a.cap;
+      const uint32_t rw[3] = {T.rk.x, T.rk.y, T.rk.z};
+      for (int j = 0; j < nk; ++j) {
+        const int pos = 1 + j;
+        const int ch = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
+        const float qv = q_lds[c * D + ch];
+        const uint2 ov = *reinterpret_cast<const uint2*>(
+            a.k_out_val + ((T.tile * a.cap + j) * kBlock + 4 * kg));
+        ok[0] = __builtin_fmaf(qv, f16_bits_to_f32(ov.x & 0xFFFFu), ok[0]);
+        ok[1] = __builtin_fmaf(qv, f16_bits_to_f32(ov.x >> 16), ok[1]);
+        ok[2] = __builtin_fmaf(qv, f16_bits_to_f32(ov.y & 0xFFFFu), ok[2]);
+        ok[3] = __builtin_fmaf(qv, f16_bits_to_f32(ov.y >> 16), ok[3]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        z[r] = valid[r] ? __builtin_fmaf(sacc[r], sk[r], ok[r]) * cz : -INFINITY;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) z[r] = valid[r] ? sacc[r] * cz : -INFINITY;
+    }
+
+    // online softmax (base 2), lazy rescale
+    const float mb = group4_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+    if (__builtin_amdgcn_ballot_w64(mb > m + kRescale) != 0) {  // wave-uniform
+      const float mn = fmaxf(m, mb);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+      m = mn;
+    }
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pr[r] = valid[r] ? __builtin_amdgcn_exp2f(z[r] - m) : 0.0f;
+      l += pr[r];
+    }
+
+    // P^T operand: hi + lo 16-bit pairs (FP4: p * s_t, the V per-token scale)
+    float pv[4];
+    if constexpr (KV == KV_FP4) {
+      const float sv[4] = {T.sv.x, T.sv.y, T.sv.z, T.sv.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pv[r] = valid[r] ? pr[r] * sv[r] : 0.0f;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pv[r] = pr[r];
+    }
+    const uint32_t h01 = pack2(pv[0], pv[1], PVB), h23 = pack2(pv[2], pv[3], PVB);
+    const uint32_t l01 = pack2(pv[0] - lo16_to_f32(h01, PVB), pv[1] - hi16_to_f32(h01, PVB), PVB);
+    const uint32_t l23 = pack2(pv[2] - lo16_to_f32(h23, PVB), pv[3] - hi16_to_f32(h23, PVB), PVB);
+    const uint2 ph = make_uint2(h01, h23), pl = make_uint2(l01, l23);
+
+    uint2 vf[NT];
+    v_fragments<KV, D, PVB>(T, vf);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      acc[n] = mfma_k16(vf[n], ph, acc[n], PVB);
+      acc[n] = mfma_k16(vf[n], pl, acc[n], PVB);
+    }
+
+    if constexpr (KV == KV_FP4) {
+      // V outliers: out[c][ch] += sum_t p_t * o_t,ch (fp16 values, unscaled p)
+      int nv = (int)(T.rv.x & 0xFFu);
+      if (nv == 0xFF) {
+        if (T.ok && lane == 0 && a.err) atomicOr(a.err, PA_DEVERR_UNCALIBRATED);
+        nv = 0;
+      }
+      if (nv > a.cap) nv = a.cap;
+      const uint32_t rw[3] = {T.rv.x, T.rv.y, T.rv.z};
+      for (int j = 0; j < nv; ++j) {
+        const int pos = 1 + j;
+        const int ch = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
+        const uint2 ov = *reinterpret_cast<const uint2*>(
+            a.v_out_val + ((T.tile * a.cap + j) * kBlock + 4 * kg));
+        const float o4[4] = {f16_bits_to_f32(ov.x & 0xFFFFu), f16_bits_to_f32(ov.x >> 16),
+                             f16_bits_to_f32(ov.y & 0xFFFFu), f16_bits_to_f32(ov.y >> 16)};
+        float part = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part += valid[r] ? pr[r] * o4[r] : 0.0f;
+        part = group4_sum(part);
+        // channel ch of head c lives in lane group ch / DL, register (ch % DL) / NT of
+        // tile ch % NT; the indices are wave-uniform, so this is a scalar branch tree.
+        const int ckg = ch / DL, ce = ch % DL;
+        const int cn = ce % NT, cr = ce / NT;
+        const float add = kg == ckg ? part : 0.0f;
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n == cn && r == cr) acc[n][r] += add;
+      }
+    }
+  };
+
+  // ---- block loop, kPrefetch tiles in flight ----
+  Tile<KV, D> tiles[kPrefetch];
+#pragma unroll
+  for (int k = 0; k < kPrefetch; ++k)
+    if (k < my_n) load_tile(tiles[k], k);
+  for (int i0 = 0; i0 < my_n; i0 += kPrefetch) {
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+      const int i = i0 + k;
+      if (i < my_n) {
+        compute(tiles[k]);
+        if (i + kPrefetch < my_n) load_tile(tiles[k], i + kPrefetch);
+      }
+    }
+  }
+
+  // ---- epilogue ----
+  const float lt = group4_sum(l);
+  const float vscale = KV == KV_FP8 ? a.v_scale[kvh] : 1.0f;
+  const int h = kvh * G + c;
+  if (W == 1) {
+    if (c < G) {
+      const float inv = lt > 0.0f ? vscale / lt : 0.0f;  // 0: every block id was bad
+      float* dst = split ? a.part_out + (((int64_t)s * Hq + h) * a.max_partitions + p) * D
+                         : a.out + ((int64_t)s * Hq + h) * D;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) dst[DL * kg + NT * r + n] = acc[n][r] * inv;
+      if (split && kg == 0)
+        a.part_lse[((int64_t)s * Hq + h) * a.max_partitions + p] = (m + __log2f(lt)) * kLn2;
+    }
+    return;
+  }
+
+  // W > 1: merge the waves' states in LDS.
+  constexpr int STRIDE = DL + 4;  // floats per lane record (padded)
+  float* m_lds = smem + (KV == KV_FP4 ? 16 * D : 0);
+  float* l_lds = m_lds + 16 * 8;
+  float* acc_lds = l_lds + 16 * 8;  // [W][64][STRIDE]
+  if (kg == 0) {
+    m_lds[wave * 16 + c] = m;
+    l_lds[wave * 16 + c] = lt;
+  }
+  float* mine = acc_lds + ((int64_t)wave * 64 + lane) * STRIDE;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) mine[NT * r + n] = acc[n][r];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * (D / 4); idx += blockDim.x) {
+    const int g = idx / (D / 4);
+    const int d = (idx % (D / 4)) * 4;
+    float M = -INFINITY;
+    for (int w = 0; w < W; ++w) M = fmaxf(M, m_lds[w * 16 + g]);
+    float Lsum = 0.0f;
+    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    const int src_lane = g + 16 * (d / DL);
+    const int e = d % DL;
+    for (int w = 0; w < W; ++w) {
+      const float f = __builtin_amdgcn_exp2f(m_lds[w * 16 + g] - M);  // 0 for idle waves
+      Lsum += f * l_lds[w * 16 + g];
+      const float4 x = *reinterpret_cast<const float4*>(acc_lds + ((int64_t)w * 64 + src_lane) * STRIDE + e);
+      o.x += f * x.x;
+      o.y += f * x.y;
+      o.z += f * x.z;
+      o.w += f * x.w;
+    }
+    const float inv = Lsum > 0.0f ? vscale / Lsum : 0.0f;
+    o.x *= inv;
+    o.y *= inv;
+    o.z *= inv;
+    o.w *= inv;
+    const int hh = kvh * G + g;
+    float* dst = split ? a.part_out + (((int64_t)s * Hq + hh) * a.max_partitions + p) * D
+                       : a.out + ((int64_t)s * Hq + hh) * D;
+    *reinterpret_cast<float4*>(dst + d) = o;
+    if (split && d == 0)
+      a.part_lse[((int64_t)s * Hq + hh) * a.max_partitions + p] = (M + __log2f(Lsum)) * kLn2;
+  }
+}
+
+template <int KV, int D, bool QBF>
+static int launch_one(const DecodeArgs& a, int waves, hipStream_t st) {
+  const int P = a.partition_size > 0 ? a.max_partitions : 1;
+  size_t lds = (KV == KV_FP4 ? 16 * D * sizeof(float) : 0);
+  if (waves > 1) lds += (2 * 16 * 8 + (size_t)waves * 64 * (D / 4 + 4)) * sizeof(float);
+  hipLaunchKernelGGL((k_decode<KV, D, QBF>), dim3(P, a.num_kv_heads, a.num_seqs),
+                     dim3(64 * waves), lds, st, a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int launch_decode(const DecodeArgs& a, int kv, bool qbf, int D, int waves, hipStream_t st) {
+  if (D == 128) {
+    switch (kv) {
+      case KV_F16: return launch_one<KV_F16, 128, false>(a, waves, st);
+      case KV_BF16: return launch_one<KV_BF16, 128, true>(a, waves, st);
+      case KV_FP8:
+        return qbf ? launch_one<KV_FP8, 128, true>(a, waves, st)
+                   : launch_one<KV_FP8, 128, false>(a, waves, st);
+      case KV_FP4:
+        return qbf ? launch_one<KV_FP4, 128, true>(a, waves, st)
+                   : launch_one<KV_FP4, 128, false>(a, waves, st);
+    }
+  } else {
+    switch (kv) {
+      case KV_F16: return launch_one<KV_F16, 64, false>(a, waves, st);
+      case KV_BF16: return launch_one<KV_BF16, 64, true>(a, waves, st);
+      case KV_FP8:
+        return qbf ? launch_one<KV_FP8, 64, true>(a, waves, st)
+                   : launch_one<KV_FP8, 64, false>(a, waves, st);
+    }
+  }
+  return PA_ERR_DTYPE;
+}
+
+}  // namespace pa

@@ -1,0 +1,53 @@
+// pa_launch.h - host-side launch entry points of the gfx950 kernels (internal to libpa).
+// The C ABI in pa_api.cpp validates arguments and then calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pa.h"
+
+namespace pa {
+
+// floor(D / (1 + 3.2^2)): the most channels that can sit at or above mean + 3.2 sigma.
+inline int outlier_capacity(int head_dim) {
+  return head_dim == 128 ? 11 : head_dim == 64 ? 5 : -1;
+}
+
+int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool bf16, int32_t T,
+                 const int64_t* slots, int32_t* err, hipStream_t st);
+int launch_fp8_scales(const void* x, bool bf16, int64_t rows, int32_t hkv, int32_t D,
+                      float* scale_out, hipStream_t st);
+int launch_reset(const pa_kv_pool& p, const int32_t* ids, int32_t n, hipStream_t st);
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* k_tok_scale;
+  const float* v_tok_scale;
+  const uint8_t* k_out_idx;
+  const uint8_t* v_out_idx;
+  const uint16_t* k_out_val;
+  const uint16_t* v_out_val;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* out;       // [S, Hq, D] when partition_size == 0
+  float* part_out;  // [S, Hq, P, D] otherwise
+  float* part_lse;  // [S, Hq, P]
+  int32_t* err;
+  int32_t num_seqs, num_q_heads, num_kv_heads, group, num_blocks, max_blocks, partition_size,
+      max_partitions, cap;
+  float sm_scale_log2;  // sm_scale * log2(e)
+};
+
+int launch_decode(const DecodeArgs& a, int kv_dtype, bool q_bf16, int head_dim, int waves,
+                  hipStream_t st);
+
+int launch_merge(const float* part_out, const float* part_lse, const int32_t* context_lens,
+                 int32_t S, int32_t Hq, int32_t D, int32_t P, int32_t ps, float* out,
+                 float* lse_out, hipStream_t st);
+
+}  // namespace pa

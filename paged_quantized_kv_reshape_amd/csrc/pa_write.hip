@@ -1,0 +1,414 @@
+// pa_write.hip - cache write ("reshape and cache") kernels for gfx950.
+//
+// Each new token row goes to its slot = physical_block * 16 + offset of a paged pool
+// (xonoai.com field report on vLLM v0.7.2, "Deconstructing the v0.7.2 Architecture";
+// inferensys glossary "vLLM", PagedAttention entry), stored as a 16-bit copy, as FP8
+// E4M3 codes with a per-head fp32 scale, or as 4-bit E2M1 codes with a per-token scale
+// and the block's outlier channels kept in fp16 (dailyaiworld.com, "vLLM 0.7 Ships
+// Unified KV Cache Compression", "Technical Breakdown: Dynamic Quantization with Outlier
+// Retention", steps 1-3).
+//
+// Pool tile of (block, kv head): 16 token rows, row-major, so one token's row is one
+// contiguous run of head_dim values (head_dim / 2 bytes for FP4).
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+__device__ __forceinline__ void flag(int32_t* err, int32_t bit) {
+  if (err) atomicOr(err, bit);
+}
+
+// ---------------------------------------------------------------------------------
+// 16-bit copy: one thread per 16 bytes of a (token, head) row.
+// ---------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_write_copy(const uint4* __restrict__ k_new,
+                                                    const uint4* __restrict__ v_new,
+                                                    uint4* __restrict__ k_pool,
+                                                    uint4* __restrict__ v_pool,
+                                                    const int64_t* __restrict__ slots,
+                                                    int64_t total, int32_t hkv, int32_t chunks,
+                                                    int64_t nslots, int32_t* err) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int64_t per_tok = (int64_t)hkv * chunks;
+  const int64_t i = idx / per_tok;
+  const int64_t rem = idx - i * per_tok;
+  const int64_t slot = slots[i];
+  if (slot < 0) return;
+  if (slot >= nslots) {
+    if (rem == 0) flag(err, PA_DEVERR_BAD_SLOT);
+    return;
+  }
+  const int64_t h = rem / chunks, c = rem - h * chunks;
+  const int64_t dst = (((slot >> 4) * hkv + h) * kBlock + (slot & 15)) * chunks + c;
+  k_pool[dst] = k_new[idx];
+  v_pool[dst] = v_new[idx];
+}
+
+// ---------------------------------------------------------------------------------
+// FP8 E4M3: one thread per 8 values of a (token, head) row, K and V.
+// code = E4M3(fp32(x / s_h)); the fp32 division is IEEE correctly rounded.
+// ---------------------------------------------------------------------------------
+template <bool BF16>
+__device__ __forceinline__ uint2 fp8_encode8(const uint4 in, float s) {
+  const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+  uint32_t out[2] = {0u, 0u};
+  if (s != 0.0f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t b16 = (w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+      const float x = act_to_f32<BF16>(b16);
+      out[e >> 2] |= encode_e4m3(x / s) << ((e & 3) * 8);
+    }
+  }
+  return make_uint2(out[0], out[1]);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_write_fp8(const uint4* __restrict__ k_new,
+                                                   const uint4* __restrict__ v_new,
+                                                   uint2* __restrict__ k_pool,
+                                                   uint2* __restrict__ v_pool,
+                                                   const float* __restrict__ k_scale,
+                                                   const float* __restrict__ v_scale,
+                                                   const int64_t* __restrict__ slots,
+                                                   int64_t total, int32_t hkv, int32_t chunks,
+                                                   int64_t nslots, int32_t* err) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int64_t per_tok = (int64_t)hkv * chunks;
+  const int64_t i = idx / per_tok;
+  const int64_t rem = idx - i * per_tok;
+  const int64_t slot = slots[i];
+  if (slot < 0) return;
+  if (slot >= nslots) {
+    if (rem == 0) flag(err, PA_DEVERR_BAD_SLOT);
+    return;
+  }
+  const int64_t h = rem / chunks, c = rem - h * chunks;
+  const int64_t dst = (((slot >> 4) * hkv + h) * kBlock + (slot & 15)) * chunks + c;
+  k_pool[dst] = fp8_encode8<BF16>(k_new[idx], k_scale[h]);
+  v_pool[dst] = fp8_encode8<BF16>(v_new[idx], v_scale[h]);
+}
+
+// ---------------------------------------------------------------------------------
+// FP4 E2M1 + fp16 outliers, three launches per call.
+//
+// A block's record (16 bytes per block, kv head, K|V) reads 0xFF.. until the block is
+// first written. A call calibrates every block it opens on the rows it puts there, so the
+// kernels must find, for each such block, the set of this call's rows in it, without
+// scratch memory of their own:
+//   mark      each row landing in an unset record clears bit `offset` of the record's last
+//             word (bytes 12..15, never an index since at most 11 channels are stored)
+//             and parks its row index in tok_scale[block, head, offset], a word the encode
+//             launch overwrites with the row's real scale;
+//   calibrate the row with the lowest cleared offset (the leader) reads the row list from
+//             the parked indices, computes the outlier set and writes record bytes 0..11;
+//             the others only read bytes 12..15, which this launch never writes;
+//   encode    every row reads the record (bytes 0..11), stores codes, scale and outliers,
+//             and sets bytes 12..15 back to 0xFF.
+// grid.z selects K (0) or V (1).
+// ---------------------------------------------------------------------------------
+struct Fp4Side {
+  const uint16_t* rows;  // new rows [T, Hkv, D] (activation bits)
+  uint8_t* codes;        // [NB, Hkv, 16, D/2]
+  float* tok_scale;      // [NB, Hkv, 16]
+  uint8_t* out_idx;      // [NB, Hkv, 16]
+  uint16_t* out_val;     // [NB, Hkv, CAP, 16]
+};
+struct Fp4Args {
+  Fp4Side side[2];
+  const int64_t* slots;
+  int32_t num_tokens, hkv, head_dim, cap;
+  int64_t nslots;
+  int32_t* err;
+};
+
+__global__ __launch_bounds__(256) void k_fp4_mark(Fp4Args a) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (int64_t)a.num_tokens * a.hkv;
+  if (idx >= n) return;
+  const Fp4Side& sd = a.side[blockIdx.z];
+  const int64_t i = idx / a.hkv, h = idx - i * a.hkv;
+  const int64_t slot = a.slots[i];
+  if (slot < 0) return;
+  if (slot >= a.nslots) {
+    if (h == 0 && blockIdx.z == 0) flag(a.err, PA_DEVERR_BAD_SLOT);
+    return;
+  }
+  const int64_t bh = (slot >> 4) * a.hkv + h;
+  const int off = (int)(slot & 15);
+  uint8_t* rec = sd.out_idx + bh * 16;
+  if (rec[0] != 0xFF) return;  // already calibrated: reuse its channel set
+  atomicAnd(reinterpret_cast<unsigned int*>(rec + 12), ~(1u << off));
+  reinterpret_cast<int32_t*>(sd.tok_scale)[bh * kBlock + off] = (int32_t)i;
+}
+
+// One wave per (row, head, K|V); only block leaders do work.
+template <bool BF16, int D>
+__global__ __launch_bounds__(64) void k_fp4_calibrate(Fp4Args a) {
+  const int i = blockIdx.x, h = blockIdx.y;
+  const Fp4Side& sd = a.side[blockIdx.z];
+  const int lane = threadIdx.x;
+  const int64_t slot = a.slots[i];
+  if (slot < 0 || slot >= a.nslots) return;
+  const int64_t bh = (slot >> 4) * a.hkv + h;
+  const int off = (int)(slot & 15);
+  uint8_t* rec = sd.out_idx + bh * 16;
+  const uint32_t pending = ~*reinterpret_cast<const volatile uint32_t*>(rec + 12) & 0xFFFFu;
+  if (!(pending & (1u << off))) return;              // not opened by this call
+  if (off != __builtin_ctz(pending)) return;          // not the leader
+  const int32_t* parked = reinterpret_cast<const int32_t*>(sd.tok_scale) + bh * kBlock;
+
+  // Per-channel RMS over this call's rows in the block, rows taken in ascending offset.
+  constexpr int CPL = D / 64;  // channels per lane: lane + 64 * k
+  float ss[CPL];
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) ss[k] = 0.0f;
+  int n = 0;
+  const int64_t blk_base = (slot >> 4) << 4;
+  for (uint32_t m = pending; m; m &= m - 1) {
+    const int o = __builtin_ctz(m);
+    const int64_t row = parked[o];
+    // a parked index is trusted only if that row really targets this slot (a record that
+    // did not start as all 0xFF could carry stray cleared bits)
+    if (row < 0 || row >= a.num_tokens || a.slots[row] != blk_base + o) continue;
+    const uint16_t* x = sd.rows + (row * a.hkv + h) * D;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const float v = act_to_f32<BF16>(x[lane + 64 * k]);
+      ss[k] = __builtin_fmaf(v, v, ss[k]);
+    }
+    ++n;
+  }
+  if (n == 0) return;
+  float r[CPL], part = 0.0f;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) {
+    r[k] = __builtin_sqrtf(ss[k] / (float)n);
+    part += r[k];
+  }
+  const float mu = wave_sum(part) / (float)D;
+  float dev = 0.0f;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) dev += (r[k] - mu) * (r[k] - mu);
+  const float sigma = __builtin_sqrtf(wave_sum(dev) / (float)D);
+  const float thr = mu + kOutlierSigmas * sigma;
+
+  // Ascending channel list via ballots (channel lane + 64 k).
+  uint32_t bytes[3] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  int count = 0;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) {
+    const bool hit = sigma != 0.0f && r[k] >= thr;
+    uint64_t mask = __ballot(hit);
+    while (mask) {
+      const int c = __builtin_ctzll(mask) + 64 * k;
+      mask &= mask - 1;
+      if (count < a.cap) {
+        const int pos = 1 + count;  // byte position in the record
+        bytes[pos >> 2] &= ~(0xFFu << ((pos & 3) * 8));
+        bytes[pos >> 2] |= (uint32_t)c << ((pos & 3) * 8);
+      }
+      ++count;
+    }
+  }
+  if (lane == 0) {
+    const int stored = count < a.cap ? count : a.cap;
+    bytes[0] = (bytes[0] & ~0xFFu) | (uint32_t)stored;
+    uint32_t* w = reinterpret_cast<uint32_t*>(rec);
+    w[0] = bytes[0];
+    w[1] = bytes[1];
+    w[2] = bytes[2];
+  }
+}
+
+// One wave per (row, head, K|V); lane l owns channels 2l and 2l + 1 (one packed byte).
+template <bool BF16, int D>
+__global__ __launch_bounds__(64) void k_fp4_encode(Fp4Args a) {
+  const int i = blockIdx.x, h = blockIdx.y;
+  const Fp4Side& sd = a.side[blockIdx.z];
+  const int lane = threadIdx.x;
+  const int64_t slot = a.slots[i];
+  if (slot < 0 || slot >= a.nslots) return;
+  const int64_t bh = (slot >> 4) * a.hkv + h;
+  const int off = (int)(slot & 15);
+  uint8_t* rec = sd.out_idx + bh * 16;
+  const uint4 r4 = *reinterpret_cast<const uint4*>(rec);  // bytes 12..15 ignored
+  const uint32_t rw[3] = {r4.x, r4.y, r4.z};
+  int count = (int)(rw[0] & 0xFFu);
+  if (count == 0xFF) {  // never calibrated: cannot happen after the calibrate launch
+    if (lane == 0) flag(a.err, PA_DEVERR_UNCALIBRATED);
+    return;
+  }
+  if (count > a.cap) count = a.cap;
+  const bool active = lane < D / 2;
+  const int c0 = 2 * lane, c1 = c0 + 1;
+  float x0 = 0.0f, x1 = 0.0f;
+  if (active) {
+    const uint32_t pair = *reinterpret_cast<const uint32_t*>(sd.rows + ((int64_t)i * a.hkv + h) * D + c0);
+    x0 = act_to_f32<BF16>(pair & 0xFFFFu);
+    x1 = act_to_f32<BF16>(pair >> 16);
+  }
+  bool out0 = false, out1 = false;
+  for (int j = 0; j < count; ++j) {
+    const int pos = 1 + j;
+    const int c = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
+    out0 |= (c == c0);
+    out1 |= (c == c1);
+  }
+  const float a0 = (active && !out0) ? __builtin_fabsf(x0) : 0.0f;
+  const float a1 = (active && !out1) ? __builtin_fabsf(x1) : 0.0f;
+  const float amax = wave_max(fmaxf(a0, a1));
+  const float s = amax / 6.0f;
+  uint32_t q0 = 0u, q1 = 0u;
+  if (s != 0.0f) {
+    q0 = out0 ? 0u : encode_e2m1(x0 / s);
+    q1 = out1 ? 0u : encode_e2m1(x1 / s);
+  }
+  const int64_t row_slot = bh * kBlock + off;
+  if (active) sd.codes[row_slot * (D / 2) + lane] = (uint8_t)(q0 | (q1 << 4));
+  for (int j = 0; j < count; ++j) {
+    const int pos = 1 + j;
+    const int c = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
+    if (active && (c >> 1) == lane) {
+      const float xv = (c & 1) ? x1 : x0;
+      sd.out_val[(bh * a.cap + j) * kBlock + off] = bitcast<uint16_t>((_Float16)xv);
+    }
+  }
+  if (lane == 0) {
+    sd.tok_scale[row_slot] = s;
+    *reinterpret_cast<uint32_t*>(rec + 12) = 0xFFFFFFFFu;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// FP8 per-head scale: fp32(absmax / 448). absmax via atomicMax on the fp32 bit pattern
+// (non-negative floats order like their bit patterns).
+// ---------------------------------------------------------------------------------
+__global__ void k_scale_init(uint32_t* bits, int32_t hkv) {
+  const int t = threadIdx.x;
+  if (t < hkv) bits[t] = 0u;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_absmax(const uint4* __restrict__ x, int64_t rows,
+                                                int32_t hkv, int32_t chunks, uint32_t* bits) {
+  const int h = blockIdx.y;
+  float m = 0.0f;
+  const int64_t n = rows * chunks;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = t / chunks, c = t - r * chunks;
+    const uint4 v = x[(r * hkv + h) * chunks + c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      m = fmaxf(m, __builtin_fabsf(act_to_f32<BF16>(w[e] & 0xFFFFu)));
+      m = fmaxf(m, __builtin_fabsf(act_to_f32<BF16>(w[e] >> 16)));
+    }
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) atomicMax(bits + h, __float_as_uint(m));
+}
+
+__global__ void k_scale_finish(uint32_t* bits, int32_t hkv) {
+  const int t = threadIdx.x;
+  if (t < hkv) {
+    const float a = __uint_as_float(bits[t]);
+    reinterpret_cast<float*>(bits)[t] = a / 448.0f;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_reset_records(uint4* idx_k, uint4* idx_v,
+                                                       const int32_t* __restrict__ ids, int32_t n,
+                                                       int32_t hkv, int32_t nb) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)n * hkv) return;
+  const int32_t b = ids[t / hkv];
+  if (b < 0 || b >= nb) return;
+  const int64_t bh = (int64_t)b * hkv + t % hkv;
+  const uint4 ff = make_uint4(~0u, ~0u, ~0u, ~0u);
+  idx_k[bh] = ff;
+  idx_v[bh] = ff;
+}
+
+// ---------------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------------
+static inline unsigned grid1(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
+
+int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool bf16,
+                 int32_t T, const int64_t* slots, int32_t* err, hipStream_t st) {
+  const int64_t nslots = (int64_t)p.num_blocks * kBlock;
+  const int D = p.head_dim, hkv = p.num_kv_heads;
+  if (T == 0) return PA_OK;
+  if (p.dtype == PA_KV_F16 || p.dtype == PA_KV_BF16) {
+    const int chunks = D * 2 / 16;
+    const int64_t total = (int64_t)T * hkv * chunks;
+    hipLaunchKernelGGL(k_write_copy, dim3(grid1(total, 256)), dim3(256), 0, st,
+                       (const uint4*)k_new, (const uint4*)v_new, (uint4*)p.k, (uint4*)p.v, slots,
+                       total, hkv, chunks, nslots, err);
+  } else if (p.dtype == PA_KV_FP8_E4M3) {
+    const int chunks = D / 8;
+    const int64_t total = (int64_t)T * hkv * chunks;
+    auto kern = bf16 ? k_write_fp8<true> : k_write_fp8<false>;
+    hipLaunchKernelGGL(kern, dim3(grid1(total, 256)), dim3(256), 0, st, (const uint4*)k_new,
+                       (const uint4*)v_new, (uint2*)p.k, (uint2*)p.v, p.k_scale, p.v_scale, slots,
+                       total, hkv, chunks, nslots, err);
+  } else {
+    Fp4Args a;
+    a.side[0] = {(const uint16_t*)k_new, (uint8_t*)p.k, p.k_tok_scale, p.k_out_idx, p.k_out_val};
+    a.side[1] = {(const uint16_t*)v_new, (uint8_t*)p.v, p.v_tok_scale, p.v_out_idx, p.v_out_val};
+    a.slots = slots;
+    a.num_tokens = T;
+    a.hkv = hkv;
+    a.head_dim = D;
+    a.cap = outlier_capacity(D);
+    a.nslots = nslots;
+    a.err = err;
+    hipLaunchKernelGGL(k_fp4_mark, dim3(grid1((int64_t)T * hkv, 256), 1, 2), dim3(256), 0, st, a);
+    const dim3 g(T, hkv, 2);
+    void (*cal)(Fp4Args);
+    void (*enc)(Fp4Args);
+    if (D == 128) {
+      cal = bf16 ? k_fp4_calibrate<true, 128> : k_fp4_calibrate<false, 128>;
+      enc = bf16 ? k_fp4_encode<true, 128> : k_fp4_encode<false, 128>;
+    } else {
+      cal = bf16 ? k_fp4_calibrate<true, 64> : k_fp4_calibrate<false, 64>;
+      enc = bf16 ? k_fp4_encode<true, 64> : k_fp4_encode<false, 64>;
+    }
+    hipLaunchKernelGGL(cal, g, dim3(64), 0, st, a);
+    hipLaunchKernelGGL(enc, g, dim3(64), 0, st, a);
+  }
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int launch_fp8_scales(const void* x, bool bf16, int64_t rows, int32_t hkv, int32_t D,
+                      float* scale_out, hipStream_t st) {
+  uint32_t* bits = reinterpret_cast<uint32_t*>(scale_out);
+  hipLaunchKernelGGL(k_scale_init, dim3(1), dim3(256), 0, st, bits, hkv);
+  if (rows > 0) {
+    const int chunks = D / 8;
+    const int64_t n = rows * chunks;
+    unsigned gx = grid1(n, 256);
+    if (gx > 1024) gx = 1024;
+    auto kern = bf16 ? k_absmax<true> : k_absmax<false>;
+    hipLaunchKernelGGL(kern, dim3(gx, hkv), dim3(256), 0, st, (const uint4*)x, rows, hkv, chunks,
+                       bits);
+  }
+  hipLaunchKernelGGL(k_scale_finish, dim3(1), dim3(256), 0, st, bits, hkv);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int launch_reset(const pa_kv_pool& p, const int32_t* ids, int32_t n, hipStream_t st) {
+  if (n == 0) return PA_OK;
+  const int64_t total = (int64_t)n * p.num_kv_heads;
+  hipLaunchKernelGGL(k_reset_records, dim3(grid1(total, 256)), dim3(256), 0, st,
+                     (uint4*)p.k_out_idx, (uint4*)p.v_out_idx, ids, n, p.num_kv_heads,
+                     p.num_blocks);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // namespace pa

@@ -1,0 +1,91 @@
+"""Device-side driver of one workload through libpa (tests, smoke check and bench).
+
+Uploads a workload's inputs to HBM, derives FP8 scales with pa_fp8_head_scales, replays
+its cache-write calls with pa_cache_write and runs pa_decode (+ pa_merge when split).
+Everything that computes runs in libpa; torch only holds memory and orders the stream.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+_TORCH_ACT = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def _dev_bits(a: np.ndarray, act: str, device) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16))
+    return t.to(device).view(_TORCH_ACT[act])
+
+
+class DeviceRun:
+    def __init__(self, w, device="cuda", partition_size=None, fill=0xA5, pool_copies=1):
+        self.w = w
+        self.device = device
+        self.ps = w.partition_size if partition_size is None else partition_size
+        self.q = _dev_bits(w.q, w.act, device)
+        self.k_rows = _dev_bits(w.k_rows, w.act, device)
+        self.v_rows = _dev_bits(w.v_rows, w.act, device)
+        self.block_tables = torch.from_numpy(w.block_tables).to(device)
+        self.context_lens = torch.from_numpy(w.context_lens.astype(np.int32)).to(device)
+        self.dev_err = torch.zeros(1, dtype=torch.int32, device=device)
+        self.k_scale = self.v_scale = None
+        if w.kv == "fp8":
+            self.k_scale = torch.empty(w.num_kv_heads, dtype=torch.float32, device=device)
+            self.v_scale = torch.empty(w.num_kv_heads, dtype=torch.float32, device=device)
+            B.pa_fp8_head_scales(self.k_rows, self.k_scale)
+            B.pa_fp8_head_scales(self.v_rows, self.v_scale)
+        self.pools = [B.KVPool(w.kv, w.num_blocks, w.num_kv_heads, w.head_dim, device=device,
+                               fill=fill, k_scale=self.k_scale, v_scale=self.v_scale)
+                      for _ in range(pool_copies)]
+        self.pool = self.pools[0]
+        sc = w.step_call
+        idx = torch.from_numpy(sc.rows).to(device)
+        self.step_k = self.k_rows.index_select(0, idx).contiguous()
+        self.step_v = self.v_rows.index_select(0, idx).contiguous()
+        self.step_slots = torch.from_numpy(sc.slots).to(device)
+        S, Hq, D = w.q.shape
+        self.out = torch.empty((S, Hq, D), dtype=torch.float32, device=device)
+        self.lse = torch.empty((S, Hq), dtype=torch.float32, device=device)
+        self.part_out = self.part_lse = None
+        if self.ps:
+            P = B.max_partitions(w.max_blocks_per_seq, self.ps)
+            self.part_out = torch.empty((S, Hq, P, D), dtype=torch.float32, device=device)
+            self.part_lse = torch.empty((S, Hq, P), dtype=torch.float32, device=device)
+
+    # -- writes ---------------------------------------------------------------------
+    def setup_writes(self, pool=None):
+        pool = pool or self.pool
+        for call in self.w.setup_calls:
+            idx = torch.from_numpy(call.rows).to(self.device)
+            slots = torch.from_numpy(call.slots).to(self.device)
+            B.pa_cache_write(pool, self.k_rows.index_select(0, idx),
+                             self.v_rows.index_select(0, idx), slots, self.dev_err)
+
+    def step_write(self, pool=None):
+        B.pa_cache_write(pool or self.pool, self.step_k, self.step_v, self.step_slots,
+                         self.dev_err)
+
+    def prepare(self):
+        for p in self.pools:
+            self.setup_writes(p)
+            self.step_write(p)
+
+    # -- decode ---------------------------------------------------------------------
+    def decode(self, pool=None):
+        pool = pool or self.pool
+        B.pa_decode(self.q, pool, self.block_tables, self.context_lens, self.w.sm_scale,
+                    self.ps, out=self.out, part_out=self.part_out, part_lse=self.part_lse,
+                    dev_err=self.dev_err)
+        if self.ps:
+            B.pa_merge(self.part_out, self.part_lse, self.context_lens, self.ps, self.out,
+                       self.lse)
+
+    def step(self, pool=None):
+        """One pass of the hot path: the step's cache write, then decode (+ merge)."""
+        self.step_write(pool)
+        self.decode(pool)
+
+    def device_error(self) -> int:
+        return B.pa_read_device_error(self.dev_err)

@@ -1,0 +1,160 @@
+"""C-ABI checks that need no GPU: libpa.so loads, exports every entry point include/pa.h
+declares, and rejects each invalid argument with its status before any HIP call.
+
+Only rejected calls (and the no-op num_tokens = 0 / num_seqs = 0 forms) are made here:
+fake device addresses never reach a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+B = pytest.importorskip("paged_quantized_kv_reshape_amd.binding")
+
+PA_OK, NULL, SHAPE, DTYPE, BLOCK, CONTEXT, PART, LAUNCH, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7, -8
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\s*\*)\s*(pa_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_entry_point():
+    lib = B.lib()
+    names = _declared()
+    assert {"pa_cache_write", "pa_decode", "pa_merge", "pa_pool_layout"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = B.lib()
+    for code in (PA_OK, NULL, SHAPE, DTYPE, BLOCK, CONTEXT, PART, LAUNCH, ALIGN):
+        s = lib.pa_status_string(code).decode()
+        assert s.startswith("PA_"), s
+    assert "unknown" in lib.pa_status_string(-99).decode()
+
+
+@pytest.mark.parametrize("kv,d,expect", [
+    ("f16", 128, [2 * 10 * 3 * 16 * 128] * 2 + [0] * 6),
+    ("bf16", 64, [2 * 10 * 3 * 16 * 64] * 2 + [0] * 6),
+    ("fp8", 128, [10 * 3 * 16 * 128] * 2 + [0] * 6),
+    ("fp4", 128, [10 * 3 * 16 * 64] * 2 + [10 * 3 * 16 * 4] * 2 + [10 * 3 * 16] * 2
+     + [10 * 3 * 11 * 16 * 2] * 2),
+])
+def test_pool_layout_sizes(kv, d, expect):
+    assert B.pa_pool_layout(kv, 10, 3, d) == expect
+
+
+def test_pool_layout_rejects():
+    lib = B.lib()
+    out = (ctypes.c_size_t * 8)()
+    assert lib.pa_pool_layout(9, 10, 1, 128, out) == DTYPE
+    assert lib.pa_pool_layout(0, 0, 1, 128, out) == SHAPE
+    assert lib.pa_pool_layout(0, 10, 1, 96, out) == SHAPE
+    assert lib.pa_pool_layout(3, 10, 1, 64, out) == SHAPE  # FP4 needs head_dim 128
+    assert lib.pa_pool_layout(0, 10, 1, 128, None) == NULL
+    assert lib.pa_outlier_capacity(128) == 11 and lib.pa_outlier_capacity(64) == 5
+    assert lib.pa_outlier_capacity(80) == SHAPE
+
+
+def _pool(dtype=2, nb=8, hkv=1, d=128, bs=16, scales=True, fp4=True):
+    s = B.pa_kv_pool()
+    s.dtype, s.num_blocks, s.block_size, s.num_kv_heads, s.head_dim = dtype, nb, bs, hkv, d
+    s.k = s.v = FAKE
+    if scales:
+        s.k_scale = s.v_scale = FAKE
+    if fp4:
+        s.k_tok_scale = s.v_tok_scale = s.k_out_idx = s.v_out_idx = FAKE
+        s.k_out_val = s.v_out_val = FAKE
+    return s
+
+
+def _write(pool, act=1, T=4, k=FAKE, v=FAKE, slots=FAKE, err=None):
+    p = None if pool is None else ctypes.byref(pool)
+    return B.lib().pa_cache_write(p, k, v, act, T, slots, err, None)
+
+
+def test_cache_write_rejects():
+    assert _write(None) == NULL
+    assert _write(_pool(bs=8)) == BLOCK
+    assert _write(_pool(dtype=7)) == DTYPE
+    assert _write(_pool(d=96)) == SHAPE
+    assert _write(_pool(nb=0)) == SHAPE
+    assert _write(_pool(dtype=3, d=64)) == SHAPE
+    assert _write(_pool(dtype=0), act=1) == DTYPE      # fp16 pool, bf16 rows
+    assert _write(_pool(dtype=1), act=0) == DTYPE      # bf16 pool, fp16 rows
+    assert _write(_pool(), act=4) == DTYPE
+    assert _write(_pool(), T=-1) == SHAPE
+    assert _write(_pool(), k=None) == NULL
+    assert _write(_pool(), slots=None) == NULL
+    assert _write(_pool(scales=False)) == NULL         # fp8 without scales
+    assert _write(_pool(dtype=3, fp4=False)) == NULL   # fp4 without its arrays
+    assert _write(_pool(), k=FAKE + 8) == ALIGN
+    assert _write(_pool(), slots=FAKE + 4) == ALIGN
+    s = _pool()
+    s.k = FAKE + 2
+    assert _write(s) == ALIGN
+    assert _write(_pool(), T=0) == PA_OK  # no rows: nothing to launch
+
+
+def _decode(pool=None, q=FAKE, qd=1, S=2, Hq=8, bt=FAKE, MB=4, cl=FAKE, ps=0, out=FAKE,
+            po=FAKE, pl=FAKE):
+    pool = pool if pool is not None else _pool()
+    return B.lib().pa_decode(q, qd, S, Hq, ctypes.byref(pool), bt, MB, cl, 0.1, ps, out, po, pl,
+                             None, None)
+
+
+def test_decode_rejects():
+    assert _decode(pool=_pool(bs=32)) == BLOCK
+    assert _decode(qd=3) == DTYPE
+    assert _decode(pool=_pool(dtype=0), qd=1) == DTYPE
+    assert _decode(pool=_pool(hkv=3), Hq=8) == SHAPE        # Hq % Hkv != 0
+    assert _decode(pool=_pool(hkv=1), Hq=32) == SHAPE       # group of 32 > 16
+    assert _decode(S=-1) == SHAPE
+    assert _decode(Hq=0) == SHAPE
+    assert _decode(MB=0) == CONTEXT
+    assert _decode(MB=2 ** 28) == CONTEXT
+    assert _decode(ps=24) == PART
+    assert _decode(ps=-16) == PART
+    assert _decode(q=None) == NULL
+    assert _decode(bt=None) == NULL
+    assert _decode(cl=None) == NULL
+    assert _decode(out=None) == NULL
+    assert _decode(ps=512, po=None) == NULL
+    assert _decode(ps=512, pl=None) == NULL
+    assert _decode(q=FAKE + 4) == ALIGN
+    assert _decode(out=FAKE + 4) == ALIGN
+    assert _decode(S=0) == PA_OK  # empty batch: nothing to launch
+
+
+def test_merge_and_scale_and_reset_reject():
+    lib = B.lib()
+    m = lambda **k: lib.pa_merge(k.get("po", FAKE), k.get("pl", FAKE), k.get("cl", FAKE),
+                                 k.get("S", 2), k.get("Hq", 8), k.get("D", 128), k.get("P", 4),
+                                 k.get("ps", 512), k.get("out", FAKE), None, None)
+    assert m(ps=0) == PART and m(ps=100) == PART
+    assert m(D=96) == SHAPE and m(P=0) == SHAPE and m(Hq=0) == SHAPE
+    assert m(out=None) == NULL and m(po=None) == NULL
+    assert m(po=FAKE + 4) == ALIGN
+    assert m(S=0) == PA_OK
+    f = lambda **k: lib.pa_fp8_head_scales(k.get("x", FAKE), k.get("act", 1), k.get("rows", 5),
+                                           k.get("hkv", 1), k.get("d", 128), k.get("out", FAKE),
+                                           None)
+    assert f(act=2) == DTYPE and f(hkv=0) == SHAPE and f(d=32) == SHAPE and f(rows=-1) == SHAPE
+    assert f(out=None) == NULL and f(x=None) == NULL and f(x=FAKE + 2) == ALIGN
+    p = _pool(dtype=3)
+    assert lib.pa_reset_blocks(ctypes.byref(p), None, 3, None) == NULL
+    assert lib.pa_reset_blocks(ctypes.byref(p), FAKE, -1, None) == SHAPE
+    assert lib.pa_reset_blocks(ctypes.byref(_pool(dtype=2)), FAKE, 3, None) == PA_OK  # no records
+    assert lib.pa_read_device_error(None, None, None) == NULL
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="libpa.so not found"):
+        B.lib()

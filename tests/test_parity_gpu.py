@@ -1,0 +1,249 @@
+"""GPU parity: libpa's HIP path against the oracle on the same seeded inputs.
+
+Cache writes (codes, scales, outlier records and values, untouched sentinel bytes) must be
+bit-exact; decode outputs within max-abs 2e-3 and relative L2 1e-2 of exact attention on
+the identical dequantized cache. Small cases check every output; the full-size workloads
+run in the launch configuration the bench times and are checked on sampled sequences."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+from oracle_side import (assert_close, assert_pool_equal, oracle_decode, replay, seq_blocks)
+from workload import config
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+# Reduced shapes: several blocks per sequence, ragged tails, every format.
+SMALL = {
+    "c1": {},
+    "c2": dict(num_seqs=4, lens_range=(200, 900)),
+    "c3": dict(num_seqs=4, lens_range=(200, 900)),
+    "c4": dict(num_seqs=4, lens=[2000, 2048, 1999, 33]),
+    "c5": dict(num_seqs=3, lens_range=(1500, 4000)),
+}
+
+_cache = {}
+
+
+def _say(*a):
+    print(*a, flush=True, file=sys.stderr)
+
+
+def _setup(cfg):
+    """Workload, prepared device run, and the oracle's replay (cached per config)."""
+    if cfg not in _cache:
+        from paged_quantized_kv_reshape_amd.harness import DeviceRun
+        w = config(cfg, **SMALL[cfg])
+        _say(f"[setup] {cfg}: S={w.num_seqs} lens={w.context_lens.tolist()} kv={w.kv}")
+        run = DeviceRun(w, partition_size=0)
+        run.prepare()
+        torch.cuda.synchronize()
+        pool, ks, vs, near = replay(w)
+        _cache[cfg] = (w, run, pool, ks, vs, near)
+    return _cache[cfg]
+
+
+@pytest.fixture(autouse=True)
+def _waves_env():
+    old = os.environ.get("PA_DECODE_WAVES")
+    yield
+    if old is None:
+        os.environ.pop("PA_DECODE_WAVES", None)
+    else:
+        os.environ["PA_DECODE_WAVES"] = old
+
+
+@pytest.mark.parametrize("cfg", list(SMALL))
+def test_cache_write_bit_exact(cfg):
+    w, run, pool, ks, vs, near = _setup(cfg)
+    _say(f"[write] {cfg}: near-ties excluded: {len(near)}")
+    if ks is not None:
+        assert np.array_equal(run.k_scale.cpu().numpy().view(np.uint32), ks.view(np.uint32))
+        assert np.array_equal(run.v_scale.cpu().numpy().view(np.uint32), vs.view(np.uint32))
+    assert_pool_equal(run.pool.numpy(), pool, near=near)
+    assert len(near) == 0
+    assert run.device_error() == 0
+
+
+@pytest.mark.parametrize("waves", [1, 2, 4])
+@pytest.mark.parametrize("ps", [0, 64, 512])
+@pytest.mark.parametrize("cfg", list(SMALL))
+def test_decode_matches_oracle(cfg, ps, waves):
+    from paged_quantized_kv_reshape_amd.harness import DeviceRun
+    w, run, pool, ks, vs, _ = _setup(cfg)
+    os.environ["PA_DECODE_WAVES"] = str(waves)
+    _say(f"[decode] {cfg} ps={ps} waves={waves}")
+    r = DeviceRun.__new__(DeviceRun)
+    r.__dict__.update(run.__dict__)
+    if ps:
+        from paged_quantized_kv_reshape_amd import max_partitions
+        S, Hq, D = w.q.shape
+        P = max_partitions(w.max_blocks_per_seq, ps)
+        r.part_out = torch.empty((S, Hq, P, D), dtype=torch.float32, device="cuda")
+        r.part_lse = torch.empty((S, Hq, P), dtype=torch.float32, device="cuda")
+    r.ps = ps
+    r.out = torch.full_like(run.out, float("nan"))
+    r.lse = torch.full_like(run.lse, float("nan"))
+    r.decode()
+    torch.cuda.synchronize()
+    got = r.out.cpu().numpy()
+    ref = oracle_decode(w, pool, ks, vs, range(w.num_seqs))
+    want = np.stack([ref[s][0] for s in range(w.num_seqs)])
+    assert_close(got, want, f"{cfg} ps={ps} W={waves} out")
+    if ps:
+        lse = r.lse.cpu().numpy()
+        want_lse = np.stack([ref[s][1] for s in range(w.num_seqs)])
+        assert np.abs(lse - want_lse).max() < 1e-3
+        parts = oracle_decode(w, pool, ks, vs, range(w.num_seqs), partition_size=ps)
+        po, pl = r.part_out.cpu().numpy(), r.part_lse.cpu().numpy()
+        for s in range(w.num_seqs):
+            o, l = parts[s]
+            n = o.shape[1]
+            assert_close(po[s, :, :n], o, f"{cfg} ps={ps} partials of seq {s}")
+            assert np.abs(pl[s, :, :n] - l).max() < 1e-3
+    assert r.device_error() == 0
+
+
+@pytest.mark.parametrize("cfg", ["c3", "c5"])
+def test_decode_is_deterministic_and_relabelling_invariant(cfg):
+    """Two runs give identical bits; moving every physical block to a new id (pool bytes
+    and block tables together) gives identical bits too."""
+    w, run, pool, ks, vs, _ = _setup(cfg)
+    run.decode()
+    a = run.out.clone()
+    run.decode()
+    assert torch.equal(a, run.out)
+    g = torch.Generator().manual_seed(7)
+    perm = torch.randperm(w.num_blocks, generator=g)  # old block i -> new id perm[i]
+    inv = torch.argsort(perm)
+    saved = {n: t.clone() for n, t in run.pool.bytes.items()}
+    for n, t in run.pool.bytes.items():
+        t.copy_(saved[n].view(w.num_blocks, -1)[inv.to(t.device)].reshape(-1))
+    bt = run.block_tables.clone()
+    live = run.block_tables >= 0
+    run.block_tables[live] = perm.to(bt.device)[bt[live].long()].int()
+    run.decode()
+    b = run.out.clone()
+    run.block_tables.copy_(bt)
+    for n, t in run.pool.bytes.items():
+        t.copy_(saved[n])
+    assert torch.equal(a, b)
+
+
+def test_device_side_checks_flag_and_skip():
+    from paged_quantized_kv_reshape_amd import describe_device_error
+    w, run, pool, ks, vs, _ = _setup("c4")
+    # a block id outside the pool: flagged, output stays finite
+    bt = run.block_tables.clone()
+    run.block_tables[0, 3] = w.num_blocks + 5
+    run.dev_err.zero_()
+    run.decode()
+    e = run.device_error()
+    run.block_tables.copy_(bt)
+    assert e & 1, describe_device_error(e)
+    assert torch.isfinite(run.out).all()
+    # a context length of 0 and one past the table: flagged, zero output for that sequence
+    cl = run.context_lens.clone()
+    run.context_lens[1] = 0
+    run.context_lens[2] = w.max_blocks_per_seq * 16 + 1
+    run.dev_err.zero_()
+    run.decode()
+    e = run.device_error()
+    run.context_lens.copy_(cl)
+    assert e & 4, describe_device_error(e)
+    assert torch.count_nonzero(run.out[1]) == 0 and torch.count_nonzero(run.out[2]) == 0
+    # a slot outside the pool: flagged, nothing written
+    before = {n: t.clone() for n, t in run.pool.bytes.items()}
+    from paged_quantized_kv_reshape_amd import pa_cache_write
+    bad = torch.tensor([w.num_blocks * 16 + 3], dtype=torch.int64, device="cuda")
+    run.dev_err.zero_()
+    pa_cache_write(run.pool, run.step_k[:1], run.step_v[:1], bad, run.dev_err)
+    e = run.device_error()
+    assert e & 2, describe_device_error(e)
+    for n, t in run.pool.bytes.items():
+        assert torch.equal(t, before[n])
+
+
+def test_fp4_reset_blocks_and_uncalibrated_read():
+    from paged_quantized_kv_reshape_amd import pa_reset_blocks
+    w, run, pool, ks, vs, _ = _setup("c5")
+    saved = {n: t.clone() for n, t in run.pool.bytes.items()}
+    n0 = -(-int(w.context_lens[0]) // 16)
+    ids = run.block_tables[0, :n0].contiguous()
+    pa_reset_blocks(run.pool, ids)
+    rec = run.pool.bytes["k_out_idx"].view(w.num_blocks, w.num_kv_heads, 16)
+    assert bool((rec[ids.long()] == 0xFF).all())
+    run.dev_err.zero_()
+    run.decode()
+    assert run.device_error() & 8
+    # rewriting sequence 0 recalibrates its blocks to the same records
+    from paged_quantized_kv_reshape_amd import pa_cache_write
+    for call in list(w.setup_calls) + [w.step_call]:
+        sel = np.isin(call.slots // 16, ids.cpu().numpy())
+        if sel.any():
+            idx = torch.from_numpy(call.rows[sel]).cuda()
+            pa_cache_write(run.pool, run.k_rows.index_select(0, idx),
+                           run.v_rows.index_select(0, idx),
+                           torch.from_numpy(call.slots[sel]).cuda(), run.dev_err)
+    torch.cuda.synchronize()
+    for n, t in run.pool.bytes.items():
+        assert torch.equal(t, saved[n]), n
+
+
+def test_edge_lengths_and_empty_batch():
+    """Contexts of 1, 15, 16, 17 and 33 tokens (single token, ragged tails, exact block
+    ends) in one batch, and a zero-sequence call."""
+    from paged_quantized_kv_reshape_amd.harness import DeviceRun
+    w = config("c4", num_seqs=5, lens=[1, 15, 16, 17, 33])
+    run = DeviceRun(w, partition_size=16)
+    run.prepare()
+    run.decode()
+    torch.cuda.synchronize()
+    pool, ks, vs, _ = replay(w)
+    ref = oracle_decode(w, pool, ks, vs, range(5))
+    assert_close(run.out.cpu().numpy(), np.stack([ref[s][0] for s in range(5)]), "edge lengths")
+    from paged_quantized_kv_reshape_amd import pa_decode
+    pa_decode(run.q[:0], run.pool, run.block_tables[:0], run.context_lens[:0], w.sm_scale,
+              out=run.out[:0])
+    assert run.device_error() == 0
+
+
+# ---------------------------------------------------------------------------------
+# Full-size workloads, in the bench's launch configuration, sampled against the oracle.
+# ---------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", ["c2", "c3", "c4", "c5"])
+def test_full_size_sampled(cfg):
+    from paged_quantized_kv_reshape_amd.harness import DeviceRun
+    w = config(cfg)
+    _say(f"[full] {cfg}: S={w.num_seqs} tokens={w.tokens} blocks={w.num_blocks} ps={w.partition_size}")
+    run = DeviceRun(w)
+    run.prepare()
+    run.decode()
+    torch.cuda.synchronize()
+    assert run.device_error() == 0
+    out = run.out.cpu().numpy()
+    assert np.isfinite(out).all()
+    seqs = [0, w.num_seqs - 1] if cfg == "c5" else [0, w.num_seqs // 2, w.num_seqs - 1]
+    blocks = seq_blocks(w, seqs)
+    pool, ks, vs, near = replay(w, only_blocks=blocks)
+    _say(f"[full] {cfg}: sampled seqs {seqs}, {len(blocks)} blocks, near-ties {len(near)}")
+    if ks is not None:
+        assert np.array_equal(run.k_scale.cpu().numpy().view(np.uint32), ks.view(np.uint32))
+        assert np.array_equal(run.v_scale.cpu().numpy().view(np.uint32), vs.view(np.uint32))
+    assert_pool_equal(run.pool.numpy(), pool, blocks=blocks, near=near)
+    ref = oracle_decode(w, pool, ks, vs, seqs)
+    for s in seqs:
+        assert_close(out[s], ref[s][0], f"{cfg} seq {s}")
+    if w.kv == "fp4":
+        # every full 16-token block calibrated by a prefill chunk flags exactly the
+        # planted x20 channel (known a priori from the generator)
+        rec = run.pool.numpy()["k_out_idx"].reshape(w.num_blocks, w.num_kv_heads, 16)
+        s = seqs[0]
+        full = w.block_tables[s, :(int(w.context_lens[s]) - 1) // 16]
+        pk = int(w.planted_k[0]) % w.head_dim
+        assert np.all(rec[full, 0, 0] == 1) and np.all(rec[full, 0, 1] == pk)
