@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Bench: one step of the paged, quantized KV-cache hot path on one MI355X.
+
+A step is the whole path over one batch of synthetic input: the step's cache write
+(pa_cache_write of the new K/V rows), the paged decode (pa_decode) and, when the context
+is split into partitions, the log-sum-exp merge (pa_merge). The default workload is the
+Llama-3.1-70B tensor-parallel one-GPU share: 256 sequences of 8192 tokens, 8 query heads
+over 1 kv head, head_dim 128, FP8 E4M3 KV cache (xonoai.com field report on vLLM v0.7.2,
+"Comparative Inference Engine Performance": 256 concurrent 8k-token streams of the 70B
+model on 8 GPUs). Inputs are resident in HBM before the timed region; the pool is kept in
+several copies, rotated step by step, so that no step finds its KV in the 256 MB
+Infinity Cache left warm by the step before.
+
+Prints one JSON line: value = algorithmic bytes of the step / step time (GB/s), plus the
+decode kernel's roofline (its algorithmic bytes / its average launch time from HIP events
+on the launch stream) and the oracle's rate on the host cores (cpu_baseline).
+
+    python bench.py [--steps K] [--warmup W] [--config c4] [--partition-size PS]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "paged decode attention: achieved KV-read GB/s (% HBM peak) + seq-tokens/s"
+KERNEL_SOURCES = ["paged_quantized_kv_reshape_amd/csrc/pa_decode.hip",
+                  "paged_quantized_kv_reshape_amd/csrc/pa_device.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(cfg: str, ps: int):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary of this
+    workload, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"k_decode_{cfg}_ps{ps}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = re.search(r"kernel_source_sha256:\s*(\w+)", text)
+    tb = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not tb or src.group(1) != kernel_source_hash():
+        return None
+    return float(tb.group(1))
+
+
+def cpu_baseline(w, budget_s: float, decode_b_per_token: float):
+    """The oracle (fp64 NumPy, unmodified) on a bounded sample of the same workload: the
+    cache-write replay of a few whole sequences (every write call of setup and step,
+    restricted to their blocks) and their exact decode, one BLAS thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as A
+    from oracle import cache as C
+
+    with threadpool_limits(limits=1):
+        ks = vs = None
+        if w.kv == "fp8":  # inputs of the method (per-head scales), not timed
+            ks = C.fp8_head_scale(w.k_rows, w.act)
+            vs = C.fp8_head_scale(w.v_rows, w.act)
+        pool = C.Pool.filled(w.kv, w.num_blocks, w.num_kv_heads, w.head_dim)
+        calls = list(w.setup_calls) + [w.step_call]
+        blk_of_call = [c.slots // 16 for c in calls]
+
+        def run(seqs):
+            blocks = set()
+            for s in seqs:
+                n = -(-int(w.context_lens[s]) // 16)
+                blocks.update(int(b) for b in w.block_tables[s, :n])
+            keep = np.asarray(sorted(blocks))
+            for c, blk in zip(calls, blk_of_call):
+                sel = np.isin(blk, keep)
+                if sel.any():
+                    C.cache_write(pool, w.k_rows[c.rows[sel]], w.v_rows[c.rows[sel]], w.act,
+                                  c.slots[sel], ks, vs)
+            A.paged_decode(w.q, w.act, pool, w.block_tables, w.context_lens, w.sm_scale, ks,
+                           vs, partition_size=w.partition_size, seqs=seqs)
+
+        order = list(range(w.num_seqs))
+        t0 = time.perf_counter()
+        run(order[:1])
+        t1 = time.perf_counter() - t0
+        n = max(1, min(w.num_seqs - 1, int(budget_s / max(t1, 1e-3))))
+        sample = order[1:1 + n]
+        t0 = time.perf_counter()
+        run(sample)
+        dt = time.perf_counter() - t0
+    tokens = int(sum(int(w.context_lens[s]) for s in sample))
+    gbs = tokens * decode_b_per_token / dt / 1e9
+    return {"value": round(gbs, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 2), "seq_tokens_per_s": round(tokens / dt, 1),
+            "sample": (f"{len(sample)} of {w.num_seqs} sequences ({tokens} KV tokens): replay of "
+                       f"every cache-write call into their blocks, then exact fp64 decode "
+                       f"(+ partitions) of the sequences; bytes counted as for the GPU step")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c4", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="override the workload's split (0 = one pass per sequence)")
+    ap.add_argument("--copies", type=int, default=3, help="pool copies rotated across steps")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the decode path needs no collective and this build "
+              "runs on a single MI355X; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from paged_quantized_kv_reshape_amd import harness as H
+    from workload import DESCRIPTIONS, config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    print(f"[bench] generating {args.config}", file=sys.stderr, flush=True)
+    w = config(args.config)
+    ps = w.partition_size if args.partition_size is None else args.partition_size
+    w.partition_size = ps
+    run = H.DeviceRun(w, device="cuda", partition_size=ps, pool_copies=args.copies)
+    run.prepare()
+    torch.cuda.synchronize()
+    if run.device_error():
+        raise SystemExit(f"device error after setup: {run.device_error()}")
+    counts = H.outlier_counts(run) if w.kv == "fp4" else None
+    dec = H.decode_bytes(w, counts)
+    step_tokens = len(w.step_call.rows)
+    wr = H.write_bytes(w, step_tokens)
+    step_bytes = dec["total"] + wr
+    print(f"[bench] {w.num_seqs} seqs, {dec['tokens']} tokens, ps={ps}, decode bytes "
+          f"{dec['total']}, write bytes {wr}", file=sys.stderr, flush=True)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.bitwise_not(src, out=dst)  # one elementwise kernel: n bytes read, n written
+        torch.cuda.synchronize()
+        print(f"[bench] copy probe: {n} bytes read + {n} written", file=sys.stderr, flush=True)
+        del src, dst
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        run.step(run.pools[i % args.copies])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        pool = run.pools[(args.warmup + i) % args.copies]
+        e = ev[i]
+        e[0].record(stream)
+        run.step_write(pool)
+        e[1].record(stream)
+        run.decode(pool, merge=False)
+        e[2].record(stream)
+        run.merge()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    err = run.device_error()
+    out = run.out.cpu().numpy()
+    if err or not np.isfinite(out).all():
+        raise SystemExit(f"bench run failed: device error {err}, finite {np.isfinite(out).all()}")
+
+    t_write = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    t_dec = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    t_merge = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) * 1e-3
+    t_step = wall / K
+    dec_gbs = dec["total"] / t_dec / 1e9
+    value = step_bytes / t_step / 1e9
+    traffic = counter_traffic(args.config, ps)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: {DESCRIPTIONS[args.config]}",
+                   "kv_cache_dtype": w.kv, "num_seqs": w.num_seqs,
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": 16, "kv_tokens": dec["tokens"],
+                   "partition_size": ps, "step_write_tokens": step_tokens,
+                   "pool_copies": args.copies},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "seq_tokens_per_s": round(dec["tokens"] / t_step, 1),
+        "decode_tokens_per_s": round(w.num_seqs / t_step, 1),
+        "step_bytes": step_bytes,
+        "kernel_ms": {"cache_write": round(t_write * 1e3, 4), "decode": round(t_dec * 1e3, 4),
+                      "merge": round(t_merge * 1e3, 4)},
+        "roofline": {"kernel": "k_decode", "bound": "hbm", "achieved": round(dec_gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes": dec["total"],
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds,
+                                           dec["total"] / max(dec["tokens"], 1))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

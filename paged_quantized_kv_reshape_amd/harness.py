@@ -73,11 +73,15 @@ class DeviceRun:
             self.step_write(p)
 
     # -- decode ---------------------------------------------------------------------
-    def decode(self, pool=None):
+    def decode(self, pool=None, merge=True):
         pool = pool or self.pool
         B.pa_decode(self.q, pool, self.block_tables, self.context_lens, self.w.sm_scale,
                     self.ps, out=self.out, part_out=self.part_out, part_lse=self.part_lse,
                     dev_err=self.dev_err)
+        if merge:
+            self.merge()
+
+    def merge(self):
         if self.ps:
             B.pa_merge(self.part_out, self.part_lse, self.context_lens, self.ps, self.out,
                        self.lse)
@@ -89,3 +93,54 @@ class DeviceRun:
 
     def device_error(self) -> int:
         return B.pa_read_device_error(self.dev_err)
+
+
+# ---------------------------------------------------------------------------------
+# Algorithmic bytes: what the method itself must move, not what a kernel happens to fetch.
+# ---------------------------------------------------------------------------------
+_KV_ELEM_BITS = {"f16": 16, "bf16": 16, "fp8": 8, "fp4": 4}
+
+
+def outlier_counts(run) -> dict:
+    """FP4 only: total outlier channels over all written (block, kv head) records, K and V
+    (read from the device pool's records; 0xFF = never written counts 0)."""
+    out = {}
+    for side in ("k", "v"):
+        rec = run.pool.bytes[side + "_out_idx"].view(-1, 16)[:, 0].to(torch.int32)
+        out[side] = int(torch.where(rec == 0xFF, torch.zeros_like(rec), rec).sum().item())
+    return out
+
+
+def decode_bytes(w, outliers=None) -> dict:
+    """Algorithmic bytes of one pa_decode (+ merge) over workload w: every stored K/V byte
+    of every attended token read once (codes; FP4 also the per-token scales, the 16-byte
+    record of each (block, kv head) and its fp16 outlier values), the block-table entries
+    of the attended blocks, the context lengths, q (16-bit) and out (fp32)."""
+    L = w.context_lens.astype(np.int64)
+    hkv, d, S, hq = w.num_kv_heads, w.head_dim, w.num_seqs, w.num_q_heads
+    tok = int(L.sum())
+    blocks = int((-(-L // 16)).sum())
+    kv = 2 * tok * hkv * d * _KV_ELEM_BITS[w.kv] // 8
+    extra = 0
+    if w.kv == "fp4":
+        extra += 2 * tok * hkv * 4            # per-token fp32 scales, K and V
+        extra += 2 * blocks * hkv * 16        # outlier records
+        if outliers is not None:              # fp16 values of every outlier channel
+            extra += (outliers["k"] + outliers["v"]) * 16 * 2
+    if w.kv == "fp8":
+        extra += 2 * hkv * 4                  # per-head scales
+    meta = blocks * 4 + S * 4
+    io = S * hq * d * 2 + S * hq * d * 4
+    return {"kv": kv + extra, "meta": meta, "io": io, "total": kv + extra + meta + io,
+            "tokens": tok, "blocks": blocks}
+
+
+def write_bytes(w, num_tokens: int) -> int:
+    """Algorithmic bytes of one pa_cache_write of num_tokens rows: read the new K and V
+    rows and their slots, store the encoded rows (FP4 also the per-token scales)."""
+    hkv, d = w.num_kv_heads, w.head_dim
+    rd = num_tokens * (2 * hkv * d * 2 + 8)
+    wr = 2 * num_tokens * hkv * d * _KV_ELEM_BITS[w.kv] // 8
+    if w.kv == "fp4":
+        wr += 2 * num_tokens * hkv * 4
+    return rd + wr
