@@ -36,6 +36,57 @@ KERNEL_SOURCES = ["paged_quantized_kv_reshape_amd/csrc/pa_decode.hip",
                   "paged_quantized_kv_reshape_amd/csrc/pa_device.h"]
 
 
+class HipTimer:
+    """HIP timing events created with hipEventReleaseToDevice, recorded on a given stream.
+    A default event performs a system-scope release when it is recorded (cache write-back
+    and invalidation), which adds microseconds between the kernels it brackets; a
+    device-scope release is enough for timing. The events come from the HIP runtime
+    already loaded in this process (the one torch and libpa share)."""
+
+    FLAGS = 0x40000000  # hipEventReleaseToDevice
+
+    def __init__(self):
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64.so" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded")
+        self.ct = ctypes
+        self.hip = ctypes.CDLL(path)
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def event(self):
+        e = self.ct.c_void_p()
+        if self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.FLAGS) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self.events.append(e)
+        return e
+
+    def record(self, e, stream: int):
+        if self.hip.hipEventRecord(e, self.ct.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b) -> float:
+        t = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(t), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return t.value
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -168,35 +219,62 @@ def main():
         print(f"[bench] copy probe: {n} bytes read + {n} written", file=sys.stderr, flush=True)
         del src, dst
 
-    stream = torch.cuda.current_stream()
+    # every libpa call goes on torch's current stream; the events are recorded on it too
+    stream = torch.cuda.current_stream().cuda_stream
     for i in range(args.warmup):
         run.step(run.pools[i % args.copies])
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    timer = HipTimer()
+
+    def pool_of(i):
+        return run.pools[(args.warmup + i) % args.copies]
+
+    # (1) the timed region: K whole steps, events only at step boundaries
+    bounds = [timer.event() for _ in range(K + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        pool = run.pools[(args.warmup + i) % args.copies]
-        e = ev[i]
-        e[0].record(stream)
-        run.step_write(pool)
-        e[1].record(stream)
-        run.decode(pool, merge=False)
-        e[2].record(stream)
-        run.merge()
-        e[3].record(stream)
+        timer.record(bounds[i], stream)
+        run.step(pool_of(i))
+    timer.record(bounds[K], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    t_step_ev = timer.ms(bounds[0], bounds[K]) * 1e-3 / K
     err = run.device_error()
     out = run.out.cpu().numpy()
     if err or not np.isfinite(out).all():
         raise SystemExit(f"bench run failed: device error {err}, finite {np.isfinite(out).all()}")
 
-    t_write = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
-    t_dec = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
-    t_merge = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) * 1e-3
+    # (2) per-kernel attribution: the same K steps with an event around every kernel (each
+    # bracket also holds the runtime's dispatch latency, a few microseconds)
+    ev = [[timer.event() for _ in range(4)] for _ in range(K)]
+    for i in range(K):
+        e = ev[i]
+        timer.record(e[0], stream)
+        run.step_write(pool_of(i))
+        timer.record(e[1], stream)
+        run.decode(pool_of(i), merge=False)
+        timer.record(e[2], stream)
+        run.merge()
+        timer.record(e[3], stream)
+    # (3) the dominant kernel's launch duration: K decode launches back to back (same
+    # pools, same stream) between one pair of events, so no marker sits between them
+    burst = [timer.event(), timer.event()]
+    timer.record(burst[0], stream)
+    for i in range(K):
+        run.decode(pool_of(i), merge=False)
+    timer.record(burst[1], stream)
+    torch.cuda.synchronize()
+    t_write = float(np.mean([timer.ms(e[0], e[1]) for e in ev])) * 1e-3
+    t_dec_br = float(np.mean([timer.ms(e[1], e[2]) for e in ev])) * 1e-3
+    t_merge = float(np.mean([timer.ms(e[2], e[3]) for e in ev])) * 1e-3
+    t_dec = timer.ms(burst[0], burst[1]) * 1e-3 / K
+    timer.close()
+    if run.device_error():
+        raise SystemExit(f"device error during timing: {run.device_error()}")
+
     t_step = wall / K
     dec_gbs = dec["total"] / t_dec / 1e9
     value = step_bytes / t_step / 1e9
@@ -225,8 +303,11 @@ def main():
         "seq_tokens_per_s": round(dec["tokens"] / t_step, 1),
         "decode_tokens_per_s": round(w.num_seqs / t_step, 1),
         "step_bytes": step_bytes,
-        "kernel_ms": {"cache_write": round(t_write * 1e3, 4), "decode": round(t_dec * 1e3, 4),
-                      "merge": round(t_merge * 1e3, 4)},
+        "kernel_ms": {"decode": round(t_dec * 1e3, 4),
+                      "bracketed": {"cache_write": round(t_write * 1e3, 4),
+                                    "decode": round(t_dec_br * 1e3, 4),
+                                    "merge": round(t_merge * 1e3, 4)},
+                      "step_events": round(t_step_ev * 1e3, 4)},
         "roofline": {"kernel": "k_decode", "bound": "hbm", "achieved": round(dec_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),

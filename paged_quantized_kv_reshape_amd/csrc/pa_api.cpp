@@ -50,6 +50,15 @@ bool act_matches_pool(int32_t act, int32_t kv) {
   return true;
 }
 
+// Compute units of the current device (256 on MI355X if the query fails).
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return 256;
+  return n;
+}
+
 int env_int(const char* name, int fallback) {
   const char* s = getenv(name);
   if (!s || !*s) return fallback;
@@ -201,10 +210,17 @@ int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
   a.cap = pa::outlier_capacity(pool->head_dim);
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
 
-  // Waves per workgroup: enough to split a partition's blocks a few ways, at most 4.
+  // Waves per workgroup. The decode streams K/V tiles from HBM; on MI355X the gather of
+  // random 16-token tiles runs fastest with about 8 resident waves per compute unit, each
+  // walking a long run of blocks (more waves only add DRAM row conflicts, fewer leave
+  // HBM idle). So pick the smallest power of two W <= 8 that brings the grid to
+  // 8 waves per CU, without giving a wave fewer than one block of its partition.
   const int64_t span = partition_size > 0 ? partition_size : cap_tokens;
   const int64_t blocks = (span + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
-  int waves = blocks >= 64 ? 4 : blocks >= 16 ? 2 : 1;
+  const int64_t wgs = (int64_t)num_seqs * pool->num_kv_heads * max_part;
+  const int64_t target_waves = 8 * (int64_t)device_cus();
+  int waves = 1;
+  while (waves < 8 && wgs * waves < target_waves && blocks >= 2 * waves) waves *= 2;
   const int forced = env_int("PA_DECODE_WAVES", 0);
   if (forced == 1 || forced == 2 || forced == 4 || forced == 8) waves = forced;
   return pa::launch_decode(a, pool->dtype, q_dtype == PA_ACT_BF16, pool->head_dim, waves,

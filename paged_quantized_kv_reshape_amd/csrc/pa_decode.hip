@@ -42,7 +42,19 @@ namespace pa {
 enum { KV_F16 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_FP4 = 3 };
 
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
-constexpr int kPrefetch = 2;      // blocks in flight per wave beyond the one in use
+#ifndef PA_DECODE_CONTIG
+#define PA_DECODE_CONTIG 0
+#endif
+#ifndef PA_DECODE_PREFETCH
+#define PA_DECODE_PREFETCH 0  // 0: the per-format depth below
+#endif
+// Tiles held in registers per wave. Measured on MI355X: one is best for the 2-4 KB tiles
+// of the 16-bit and FP8 formats (more only costs registers; other waves hide the
+// latency), two for the smaller FP4 tiles.
+template <int KV>
+constexpr int prefetch_depth() {
+  return PA_DECODE_PREFETCH > 0 ? PA_DECODE_PREFETCH : (KV == KV_FP4 ? 2 : 1);
+}
 
 template <int KV, int D>
 struct Geo {
@@ -103,6 +115,8 @@ struct Tile {
   uint32_t v[4][G_::VW];
   float4 sk, sv;  // FP4 per-token scales of tokens 4 kg .. 4 kg + 3
   uint4 rk, rv;   // FP4 outlier records
+  uint2 k_o0, v_o0;  // FP4 outlier slot 0 of tokens 4 kg .. 4 kg + 3 (fp16), fetched with
+                     // the tile since a full block usually holds exactly one outlier
   int64_t tile;   // b * Hkv + kv head
   int jb;         // logical block index in the sequence
   bool ok;        // block id in range
@@ -209,7 +223,17 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   const int end = split ? min(start + a.partition_size, L) : L;
   const int jb0 = start / kBlock;
   const int nblk = (end + kBlock - 1) / kBlock - jb0;
+#if PA_DECODE_CONTIG
+  // wave w takes the contiguous run of blocks [w * nblk / W, (w + 1) * nblk / W)
+  const int my_lo = (int)((int64_t)wave * nblk / W);
+  const int my_n = (int)((int64_t)(wave + 1) * nblk / W) - my_lo;
+  constexpr int kStep = 1;
+#else
+  // wave w takes blocks w, w + W, w + 2W, ...
+  const int my_lo = wave;
   const int my_n = wave < nblk ? (nblk - wave + W - 1) / W : 0;
+  const int kStep = W;
+#endif
 
   // ---- query fragments (B operand of S^T = K Q^T), zero for padded heads ----
   uint4 qf[KS];
@@ -241,10 +265,10 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   if constexpr (KV == KV_FP8) cz *= a.k_scale[kvh];
 
   // ---- block ids: 64 of this wave's blocks per register, two registers ahead ----
-  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks + jb0 + wave;
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks + jb0 + my_lo;
   auto load_ids = [&](int chunk) -> int {
     const int x = chunk * 64 + lane;
-    return x < my_n ? bt[(int64_t)x * W] : 0;
+    return x < my_n ? bt[(int64_t)x * kStep] : 0;
   };
   int ids_a = load_ids(0), ids_b = load_ids(1);
 
@@ -259,7 +283,7 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
       ids_b = load_ids((x >> 6) + 1);
     }
     int b = __builtin_amdgcn_readlane(ids_a, x & 63);
-    T.jb = jb0 + wave + x * W;
+    T.jb = jb0 + my_lo + x * kStep;
     T.ok = (unsigned)b < (unsigned)a.num_blocks;
     if (!T.ok) {
       if (lane == 0 && a.err) atomicOr(a.err, PA_DEVERR_BAD_BLOCK);
@@ -275,6 +299,10 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
       T.sv = reinterpret_cast<const float4*>(a.v_tok_scale + T.tile * kBlock)[kg];
       T.rk = *reinterpret_cast<const uint4*>(a.k_out_idx + T.tile * 16);
       T.rv = *reinterpret_cast<const uint4*>(a.v_out_idx + T.tile * 16);
+      // slot 0 always exists (capacity >= 1); its bytes are used only if the record's
+      // count is at least 1
+      T.k_o0 = *reinterpret_cast<const uint2*>(a.k_out_val + T.tile * a.cap * kBlock + 4 * kg);
+      T.v_o0 = *reinterpret_cast<const uint2*>(a.v_out_val + T.tile * a.cap * kBlock + 4 * kg);
     }
   };
 
@@ -317,8 +345,9 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
         const int pos = 1 + j;
         const int ch = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
         const float qv = q_lds[c * D + ch];
-        const uint2 ov = *reinterpret_cast<const uint2*>(
-            a.k_out_val + ((T.tile * a.cap + j) * kBlock + 4 * kg));
+        const uint2 ov = j == 0 ? T.k_o0
+                                : *reinterpret_cast<const uint2*>(
+                                      a.k_out_val + ((T.tile * a.cap + j) * kBlock + 4 * kg));
         ok[0] = __builtin_fmaf(qv, f16_bits_to_f32(ov.x & 0xFFFFu), ok[0]);
         ok[1] = __builtin_fmaf(qv, f16_bits_to_f32(ov.x >> 16), ok[1]);
         ok[2] = __builtin_fmaf(qv, f16_bits_to_f32(ov.y & 0xFFFFu), ok[2]);
@@ -384,8 +413,9 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
       for (int j = 0; j < nv; ++j) {
         const int pos = 1 + j;
         const int ch = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
-        const uint2 ov = *reinterpret_cast<const uint2*>(
-            a.v_out_val + ((T.tile * a.cap + j) * kBlock + 4 * kg));
+        const uint2 ov = j == 0 ? T.v_o0
+                                : *reinterpret_cast<const uint2*>(
+                                      a.v_out_val + ((T.tile * a.cap + j) * kBlock + 4 * kg));
         const float o4[4] = {f16_bits_to_f32(ov.x & 0xFFFFu), f16_bits_to_f32(ov.x >> 16),
                              f16_bits_to_f32(ov.y & 0xFFFFu), f16_bits_to_f32(ov.y >> 16)};
         float part = 0.0f;
@@ -407,6 +437,7 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   };
 
   // ---- block loop, kPrefetch tiles in flight ----
+  constexpr int kPrefetch = prefetch_depth<KV>();
   Tile<KV, D> tiles[kPrefetch];
 #pragma unroll
   for (int k = 0; k < kPrefetch; ++k)

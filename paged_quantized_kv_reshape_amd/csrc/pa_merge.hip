@@ -6,54 +6,89 @@
 // merge is exact: out = sum_p exp(lse_p - M) o_p / sum_p exp(lse_p - M), M = max_p lse_p,
 // and the merged lse = M + ln sum_p exp(lse_p - M).
 //
-// One wave per (sequence, query head); lane l owns channels {l, l + 64} (D = 128) or {l}
-// (D = 64). The partitions' outputs are read once each, coalesced.
+// One workgroup of W waves per (sequence, query head). Wave w folds partitions w, w + W,
+// ... into (M_w, sum_w, acc_w) with its own maximum M_w (lane l owns channels l and
+// l + 64, so each partition's row is one coalesced read); the W partial states are then
+// combined through LDS. A long context (hundreds of partitions) is thus read by W waves
+// in parallel instead of one, which keeps the merge bandwidth-bound.
 #include "pa_device.h"
 #include "pa_launch.h"
 
 namespace pa {
 
 template <int D>
-__global__ __launch_bounds__(256) void k_merge(const float* __restrict__ po,
+__global__ __launch_bounds__(512) void k_merge(const float* __restrict__ po,
                                                const float* __restrict__ pl,
-                                               const int32_t* __restrict__ cl, int32_t S,
-                                               int32_t Hq, int32_t P, int32_t ps,
+                                               const int32_t* __restrict__ cl, int32_t Hq,
+                                               int32_t P, int32_t ps,
                                                float* __restrict__ out,
                                                float* __restrict__ lse_out) {
   constexpr int CPL = D / 64;
+  __shared__ float s_m[8], s_w[8];
+  __shared__ float s_acc[8][D];
   const int lane = threadIdx.x & 63;
-  const int64_t sh = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (sh >= (int64_t)S * Hq) return;
+  const int wave = threadIdx.x >> 6;
+  const int W = blockDim.x >> 6;
+  const int64_t sh = blockIdx.x;  // s * Hq + h
   const int s = (int)(sh / Hq);
   const int L = cl[s];
   const int np = L >= 1 ? min((L + ps - 1) / ps, P) : 0;
   float* o = out + sh * D;
   if (np == 0) {
+    if (wave == 0) {
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) o[lane + 64 * k] = 0.0f;
-    if (lse_out && lane == 0) lse_out[sh] = -INFINITY;
+      for (int k = 0; k < CPL; ++k) o[lane + 64 * k] = 0.0f;
+      if (lse_out && lane == 0) lse_out[sh] = -INFINITY;
+    }
     return;
   }
   const float* lse = pl + sh * P;
-  float M = -INFINITY;
-  for (int p = lane; p < np; p += 64) M = fmaxf(M, lse[p]);
-  M = wave_max(M);
+  float m = -INFINITY;
+  for (int p = wave + W * lane; p < np; p += 64 * W) m = fmaxf(m, lse[p]);
+  m = wave_max(m);
   float acc[CPL], wsum = 0.0f;
 #pragma unroll
   for (int k = 0; k < CPL; ++k) acc[k] = 0.0f;
   const float* base = po + sh * (int64_t)P * D;
 #pragma unroll 4
-  for (int p = 0; p < np; ++p) {
+  for (int p = wave; p < np; p += W) {
     const float x = lse[p];
-    const float w = x == -INFINITY ? 0.0f : __expf(x - M);
+    const float w = x == -INFINITY ? 0.0f : __expf(x - m);
     wsum += w;
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) acc[k] = __builtin_fmaf(w, base[(int64_t)p * D + lane + 64 * k], acc[k]);
+    for (int k = 0; k < CPL; ++k)
+      acc[k] = __builtin_fmaf(w, base[(int64_t)p * D + lane + 64 * k], acc[k]);
   }
-  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  if (W == 1) {
+    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
 #pragma unroll
-  for (int k = 0; k < CPL; ++k) o[lane + 64 * k] = acc[k] * inv;
-  if (lse_out && lane == 0) lse_out[sh] = M + __logf(wsum);
+    for (int k = 0; k < CPL; ++k) o[lane + 64 * k] = acc[k] * inv;
+    if (lse_out && lane == 0) lse_out[sh] = m + __logf(wsum);
+    return;
+  }
+  if (lane == 0) {
+    s_m[wave] = m;  // -inf for a wave that saw no partition
+    s_w[wave] = wsum;
+  }
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) s_acc[wave][lane + 64 * k] = acc[k];
+  __syncthreads();
+  if (wave != 0) return;
+  float M = -INFINITY;
+  for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w]);
+  float tot = 0.0f, o_acc[CPL];
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) o_acc[k] = 0.0f;
+  for (int w = 0; w < W; ++w) {
+    const float f = s_m[w] == -INFINITY ? 0.0f : __expf(s_m[w] - M);
+    tot += f * s_w[w];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) o_acc[k] = __builtin_fmaf(f, s_acc[w][lane + 64 * k], o_acc[k]);
+  }
+  const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) o[lane + 64 * k] = o_acc[k] * inv;
+  if (lse_out && lane == 0) lse_out[sh] = M + __logf(tot);
 }
 
 int launch_merge(const float* part_out, const float* part_lse, const int32_t* context_lens,
@@ -61,13 +96,16 @@ int launch_merge(const float* part_out, const float* part_lse, const int32_t* co
                  float* lse_out, hipStream_t st) {
   const int64_t pairs = (int64_t)S * Hq;
   if (pairs == 0) return PA_OK;
-  const dim3 grid((unsigned)((pairs + 3) / 4));
+  // about 16 partitions per wave, 1..8 waves
+  int waves = 1;
+  while (waves < 8 && P > 16 * waves) waves *= 2;
+  const dim3 grid((unsigned)pairs);
   if (D == 128)
-    hipLaunchKernelGGL(k_merge<128>, grid, dim3(256), 0, st, part_out, part_lse, context_lens, S,
-                       Hq, P, ps, out, lse_out);
+    hipLaunchKernelGGL(k_merge<128>, grid, dim3(64 * waves), 0, st, part_out, part_lse,
+                       context_lens, Hq, P, ps, out, lse_out);
   else
-    hipLaunchKernelGGL(k_merge<64>, grid, dim3(256), 0, st, part_out, part_lse, context_lens, S,
-                       Hq, P, ps, out, lse_out);
+    hipLaunchKernelGGL(k_merge<64>, grid, dim3(64 * waves), 0, st, part_out, part_lse,
+                       context_lens, Hq, P, ps, out, lse_out);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -69,7 +69,7 @@ def test_cache_write_bit_exact(cfg):
     assert run.device_error() == 0
 
 
-@pytest.mark.parametrize("waves", [1, 2, 4])
+@pytest.mark.parametrize("waves", [1, 2, 4, 8])
 @pytest.mark.parametrize("ps", [0, 64, 512])
 @pytest.mark.parametrize("cfg", list(SMALL))
 def test_decode_matches_oracle(cfg, ps, waves):

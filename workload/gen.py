@@ -207,7 +207,7 @@ CONFIGS = {
                act="bf16", lens_range=(1024, 8192), planted=True, step_tokens=8,
                partition_size=512),
     "c4": dict(seed=3, num_seqs=256, num_q_heads=8, num_kv_heads=1, head_dim=128, kv="fp8",
-               act="bf16", lens=[8192] * 256, planted=True, partition_size=512),
+               act="bf16", lens=[8192] * 256, planted=True, partition_size=0),
     "c5": dict(seed=4, num_seqs=32, num_q_heads=8, num_kv_heads=1, head_dim=128, kv="fp4",
                act="bf16", lens_range=(65536, 122880), planted=True, prefill_chunk=512,
                partition_size=512),
