@@ -170,6 +170,8 @@ int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
   const int64_t cap_tokens = (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE;
   const int max_part =
       partition_size > 0 ? (int)((cap_tokens + partition_size - 1) / partition_size) : 1;
+  // the launch grid's x dimension counts (partition, kv head) pairs
+  if ((int64_t)max_part * pool->num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
   if (partition_size == 0) {
     if (!out) return PA_ERR_NULL;
     if (!aligned(out, 16)) return PA_ERR_ALIGN;
@@ -210,15 +212,19 @@ int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
   a.cap = pa::outlier_capacity(pool->head_dim);
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
 
-  // Waves per workgroup. The decode streams K/V tiles from HBM; on MI355X the gather of
-  // random 16-token tiles runs fastest with about 8 resident waves per compute unit, each
-  // walking a long run of blocks (more waves only add DRAM row conflicts, fewer leave
-  // HBM idle). So pick the smallest power of two W <= 8 that brings the grid to
-  // 8 waves per CU, without giving a wave fewer than one block of its partition.
+  // Waves per workgroup. The decode streams K/V tiles from HBM. Measured on MI355X: with
+  // one kv head the gather of random 16-token tiles runs fastest with about 8 waves per
+  // compute unit in the grid, each walking a long run of blocks (more waves only open
+  // more DRAM rows at once); with several kv heads the workgroups of one block's heads
+  // run side by side and read neighbouring tiles, and about 8 waves per CU per kv head
+  // (up to 8 heads) keeps those reads together. So pick the smallest power of two
+  // W <= 8 that brings the grid to that many waves, without giving a wave fewer than two
+  // blocks of its partition.
   const int64_t span = partition_size > 0 ? partition_size : cap_tokens;
   const int64_t blocks = (span + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
   const int64_t wgs = (int64_t)num_seqs * pool->num_kv_heads * max_part;
-  const int64_t target_waves = 8 * (int64_t)device_cus();
+  const int64_t heads = pool->num_kv_heads < 8 ? pool->num_kv_heads : 8;
+  const int64_t target_waves = 8 * heads * (int64_t)device_cus();
   int waves = 1;
   while (waves < 8 && wgs * waves < target_waves && blocks >= 2 * waves) waves *= 2;
   const int forced = env_int("PA_DECODE_WAVES", 0);

@@ -42,18 +42,21 @@ namespace pa {
 enum { KV_F16 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_FP4 = 3 };
 
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
+#ifndef PA_GRID_HEAD_FAST
+#define PA_GRID_HEAD_FAST 1
+#endif
 #ifndef PA_DECODE_CONTIG
 #define PA_DECODE_CONTIG 0
 #endif
 #ifndef PA_DECODE_PREFETCH
 #define PA_DECODE_PREFETCH 0  // 0: the per-format depth below
 #endif
-// Tiles held in registers per wave. Measured on MI355X: one is best for the 2-4 KB tiles
-// of the 16-bit and FP8 formats (more only costs registers; other waves hide the
-// latency), two for the smaller FP4 tiles.
+// Tiles held in registers per wave. Measured on MI355X: one is best for every format;
+// a second costs a tile's worth of registers, hence resident waves, and the other waves
+// of the compute unit hide the load latency better than the wave itself can.
 template <int KV>
 constexpr int prefetch_depth() {
-  return PA_DECODE_PREFETCH > 0 ? PA_DECODE_PREFETCH : (KV == KV_FP4 ? 2 : 1);
+  return PA_DECODE_PREFETCH > 0 ? PA_DECODE_PREFETCH : 1;
 }
 
 template <int KV, int D>
@@ -114,7 +117,7 @@ struct Tile {
   uint32_t k[G_::KW];
   uint32_t v[4][G_::VW];
   float4 sk, sv;  // FP4 per-token scales of tokens 4 kg .. 4 kg + 3
-  uint4 rk, rv;   // FP4 outlier records
+  uint4 rk, rv;   // FP4 outlier records (wave-uniform: scalar registers)
   uint2 k_o0, v_o0;  // FP4 outlier slot 0 of tokens 4 kg .. 4 kg + 3 (fp16), fetched with
                      // the tile since a full block usually holds exactly one outlier
   int64_t tile;   // b * Hkv + kv head
@@ -191,8 +194,17 @@ __device__ __forceinline__ void v_fragments(const Tile<KV, D>& T, uint2 (&vf)[Ge
   }
 }
 
+#ifndef PA_WAVES_PER_EU
+#define PA_WAVES_PER_EU 0
+#endif
+#if PA_WAVES_PER_EU > 0
+#define PA_DECODE_ATTR __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU)))
+#else
+#define PA_DECODE_ATTR
+#endif
+
 template <int KV, int D, bool QBF>
-__global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
+__global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
   using G_ = Geo<KV, D>;
   constexpr int KS = G_::KS, NT = G_::NT, DL = G_::DL;
   constexpr bool PVB = QBF || KV == KV_FP4;  // PV MFMA in bf16 (else fp16)
@@ -203,7 +215,15 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   const int W = blockDim.x >> 6;
   const int c = lane & 15;  // MFMA column: query head (QK, PV); K row token; V channel group
   const int kg = lane >> 4;
+#if PA_GRID_HEAD_FAST
+  // grid.x = kv head fastest, then partition: the workgroups of one block's kv heads run
+  // side by side and read neighbouring tiles ([block][kv head][16][D] is contiguous)
+  const int kvh = (int)(blockIdx.x % (unsigned)a.num_kv_heads);
+  const int p = (int)(blockIdx.x / (unsigned)a.num_kv_heads);
+  const int s = blockIdx.y;
+#else
   const int p = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+#endif
   const int G = a.group;
   const int Hq = a.num_q_heads;
 
@@ -259,6 +279,17 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
     }
     __syncthreads();
   }
+  // FP4 only: this wave's side accumulator of the V-outlier terms, [D channels][16 heads]
+  // fp32. The outlier channel of a block is known only at run time, and a run-time
+  // index into the accumulator registers would cost a copy of all of them per case; so
+  // the terms are summed here and folded into the registers at the end (and before a
+  // rescale, which must scale both).
+  float* side = smem + 16 * D + (int64_t)wave * D * 16;
+  if constexpr (KV == KV_FP4) {
+#pragma unroll
+    for (int i = lane; i < D * 16 / 4; i += 64)
+      reinterpret_cast<float4*>(side)[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
 
   // ---- scale of the logits (base 2) ----
   float cz = a.sm_scale_log2;
@@ -282,13 +313,14 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
       ids_a = ids_b;
       ids_b = load_ids((x >> 6) + 1);
     }
-    int b = __builtin_amdgcn_readlane(ids_a, x & 63);
+    const int b_raw = __builtin_amdgcn_readlane(ids_a, x & 63);
     T.jb = jb0 + my_lo + x * kStep;
-    T.ok = (unsigned)b < (unsigned)a.num_blocks;
-    if (!T.ok) {
-      if (lane == 0 && a.err) atomicOr(a.err, PA_DEVERR_BAD_BLOCK);
-      b = 0;
-    }
+    T.ok = (unsigned)b_raw < (unsigned)a.num_blocks;
+    if (!T.ok && lane == 0 && a.err) atomicOr(a.err, PA_DEVERR_BAD_BLOCK);
+    // readfirstlane pins the id as wave-uniform, so the tile addresses below are
+    // computed in scalar registers (the lane-0 branch above would otherwise turn the
+    // substituted id into a per-lane value)
+    const int b = __builtin_amdgcn_readfirstlane(T.ok ? b_raw : 0);
     T.tile = (int64_t)b * a.num_kv_heads + kvh;
     load_words(T.k, kpool + T.tile * G_::TILEB + k_lane_off);
 #pragma unroll
@@ -297,8 +329,9 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
     if constexpr (KV == KV_FP4) {
       T.sk = reinterpret_cast<const float4*>(a.k_tok_scale + T.tile * kBlock)[kg];
       T.sv = reinterpret_cast<const float4*>(a.v_tok_scale + T.tile * kBlock)[kg];
-      T.rk = *reinterpret_cast<const uint4*>(a.k_out_idx + T.tile * 16);
-      T.rv = *reinterpret_cast<const uint4*>(a.v_out_idx + T.tile * 16);
+      // the records are wave-uniform and read-only while decoding: scalar loads
+      T.rk = load_uniform16(a.k_out_idx + T.tile * 16);
+      T.rv = load_uniform16(a.v_out_idx + T.tile * 16);
       // slot 0 always exists (capacity >= 1); its bytes are used only if the record's
       // count is at least 1
       T.k_o0 = *reinterpret_cast<const uint2*>(a.k_out_val + T.tile * a.cap * kBlock + 4 * kg);
@@ -312,6 +345,20 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   f32x4 acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // add the side accumulator into acc (lane (c, kg) holds channel DL kg + NT r + n of
+  // head c in acc[n][r]) and clear it
+  auto fold_side = [&]() {
+    if constexpr (KV == KV_FP4) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float* e = side + (DL * kg + NT * r + n) * 16 + c;
+          acc[n][r] += *e;
+          *e = 0.0f;
+        }
+    }
+  };
 
   auto compute = [&](Tile<KV, D>& T) {
     const int tok0 = T.jb * kBlock + 4 * kg;
@@ -334,13 +381,15 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
     if constexpr (KV == KV_FP4) {
       const float sk[4] = {T.sk.x, T.sk.y, T.sk.z, T.sk.w};
       float ok[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      int nk = (int)(T.rk.x & 0xFFu);
+      // The record sits in scalar registers, so the channel indices below are
+      // wave-uniform.
+      const uint32_t rw[3] = {T.rk.x, T.rk.y, T.rk.z};
+      int nk = (int)(rw[0] & 0xFFu);
       if (nk == 0xFF) {
         if (T.ok && lane == 0 && a.err) atomicOr(a.err, PA_DEVERR_UNCALIBRATED);
         nk = 0;
       }
       if (nk > a.cap) nk = a.cap;
-      const uint32_t rw[3] = {T.rk.x, T.rk.y, T.rk.z};
       for (int j = 0; j < nk; ++j) {
         const int pos = 1 + j;
         const int ch = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
@@ -366,6 +415,7 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
     if (__builtin_amdgcn_ballot_w64(mb > m + kRescale) != 0) {  // wave-uniform
       const float mn = fmaxf(m, mb);
       const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      fold_side();
       l *= alpha;
 #pragma unroll
       for (int n = 0; n < NT; ++n) acc[n] *= alpha;
@@ -402,36 +452,31 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
     }
 
     if constexpr (KV == KV_FP4) {
-      // V outliers: out[c][ch] += sum_t p_t * o_t,ch (fp16 values, unscaled p)
-      int nv = (int)(T.rv.x & 0xFFu);
+      // V outliers: out[c][ch] += sum_t p_t * o_t,ch (fp16 values, unscaled p); ch is
+      // wave-uniform (the record sits in scalar registers).
+      const uint32_t rw[3] = {T.rv.x, T.rv.y, T.rv.z};
+      int nv = (int)(rw[0] & 0xFFu);
       if (nv == 0xFF) {
         if (T.ok && lane == 0 && a.err) atomicOr(a.err, PA_DEVERR_UNCALIBRATED);
         nv = 0;
       }
       if (nv > a.cap) nv = a.cap;
-      const uint32_t rw[3] = {T.rv.x, T.rv.y, T.rv.z};
       for (int j = 0; j < nv; ++j) {
         const int pos = 1 + j;
         const int ch = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
         const uint2 ov = j == 0 ? T.v_o0
                                 : *reinterpret_cast<const uint2*>(
                                       a.v_out_val + ((T.tile * a.cap + j) * kBlock + 4 * kg));
-        const float o4[4] = {f16_bits_to_f32(ov.x & 0xFFFFu), f16_bits_to_f32(ov.x >> 16),
-                             f16_bits_to_f32(ov.y & 0xFFFFu), f16_bits_to_f32(ov.y >> 16)};
-        float part = 0.0f;
+        // slots of tokens past the context hold arbitrary bits (maybe NaN): masked
+        const float o4[4] = {valid[0] ? f16_bits_to_f32(ov.x & 0xFFFFu) : 0.0f,
+                             valid[1] ? f16_bits_to_f32(ov.x >> 16) : 0.0f,
+                             valid[2] ? f16_bits_to_f32(ov.y & 0xFFFFu) : 0.0f,
+                             valid[3] ? f16_bits_to_f32(ov.y >> 16) : 0.0f};
+        float part = pr[0] * o4[0];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part += valid[r] ? pr[r] * o4[r] : 0.0f;
+        for (int r = 1; r < 4; ++r) part = __builtin_fmaf(pr[r], o4[r], part);
         part = group4_sum(part);
-        // channel ch of head c lives in lane group ch / DL, register (ch % DL) / NT of
-        // tile ch % NT; the indices are wave-uniform, so this is a scalar branch tree.
-        const int ckg = ch / DL, ce = ch % DL;
-        const int cn = ce % NT, cr = ce / NT;
-        const float add = kg == ckg ? part : 0.0f;
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (n == cn && r == cr) acc[n][r] += add;
+        if (kg == 0) side[ch * 16 + c] += part;
       }
     }
   };
@@ -454,6 +499,7 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
   }
 
   // ---- epilogue ----
+  fold_side();
   const float lt = group4_sum(l);
   const float vscale = KV == KV_FP8 ? a.v_scale[kvh] : 1.0f;
   const int h = kvh * G + c;
@@ -474,7 +520,7 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
 
   // W > 1: merge the waves' states in LDS.
   constexpr int STRIDE = DL + 4;  // floats per lane record (padded)
-  float* m_lds = smem + (KV == KV_FP4 ? 16 * D : 0);
+  float* m_lds = smem + (KV == KV_FP4 ? 16 * D + W * D * 16 : 0);
   float* l_lds = m_lds + 16 * 8;
   float* acc_lds = l_lds + 16 * 8;  // [W][64][STRIDE]
   if (kg == 0) {
@@ -522,9 +568,14 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
 template <int KV, int D, bool QBF>
 static int launch_one(const DecodeArgs& a, int waves, hipStream_t st) {
   const int P = a.partition_size > 0 ? a.max_partitions : 1;
-  size_t lds = (KV == KV_FP4 ? 16 * D * sizeof(float) : 0);
+  size_t lds = (KV == KV_FP4 ? (16 * D + (size_t)waves * D * 16) * sizeof(float) : 0);
   if (waves > 1) lds += (2 * 16 * 8 + (size_t)waves * 64 * (D / 4 + 4)) * sizeof(float);
-  hipLaunchKernelGGL((k_decode<KV, D, QBF>), dim3(P, a.num_kv_heads, a.num_seqs),
+#if PA_GRID_HEAD_FAST
+  const dim3 grid((unsigned)((int64_t)P * a.num_kv_heads), (unsigned)a.num_seqs, 1);
+#else
+  const dim3 grid(P, a.num_kv_heads, a.num_seqs);
+#endif
+  hipLaunchKernelGGL((k_decode<KV, D, QBF>), grid,
                      dim3(64 * waves), lds, st, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }

@@ -31,6 +31,15 @@ __device__ __forceinline__ T bitcast(const F& f) {
   return __builtin_bit_cast(T, f);
 }
 
+// Load 16 bytes that are the same for the whole wave and are not written while the
+// kernel runs (an address computed from wave-uniform values): reading them through the
+// constant address space makes the compiler use a scalar load into scalar registers.
+__device__ __forceinline__ uint4 load_uniform16(const void* p) {
+  typedef __attribute__((address_space(4))) const uint32_t cu32;
+  cu32* q = (cu32*)(uintptr_t)p;
+  return make_uint4(q[0], q[1], q[2], q[3]);
+}
+
 // ---------------------------------------------------------------------------------
 // 16-bit activations -> fp32 (exact)
 // ---------------------------------------------------------------------------------
@@ -94,14 +103,32 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // Combine the four lanes {l, l^16, l^32, l^48}: the four k-groups of one MFMA column.
-__device__ __forceinline__ float group4_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+// gfx950's v_permlane16_swap / v_permlane32_swap exchange 16-lane rows (resp. 32-lane
+// halves) between two registers in the vector ALU; swapping a value with itself leaves
+// x_l in one result and x_(l^16) (resp. x_(l^32)) in the other, so combining the two
+// results is one butterfly step, with no trip through the LDS crossbar.
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float group4_sum(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float group4_max(float x) { return xor32_max(xor16_max(x)); }
+__device__ __forceinline__ float group4_sum(float x) { return xor32_sum(xor16_sum(x)); }
 
 // ---------------------------------------------------------------------------------
 // MFMA wrappers (16x16 output tiles; lane l holds column l%16, rows 4*(l/16)+r).
