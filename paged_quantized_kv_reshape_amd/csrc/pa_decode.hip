@@ -73,6 +73,14 @@ struct Geo {
   static constexpr int VLANEB = NT * EBITS / 8;    // V bytes per lane per token
 };
 
+// LDS of the FP4 kernel, in floats, for GP head columns (shared by the kernel and its
+// launch): the q copy ([D + D/DL rows][GP], DL = D / 4) and each wave's side accumulator
+// ([D rows][GP], plus DL spare rows that take the entries of padding heads when GP < 16).
+template <int D, int GP>
+constexpr int fp4_qlds_floats() { return (D + 4) * GP; }
+template <int D, int GP>
+constexpr int fp4_side_floats() { return (D + (GP < 16 ? D / 4 : 0)) * GP; }
+
 template <int N>
 __device__ __forceinline__ void load_words(uint32_t (&w)[N], const uint8_t* p) {
   if constexpr (N % 4 == 0) {
@@ -203,15 +211,24 @@ __device__ __forceinline__ void v_fragments(const Tile<KV, D>& T, uint2 (&vf)[Ge
 #define PA_DECODE_ATTR
 #endif
 
-template <int KV, int D, bool QBF>
+template <int KV, int D, bool QBF, int GP>
 __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
   using G_ = Geo<KV, D>;
   constexpr int KS = G_::KS, NT = G_::NT, DL = G_::DL;
+  // FP4 LDS buffers hold GP head columns (GP = 8 or 16 >= the GQA group): the q copy and
+  // each wave's side accumulator, which has DL spare rows that lanes of padding heads
+  // (c >= GP) use instead of real entries (so every lane's entries sit at one base
+  // address plus compile-time offsets).
+  constexpr int kQLds = fp4_qlds_floats<D, GP>();  // floats of the FP4 q copy
+  constexpr int kSide = fp4_side_floats<D, GP>();  // floats of one wave's side accumulator
+  static_assert(kQLds == (D + D / DL) * GP && kSide == (D + (GP < 16 ? DL : 0)) * GP,
+                "FP4 LDS layout");
   constexpr bool PVB = QBF || KV == KV_FP4;  // PV MFMA in bf16 (else fp16)
   extern __shared__ float smem[];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index, pinned as wave-uniform (the compiler cannot prove threadIdx.x / 64 is)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
   const int c = lane & 15;  // MFMA column: query head (QK, PV); K row token; V channel group
   const int kg = lane >> 4;
@@ -264,7 +281,11 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
     for (int t = 0; t < KS; ++t)
       qf[t] = c < G ? reinterpret_cast<const uint4*>(qrow)[t] : make_uint4(0, 0, 0, 0);
   }
-  float* q_lds = smem;  // FP4 only: q in fp32, [16][D]
+  // FP4 only: q in fp32 for the K-outlier term, channel-major: head c of channel ch at
+  // (ch + ch / DL) * 16 + c. A column's 16 heads are 16 consecutive words (one read per
+  // outlier is conflict-free) and the pad of 16 words after each DL channels puts the
+  // four lane groups of a write on different banks.
+  float* q_lds = smem;
   if constexpr (KV == KV_FP4) {
     if (wave == 0) {
 #pragma unroll
@@ -273,21 +294,29 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t b16 = (w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-          q_lds[c * D + DL * kg + 8 * t + e] = act_to_f32<QBF>(b16);
+          if (c < GP) q_lds[(DL * kg + 8 * t + e + kg) * GP + c] = act_to_f32<QBF>(b16);
         }
       }
     }
     __syncthreads();
   }
-  // FP4 only: this wave's side accumulator of the V-outlier terms, [D channels][16 heads]
-  // fp32. The outlier channel of a block is known only at run time, and a run-time
+  // FP4 only: this wave's side accumulator of the V-outlier terms, [D channels][GP heads]
+  // fp32 (plus the spare row). The outlier channel of a block is known only at run time, and a run-time
   // index into the accumulator registers would cost a copy of all of them per case; so
   // the terms are summed here and folded into the registers at the end (and before a
   // rescale, which must scale both).
-  float* side = smem + 16 * D + (int64_t)wave * D * 16;
+  float* side = smem + kQLds + (int64_t)wave * kSide;
+  // this lane's entry for channel ch (a spare row for a padding head)
+  auto side_at = [&](int ch) -> float* {
+    return side + (c < GP ? ch * GP + c : D * GP + (c - GP));
+  };
+  // base of the entries lane (c, kg) folds into its registers: channel DL kg + NT r + n
+  // sits at fold_base + (NT r + n) GP
+  float* const fold_base = side + (c < GP ? DL * kg * GP + c : D * GP + (c - GP));
   if constexpr (KV == KV_FP4) {
+    static_assert(kSide % 4 == 0, "side accumulator is cleared in float4 units");
 #pragma unroll
-    for (int i = lane; i < D * 16 / 4; i += 64)
+    for (int i = lane; i < kSide / 4; i += 64)
       reinterpret_cast<float4*>(side)[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   }
 
@@ -308,6 +337,11 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
   const int k_lane_off = c * G_::ROWB + kg * G_::KLANEB;
   const int v_lane_off = 4 * kg * G_::ROWB + c * G_::VLANEB;
 
+  // Device-side error bits seen by this wave. They are kept wave-uniform and flagged
+  // once at the end: a lane-divergent branch inside the block loop would make the
+  // compiler carry the loop's scalar values (block ids, FP4 records) in vector
+  // registers, and wait for every scalar load as soon as it is issued.
+  int err_bits = 0;
   auto load_tile = [&](Tile<KV, D>& T, int x) {
     if (x > 0 && (x & 63) == 0) {
       ids_a = ids_b;
@@ -316,11 +350,8 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
     const int b_raw = __builtin_amdgcn_readlane(ids_a, x & 63);
     T.jb = jb0 + my_lo + x * kStep;
     T.ok = (unsigned)b_raw < (unsigned)a.num_blocks;
-    if (!T.ok && lane == 0 && a.err) atomicOr(a.err, PA_DEVERR_BAD_BLOCK);
-    // readfirstlane pins the id as wave-uniform, so the tile addresses below are
-    // computed in scalar registers (the lane-0 branch above would otherwise turn the
-    // substituted id into a per-lane value)
-    const int b = __builtin_amdgcn_readfirstlane(T.ok ? b_raw : 0);
+    err_bits |= T.ok ? 0 : PA_DEVERR_BAD_BLOCK;
+    const int b = T.ok ? b_raw : 0;
     T.tile = (int64_t)b * a.num_kv_heads + kvh;
     load_words(T.k, kpool + T.tile * G_::TILEB + k_lane_off);
 #pragma unroll
@@ -347,18 +378,22 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   // add the side accumulator into acc (lane (c, kg) holds channel DL kg + NT r + n of
   // head c in acc[n][r]) and clear it
-  auto fold_side = [&]() {
+  bool side_used = false;  // wave-uniform: some V-outlier term went to the side buffer
+  auto fold_side = [&](bool clear) {
     if constexpr (KV == KV_FP4) {
+      if (!side_used) return;
+      side_used = !clear;
 #pragma unroll
       for (int n = 0; n < NT; ++n)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float* e = side + (DL * kg + NT * r + n) * 16 + c;
+          float* e = fold_base + (NT * r + n) * GP;
           acc[n][r] += *e;
-          *e = 0.0f;
+          if (clear) *e = 0.0f;
         }
     }
   };
+  bool started = false;  // wave-uniform: a block has been folded into (m, l, acc)
 
   auto compute = [&](Tile<KV, D>& T) {
     const int tok0 = T.jb * kBlock + 4 * kg;
@@ -386,14 +421,15 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
       const uint32_t rw[3] = {T.rk.x, T.rk.y, T.rk.z};
       int nk = (int)(rw[0] & 0xFFu);
       if (nk == 0xFF) {
-        if (T.ok && lane == 0 && a.err) atomicOr(a.err, PA_DEVERR_UNCALIBRATED);
+        err_bits |= T.ok ? PA_DEVERR_UNCALIBRATED : 0;
         nk = 0;
       }
       if (nk > a.cap) nk = a.cap;
       for (int j = 0; j < nk; ++j) {
         const int pos = 1 + j;
         const int ch = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
-        const float qv = q_lds[c * D + ch];
+        // padding heads read some real column: their logits are never used
+        const float qv = q_lds[(ch + ch / DL) * GP + (c & (GP - 1))];
         const uint2 ov = j == 0 ? T.k_o0
                                 : *reinterpret_cast<const uint2*>(
                                       a.k_out_val + ((T.tile * a.cap + j) * kBlock + 4 * kg));
@@ -414,13 +450,16 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
     const float mb = group4_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
     if (__builtin_amdgcn_ballot_w64(mb > m + kRescale) != 0) {  // wave-uniform
       const float mn = fmaxf(m, mb);
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
-      fold_side();
-      l *= alpha;
+      if (started) {  // before the first block l, acc and the side buffer are all zero
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);
+        fold_side(true);
+        l *= alpha;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+        for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+      }
       m = mn;
     }
+    started = true;
     float pr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -457,7 +496,7 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
       const uint32_t rw[3] = {T.rv.x, T.rv.y, T.rv.z};
       int nv = (int)(rw[0] & 0xFFu);
       if (nv == 0xFF) {
-        if (T.ok && lane == 0 && a.err) atomicOr(a.err, PA_DEVERR_UNCALIBRATED);
+        err_bits |= T.ok ? PA_DEVERR_UNCALIBRATED : 0;
         nv = 0;
       }
       if (nv > a.cap) nv = a.cap;
@@ -476,7 +515,10 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
 #pragma unroll
         for (int r = 1; r < 4; ++r) part = __builtin_fmaf(pr[r], o4[r], part);
         part = group4_sum(part);
-        if (kg == 0) side[ch * 16 + c] += part;
+        // the four lanes of column c hold the same reduced term and read the same old
+        // value, so they all write the same sum: no lane branch is needed
+        *side_at(ch) += part;
+        side_used = true;
       }
     }
   };
@@ -499,7 +541,8 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
   }
 
   // ---- epilogue ----
-  fold_side();
+  if (err_bits != 0 && lane == 0 && a.err) atomicOr(a.err, err_bits);
+  fold_side(false);
   const float lt = group4_sum(l);
   const float vscale = KV == KV_FP8 ? a.v_scale[kvh] : 1.0f;
   const int h = kvh * G + c;
@@ -520,7 +563,7 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
 
   // W > 1: merge the waves' states in LDS.
   constexpr int STRIDE = DL + 4;  // floats per lane record (padded)
-  float* m_lds = smem + (KV == KV_FP4 ? 16 * D + W * D * 16 : 0);
+  float* m_lds = smem + (KV == KV_FP4 ? kQLds + W * kSide : 0);
   float* l_lds = m_lds + 16 * 8;
   float* acc_lds = l_lds + 16 * 8;  // [W][64][STRIDE]
   if (kg == 0) {
@@ -565,17 +608,31 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
   }
 }
 
-template <int KV, int D, bool QBF>
+template <int KV, int D, int GP>
+static size_t decode_lds_bytes(int waves) {
+  size_t f = KV == KV_FP4 ? fp4_qlds_floats<D, GP>() + (size_t)waves * fp4_side_floats<D, GP>()
+                          : 0;
+  if (waves > 1) f += 2 * 16 * 8 + (size_t)waves * 64 * (D / 4 + 4);  // the wave merge
+  return f * sizeof(float);
+}
+
+template <int KV, int D, bool QBF, int GP = 16>
 static int launch_one(const DecodeArgs& a, int waves, hipStream_t st) {
   const int P = a.partition_size > 0 ? a.max_partitions : 1;
-  size_t lds = (KV == KV_FP4 ? (16 * D + (size_t)waves * D * 16) * sizeof(float) : 0);
-  if (waves > 1) lds += (2 * 16 * 8 + (size_t)waves * 64 * (D / 4 + 4)) * sizeof(float);
+  // fewer waves per workgroup if their LDS would not fit the device's limit
+  int dev = 0, max_lds = 65536;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+          hipSuccess)
+    max_lds = 65536;
+  while (waves > 1 && decode_lds_bytes<KV, D, GP>(waves) > (size_t)max_lds) waves /= 2;
+  const size_t lds = decode_lds_bytes<KV, D, GP>(waves);
 #if PA_GRID_HEAD_FAST
   const dim3 grid((unsigned)((int64_t)P * a.num_kv_heads), (unsigned)a.num_seqs, 1);
 #else
   const dim3 grid(P, a.num_kv_heads, a.num_seqs);
 #endif
-  hipLaunchKernelGGL((k_decode<KV, D, QBF>), grid,
+  hipLaunchKernelGGL((k_decode<KV, D, QBF, GP>), grid,
                      dim3(64 * waves), lds, st, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
@@ -589,8 +646,11 @@ int launch_decode(const DecodeArgs& a, int kv, bool qbf, int D, int waves, hipSt
         return qbf ? launch_one<KV_FP8, 128, true>(a, waves, st)
                    : launch_one<KV_FP8, 128, false>(a, waves, st);
       case KV_FP4:
-        return qbf ? launch_one<KV_FP4, 128, true>(a, waves, st)
-                   : launch_one<KV_FP4, 128, false>(a, waves, st);
+        if (a.group <= 8)
+          return qbf ? launch_one<KV_FP4, 128, true, 8>(a, waves, st)
+                     : launch_one<KV_FP4, 128, false, 8>(a, waves, st);
+        return qbf ? launch_one<KV_FP4, 128, true, 16>(a, waves, st)
+                   : launch_one<KV_FP4, 128, false, 16>(a, waves, st);
     }
   } else {
     switch (kv) {

@@ -212,6 +212,31 @@ def test_edge_lengths_and_empty_batch():
     assert run.device_error() == 0
 
 
+@pytest.mark.parametrize("ps", [0, 128])
+@pytest.mark.parametrize("hq", [1, 2, 16])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "fp4"])
+def test_gqa_group_sizes(kv, hq, ps):
+    """Query-head groups of 1, 2 and 16 per kv head (the FP4 kernel keeps 8 or 16 head
+    columns in LDS depending on the group), single pass and split, against the oracle."""
+    from paged_quantized_kv_reshape_amd.harness import DeviceRun
+    base = "c5" if kv == "fp4" else "c4"
+    over = dict(num_seqs=3, lens=[300, 77, 16], num_q_heads=hq)
+    if kv == "bf16":
+        over.update(kv="bf16", planted=False)
+    w = config(base, **over)
+    _say(f"[gqa] {kv} Hq={hq} ps={ps}")
+    run = DeviceRun(w, partition_size=ps)
+    run.prepare()
+    run.decode()
+    torch.cuda.synchronize()
+    assert run.device_error() == 0
+    pool, ks, vs, near = replay(w)
+    assert_pool_equal(run.pool.numpy(), pool, near=near)
+    ref = oracle_decode(w, pool, ks, vs, range(w.num_seqs))
+    assert_close(run.out.cpu().numpy(), np.stack([ref[s][0] for s in range(w.num_seqs)]),
+                 f"{kv} Hq={hq} ps={ps}")
+
+
 # ---------------------------------------------------------------------------------
 # Full-size workloads, in the bench's launch configuration, sampled against the oracle.
 # ---------------------------------------------------------------------------------
