@@ -34,6 +34,8 @@
 //                 16-bit values (about 16 significant bits), so PV loses nothing to
 //                 16-bit rounding of P. After the block loop lane (c, kg) holds head c's
 //                 output channels [D/4 kg, D/4 (kg+1)).
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -48,16 +50,7 @@ constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
 #ifndef PA_DECODE_CONTIG
 #define PA_DECODE_CONTIG 0
 #endif
-#ifndef PA_DECODE_PREFETCH
-#define PA_DECODE_PREFETCH 0  // 0: the per-format depth below
-#endif
-// Tiles held in registers per wave. Measured on MI355X: one is best for every format;
-// a second costs a tile's worth of registers, hence resident waves, and the other waves
-// of the compute unit hide the load latency better than the wave itself can.
-template <int KV>
-constexpr int prefetch_depth() {
-  return PA_DECODE_PREFETCH > 0 ? PA_DECODE_PREFETCH : 1;
-}
+
 
 template <int KV, int D>
 struct Geo {
@@ -395,13 +388,16 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
   };
   bool started = false;  // wave-uniform: a block has been folded into (m, l, acc)
 
-  auto compute = [&](Tile<KV, D>& T) {
+  // One block. kFull (a compile-time tag) says the block is in range and all 16 of its
+  // tokens are inside the partition, which holds for every block but the last one of a
+  // partition; that version carries no per-token masks.
+  auto compute = [&](Tile<KV, D>& T, auto kFull) {
+    constexpr bool FULL = decltype(kFull)::value;
     const int tok0 = T.jb * kBlock + 4 * kg;
     bool valid[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) valid[r] = T.ok && (tok0 + r < end);
-    const bool partial = !T.ok || (T.jb * kBlock + kBlock > end);  // wave-uniform
-    if (partial) {
+    for (int r = 0; r < 4; ++r) valid[r] = FULL || (T.ok && (tok0 + r < end));
+    if constexpr (!FULL) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -511,9 +507,9 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
                              valid[1] ? f16_bits_to_f32(ov.x >> 16) : 0.0f,
                              valid[2] ? f16_bits_to_f32(ov.y & 0xFFFFu) : 0.0f,
                              valid[3] ? f16_bits_to_f32(ov.y >> 16) : 0.0f};
-        float part = pr[0] * o4[0];
+        float part = 0.0f;
 #pragma unroll
-        for (int r = 1; r < 4; ++r) part = __builtin_fmaf(pr[r], o4[r], part);
+        for (int r = 0; r < 4; ++r) part = __builtin_fmaf(pr[r], o4[r], part);
         part = group4_sum(part);
         // the four lanes of column c hold the same reduced term and read the same old
         // value, so they all write the same sum: no lane branch is needed
@@ -523,22 +519,19 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
     }
   };
 
-  // ---- block loop, kPrefetch tiles in flight ----
-  constexpr int kPrefetch = prefetch_depth<KV>();
-  Tile<KV, D> tiles[kPrefetch];
-#pragma unroll
-  for (int k = 0; k < kPrefetch; ++k)
-    if (k < my_n) load_tile(tiles[k], k);
-  for (int i0 = 0; i0 < my_n; i0 += kPrefetch) {
-#pragma unroll
-    for (int k = 0; k < kPrefetch; ++k) {
-      const int i = i0 + k;
-      if (i < my_n) {
-        compute(tiles[k]);
-        if (i + kPrefetch < my_n) load_tile(tiles[k], i + kPrefetch);
-      }
-    }
+  // ---- block loop: one tile in flight (the next one is loaded while nothing else of
+  // this wave is outstanding; the other waves of the compute unit cover its latency) ----
+  // Every block of the loop body is full: a partition starts on a block boundary, so only
+  // its last block can end early, and that block is the last one of some wave's run. It
+  // is handled after the loop with per-token masks. A block whose id is out of range is
+  // skipped (and flagged).
+  Tile<KV, D> tile;
+  if (my_n > 0) load_tile(tile, 0);
+  for (int i = 0; i + 1 < my_n; ++i) {
+    if (tile.ok) compute(tile, std::true_type{});
+    load_tile(tile, i + 1);
   }
+  if (my_n > 0 && tile.ok) compute(tile, std::false_type{});
 
   // ---- epilogue ----
   if (err_bits != 0 && lane == 0 && a.err) atomicOr(a.err, err_bits);
