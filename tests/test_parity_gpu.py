@@ -237,6 +237,30 @@ def test_gqa_group_sizes(kv, hq, ps):
                  f"{kv} Hq={hq} ps={ps}")
 
 
+@pytest.mark.parametrize("ps", [0, 128])
+@pytest.mark.parametrize("kv,act,d", [("fp8", "f16", 128), ("fp4", "f16", 128),
+                                      ("fp8", "bf16", 64), ("fp8", "f16", 64),
+                                      ("f16", "f16", 128), ("bf16", "bf16", 64)])
+def test_activation_dtypes_and_head_dims(kv, act, d, ps):
+    """fp16 activations with the quantized pools (their fp16 MFMA variants), head_dim 64
+    with FP8 and 16-bit pools, two kv heads: pools bit-exact, outputs within tolerance."""
+    from paged_quantized_kv_reshape_amd.harness import DeviceRun
+    base = "c5" if kv == "fp4" else "c4"
+    w = config(base, num_seqs=3, lens=[300, 77, 16], num_q_heads=8, num_kv_heads=2,
+               head_dim=d, kv=kv, act=act, planted=kv in ("fp8", "fp4"))
+    _say(f"[dtypes] kv={kv} act={act} D={d} ps={ps}")
+    run = DeviceRun(w, partition_size=ps)
+    run.prepare()
+    run.decode()
+    torch.cuda.synchronize()
+    assert run.device_error() == 0
+    pool, ks, vs, near = replay(w)
+    assert_pool_equal(run.pool.numpy(), pool, near=near)
+    ref = oracle_decode(w, pool, ks, vs, range(w.num_seqs))
+    assert_close(run.out.cpu().numpy(), np.stack([ref[s][0] for s in range(w.num_seqs)]),
+                 f"kv={kv} act={act} D={d} ps={ps}")
+
+
 # ---------------------------------------------------------------------------------
 # Full-size workloads, in the bench's launch configuration, sampled against the oracle.
 # ---------------------------------------------------------------------------------
