@@ -81,47 +81,55 @@ typedef enum {
  *                            k_scale, v_scale [num_kv_heads] fp32 (inputs, read-only):
  *                            the stored value is code * scale (per layer and kv head;
  *                            see pa_fp8_head_scales).
- *   PA_KV_FP4_E2M1_OUTL    : k, v   [num_blocks, num_kv_heads, 16, head_dim / 2] uint8,
- *                                   two E2M1 codes per byte, even channel in the low nibble
- *                            *_tok_scale [num_blocks, num_kv_heads, 16] fp32, per token
- *                            *_out_idx   [num_blocks, num_kv_heads, 16] uint8 record per
- *                                        (block, kv head): byte 0 = outlier count, or 0xFF
- *                                        while the block has never been written; bytes
- *                                        1..count = ascending channel indices; the other
- *                                        bytes 0xFF. The caller fills a block's record with
- *                                        0xFF before the block is first written (see
- *                                        pa_reset_blocks).
- *                            *_out_val   [num_blocks, num_kv_heads, CAP, 16] fp16 bits:
- *                                        slot j holds the j-th outlier channel's value for
- *                                        each token offset; CAP = pa_outlier_capacity(D).
+ *   PA_KV_FP4_E2M1_OUTL    : k, v   [num_blocks, num_kv_heads, PA_FP4_TILE_BYTES(head_dim)]
+ *                                   bytes: one contiguous run per (block, kv head) holding
+ *                                   everything a decode reads for that block, so it is
+ *                                   fetched in whole 128-byte lines:
+ *                            [0, 8 D)       codes [16 tokens][D/2], two E2M1 codes per
+ *                                           byte, even channel in the low nibble
+ *                            PA_FP4_SCALE_OFF   16 per-token fp32 scales (value = code *
+ *                                               scale for the inlier channels)
+ *                            PA_FP4_RECORD_OFF  16-byte outlier record: byte 0 = outlier
+ *                                               count, or 0xFF while the block has never
+ *                                               been written; bytes 1..count = ascending
+ *                                               channel indices; the other bytes 0xFF
+ *                            PA_FP4_SLOT0_OFF   fp16 bits of the first outlier channel's
+ *                                               value, one per token (16 x 2 bytes)
+ *                            then padding to a multiple of 128 bytes.
+ *                            *_out_val [num_blocks, num_kv_heads, CAP - 1, 16] fp16 bits:
+ *                                      slot j holds the (j + 1)-th outlier channel's value
+ *                                      for each token offset; CAP = pa_outlier_capacity(D).
+ *                            Every block's record must read 0xFF before the block is first
+ *                            written: call pa_reset_blocks on new and on reused blocks.
  *   Fields a format does not use are ignored (may be NULL).
  */
+#define PA_FP4_SCALE_OFF(head_dim) (8 * (head_dim))
+#define PA_FP4_RECORD_OFF(head_dim) (8 * (head_dim) + 64)
+#define PA_FP4_SLOT0_OFF(head_dim) (8 * (head_dim) + 80)
+#define PA_FP4_TILE_BYTES(head_dim) ((8 * (head_dim) + 112 + 127) / 128 * 128)
+
 typedef struct pa_kv_pool {
   int32_t dtype;          /* pa_kv_dtype */
   int32_t num_blocks;
   int32_t block_size;     /* must be 16 */
   int32_t num_kv_heads;
-  int32_t head_dim;       /* 64 or 128 */
+  int32_t head_dim;       /* 64 or 128 (FP4: 128) */
   int32_t reserved;
   void* k;
   void* v;
-  float* k_tok_scale;
-  float* v_tok_scale;
-  uint8_t* k_out_idx;
-  uint8_t* v_out_idx;
-  uint16_t* k_out_val;
-  uint16_t* v_out_val;
-  const float* k_scale;
-  const float* v_scale;
+  uint16_t* k_out_val;    /* FP4 only */
+  uint16_t* v_out_val;    /* FP4 only */
+  const float* k_scale;   /* FP8 only */
+  const float* v_scale;   /* FP8 only */
 } pa_kv_pool;
 
 /*
  * Host-only. Byte sizes of the pool arrays for a format, in the order
- * {k, v, k_tok_scale, v_tok_scale, k_out_idx, v_out_idx, k_out_val, v_out_val}
- * (0 for arrays the format does not use). Returns PA_OK or an error status.
+ * {k, v, k_out_val, v_out_val} (0 for arrays the format does not use). Returns PA_OK or an
+ * error status.
  */
 int pa_pool_layout(int32_t dtype, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
-                   size_t bytes_out[8]);
+                   size_t bytes_out[4]);
 
 /*
  * Host-only. Outlier slots per (block, kv head) of the FP4 format: the largest number of
@@ -169,8 +177,8 @@ int pa_fp8_head_scales(const void* x, int32_t act, int64_t num_rows, int32_t num
 
 /*
  * Mark the listed physical blocks as never written (FP4 records set to 0xFF), so the next
- * write into each one calibrates it afresh: the engine calls this when it hands a freed
- * block to a new sequence (inferensys glossary "vLLM", continuous batching entry: finished
+ * write into each one calibrates it afresh: call it once for every block of a new pool,
+ * and when the engine hands a freed block to a new sequence (inferensys glossary "vLLM", continuous batching entry: finished
  * sequences release their blocks to the pool). block_ids [n] int32, device memory.
  * No-op (PA_OK) for formats without records.
  */

@@ -32,12 +32,16 @@ Readings where the pages are silent (each listed in the design notes):
 Pool layout (the boundary's layout, row-major, one array per field):
   f16 / bf16 : k, v          uint16 [NB, Hkv, 16, D]
   fp8        : k, v          uint8  [NB, Hkv, 16, D]        (+ per-head fp32 scales)
-  fp4        : k, v          uint8  [NB, Hkv, 16, D/2]
-               *_tok_scale   fp32   [NB, Hkv, 16]
-               *_out_idx     uint8  [NB, Hkv, 16]  byte 0 = count (0xFF = not yet
-                                    calibrated), then the ascending channel indices,
-                                    then 0xFF in the unused bytes
-               *_out_val     uint16 [NB, Hkv, CAP, 16]  fp16 bits, slot j = j-th outlier
+  fp4        : k, v          uint8  [NB, Hkv, TILE] one run of bytes per (block, head):
+                 [0, 8 D)          codes [16 tokens][D/2], two per byte
+                 [8 D, 8 D + 64)   per-token scales, fp32 [16]
+                 next 16 bytes     record: byte 0 = outlier count (0xFF = not yet
+                                   calibrated), then the ascending channel indices,
+                                   then 0xFF in the unused bytes
+                 next 32 bytes     fp16 values of the first outlier, one per token
+                 the rest          padding up to a multiple of 128 bytes (TILE = 1152
+                                   for D = 128)
+               *_out_val     uint16 [NB, Hkv, CAP - 1, 16]  fp16 bits of outliers 1.. CAP-1
 """
 from __future__ import annotations
 
@@ -91,10 +95,8 @@ class Pool:
             cap = outlier_capacity(d)
             out = {}
             for kv in ("k", "v"):
-                out[kv] = ((nb, hkv, 16, d // 2), np.uint8)
-                out[kv + "_tok_scale"] = ((nb, hkv, 16), np.float32)
-                out[kv + "_out_idx"] = ((nb, hkv, 16), np.uint8)
-                out[kv + "_out_val"] = ((nb, hkv, cap, 16), np.uint16)
+                out[kv] = ((nb, hkv, fp4_tile_bytes(d)), np.uint8)
+                out[kv + "_out_val"] = ((nb, hkv, cap - 1, 16), np.uint16)
             return out
         raise ValueError(kind)
 
@@ -105,9 +107,59 @@ class Pool:
         p = cls(kind, nb, hkv, d)
         for name, (shape, dt) in cls.shapes(kind, nb, hkv, d).items():
             n = int(np.prod(shape)) * np.dtype(dt).itemsize
-            fill = UNCALIBRATED if name.endswith("_out_idx") else sentinel
-            p.arrays[name] = np.full(n, fill, dtype=np.uint8).view(dt).reshape(shape)
+            p.arrays[name] = np.full(n, sentinel, dtype=np.uint8).view(dt).reshape(shape)
+        if kind == "fp4":
+            for kv in ("k", "v"):
+                fp4_records(p, kv)[...] = UNCALIBRATED
         return p
+
+
+# ----------------------------------------------------------------------------------
+# FP4 tile regions (views into a pool's k / v byte arrays)
+# ----------------------------------------------------------------------------------
+
+
+def fp4_tile_bytes(head_dim: int) -> int:
+    """Bytes of one FP4 (block, head) run: codes, 16 fp32 scales, a 16-byte record and the
+    first outlier's 16 fp16 values, rounded up to a multiple of 128 bytes."""
+    used = 16 * head_dim // 2 + 16 * 4 + 16 + 16 * 2
+    return -(-used // 128) * 128
+
+
+def _fp4_offsets(d):
+    codes = 16 * d // 2
+    return codes, codes + 64, codes + 80, codes + 112  # scales, record, slot 0, end
+
+
+def fp4_codes(pool: Pool, kv: str) -> np.ndarray:
+    """Packed codes, a view [NB, Hkv, 16, D/2] uint8."""
+    d = pool.head_dim
+    a = pool.arrays[kv]
+    return a[..., :16 * d // 2].reshape(a.shape[0], a.shape[1], 16, d // 2)
+
+
+def fp4_scales(pool: Pool, kv: str) -> np.ndarray:
+    """Per-token scales, a view [NB, Hkv, 16] fp32."""
+    s0, r0, _, _ = _fp4_offsets(pool.head_dim)
+    return pool.arrays[kv][..., s0:r0].view(np.float32)
+
+
+def fp4_records(pool: Pool, kv: str) -> np.ndarray:
+    """Outlier records, a view [NB, Hkv, 16] uint8."""
+    _, r0, z0, _ = _fp4_offsets(pool.head_dim)
+    return pool.arrays[kv][..., r0:z0]
+
+
+def fp4_slot0(pool: Pool, kv: str) -> np.ndarray:
+    """fp16 bits of the first outlier, a view [NB, Hkv, 16] uint16."""
+    _, _, z0, e0 = _fp4_offsets(pool.head_dim)
+    return pool.arrays[kv][..., z0:e0].view(np.uint16)
+
+
+def fp4_outlier_values(pool: Pool, kv: str, blk, h) -> np.ndarray:
+    """All CAP outlier slots of one (block, head) as fp16 bits [CAP, 16] (a copy)."""
+    return np.concatenate([fp4_slot0(pool, kv)[blk, h][None, :],
+                           pool.arrays[kv + "_out_val"][blk, h]], axis=0)
 
 
 # ----------------------------------------------------------------------------------
@@ -213,7 +265,9 @@ def cache_write(pool: Pool, k_rows, v_rows, act: str, slots, k_scale=None, v_sca
         hkv = pool.num_kv_heads
         for name, rows in (("k", k_rows), ("v", v_rows)):
             x_all = act_decode(np.asarray(rows)[live], act)  # [n, Hkv, D]
-            idx_arr, val_arr = A[name + "_out_idx"], A[name + "_out_val"]
+            idx_arr = fp4_records(pool, name)
+            codes_arr, scale_arr = fp4_codes(pool, name), fp4_scales(pool, name)
+            slot0_arr, val_arr = fp4_slot0(pool, name), A[name + "_out_val"]
             # step 1-2: calibrate blocks this call opens, on this call's tokens
             for b in np.unique(blk):
                 rows_in_b = np.nonzero(blk == b)[0]
@@ -234,9 +288,11 @@ def cache_write(pool: Pool, k_rows, v_rows, act: str, slots, k_scale=None, v_sca
                     rec = idx_arr[blk[i], h]
                     o = rec[1:1 + rec[0]].astype(np.int64)
                     packed, s, ov = fp4_encode_row(x_all[i, h, :], o)
-                    A[name][blk[i], h, off[i], :] = packed
-                    A[name + "_tok_scale"][blk[i], h, off[i]] = s
-                    val_arr[blk[i], h, :len(o), off[i]] = ov
+                    codes_arr[blk[i], h, off[i], :] = packed
+                    scale_arr[blk[i], h, off[i]] = s
+                    if len(o):
+                        slot0_arr[blk[i], h, off[i]] = ov[0]
+                        val_arr[blk[i], h, :len(o) - 1, off[i]] = ov[1:]
         return
     raise ValueError(pool.kind)
 
@@ -261,21 +317,23 @@ def dequant_slot_rows(pool: Pool, blk, off, k_scale=None, v_scale=None):
             s = np.asarray(sc, dtype=np.float32).astype(np.float64)[None, :, None]
             out.append(e4m3_decode(A[name][blk, :, off, :]) * s)
         elif pool.kind == "fp4":
-            packed = A[name][blk, :, off, :]  # [n, Hkv, D/2]
+            packed = fp4_codes(pool, name)[blk, :, off, :]  # [n, Hkv, D/2]
             n, hkv, half = packed.shape
             codes = np.empty((n, hkv, 2 * half), dtype=np.uint8)
             codes[..., 0::2] = packed & 0xF
             codes[..., 1::2] = packed >> 4
-            s = A[name + "_tok_scale"][blk, :, off].astype(np.float64)[..., None]
+            s = fp4_scales(pool, name)[blk, :, off].astype(np.float64)[..., None]
             x = e2m1_decode(codes) * s
-            rec = A[name + "_out_idx"][blk]  # [n, Hkv, 16]
-            vals = A[name + "_out_val"][blk]  # [n, Hkv, CAP, 16]
+            rec = fp4_records(pool, name)[blk]  # [n, Hkv, 16]
             for i in range(n):
                 for h in range(hkv):
                     cnt = int(rec[i, h, 0])
                     assert cnt != UNCALIBRATED, "read of a block that was never written"
+                    if cnt == 0:
+                        continue
+                    vals = fp4_outlier_values(pool, name, blk[i], h)  # [CAP, 16]
                     for j in range(cnt):
-                        x[i, h, rec[i, h, 1 + j]] = f16_decode(vals[i, h, j, off[i]])
+                        x[i, h, rec[i, h, 1 + j]] = f16_decode(vals[j, off[i]])
             out.append(x)
         else:
             raise ValueError(pool.kind)
@@ -293,6 +351,8 @@ def gather_sequence(pool: Pool, block_table_row, context_len, k_scale=None, v_sc
 
 __all__ = [
     "BLOCK_TOKENS", "OUTLIER_SIGMAS", "UNCALIBRATED", "Pool", "outlier_capacity",
+    "fp4_tile_bytes", "fp4_codes", "fp4_scales", "fp4_records", "fp4_slot0",
+    "fp4_outlier_values",
     "fp8_head_scale", "fp4_calibrate", "fp4_calibration_margin", "fp4_encode_row",
     "cache_write", "dequant_slot_rows", "gather_sequence", "f32_round",
 ]

@@ -35,11 +35,19 @@ class pa_kv_pool(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
         ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
-        ("k_tok_scale", ctypes.c_void_p), ("v_tok_scale", ctypes.c_void_p),
-        ("k_out_idx", ctypes.c_void_p), ("v_out_idx", ctypes.c_void_p),
         ("k_out_val", ctypes.c_void_p), ("v_out_val", ctypes.c_void_p),
         ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
     ]
+
+
+def fp4_tile_bytes(head_dim: int) -> int:
+    """PA_FP4_TILE_BYTES of include/pa.h."""
+    return (8 * head_dim + 112 + 127) // 128 * 128
+
+
+def fp4_record_offset(head_dim: int) -> int:
+    """PA_FP4_RECORD_OFF of include/pa.h."""
+    return 8 * head_dim + 64
 
 
 def lib():
@@ -85,7 +93,7 @@ def _check(fn, status):
 
 
 def pa_pool_layout(kv_dtype: str, num_blocks: int, num_kv_heads: int, head_dim: int):
-    out = (ctypes.c_size_t * 8)()
+    out = (ctypes.c_size_t * 4)()
     _check("pa_pool_layout", lib().pa_pool_layout(KV_DTYPES[kv_dtype], num_blocks, num_kv_heads,
                                                   head_dim, out))
     return list(out)
@@ -101,11 +109,11 @@ def pa_outlier_capacity(head_dim: int) -> int:
 class KVPool:
     """Device arrays of one paged pool (caller-owned memory, as the ABI requires).
 
-    `fill` is the byte every array starts with (FP4 outlier records always start as 0xFF,
-    i.e. never written). FP8 pools need k_scale / v_scale [Hkv] fp32 device tensors."""
+    `fill` is the byte every array starts with; FP4 outlier records are then reset to
+    0xFF (never written) with pa_reset_blocks. FP8 pools need k_scale / v_scale [Hkv] fp32
+    device tensors."""
 
-    NAMES = ["k", "v", "k_tok_scale", "v_tok_scale", "k_out_idx", "v_out_idx", "k_out_val",
-             "v_out_val"]
+    NAMES = ["k", "v", "k_out_val", "v_out_val"]
 
     def __init__(self, kv_dtype, num_blocks, num_kv_heads, head_dim, device="cuda", fill=0,
                  k_scale=None, v_scale=None):
@@ -115,11 +123,19 @@ class KVPool:
         self.bytes = {}
         for name, n in zip(self.NAMES, sizes):
             if n:
-                f = 0xFF if name.endswith("_out_idx") else fill
-                self.bytes[name] = torch.full((n,), f, dtype=torch.uint8, device=device)
+                self.bytes[name] = torch.full((n,), fill, dtype=torch.uint8, device=device)
         self.k_scale, self.v_scale = k_scale, v_scale
         if kv_dtype == "fp8" and (k_scale is None or v_scale is None):
             raise ValueError("an fp8 pool needs k_scale and v_scale")
+        if kv_dtype == "fp4":
+            pa_reset_blocks(self, torch.arange(num_blocks, dtype=torch.int32, device=device))
+
+    def fp4_records(self, side: str):
+        """FP4 only: the 16-byte outlier records [NB, Hkv, 16] (a view of the k or v tiles)."""
+        t = self.bytes[side].view(self.num_blocks, self.num_kv_heads,
+                                  fp4_tile_bytes(self.head_dim))
+        o = fp4_record_offset(self.head_dim)
+        return t[:, :, o:o + 16]
 
     def struct(self) -> pa_kv_pool:
         s = pa_kv_pool()

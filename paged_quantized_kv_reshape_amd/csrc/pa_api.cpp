@@ -30,13 +30,8 @@ int check_pool(const pa_kv_pool* p) {
   }
   if (p->dtype == PA_KV_FP4_E2M1_OUTL) {
     if (p->head_dim != 128) return PA_ERR_SHAPE;  // 4-bit format: head_dim 128 only
-    if (!p->k_tok_scale || !p->v_tok_scale || !p->k_out_idx || !p->v_out_idx ||
-        !p->k_out_val || !p->v_out_val)
-      return PA_ERR_NULL;
-    if (!aligned(p->k_tok_scale, 16) || !aligned(p->v_tok_scale, 16) ||
-        !aligned(p->k_out_idx, 16) || !aligned(p->v_out_idx, 16) || !aligned(p->k_out_val, 8) ||
-        !aligned(p->v_out_val, 8))
-      return PA_ERR_ALIGN;
+    if (!p->k_out_val || !p->v_out_val) return PA_ERR_NULL;
+    if (!aligned(p->k_out_val, 8) || !aligned(p->v_out_val, 8)) return PA_ERR_ALIGN;
   }
   return PA_OK;
 }
@@ -90,13 +85,13 @@ int pa_outlier_capacity(int32_t head_dim) {
 }
 
 int pa_pool_layout(int32_t dtype, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
-                   size_t bytes_out[8]) {
+                   size_t bytes_out[4]) {
   if (!bytes_out) return PA_ERR_NULL;
   if (dtype < PA_KV_F16 || dtype > PA_KV_FP4_E2M1_OUTL) return PA_ERR_DTYPE;
   if (num_blocks < 1 || num_kv_heads < 1 || (head_dim != 64 && head_dim != 128))
     return PA_ERR_SHAPE;
   if (dtype == PA_KV_FP4_E2M1_OUTL && head_dim != 128) return PA_ERR_SHAPE;
-  for (int i = 0; i < 8; ++i) bytes_out[i] = 0;
+  for (int i = 0; i < 4; ++i) bytes_out[i] = 0;
   const size_t bh = (size_t)num_blocks * num_kv_heads;
   const size_t rows = bh * PA_BLOCK_SIZE;
   switch (dtype) {
@@ -104,11 +99,9 @@ int pa_pool_layout(int32_t dtype, int32_t num_blocks, int32_t num_kv_heads, int3
     case PA_KV_BF16: bytes_out[0] = bytes_out[1] = rows * head_dim * 2; break;
     case PA_KV_FP8_E4M3: bytes_out[0] = bytes_out[1] = rows * head_dim; break;
     default:
-      bytes_out[0] = bytes_out[1] = rows * head_dim / 2;
-      bytes_out[2] = bytes_out[3] = rows * sizeof(float);
-      bytes_out[4] = bytes_out[5] = bh * 16;
-      bytes_out[6] = bytes_out[7] =
-          bh * (size_t)pa::outlier_capacity(head_dim) * PA_BLOCK_SIZE * sizeof(uint16_t);
+      bytes_out[0] = bytes_out[1] = bh * (size_t)PA_FP4_TILE_BYTES(head_dim);
+      bytes_out[2] = bytes_out[3] = bh * (size_t)(pa::outlier_capacity(head_dim) - 1) *
+                                    PA_BLOCK_SIZE * sizeof(uint16_t);
   }
   return PA_OK;
 }
@@ -187,10 +180,6 @@ int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
   a.q = q;
   a.k = pool->k;
   a.v = pool->v;
-  a.k_tok_scale = pool->k_tok_scale;
-  a.v_tok_scale = pool->v_tok_scale;
-  a.k_out_idx = pool->k_out_idx;
-  a.v_out_idx = pool->v_out_idx;
   a.k_out_val = pool->k_out_val;
   a.v_out_val = pool->v_out_val;
   a.k_scale = pool->k_scale;

@@ -59,7 +59,9 @@ struct Geo {
   static constexpr int DL = D / 4;   // channels per lane in K fragments and outputs
   static constexpr int EBITS = KV == KV_FP8 ? 8 : KV == KV_FP4 ? 4 : 16;
   static constexpr int ROWB = D * EBITS / 8;       // bytes of one token row
-  static constexpr int TILEB = kBlock * ROWB;      // bytes of one (block, head) tile
+  // bytes between consecutive (block, head) tiles; an FP4 tile also holds its per-token
+  // scales, its outlier record and its first outlier slot after the codes
+  static constexpr int TILEB = KV == KV_FP4 ? PA_FP4_TILE_BYTES(D) : kBlock * ROWB;
   static constexpr int KW = DL * EBITS / 32;       // K words per lane
   static constexpr int VW = NT * EBITS / 32;       // V words per lane per token
   static constexpr int KLANEB = DL * EBITS / 8;    // K bytes per lane
@@ -351,15 +353,17 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
     for (int r = 0; r < 4; ++r)
       load_words(T.v[r], vpool + T.tile * G_::TILEB + v_lane_off + r * G_::ROWB);
     if constexpr (KV == KV_FP4) {
-      T.sk = reinterpret_cast<const float4*>(a.k_tok_scale + T.tile * kBlock)[kg];
-      T.sv = reinterpret_cast<const float4*>(a.v_tok_scale + T.tile * kBlock)[kg];
+      const uint8_t* kt = kpool + T.tile * G_::TILEB;
+      const uint8_t* vt = vpool + T.tile * G_::TILEB;
+      T.sk = reinterpret_cast<const float4*>(kt + PA_FP4_SCALE_OFF(D))[kg];
+      T.sv = reinterpret_cast<const float4*>(vt + PA_FP4_SCALE_OFF(D))[kg];
       // the records are wave-uniform and read-only while decoding: scalar loads
-      T.rk = load_uniform16(a.k_out_idx + T.tile * 16);
-      T.rv = load_uniform16(a.v_out_idx + T.tile * 16);
-      // slot 0 always exists (capacity >= 1); its bytes are used only if the record's
-      // count is at least 1
-      T.k_o0 = *reinterpret_cast<const uint2*>(a.k_out_val + T.tile * a.cap * kBlock + 4 * kg);
-      T.v_o0 = *reinterpret_cast<const uint2*>(a.v_out_val + T.tile * a.cap * kBlock + 4 * kg);
+      T.rk = load_uniform16(kt + PA_FP4_RECORD_OFF(D));
+      T.rv = load_uniform16(vt + PA_FP4_RECORD_OFF(D));
+      // the first outlier slot is part of the tile; its bytes are used only if the
+      // record's count is at least 1
+      T.k_o0 = reinterpret_cast<const uint2*>(kt + PA_FP4_SLOT0_OFF(D))[kg];
+      T.v_o0 = reinterpret_cast<const uint2*>(vt + PA_FP4_SLOT0_OFF(D))[kg];
     }
   };
 
@@ -428,7 +432,8 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
         const float qv = q_lds[(ch + ch / DL) * GP + (c & (GP - 1))];
         const uint2 ov = j == 0 ? T.k_o0
                                 : *reinterpret_cast<const uint2*>(
-                                      a.k_out_val + ((T.tile * a.cap + j) * kBlock + 4 * kg));
+                                      a.k_out_val + ((T.tile * (a.cap - 1) + (j - 1)) * kBlock +
+                                                     4 * kg));
         ok[0] = __builtin_fmaf(qv, f16_bits_to_f32(ov.x & 0xFFFFu), ok[0]);
         ok[1] = __builtin_fmaf(qv, f16_bits_to_f32(ov.x >> 16), ok[1]);
         ok[2] = __builtin_fmaf(qv, f16_bits_to_f32(ov.y & 0xFFFFu), ok[2]);
@@ -501,7 +506,8 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
         const int ch = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
         const uint2 ov = j == 0 ? T.v_o0
                                 : *reinterpret_cast<const uint2*>(
-                                      a.v_out_val + ((T.tile * a.cap + j) * kBlock + 4 * kg));
+                                      a.v_out_val + ((T.tile * (a.cap - 1) + (j - 1)) * kBlock +
+                                                     4 * kg));
         // slots of tokens past the context hold arbitrary bits (maybe NaN): masked
         const float o4[4] = {valid[0] ? f16_bits_to_f32(ov.x & 0xFFFFu) : 0.0f,
                              valid[1] ? f16_bits_to_f32(ov.x >> 16) : 0.0f,

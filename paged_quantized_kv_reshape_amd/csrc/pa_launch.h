@@ -24,11 +24,7 @@ struct DecodeArgs {
   const void* q;
   const void* k;
   const void* v;
-  const float* k_tok_scale;
-  const float* v_tok_scale;
-  const uint8_t* k_out_idx;
-  const uint8_t* v_out_idx;
-  const uint16_t* k_out_val;
+  const uint16_t* k_out_val;  // FP4 outlier slots 1 .. cap - 1
   const uint16_t* v_out_val;
   const float* k_scale;
   const float* v_scale;

@@ -101,8 +101,8 @@ __global__ __launch_bounds__(256) void k_write_fp8(const uint4* __restrict__ k_n
 // scratch memory of their own:
 //   mark      each row landing in an unset record clears bit `offset` of the record's last
 //             word (bytes 12..15, never an index since at most 11 channels are stored)
-//             and parks its row index in tok_scale[block, head, offset], a word the encode
-//             launch overwrites with the row's real scale;
+//             and parks its row index in the tile's scale word for that offset, a word the
+//             encode launch overwrites with the row's real scale;
 //   calibrate the row with the lowest cleared offset (the leader) reads the row list from
 //             the parked indices, computes the outlier set and writes record bytes 0..11;
 //             the others only read bytes 12..15, which this launch never writes;
@@ -112,10 +112,18 @@ __global__ __launch_bounds__(256) void k_write_fp8(const uint4* __restrict__ k_n
 // ---------------------------------------------------------------------------------
 struct Fp4Side {
   const uint16_t* rows;  // new rows [T, Hkv, D] (activation bits)
-  uint8_t* codes;        // [NB, Hkv, 16, D/2]
-  float* tok_scale;      // [NB, Hkv, 16]
-  uint8_t* out_idx;      // [NB, Hkv, 16]
-  uint16_t* out_val;     // [NB, Hkv, CAP, 16]
+  uint8_t* tiles;        // [NB, Hkv, PA_FP4_TILE_BYTES(D)]: codes, scales, record, slot 0
+  uint16_t* out_val;     // [NB, Hkv, CAP - 1, 16]: outlier slots 1 .. CAP - 1
+};
+
+// Regions of one (block, head) FP4 tile.
+template <int D>
+struct Fp4Tile {
+  static constexpr int kBytes = PA_FP4_TILE_BYTES(D);
+  static constexpr int kScale = PA_FP4_SCALE_OFF(D);
+  static constexpr int kRecord = PA_FP4_RECORD_OFF(D);
+  static constexpr int kSlot0 = PA_FP4_SLOT0_OFF(D);
+  static_assert(kScale % 16 == 0 && kRecord % 16 == 0 && kSlot0 % 8 == 0, "FP4 tile layout");
 };
 struct Fp4Args {
   Fp4Side side[2];
@@ -125,7 +133,9 @@ struct Fp4Args {
   int32_t* err;
 };
 
+template <int D>
 __global__ __launch_bounds__(256) void k_fp4_mark(Fp4Args a) {
+  using TL = Fp4Tile<D>;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t n = (int64_t)a.num_tokens * a.hkv;
   if (idx >= n) return;
@@ -139,15 +149,17 @@ __global__ __launch_bounds__(256) void k_fp4_mark(Fp4Args a) {
   }
   const int64_t bh = (slot >> 4) * a.hkv + h;
   const int off = (int)(slot & 15);
-  uint8_t* rec = sd.out_idx + bh * 16;
+  uint8_t* tile = sd.tiles + bh * TL::kBytes;
+  uint8_t* rec = tile + TL::kRecord;
   if (rec[0] != 0xFF) return;  // already calibrated: reuse its channel set
   atomicAnd(reinterpret_cast<unsigned int*>(rec + 12), ~(1u << off));
-  reinterpret_cast<int32_t*>(sd.tok_scale)[bh * kBlock + off] = (int32_t)i;
+  reinterpret_cast<int32_t*>(tile + TL::kScale)[off] = (int32_t)i;
 }
 
 // One wave per (row, head, K|V); only block leaders do work.
 template <bool BF16, int D>
 __global__ __launch_bounds__(64) void k_fp4_calibrate(Fp4Args a) {
+  using TL = Fp4Tile<D>;
   const int i = blockIdx.x, h = blockIdx.y;
   const Fp4Side& sd = a.side[blockIdx.z];
   const int lane = threadIdx.x;
@@ -155,11 +167,12 @@ __global__ __launch_bounds__(64) void k_fp4_calibrate(Fp4Args a) {
   if (slot < 0 || slot >= a.nslots) return;
   const int64_t bh = (slot >> 4) * a.hkv + h;
   const int off = (int)(slot & 15);
-  uint8_t* rec = sd.out_idx + bh * 16;
+  uint8_t* tile = sd.tiles + bh * TL::kBytes;
+  uint8_t* rec = tile + TL::kRecord;
   const uint32_t pending = ~*reinterpret_cast<const volatile uint32_t*>(rec + 12) & 0xFFFFu;
   if (!(pending & (1u << off))) return;              // not opened by this call
   if (off != __builtin_ctz(pending)) return;          // not the leader
-  const int32_t* parked = reinterpret_cast<const int32_t*>(sd.tok_scale) + bh * kBlock;
+  const int32_t* parked = reinterpret_cast<const int32_t*>(tile + TL::kScale);
 
   // Per-channel RMS over this call's rows in the block, rows taken in ascending offset.
   constexpr int CPL = D / 64;  // channels per lane: lane + 64 * k
@@ -227,6 +240,7 @@ __global__ __launch_bounds__(64) void k_fp4_calibrate(Fp4Args a) {
 // One wave per (row, head, K|V); lane l owns channels 2l and 2l + 1 (one packed byte).
 template <bool BF16, int D>
 __global__ __launch_bounds__(64) void k_fp4_encode(Fp4Args a) {
+  using TL = Fp4Tile<D>;
   const int i = blockIdx.x, h = blockIdx.y;
   const Fp4Side& sd = a.side[blockIdx.z];
   const int lane = threadIdx.x;
@@ -234,7 +248,8 @@ __global__ __launch_bounds__(64) void k_fp4_encode(Fp4Args a) {
   if (slot < 0 || slot >= a.nslots) return;
   const int64_t bh = (slot >> 4) * a.hkv + h;
   const int off = (int)(slot & 15);
-  uint8_t* rec = sd.out_idx + bh * 16;
+  uint8_t* tile = sd.tiles + bh * TL::kBytes;
+  uint8_t* rec = tile + TL::kRecord;
   const uint4 r4 = *reinterpret_cast<const uint4*>(rec);  // bytes 12..15 ignored
   const uint32_t rw[3] = {r4.x, r4.y, r4.z};
   int count = (int)(rw[0] & 0xFFu);
@@ -267,18 +282,21 @@ __global__ __launch_bounds__(64) void k_fp4_encode(Fp4Args a) {
     q0 = out0 ? 0u : encode_e2m1(x0 / s);
     q1 = out1 ? 0u : encode_e2m1(x1 / s);
   }
-  const int64_t row_slot = bh * kBlock + off;
-  if (active) sd.codes[row_slot * (D / 2) + lane] = (uint8_t)(q0 | (q1 << 4));
+  if (active) tile[off * (D / 2) + lane] = (uint8_t)(q0 | (q1 << 4));
   for (int j = 0; j < count; ++j) {
     const int pos = 1 + j;
     const int c = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
     if (active && (c >> 1) == lane) {
       const float xv = (c & 1) ? x1 : x0;
-      sd.out_val[(bh * a.cap + j) * kBlock + off] = bitcast<uint16_t>((_Float16)xv);
+      const uint16_t hv = bitcast<uint16_t>((_Float16)xv);
+      if (j == 0)
+        reinterpret_cast<uint16_t*>(tile + TL::kSlot0)[off] = hv;
+      else
+        sd.out_val[(bh * (a.cap - 1) + (j - 1)) * kBlock + off] = hv;
     }
   }
   if (lane == 0) {
-    sd.tok_scale[row_slot] = s;
+    reinterpret_cast<float*>(tile + TL::kScale)[off] = s;
     *reinterpret_cast<uint32_t*>(rec + 12) = 0xFFFFFFFFu;
   }
 }
@@ -321,17 +339,19 @@ __global__ void k_scale_finish(uint32_t* bits, int32_t hkv) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_reset_records(uint4* idx_k, uint4* idx_v,
+template <int D>
+__global__ __launch_bounds__(256) void k_reset_records(uint8_t* tiles_k, uint8_t* tiles_v,
                                                        const int32_t* __restrict__ ids, int32_t n,
                                                        int32_t hkv, int32_t nb) {
+  using TL = Fp4Tile<D>;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= (int64_t)n * hkv) return;
   const int32_t b = ids[t / hkv];
   if (b < 0 || b >= nb) return;
   const int64_t bh = (int64_t)b * hkv + t % hkv;
   const uint4 ff = make_uint4(~0u, ~0u, ~0u, ~0u);
-  idx_k[bh] = ff;
-  idx_v[bh] = ff;
+  *reinterpret_cast<uint4*>(tiles_k + bh * TL::kBytes + TL::kRecord) = ff;
+  *reinterpret_cast<uint4*>(tiles_v + bh * TL::kBytes + TL::kRecord) = ff;
 }
 
 // ---------------------------------------------------------------------------------
@@ -359,8 +379,8 @@ int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool
                        total, hkv, chunks, nslots, err);
   } else {
     Fp4Args a;
-    a.side[0] = {(const uint16_t*)k_new, (uint8_t*)p.k, p.k_tok_scale, p.k_out_idx, p.k_out_val};
-    a.side[1] = {(const uint16_t*)v_new, (uint8_t*)p.v, p.v_tok_scale, p.v_out_idx, p.v_out_val};
+    a.side[0] = {(const uint16_t*)k_new, (uint8_t*)p.k, p.k_out_val};
+    a.side[1] = {(const uint16_t*)v_new, (uint8_t*)p.v, p.v_out_val};
     a.slots = slots;
     a.num_tokens = T;
     a.hkv = hkv;
@@ -368,17 +388,15 @@ int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool
     a.cap = outlier_capacity(D);
     a.nslots = nslots;
     a.err = err;
-    hipLaunchKernelGGL(k_fp4_mark, dim3(grid1((int64_t)T * hkv, 256), 1, 2), dim3(256), 0, st, a);
+    // (the FP4 format exists for head_dim 128 only)
+    hipLaunchKernelGGL(k_fp4_mark<128>, dim3(grid1((int64_t)T * hkv, 256), 1, 2), dim3(256), 0,
+                       st, a);
     const dim3 g(T, hkv, 2);
     void (*cal)(Fp4Args);
     void (*enc)(Fp4Args);
-    if (D == 128) {
-      cal = bf16 ? k_fp4_calibrate<true, 128> : k_fp4_calibrate<false, 128>;
-      enc = bf16 ? k_fp4_encode<true, 128> : k_fp4_encode<false, 128>;
-    } else {
-      cal = bf16 ? k_fp4_calibrate<true, 64> : k_fp4_calibrate<false, 64>;
-      enc = bf16 ? k_fp4_encode<true, 64> : k_fp4_encode<false, 64>;
-    }
+    if (D != 128) return PA_ERR_SHAPE;
+    cal = bf16 ? k_fp4_calibrate<true, 128> : k_fp4_calibrate<false, 128>;
+    enc = bf16 ? k_fp4_encode<true, 128> : k_fp4_encode<false, 128>;
     hipLaunchKernelGGL(cal, g, dim3(64), 0, st, a);
     hipLaunchKernelGGL(enc, g, dim3(64), 0, st, a);
   }
@@ -405,9 +423,9 @@ int launch_fp8_scales(const void* x, bool bf16, int64_t rows, int32_t hkv, int32
 int launch_reset(const pa_kv_pool& p, const int32_t* ids, int32_t n, hipStream_t st) {
   if (n == 0) return PA_OK;
   const int64_t total = (int64_t)n * p.num_kv_heads;
-  hipLaunchKernelGGL(k_reset_records, dim3(grid1(total, 256)), dim3(256), 0, st,
-                     (uint4*)p.k_out_idx, (uint4*)p.v_out_idx, ids, n, p.num_kv_heads,
-                     p.num_blocks);
+  if (p.head_dim != 128) return PA_ERR_SHAPE;
+  hipLaunchKernelGGL(k_reset_records<128>, dim3(grid1(total, 256)), dim3(256), 0, st,
+                     (uint8_t*)p.k, (uint8_t*)p.v, ids, n, p.num_kv_heads, p.num_blocks);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

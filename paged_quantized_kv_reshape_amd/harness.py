@@ -106,7 +106,7 @@ def outlier_counts(run) -> dict:
     (read from the device pool's records; 0xFF = never written counts 0)."""
     out = {}
     for side in ("k", "v"):
-        rec = run.pool.bytes[side + "_out_idx"].view(-1, 16)[:, 0].to(torch.int32)
+        rec = run.pool.fp4_records(side)[:, :, 0].to(torch.int32)
         out[side] = int(torch.where(rec == 0xFF, torch.zeros_like(rec), rec).sum().item())
     return out
 

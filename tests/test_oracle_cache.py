@@ -180,18 +180,22 @@ def test_fp4_calibrates_once_per_block_and_reuses():
     k1, k2 = _bf16_bits(x1), _bf16_bits(x2)
     pool = C.Pool.filled("fp4", 4, hkv, d)
     C.cache_write(pool, k1, k1, "bf16", np.array([32, 33, 34, 35]))  # block 2, offsets 0-3
-    rec = pool.arrays["k_out_idx"][2, 0]
+    rec = C.fp4_records(pool, "k")[2, 0].copy()
     assert rec[0] == 1 and rec[1] == 9 and np.all(rec[2:] == 0xFF)
     C.cache_write(pool, k2, k2, "bf16", np.array([36, 37, 38, 39]))
-    assert np.array_equal(pool.arrays["k_out_idx"][2, 0], rec)  # reused, not recomputed
+    assert np.array_equal(C.fp4_records(pool, "k")[2, 0], rec)  # reused, not recomputed
     kd, _ = C.dequant_slot_rows(pool, np.full(8, 2), np.arange(8))
     xall = F.bf16_decode(np.concatenate([k1, k2]))
     # the outlier channel comes back exactly (fp16 holds bf16 values exactly)
     assert np.array_equal(kd[:, 0, 9], xall[:, 0, 9])
-    # untouched offsets and the unused outlier slots keep their sentinel bytes
-    assert np.all(pool.arrays["k"][2, 0, 8:].view(np.uint8) == 0xA5)
-    assert np.all(pool.arrays["k_out_val"][2, 0, 1:].view(np.uint8) == 0xA5)
-    assert np.all(pool.arrays["k_out_idx"][[0, 1, 3]] == 0xFF)
+    # untouched offsets (codes, scales, first-outlier values), the unused outlier slots
+    # and the tile's padding keep their sentinel bytes
+    assert np.all(C.fp4_codes(pool, "k")[2, 0, 8:] == 0xA5)
+    assert np.all(C.fp4_scales(pool, "k")[2, 0, 8:].view(np.uint8) == 0xA5)
+    assert np.all(C.fp4_slot0(pool, "k")[2, 0, 8:] == 0xA5A5)
+    assert np.all(pool.arrays["k_out_val"][2, 0].view(np.uint8) == 0xA5)
+    assert np.all(pool.arrays["k"][2, 0, 16 * d // 2 + 112:] == 0xA5)
+    assert np.all(C.fp4_records(pool, "k")[[0, 1, 3]] == 0xFF)
 
 
 def test_fp4_calibration_uses_only_the_calls_tokens_in_the_block():
@@ -203,8 +207,8 @@ def test_fp4_calibration_uses_only_the_calls_tokens_in_the_block():
     bits = _bf16_bits(x)
     pool = C.Pool.filled("fp4", 2, 1, d)
     C.cache_write(pool, bits, bits, "bf16", np.array([3, 16, 17]))
-    assert pool.arrays["k_out_idx"][0, 0, :2].tolist() == [1, 10]
-    assert pool.arrays["k_out_idx"][1, 0, :3].tolist() == [2, 20, 21]
+    assert C.fp4_records(pool, "k")[0, 0, :2].tolist() == [1, 10]
+    assert C.fp4_records(pool, "k")[1, 0, :3].tolist() == [2, 20, 21]
 
 
 def test_fp8_code_is_e4m3_of_the_fp32_quotient():

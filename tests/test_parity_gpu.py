@@ -175,7 +175,7 @@ def test_fp4_reset_blocks_and_uncalibrated_read():
     n0 = -(-int(w.context_lens[0]) // 16)
     ids = run.block_tables[0, :n0].contiguous()
     pa_reset_blocks(run.pool, ids)
-    rec = run.pool.bytes["k_out_idx"].view(w.num_blocks, w.num_kv_heads, 16)
+    rec = run.pool.fp4_records("k")
     assert bool((rec[ids.long()] == 0xFF).all())
     run.dev_err.zero_()
     run.decode()
@@ -291,7 +291,7 @@ def test_full_size_sampled(cfg):
     if w.kv == "fp4":
         # every full 16-token block calibrated by a prefill chunk flags exactly the
         # planted x20 channel (known a priori from the generator)
-        rec = run.pool.numpy()["k_out_idx"].reshape(w.num_blocks, w.num_kv_heads, 16)
+        rec = run.pool.fp4_records("k").cpu().numpy()
         s = seqs[0]
         full = w.block_tables[s, :(int(w.context_lens[s]) - 1) // 16]
         pk = int(w.planted_k[0]) % w.head_dim
