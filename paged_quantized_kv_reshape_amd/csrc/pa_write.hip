@@ -157,12 +157,16 @@ __global__ __launch_bounds__(256) void k_fp4_mark(Fp4Args a) {
 }
 
 // One wave per (row, head, K|V); only block leaders do work.
+constexpr int kRowsPerWg = 4;  // FP4 calibrate / encode: one wave per row, 4 rows per workgroup
+
 template <bool BF16, int D>
-__global__ __launch_bounds__(64) void k_fp4_calibrate(Fp4Args a) {
+__global__ __launch_bounds__(64 * kRowsPerWg) void k_fp4_calibrate(Fp4Args a) {
   using TL = Fp4Tile<D>;
-  const int i = blockIdx.x, h = blockIdx.y;
+  const int i = blockIdx.x * kRowsPerWg + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.y;
   const Fp4Side& sd = a.side[blockIdx.z];
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  if (i >= a.num_tokens) return;
   const int64_t slot = a.slots[i];
   if (slot < 0 || slot >= a.nslots) return;
   const int64_t bh = (slot >> 4) * a.hkv + h;
@@ -175,27 +179,39 @@ __global__ __launch_bounds__(64) void k_fp4_calibrate(Fp4Args a) {
   const int32_t* parked = reinterpret_cast<const int32_t*>(tile + TL::kScale);
 
   // Per-channel RMS over this call's rows in the block, rows taken in ascending offset.
+  // Lane o < 16 fetches the parked row index of offset o and checks it against the slot
+  // mapping (a parked index is trusted only if that row really targets this slot: a
+  // record that did not start as all 0xFF could carry stray cleared bits); then every
+  // row's values are loaded before any is summed, so the loads overlap.
   constexpr int CPL = D / 64;  // channels per lane: lane + 64 * k
+  const int64_t blk_base = (slot >> 4) << 4;
+  int my_row = -1;
+  if (lane < 16 && ((pending >> lane) & 1u)) {
+    const int32_t row = parked[lane];
+    if (row >= 0 && row < a.num_tokens && a.slots[row] == blk_base + lane) my_row = row;
+  }
+  const uint32_t rows = (uint32_t)__builtin_amdgcn_ballot_w64(my_row >= 0) & 0xFFFFu;
+  if (rows == 0) return;
+  const int n = __builtin_popcount(rows);
+  float xv[kBlock][CPL];
+#pragma unroll
+  for (int o = 0; o < kBlock; ++o) {
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) xv[o][k] = 0.0f;
+    if (rows & (1u << o)) {  // wave-uniform
+      const int64_t row = __builtin_amdgcn_readlane(my_row, o);
+      const uint16_t* x = sd.rows + (row * a.hkv + h) * D;
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) xv[o][k] = act_to_f32<BF16>(x[lane + 64 * k]);
+    }
+  }
   float ss[CPL];
 #pragma unroll
-  for (int k = 0; k < CPL; ++k) ss[k] = 0.0f;
-  int n = 0;
-  const int64_t blk_base = (slot >> 4) << 4;
-  for (uint32_t m = pending; m; m &= m - 1) {
-    const int o = __builtin_ctz(m);
-    const int64_t row = parked[o];
-    // a parked index is trusted only if that row really targets this slot (a record that
-    // did not start as all 0xFF could carry stray cleared bits)
-    if (row < 0 || row >= a.num_tokens || a.slots[row] != blk_base + o) continue;
-    const uint16_t* x = sd.rows + (row * a.hkv + h) * D;
+  for (int k = 0; k < CPL; ++k) {
+    ss[k] = 0.0f;
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-      const float v = act_to_f32<BF16>(x[lane + 64 * k]);
-      ss[k] = __builtin_fmaf(v, v, ss[k]);
-    }
-    ++n;
+    for (int o = 0; o < kBlock; ++o) ss[k] = __builtin_fmaf(xv[o][k], xv[o][k], ss[k]);  // +0 for absent rows
   }
-  if (n == 0) return;
   float r[CPL], part = 0.0f;
 #pragma unroll
   for (int k = 0; k < CPL; ++k) {
@@ -239,11 +255,13 @@ __global__ __launch_bounds__(64) void k_fp4_calibrate(Fp4Args a) {
 
 // One wave per (row, head, K|V); lane l owns channels 2l and 2l + 1 (one packed byte).
 template <bool BF16, int D>
-__global__ __launch_bounds__(64) void k_fp4_encode(Fp4Args a) {
+__global__ __launch_bounds__(64 * kRowsPerWg) void k_fp4_encode(Fp4Args a) {
   using TL = Fp4Tile<D>;
-  const int i = blockIdx.x, h = blockIdx.y;
+  const int i = blockIdx.x * kRowsPerWg + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = blockIdx.y;
   const Fp4Side& sd = a.side[blockIdx.z];
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  if (i >= a.num_tokens) return;
   const int64_t slot = a.slots[i];
   if (slot < 0 || slot >= a.nslots) return;
   const int64_t bh = (slot >> 4) * a.hkv + h;
@@ -391,14 +409,14 @@ int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool
     // (the FP4 format exists for head_dim 128 only)
     hipLaunchKernelGGL(k_fp4_mark<128>, dim3(grid1((int64_t)T * hkv, 256), 1, 2), dim3(256), 0,
                        st, a);
-    const dim3 g(T, hkv, 2);
+    const dim3 g((unsigned)((T + kRowsPerWg - 1) / kRowsPerWg), hkv, 2);
     void (*cal)(Fp4Args);
     void (*enc)(Fp4Args);
     if (D != 128) return PA_ERR_SHAPE;
     cal = bf16 ? k_fp4_calibrate<true, 128> : k_fp4_calibrate<false, 128>;
     enc = bf16 ? k_fp4_encode<true, 128> : k_fp4_encode<false, 128>;
-    hipLaunchKernelGGL(cal, g, dim3(64), 0, st, a);
-    hipLaunchKernelGGL(enc, g, dim3(64), 0, st, a);
+    hipLaunchKernelGGL(cal, g, dim3(64 * kRowsPerWg), 0, st, a);
+    hipLaunchKernelGGL(enc, g, dim3(64 * kRowsPerWg), 0, st, a);
   }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
