@@ -20,76 +20,130 @@ __device__ __forceinline__ void flag(int32_t* err, int32_t bit) {
 }
 
 // ---------------------------------------------------------------------------------
-// 16-bit copy: one thread per 16 bytes of a (token, head) row.
+// 16-bit copy and FP8: grid (row chunks, kv head). Thread t of the x range handles chunk
+// t % CH of token t / CH for the head blockIdx.y, CH = threads per (token, head) row (a
+// power of two, so the split is a shift).
 // ---------------------------------------------------------------------------------
+template <int CH>
+__device__ __forceinline__ bool row_chunk(int32_t T, int32_t hkv, const int64_t* __restrict__ slots,
+                                          int64_t nslots, int32_t* err, int64_t& src,
+                                          int64_t& dst) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = idx / CH;
+  const int c = (int)(idx & (CH - 1));
+  const int h = blockIdx.y;
+  if (i >= T) return false;
+  const int64_t slot = slots[i];
+  if (slot < 0) return false;
+  if (slot >= nslots) {
+    if (c == 0) flag(err, PA_DEVERR_BAD_SLOT);
+    return false;
+  }
+  src = (i * hkv + h) * CH + c;
+  dst = (((slot >> 4) * hkv + h) * kBlock + (slot & 15)) * CH + c;
+  return true;
+}
+
+template <int CH>
 __global__ __launch_bounds__(256) void k_write_copy(const uint4* __restrict__ k_new,
                                                     const uint4* __restrict__ v_new,
                                                     uint4* __restrict__ k_pool,
                                                     uint4* __restrict__ v_pool,
                                                     const int64_t* __restrict__ slots,
-                                                    int64_t total, int32_t hkv, int32_t chunks,
-                                                    int64_t nslots, int32_t* err) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int64_t per_tok = (int64_t)hkv * chunks;
-  const int64_t i = idx / per_tok;
-  const int64_t rem = idx - i * per_tok;
-  const int64_t slot = slots[i];
-  if (slot < 0) return;
-  if (slot >= nslots) {
-    if (rem == 0) flag(err, PA_DEVERR_BAD_SLOT);
-    return;
-  }
-  const int64_t h = rem / chunks, c = rem - h * chunks;
-  const int64_t dst = (((slot >> 4) * hkv + h) * kBlock + (slot & 15)) * chunks + c;
-  k_pool[dst] = k_new[idx];
-  v_pool[dst] = v_new[idx];
+                                                    int32_t T, int32_t hkv, int64_t nslots,
+                                                    int32_t* err) {
+  int64_t src, dst;
+  if (!row_chunk<CH>(T, hkv, slots, nslots, err, src, dst)) return;
+  k_pool[dst] = k_new[src];
+  v_pool[dst] = v_new[src];
 }
 
-// ---------------------------------------------------------------------------------
-// FP8 E4M3: one thread per 8 values of a (token, head) row, K and V.
-// code = E4M3(fp32(x / s_h)); the fp32 division is IEEE correctly rounded.
-// ---------------------------------------------------------------------------------
+// FP8 E4M3, 16 values per thread: code = E4M3(fp32(x / s_h)), with the fp32 quotient
+// correctly rounded.
+//
+// The quotient x / |s| comes from y = fp32(1 / |s|) (correctly rounded, once per thread)
+// and two correction steps: q <- q - (|s| q - x) y, each remainder |s| q - x formed by one
+// fma; a negative scale then flips the codes' sign bits (the encoding is symmetric).
+// Starting from q = fp32(x y), within 2 ulps of x / s, the first step lands within one
+// ulp, and from there one step with a correctly rounded reciprocal gives the correctly
+// rounded quotient (Markstein's theorem on fma-based division), so the fast form is
+// exact, not a guess with a fallback. It needs no overflow and no underflow of the
+// remainder where the code is decided: x is first clamped to +-fp32(440 |s|) (any
+// |x / s| > 440 saturates to the code of 448 either way, and the clamped quotient stays
+// inside the E4M3 range), and 2^-80 <= |s| <= 2^100 keeps every remainder of a quotient
+// above 2^-20 exact (smaller quotients encode as a signed zero, and the steps keep the
+// quotient's sign, that of zero included, as y > 0). Other scales, and NaN inputs, take
+// the IEEE division and the software encoder.
+//
+// gfx950's fp32 -> E4M3 conversion (v_cvt_pk_fp8_f32: nearest, ties to even) gives the
+// same byte as the software encoder for every non-NaN fp32 input in [-448, 448].
 template <bool BF16>
-__device__ __forceinline__ uint2 fp8_encode8(const uint4 in, float s) {
-  const uint32_t w[4] = {in.x, in.y, in.z, in.w};
-  uint32_t out[2] = {0u, 0u};
-  if (s != 0.0f) {
+__device__ __forceinline__ uint32_t act_nan_pair(uint32_t u) {
+  // nonzero when a 16-bit half is a NaN: |bits| above the infinity pattern (0x7F80 bf16,
+  // 0x7C00 fp16) carries into bit 15
+  return ((u & 0x7FFF7FFFu) + (BF16 ? 0x007F007Fu : 0x03FF03FFu)) & 0x80008000u;
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint4 fp8_encode16(const uint4 lo, const uint4 hi, float s, bool fast) {
+  const float sa = __builtin_fabsf(s);
+  const float y = 1.0f / sa, bound = 440.0f * sa;
+  const uint32_t flip = s < 0.0f ? 0x80808080u : 0u;
+  const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  float x[16], q[16];
+  uint32_t nan = 0u;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t b16 = (w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-      const float x = act_to_f32<BF16>(b16);
-      out[e >> 2] |= encode_e4m3(x / s) << ((e & 3) * 8);
+  for (int e = 0; e < 16; ++e) {
+    x[e] = act_to_f32<BF16>((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+    const float xc = __builtin_amdgcn_fmed3f(x[e], -bound, bound);
+    float t = xc * y;
+    float r = __builtin_fmaf(sa, t, -xc);
+    t = __builtin_fmaf(-r, y, t);
+    r = __builtin_fmaf(sa, t, -xc);
+    q[e] = __builtin_fmaf(-r, y, t);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) nan |= act_nan_pair<BF16>(w[i]);
+  // byte j of the result holds value j
+  uint32_t out[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[4 * i], q[4 * i + 1], 0, false);
+    out[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[4 * i + 2], q[4 * i + 3], (int)out[i],
+                                                       true) ^ flip;
+  }
+  if (!fast || nan != 0u) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[i] = 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[i] |= encode_e4m3(x[4 * i + j] / s) << (8 * j);
     }
   }
-  return make_uint2(out[0], out[1]);
+  if (s == 0.0f) out[0] = out[1] = out[2] = out[3] = 0u;  // a zero scale stores zero codes
+  return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
-template <bool BF16>
+template <bool BF16, int CH>
 __global__ __launch_bounds__(256) void k_write_fp8(const uint4* __restrict__ k_new,
                                                    const uint4* __restrict__ v_new,
-                                                   uint2* __restrict__ k_pool,
-                                                   uint2* __restrict__ v_pool,
+                                                   uint4* __restrict__ k_pool,
+                                                   uint4* __restrict__ v_pool,
                                                    const float* __restrict__ k_scale,
                                                    const float* __restrict__ v_scale,
                                                    const int64_t* __restrict__ slots,
-                                                   int64_t total, int32_t hkv, int32_t chunks,
-                                                   int64_t nslots, int32_t* err) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int64_t per_tok = (int64_t)hkv * chunks;
-  const int64_t i = idx / per_tok;
-  const int64_t rem = idx - i * per_tok;
-  const int64_t slot = slots[i];
-  if (slot < 0) return;
-  if (slot >= nslots) {
-    if (rem == 0) flag(err, PA_DEVERR_BAD_SLOT);
-    return;
-  }
-  const int64_t h = rem / chunks, c = rem - h * chunks;
-  const int64_t dst = (((slot >> 4) * hkv + h) * kBlock + (slot & 15)) * chunks + c;
-  k_pool[dst] = fp8_encode8<BF16>(k_new[idx], k_scale[h]);
-  v_pool[dst] = fp8_encode8<BF16>(v_new[idx], v_scale[h]);
+                                                   int32_t T, int32_t hkv, int64_t nslots,
+                                                   int32_t* err) {
+  int64_t src, dst;  // in 16-value chunks
+  if (!row_chunk<CH>(T, hkv, slots, nslots, err, src, dst)) return;
+  const int h = blockIdx.y;
+  const float sk = k_scale[h], sv = v_scale[h];
+  const bool fk = __builtin_fabsf(sk) >= 0x1p-80f && __builtin_fabsf(sk) <= 0x1p100f;
+  const bool fv = __builtin_fabsf(sv) >= 0x1p-80f && __builtin_fabsf(sv) <= 0x1p100f;
+  const uint4 k0 = k_new[2 * src], k1 = k_new[2 * src + 1];
+  const uint4 v0 = v_new[2 * src], v1 = v_new[2 * src + 1];
+  k_pool[dst] = fp8_encode16<BF16>(k0, k1, sk, fk);
+  v_pool[dst] = fp8_encode16<BF16>(v0, v1, sv, fv);
 }
 
 // ---------------------------------------------------------------------------------
@@ -382,19 +436,21 @@ int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool
   const int64_t nslots = (int64_t)p.num_blocks * kBlock;
   const int D = p.head_dim, hkv = p.num_kv_heads;
   if (T == 0) return PA_OK;
+  if (hkv > 65535) return PA_ERR_SHAPE;  // heads index grid.y
   if (p.dtype == PA_KV_F16 || p.dtype == PA_KV_BF16) {
     const int chunks = D * 2 / 16;
-    const int64_t total = (int64_t)T * hkv * chunks;
-    hipLaunchKernelGGL(k_write_copy, dim3(grid1(total, 256)), dim3(256), 0, st,
-                       (const uint4*)k_new, (const uint4*)v_new, (uint4*)p.k, (uint4*)p.v, slots,
-                       total, hkv, chunks, nslots, err);
+    const dim3 g(grid1((int64_t)T * chunks, 256), hkv);
+    auto kern = D == 128 ? k_write_copy<16> : k_write_copy<8>;
+    hipLaunchKernelGGL(kern, g, dim3(256), 0, st, (const uint4*)k_new, (const uint4*)v_new,
+                       (uint4*)p.k, (uint4*)p.v, slots, T, hkv, nslots, err);
   } else if (p.dtype == PA_KV_FP8_E4M3) {
-    const int chunks = D / 8;
-    const int64_t total = (int64_t)T * hkv * chunks;
-    auto kern = bf16 ? k_write_fp8<true> : k_write_fp8<false>;
-    hipLaunchKernelGGL(kern, dim3(grid1(total, 256)), dim3(256), 0, st, (const uint4*)k_new,
-                       (const uint4*)v_new, (uint2*)p.k, (uint2*)p.v, p.k_scale, p.v_scale, slots,
-                       total, hkv, chunks, nslots, err);
+    const int chunks = D / 16;
+    const dim3 g(grid1((int64_t)T * chunks, 256), hkv);
+    auto kern = bf16 ? (D == 128 ? k_write_fp8<true, 8> : k_write_fp8<true, 4>)
+                     : (D == 128 ? k_write_fp8<false, 8> : k_write_fp8<false, 4>);
+    hipLaunchKernelGGL(kern, g, dim3(256), 0, st, (const uint4*)k_new, (const uint4*)v_new,
+                       (uint4*)p.k, (uint4*)p.v, p.k_scale, p.v_scale, slots, T, hkv, nslots,
+                       err);
   } else {
     Fp4Args a;
     a.side[0] = {(const uint16_t*)k_new, (uint8_t*)p.k, p.k_out_val};

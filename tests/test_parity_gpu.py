@@ -296,3 +296,78 @@ def test_full_size_sampled(cfg):
         full = w.block_tables[s, :(int(w.context_lens[s]) - 1) // 16]
         pk = int(w.planted_k[0]) % w.head_dim
         assert np.all(rec[full, 0, 0] == 1) and np.all(rec[full, 0, 1] == pk)
+
+
+# Scales of the FP8 sweep: reciprocals that are exact and inexact, a negative scale, a zero
+# scale (zero codes); absmax / 448 scales as the head-scale call makes them (quotients
+# 448 x / absmax of two 16-bit values land on and beside E4M3 midpoints); scales at both
+# ends of the range the fast quotient accepts and just outside it (2^-81, 2^101, 1e-39,
+# 2^126), a large scale that drives quotients of small inputs below fp32's normal range;
+# and 3 moved by k = +-1..8 fp32 ulps, which puts the quotients of x = 3 m (m an E4M3
+# midpoint) within a few ulps on either side of m.
+FP8_SWEEP_SCALES = (
+    [3.0, 1.0 / 3.0, 0.0123, -0.37, 1.0, 0.0]
+    + [float(np.float32(b) / np.float32(448.0)) for b in (108.0, 96.0, 6.5, 0.8125, 21.25)]
+    + [2.0 ** -80, 2.0 ** -81, 2.0 ** 100, 2.0 ** 101, 1e-39, 2.0 ** 126, 2.0 ** 17, -(2.0 ** 40)]
+    + [float(np.float32(3.0) + np.float32(k) * np.spacing(np.float32(3.0)))
+       for k in range(-8, 9) if k != 0])
+
+
+@pytest.mark.parametrize("act,d", [("bf16", 128), ("f16", 128), ("bf16", 64), ("f16", 64)])
+def test_fp8_write_every_input(act, d):
+    """Every non-NaN 16-bit activation pattern through the FP8 write, under scales that put
+    exact quotients on E4M3 rounding midpoints (x = 3 m for a midpoint m and s = 3), must
+    give the oracle's codes bit for bit."""
+    from oracle import cache as C
+    from oracle.formats import act_decode, e4m3_magnitudes, f32_quotient
+    from paged_quantized_kv_reshape_amd import KVPool, pa_cache_write
+    pats = np.arange(65536, dtype=np.uint32)
+    inf_bits = 0x7F80 if act == "bf16" else 0x7C00
+    pats = np.where((pats & 0x7FFF) > inf_bits, 0, pats).astype(np.uint16)
+    hkv, T = len(FP8_SWEEP_SCALES), 65536 // d
+    rng = np.random.default_rng(7)
+    k_rows = np.stack([rng.permutation(pats) for _ in range(hkv)], 1).reshape(T, d, hkv)
+    k_rows = np.ascontiguousarray(k_rows.transpose(0, 2, 1))
+    v_rows = np.ascontiguousarray(k_rows[::-1])
+    nb = T // 16 + 3
+    slots = rng.permutation(nb * 16)[:T].astype(np.int64)
+    scales = np.asarray(FP8_SWEEP_SCALES, dtype=np.float32)
+
+    # the sweep holds quotients that sit exactly on an E4M3 midpoint
+    mags = e4m3_magnitudes()
+    mids = (mags[1:] + mags[:-1]) / 2
+    x = act_decode(k_rows, act)
+    q = np.abs(f32_quotient(x[:, 0, :], np.float64(scales[0])))
+    assert np.isin(q, mids).sum() > 0
+    # ... and quotients a few ulps beside one (up to 8 ulps on each side)
+    q = np.abs(f32_quotient(x[:, -16:, :], scales[None, -16:, None].astype(np.float64)))
+    j = np.clip(np.searchsorted(mids, q), 1, len(mids) - 1)
+    gap = np.minimum(np.abs(q - mids[j]), np.abs(q - mids[j - 1]))
+    ulps = gap / np.spacing(q.astype(np.float32)).astype(np.float64)
+    assert ((ulps > 0) & (ulps <= 8)).sum() > 100
+
+    opool = C.Pool.filled("fp8", nb, hkv, d)
+    C.cache_write(opool, k_rows, v_rows, act, slots, k_scale=scales, v_scale=scales[::-1].copy())
+    ks = torch.from_numpy(scales).cuda()
+    vs = torch.from_numpy(scales[::-1].copy()).cuda()
+    pool = KVPool("fp8", nb, hkv, d, fill=0xA5, k_scale=ks, v_scale=vs)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tdt = torch.bfloat16 if act == "bf16" else torch.float16
+    kt = torch.from_numpy(k_rows.view(np.int16)).cuda().view(tdt)
+    vt = torch.from_numpy(v_rows.view(np.int16)).cuda().view(tdt)
+    _say(f"[fp8 sweep] act={act} d={d} T={T} hkv={hkv}")
+    pa_cache_write(pool, kt, vt, torch.from_numpy(slots).cuda(), err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    tok = np.full(nb * 16, -1)
+    tok[slots] = np.arange(T)
+    got = pool.numpy()
+    for name, rows, sc in (("k", k_rows, scales), ("v", v_rows, scales[::-1])):
+        g = got[name].reshape(nb, hkv, 16, d)
+        o = opool.arrays[name]
+        bad = np.argwhere(g != o)
+        msg = [f"{name}: x=0x{int(rows[tok[b * 16 + r], h, c]):04x} s={sc[h]!r} "
+               f"gpu=0x{int(g[b, h, r, c]):02x} oracle=0x{int(o[b, h, r, c]):02x}"
+               for b, h, r, c in bad[:8]]
+        assert len(bad) == 0, f"{len(bad)} codes differ:\n" + "\n".join(msg)
+    assert_pool_equal(got, opool)
