@@ -20,26 +20,29 @@ __device__ __forceinline__ void flag(int32_t* err, int32_t bit) {
 }
 
 // ---------------------------------------------------------------------------------
-// 16-bit copy and FP8: grid (row chunks, kv head). Thread t of the x range handles chunk
-// t % CH of token t / CH for the head blockIdx.y, CH = threads per (token, head) row (a
-// power of two, so the split is a shift).
+// 16-bit copy and FP8: one thread per 16-byte input chunk (copy) or per 16 values (FP8)
+// of a (token, head) row; consecutive threads walk chunk, then head, then token, so a
+// workgroup reads whole token rows. CH = threads per (token, head) row, a power of two.
+// The launcher keeps T * Hkv * CH below 2^31, so the index math is 32-bit.
 // ---------------------------------------------------------------------------------
 template <int CH>
 __device__ __forceinline__ bool row_chunk(int32_t T, int32_t hkv, const int64_t* __restrict__ slots,
                                           int64_t nslots, int32_t* err, int64_t& src,
-                                          int64_t& dst) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t i = idx / CH;
-  const int c = (int)(idx & (CH - 1));
-  const int h = blockIdx.y;
-  if (i >= T) return false;
+                                          int64_t& dst, int& h) {
+  const uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t per_tok = (uint32_t)hkv * CH;
+  const uint32_t i = idx / per_tok;
+  const uint32_t rem = idx - i * per_tok;
+  const int c = (int)(rem & (CH - 1));
+  h = (int)(rem / CH);
+  if (i >= (uint32_t)T) return false;
   const int64_t slot = slots[i];
   if (slot < 0) return false;
   if (slot >= nslots) {
     if (c == 0) flag(err, PA_DEVERR_BAD_SLOT);
     return false;
   }
-  src = (i * hkv + h) * CH + c;
+  src = ((int64_t)i * hkv + h) * CH + c;
   dst = (((slot >> 4) * hkv + h) * kBlock + (slot & 15)) * CH + c;
   return true;
 }
@@ -53,7 +56,8 @@ __global__ __launch_bounds__(256) void k_write_copy(const uint4* __restrict__ k_
                                                     int32_t T, int32_t hkv, int64_t nslots,
                                                     int32_t* err) {
   int64_t src, dst;
-  if (!row_chunk<CH>(T, hkv, slots, nslots, err, src, dst)) return;
+  int h;
+  if (!row_chunk<CH>(T, hkv, slots, nslots, err, src, dst, h)) return;
   k_pool[dst] = k_new[src];
   v_pool[dst] = v_new[src];
 }
@@ -135,8 +139,8 @@ __global__ __launch_bounds__(256) void k_write_fp8(const uint4* __restrict__ k_n
                                                    int32_t T, int32_t hkv, int64_t nslots,
                                                    int32_t* err) {
   int64_t src, dst;  // in 16-value chunks
-  if (!row_chunk<CH>(T, hkv, slots, nslots, err, src, dst)) return;
-  const int h = blockIdx.y;
+  int h;
+  if (!row_chunk<CH>(T, hkv, slots, nslots, err, src, dst, h)) return;
   const float sk = k_scale[h], sv = v_scale[h];
   const bool fk = __builtin_fabsf(sk) >= 0x1p-80f && __builtin_fabsf(sk) <= 0x1p100f;
   const bool fv = __builtin_fabsf(sv) >= 0x1p-80f && __builtin_fabsf(sv) <= 0x1p100f;
@@ -436,22 +440,32 @@ int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool
   const int64_t nslots = (int64_t)p.num_blocks * kBlock;
   const int D = p.head_dim, hkv = p.num_kv_heads;
   if (T == 0) return PA_OK;
-  if (hkv > 65535) return PA_ERR_SHAPE;  // heads index grid.y
-  if (p.dtype == PA_KV_F16 || p.dtype == PA_KV_BF16) {
-    const int chunks = D * 2 / 16;
-    const dim3 g(grid1((int64_t)T * chunks, 256), hkv);
-    auto kern = D == 128 ? k_write_copy<16> : k_write_copy<8>;
-    hipLaunchKernelGGL(kern, g, dim3(256), 0, st, (const uint4*)k_new, (const uint4*)v_new,
-                       (uint4*)p.k, (uint4*)p.v, slots, T, hkv, nslots, err);
-  } else if (p.dtype == PA_KV_FP8_E4M3) {
-    const int chunks = D / 16;
-    const dim3 g(grid1((int64_t)T * chunks, 256), hkv);
-    auto kern = bf16 ? (D == 128 ? k_write_fp8<true, 8> : k_write_fp8<true, 4>)
-                     : (D == 128 ? k_write_fp8<false, 8> : k_write_fp8<false, 4>);
-    hipLaunchKernelGGL(kern, g, dim3(256), 0, st, (const uint4*)k_new, (const uint4*)v_new,
-                       (uint4*)p.k, (uint4*)p.v, p.k_scale, p.v_scale, slots, T, hkv, nslots,
-                       err);
+  if (p.dtype == PA_KV_F16 || p.dtype == PA_KV_BF16 || p.dtype == PA_KV_FP8_E4M3) {
+    const bool fp8 = p.dtype == PA_KV_FP8_E4M3;
+    // threads per (token, head) row: 16-byte chunks of the copy, 16 values for FP8
+    const int ch = fp8 ? D / 16 : D * 2 / 16;
+    const int64_t per_tok = (int64_t)hkv * ch;
+    const int64_t row_u4 = (int64_t)hkv * D * 2 / 16;  // one input token row in 16 B units
+    const int64_t max_tok = ((int64_t)1 << 31) / per_tok;
+    for (int64_t t0 = 0; t0 < T; t0 += max_tok) {
+      const int32_t n = (int32_t)(T - t0 < max_tok ? T - t0 : max_tok);
+      const uint4* kn = (const uint4*)k_new + t0 * row_u4;
+      const uint4* vn = (const uint4*)v_new + t0 * row_u4;
+      const dim3 g(grid1((int64_t)n * per_tok, 256));
+      if (!fp8) {
+        auto kern = D == 128 ? k_write_copy<16> : k_write_copy<8>;
+        hipLaunchKernelGGL(kern, g, dim3(256), 0, st, kn, vn, (uint4*)p.k, (uint4*)p.v,
+                           slots + t0, n, hkv, nslots, err);
+      } else {
+        auto kern = bf16 ? (D == 128 ? k_write_fp8<true, 8> : k_write_fp8<true, 4>)
+                         : (D == 128 ? k_write_fp8<false, 8> : k_write_fp8<false, 4>);
+        hipLaunchKernelGGL(kern, g, dim3(256), 0, st, kn, vn, (uint4*)p.k, (uint4*)p.v,
+                           p.k_scale, p.v_scale, slots + t0, n, hkv, nslots, err);
+      }
+    }
   } else {
+    // (the FP4 format exists for head_dim 128 only; heads index grid.y)
+    if (D != 128 || hkv > 65535) return PA_ERR_SHAPE;
     Fp4Args a;
     a.side[0] = {(const uint16_t*)k_new, (uint8_t*)p.k, p.k_out_val};
     a.side[1] = {(const uint16_t*)v_new, (uint8_t*)p.v, p.v_out_val};
@@ -462,15 +476,11 @@ int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool
     a.cap = outlier_capacity(D);
     a.nslots = nslots;
     a.err = err;
-    // (the FP4 format exists for head_dim 128 only)
     hipLaunchKernelGGL(k_fp4_mark<128>, dim3(grid1((int64_t)T * hkv, 256), 1, 2), dim3(256), 0,
                        st, a);
     const dim3 g((unsigned)((T + kRowsPerWg - 1) / kRowsPerWg), hkv, 2);
-    void (*cal)(Fp4Args);
-    void (*enc)(Fp4Args);
-    if (D != 128) return PA_ERR_SHAPE;
-    cal = bf16 ? k_fp4_calibrate<true, 128> : k_fp4_calibrate<false, 128>;
-    enc = bf16 ? k_fp4_encode<true, 128> : k_fp4_encode<false, 128>;
+    auto cal = bf16 ? k_fp4_calibrate<true, 128> : k_fp4_calibrate<false, 128>;
+    auto enc = bf16 ? k_fp4_encode<true, 128> : k_fp4_encode<false, 128>;
     hipLaunchKernelGGL(cal, g, dim3(64 * kRowsPerWg), 0, st, a);
     hipLaunchKernelGGL(enc, g, dim3(64 * kRowsPerWg), 0, st, a);
   }
