@@ -95,10 +95,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic(cfg: str, ps: int):
+def decode_kernel_name(kv: str) -> str:
+    """The decode kernel that runs for a pool format (FP4 has its own entry point)."""
+    return "k_decode_fp4" if kv == "fp4" else "k_decode"
+
+
+def counter_traffic(kernel: str, cfg: str, ps: int):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary of this
     workload, if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"k_decode_{cfg}_ps{ps}_counters.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{cfg}_ps{ps}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -278,7 +283,7 @@ def main():
     t_step = wall / K
     dec_gbs = dec["total"] / t_dec / 1e9
     value = step_bytes / t_step / 1e9
-    traffic = counter_traffic(args.config, ps)
+    traffic = counter_traffic(decode_kernel_name(w.kv), args.config, ps)
 
     res = {
         "metric": METRIC,
@@ -308,7 +313,7 @@ def main():
                                     "decode": round(t_dec_br * 1e3, 4),
                                     "merge": round(t_merge * 1e3, 4)},
                       "step_events": round(t_step_ev * 1e3, 4)},
-        "roofline": {"kernel": "k_decode", "bound": "hbm", "achieved": round(dec_gbs, 2),
+        "roofline": {"kernel": decode_kernel_name(w.kv), "bound": "hbm", "achieved": round(dec_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes": dec["total"],

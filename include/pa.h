@@ -85,8 +85,15 @@ typedef enum {
  *                                   bytes: one contiguous run per (block, kv head) holding
  *                                   everything a decode reads for that block, so it is
  *                                   fetched in whole 128-byte lines:
- *                            [0, 8 D)       codes [16 tokens][D/2], two E2M1 codes per
- *                                           byte, even channel in the low nibble
+ *                            [0, 8 D)       E2M1 codes, 4 bits each. K: token rows
+ *                                           [16][D/2], even channel in the low nibble.
+ *                                           V: 16-byte chunks, chunk (ch / 8) * 4 + t / 4
+ *                                           holds channels 8 g .. 8 g + 7 of tokens
+ *                                           4 j .. 4 j + 3; in it byte 2 (ch % 8) holds
+ *                                           tokens 4 j, 4 j + 1 and the next byte tokens
+ *                                           4 j + 2, 4 j + 3 of channel ch, the even
+ *                                           token in the low nibble (a decode lane reads
+ *                                           one chunk and converts token pairs).
  *                            PA_FP4_SCALE_OFF   16 per-token fp32 scales (value = code *
  *                                               scale for the inlier channels)
  *                            PA_FP4_RECORD_OFF  16-byte outlier record: byte 0 = outlier

@@ -131,11 +131,50 @@ def _fp4_offsets(d):
     return codes, codes + 64, codes + 80, codes + 112  # scales, record, slot 0, end
 
 
-def fp4_codes(pool: Pool, kv: str) -> np.ndarray:
-    """Packed codes, a view [NB, Hkv, 16, D/2] uint8."""
-    d = pool.head_dim
-    a = pool.arrays[kv]
-    return a[..., :16 * d // 2].reshape(a.shape[0], a.shape[1], 16, d // 2)
+def fp4_code_map(kv: str, d: int):
+    """Where the 4-bit code of (token t, channel ch) sits in a run's first 8 d bytes:
+    (byte index [16, d], bit shift [16, d]).
+
+    K codes are token rows: byte t * d/2 + ch // 2, the even channel in the low nibble.
+    V codes are grouped for a transposed read: 16-byte chunk (ch // 8) * 4 + t // 4 holds
+    channels 8 g .. 8 g + 7 of tokens 4 j .. 4 j + 3; inside it, channel ch % 8 takes
+    bytes 2 (ch % 8) and 2 (ch % 8) + 1 (tokens 0-1 and 2-3 of the four), the even
+    token in the low nibble."""
+    t = np.arange(16)[:, None]
+    ch = np.arange(d)[None, :]
+    if kv == "k":
+        byte = t * (d // 2) + ch // 2
+        shift = 4 * (ch % 2)
+    elif kv == "v":
+        byte = ((ch // 8) * 4 + t // 4) * 16 + (ch % 8) * 2 + (t % 4) // 2
+        shift = 4 * (t % 2)
+    else:
+        raise ValueError(kv)
+    return np.broadcast_to(byte, (16, d)).copy(), np.broadcast_to(shift, (16, d)).copy()
+
+
+def fp4_code_bytes(pool: Pool, kv: str) -> np.ndarray:
+    """The code bytes of every run, a view [NB, Hkv, 8 D] uint8 (layout: fp4_code_map)."""
+    return pool.arrays[kv][..., :8 * pool.head_dim]
+
+
+def fp4_get_codes(pool: Pool, kv: str) -> np.ndarray:
+    """All 4-bit codes as [NB, Hkv, 16, D] uint8 (a copy)."""
+    byte, shift = fp4_code_map(kv, pool.head_dim)
+    raw = fp4_code_bytes(pool, kv)
+    return ((raw[..., byte] >> shift.astype(np.uint8)) & 0xF).astype(np.uint8)
+
+
+def fp4_put_codes(pool: Pool, kv: str, blk: int, h: int, t: int, codes: np.ndarray) -> None:
+    """Store the D codes of token t of run (blk, h); the other tokens' nibbles stay."""
+    byte, shift = fp4_code_map(kv, pool.head_dim)
+    raw = fp4_code_bytes(pool, kv)[blk, h]
+    b, sh = byte[t], shift[t].astype(np.uint8)
+    clear = np.zeros(raw.shape, dtype=np.uint8)
+    put = np.zeros(raw.shape, dtype=np.uint8)
+    np.bitwise_or.at(clear, b, np.uint8(0xF) << sh)  # a byte may hold two of the nibbles
+    np.bitwise_or.at(put, b, np.asarray(codes, dtype=np.uint8) << sh)
+    raw[:] = (raw & ~clear) | put
 
 
 def fp4_scales(pool: Pool, kv: str) -> np.ndarray:
@@ -266,7 +305,7 @@ def cache_write(pool: Pool, k_rows, v_rows, act: str, slots, k_scale=None, v_sca
         for name, rows in (("k", k_rows), ("v", v_rows)):
             x_all = act_decode(np.asarray(rows)[live], act)  # [n, Hkv, D]
             idx_arr = fp4_records(pool, name)
-            codes_arr, scale_arr = fp4_codes(pool, name), fp4_scales(pool, name)
+            scale_arr = fp4_scales(pool, name)
             slot0_arr, val_arr = fp4_slot0(pool, name), A[name + "_out_val"]
             # step 1-2: calibrate blocks this call opens, on this call's tokens
             for b in np.unique(blk):
@@ -288,7 +327,9 @@ def cache_write(pool: Pool, k_rows, v_rows, act: str, slots, k_scale=None, v_sca
                     rec = idx_arr[blk[i], h]
                     o = rec[1:1 + rec[0]].astype(np.int64)
                     packed, s, ov = fp4_encode_row(x_all[i, h, :], o)
-                    codes_arr[blk[i], h, off[i], :] = packed
+                    codes = np.empty(2 * len(packed), dtype=np.uint8)
+                    codes[0::2], codes[1::2] = packed & 0xF, packed >> 4
+                    fp4_put_codes(pool, name, blk[i], h, off[i], codes)
                     scale_arr[blk[i], h, off[i]] = s
                     if len(o):
                         slot0_arr[blk[i], h, off[i]] = ov[0]
@@ -317,11 +358,8 @@ def dequant_slot_rows(pool: Pool, blk, off, k_scale=None, v_scale=None):
             s = np.asarray(sc, dtype=np.float32).astype(np.float64)[None, :, None]
             out.append(e4m3_decode(A[name][blk, :, off, :]) * s)
         elif pool.kind == "fp4":
-            packed = fp4_codes(pool, name)[blk, :, off, :]  # [n, Hkv, D/2]
-            n, hkv, half = packed.shape
-            codes = np.empty((n, hkv, 2 * half), dtype=np.uint8)
-            codes[..., 0::2] = packed & 0xF
-            codes[..., 1::2] = packed >> 4
+            codes = fp4_get_codes(pool, name)[blk, :, off, :]  # [n, Hkv, D]
+            n, hkv = codes.shape[:2]
             s = fp4_scales(pool, name)[blk, :, off].astype(np.float64)[..., None]
             x = e2m1_decode(codes) * s
             rec = fp4_records(pool, name)[blk]  # [n, Hkv, 16]
@@ -351,7 +389,8 @@ def gather_sequence(pool: Pool, block_table_row, context_len, k_scale=None, v_sc
 
 __all__ = [
     "BLOCK_TOKENS", "OUTLIER_SIGMAS", "UNCALIBRATED", "Pool", "outlier_capacity",
-    "fp4_tile_bytes", "fp4_codes", "fp4_scales", "fp4_records", "fp4_slot0",
+    "fp4_tile_bytes", "fp4_code_map", "fp4_code_bytes", "fp4_get_codes", "fp4_put_codes",
+    "fp4_scales", "fp4_records", "fp4_slot0",
     "fp4_outlier_values",
     "fp8_head_scale", "fp4_calibrate", "fp4_calibration_margin", "fp4_encode_row",
     "cache_write", "dequant_slot_rows", "gather_sequence", "f32_round",

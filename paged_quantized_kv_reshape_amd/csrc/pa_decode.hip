@@ -73,6 +73,8 @@ struct Geo {
 // ([D rows][GP], plus DL spare rows that take the entries of padding heads when GP < 16).
 template <int D, int GP>
 constexpr int fp4_qlds_floats() { return (D + 4) * GP; }
+// words of one wave's block-id slot (FP4 kernel)
+constexpr int kIdsLds = 64;
 template <int D, int GP>
 constexpr int fp4_side_floats() { return (D + (GP < 16 ? D / 4 : 0)) * GP; }
 
@@ -118,9 +120,9 @@ template <int KV, int D>
 struct Tile {
   using G_ = Geo<KV, D>;
   uint32_t k[G_::KW];
-  uint32_t v[4][G_::VW];
+  uint32_t v[4][G_::VW];  // token rows 4 kg .. 4 kg + 3 (FP4: words of one channel chunk)
   float4 sk, sv;  // FP4 per-token scales of tokens 4 kg .. 4 kg + 3
-  uint4 rk, rv;   // FP4 outlier records (wave-uniform: scalar registers)
+  uint32_t r0;    // FP4: first word of the K (lanes 0-31) and V (lanes 32-63) records
   uint2 k_o0, v_o0;  // FP4 outlier slot 0 of tokens 4 kg .. 4 kg + 3 (fp16), fetched with
                      // the tile since a full block usually holds exactly one outlier
   int64_t tile;   // b * Hkv + kv head
@@ -149,23 +151,24 @@ __device__ __forceinline__ uint4 k_fragment(const Tile<KV, D>& T, int t) {
 template <int KV, int D, bool PVB>
 __device__ __forceinline__ void v_fragments(const Tile<KV, D>& T, uint2 (&vf)[Geo<KV, D>::NT]) {
   constexpr int NT = Geo<KV, D>::NT;
-  if constexpr (KV == KV_F16 || KV == KV_BF16 || KV == KV_FP4) {
+  if constexpr (KV == KV_FP4) {
+    // V is stored by channel: word w of the lane's chunk holds channels 2w, 2w+1, each as
+    // two bytes of token pairs (4 kg, 4 kg + 1) and (4 kg + 2, 4 kg + 3); one conversion
+    // per byte gives a fragment half directly
+#pragma unroll
+    for (int w = 0; w < NT / 2; ++w) {
+      vf[2 * w].x = cvt_fp4x2<true, 0>(T.v[w][0]);
+      vf[2 * w].y = cvt_fp4x2<true, 1>(T.v[w][0]);
+      vf[2 * w + 1].x = cvt_fp4x2<true, 2>(T.v[w][0]);
+      vf[2 * w + 1].y = cvt_fp4x2<true, 3>(T.v[w][0]);
+    }
+  } else if constexpr (KV == KV_F16 || KV == KV_BF16) {
     // pairs[r][i] = 16-bit channels (2i, 2i+1) of token r
     uint32_t pairs[4][NT / 2];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      if constexpr (KV == KV_FP4) {
-        const uint32_t w = T.v[r][0];
-        pairs[r][0] = cvt_fp4x2<true, 0>(w);
-        pairs[r][1] = cvt_fp4x2<true, 1>(w);
-        if constexpr (NT / 2 > 2) {
-          pairs[r][2] = cvt_fp4x2<true, 2>(w);
-          pairs[r][3] = cvt_fp4x2<true, 3>(w);
-        }
-      } else {
 #pragma unroll
-        for (int i = 0; i < NT / 2; ++i) pairs[r][i] = T.v[r][i];
-      }
+      for (int i = 0; i < NT / 2; ++i) pairs[r][i] = T.v[r][i];
     }
 #pragma unroll
     for (int i = 0; i < NT / 2; ++i) {
@@ -197,17 +200,13 @@ __device__ __forceinline__ void v_fragments(const Tile<KV, D>& T, uint2 (&vf)[Ge
   }
 }
 
-#ifndef PA_WAVES_PER_EU
-#define PA_WAVES_PER_EU 0
-#endif
-#if PA_WAVES_PER_EU > 0
-#define PA_DECODE_ATTR __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU)))
-#else
-#define PA_DECODE_ATTR
-#endif
 
-template <int KV, int D, bool QBF, int GP>
-__global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
+// The decode of one workgroup. DB selects the block loop: false keeps one tile in flight
+// (the next tile is loaded after the current one is consumed; the other waves of the
+// compute unit cover the latency), true double-buffers (the next tile's loads are issued
+// before the current tile's math, so each wave keeps a tile in flight while it computes).
+template <int KV, int D, bool QBF, int GP, bool DB>
+__device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   using G_ = Geo<KV, D>;
   constexpr int KS = G_::KS, NT = G_::NT, DL = G_::DL;
   // FP4 LDS buffers hold GP head columns (GP = 8 or 16 >= the GQA group): the q copy and
@@ -216,6 +215,7 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
   // address plus compile-time offsets).
   constexpr int kQLds = fp4_qlds_floats<D, GP>();  // floats of the FP4 q copy
   constexpr int kSide = fp4_side_floats<D, GP>();  // floats of one wave's side accumulator
+  static_assert(!DB || KV == KV_FP4, "the double-buffered loop is the FP4 kernel's");
   static_assert(kQLds == (D + D / DL) * GP && kSide == (D + (GP < 16 ? DL : 0)) * GP,
                 "FP4 LDS layout");
   constexpr bool PVB = QBF || KV == KV_FP4;  // PV MFMA in bf16 (else fp16)
@@ -319,13 +319,27 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
   float cz = a.sm_scale_log2;
   if constexpr (KV == KV_FP8) cz *= a.k_scale[kvh];
 
-  // ---- block ids: 64 of this wave's blocks per register, two registers ahead ----
+  // ---- block ids ----
+  // Single buffer: 64 of this wave's block ids per register, one register ahead, read
+  // with readlane. Double buffer: the same 64-id chunks staged in this wave's LDS slot
+  // and each id read one block ahead, so that no vector load of ids is pending when the
+  // next tile's loads are issued and no scalar load is pending during a block's math (a
+  // scalar load may complete out of order, so any wait on LDS would wait for it too).
   const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks + jb0 + my_lo;
   auto load_ids = [&](int chunk) -> int {
     const int x = chunk * 64 + lane;
     return x < my_n ? bt[(int64_t)x * kStep] : 0;
   };
-  int ids_a = load_ids(0), ids_b = load_ids(1);
+  int ids_a = 0, ids_b = 0, nid_v = 0;
+  int* const ids_lds = reinterpret_cast<int*>(smem + kQLds + W * kSide) + wave * kIdsLds;
+  if constexpr (DB) {
+    ids_lds[lane] = load_ids(0);
+    ids_b = load_ids(1);
+    nid_v = ids_lds[0];
+  } else {
+    ids_a = load_ids(0);
+    ids_b = load_ids(1);
+  }
 
   const uint8_t* kpool = reinterpret_cast<const uint8_t*>(a.k);
   const uint8_t* vpool = reinterpret_cast<const uint8_t*>(a.v);
@@ -338,28 +352,49 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
   // registers, and wait for every scalar load as soon as it is issued.
   int err_bits = 0;
   auto load_tile = [&](Tile<KV, D>& T, int x) {
-    if (x > 0 && (x & 63) == 0) {
-      ids_a = ids_b;
-      ids_b = load_ids((x >> 6) + 1);
+    int b_raw;
+    if constexpr (DB) {
+      b_raw = __builtin_amdgcn_readfirstlane(nid_v);
+      if (((x + 1) & 63) == 0) {  // the next chunk replaces this one in the slot
+        ids_lds[lane] = ids_b;
+        ids_b = load_ids(((x + 1) >> 6) + 1);
+      }
+      nid_v = ids_lds[(x + 1) & 63];
+    } else {
+      if (x > 0 && (x & 63) == 0) {
+        ids_a = ids_b;
+        ids_b = load_ids((x >> 6) + 1);
+      }
+      b_raw = __builtin_amdgcn_readlane(ids_a, x & 63);
     }
-    const int b_raw = __builtin_amdgcn_readlane(ids_a, x & 63);
     T.jb = jb0 + my_lo + x * kStep;
     T.ok = (unsigned)b_raw < (unsigned)a.num_blocks;
     err_bits |= T.ok ? 0 : PA_DEVERR_BAD_BLOCK;
     const int b = T.ok ? b_raw : 0;
     T.tile = (int64_t)b * a.num_kv_heads + kvh;
     load_words(T.k, kpool + T.tile * G_::TILEB + k_lane_off);
+    if constexpr (KV == KV_FP4) {
+      // one 16-byte chunk: channels 8 c .. 8 c + 7 of tokens 4 kg .. 4 kg + 3
+      const uint4 x =
+          *reinterpret_cast<const uint4*>(vpool + T.tile * G_::TILEB + (c * 4 + kg) * 16);
+      T.v[0][0] = x.x;
+      T.v[1][0] = x.y;
+      T.v[2][0] = x.z;
+      T.v[3][0] = x.w;
+    } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      load_words(T.v[r], vpool + T.tile * G_::TILEB + v_lane_off + r * G_::ROWB);
+      for (int r = 0; r < 4; ++r)
+        load_words(T.v[r], vpool + T.tile * G_::TILEB + v_lane_off + r * G_::ROWB);
+    }
     if constexpr (KV == KV_FP4) {
       const uint8_t* kt = kpool + T.tile * G_::TILEB;
       const uint8_t* vt = vpool + T.tile * G_::TILEB;
       T.sk = reinterpret_cast<const float4*>(kt + PA_FP4_SCALE_OFF(D))[kg];
       T.sv = reinterpret_cast<const float4*>(vt + PA_FP4_SCALE_OFF(D))[kg];
-      // the records are wave-uniform and read-only while decoding: scalar loads
-      T.rk = load_uniform16(kt + PA_FP4_RECORD_OFF(D));
-      T.rv = load_uniform16(vt + PA_FP4_RECORD_OFF(D));
+      // first word of each outlier record (count and the first three channels): lanes
+      // 0-31 read K's, lanes 32-63 V's, into one register; a vector load, so that no
+      // scalar load is in flight during the previous tile's math
+      T.r0 = *reinterpret_cast<const uint32_t*>((lane < 32 ? kt : vt) + PA_FP4_RECORD_OFF(D));
       // the first outlier slot is part of the tile; its bytes are used only if the
       // record's count is at least 1
       T.k_o0 = reinterpret_cast<const uint2*>(kt + PA_FP4_SLOT0_OFF(D))[kg];
@@ -401,7 +436,9 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
     bool valid[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) valid[r] = FULL || (T.ok && (tok0 + r < end));
-    if constexpr (!FULL) {
+    // V bytes of tokens past the context are arbitrary: zeroed, as a NaN code times p = 0
+    // would still be NaN (E2M1 has no NaN, and FP4's p already carries the mask)
+    if constexpr (!FULL && KV != KV_FP4) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -418,8 +455,13 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
       float ok[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       // The record sits in scalar registers, so the channel indices below are
       // wave-uniform.
-      const uint32_t rw[3] = {T.rk.x, T.rk.y, T.rk.z};
+      uint32_t rw[3] = {(uint32_t)__builtin_amdgcn_readlane((int)T.r0, 0), 0u, 0u};
       int nk = (int)(rw[0] & 0xFFu);
+      if (nk > 3 && nk != 0xFF) {  // more channels than the first word holds (rare)
+        const uint4 r = load_uniform16(kpool + T.tile * G_::TILEB + PA_FP4_RECORD_OFF(D));
+        rw[1] = r.y;
+        rw[2] = r.z;
+      }
       if (nk == 0xFF) {
         err_bits |= T.ok ? PA_DEVERR_UNCALIBRATED : 0;
         nk = 0;
@@ -494,8 +536,13 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
     if constexpr (KV == KV_FP4) {
       // V outliers: out[c][ch] += sum_t p_t * o_t,ch (fp16 values, unscaled p); ch is
       // wave-uniform (the record sits in scalar registers).
-      const uint32_t rw[3] = {T.rv.x, T.rv.y, T.rv.z};
+      uint32_t rw[3] = {(uint32_t)__builtin_amdgcn_readlane((int)T.r0, 32), 0u, 0u};
       int nv = (int)(rw[0] & 0xFFu);
+      if (nv > 3 && nv != 0xFF) {
+        const uint4 r = load_uniform16(vpool + T.tile * G_::TILEB + PA_FP4_RECORD_OFF(D));
+        rw[1] = r.y;
+        rw[2] = r.z;
+      }
       if (nv == 0xFF) {
         err_bits |= T.ok ? PA_DEVERR_UNCALIBRATED : 0;
         nv = 0;
@@ -525,19 +572,37 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
     }
   };
 
-  // ---- block loop: one tile in flight (the next one is loaded while nothing else of
-  // this wave is outstanding; the other waves of the compute unit cover its latency) ----
+  // ---- block loop (single or double buffered, see DB) ----
   // Every block of the loop body is full: a partition starts on a block boundary, so only
   // its last block can end early, and that block is the last one of some wave's run. It
   // is handled after the loop with per-token masks. A block whose id is out of range is
   // skipped (and flagged).
-  Tile<KV, D> tile;
-  if (my_n > 0) load_tile(tile, 0);
-  for (int i = 0; i + 1 < my_n; ++i) {
-    if (tile.ok) compute(tile, std::true_type{});
-    load_tile(tile, i + 1);
+  if constexpr (DB) {
+    Tile<KV, D> ta, tb;
+    if (my_n > 0) load_tile(ta, 0);
+    int i = 0;
+    for (; i + 2 < my_n; i += 2) {
+      load_tile(tb, i + 1);
+      if (ta.ok) compute(ta, std::true_type{});
+      load_tile(ta, i + 2);
+      if (tb.ok) compute(tb, std::true_type{});
+    }
+    if (i + 2 == my_n) {
+      load_tile(tb, i + 1);
+      if (ta.ok) compute(ta, std::true_type{});
+      if (tb.ok) compute(tb, std::false_type{});
+    } else if (my_n > 0 && ta.ok) {
+      compute(ta, std::false_type{});
+    }
+  } else {
+    Tile<KV, D> tile;
+    if (my_n > 0) load_tile(tile, 0);
+    for (int i = 0; i + 1 < my_n; ++i) {
+      if (tile.ok) compute(tile, std::true_type{});
+      load_tile(tile, i + 1);
+    }
+    if (my_n > 0 && tile.ok) compute(tile, std::false_type{});
   }
-  if (my_n > 0 && tile.ok) compute(tile, std::false_type{});
 
   // ---- epilogue ----
   if (err_bits != 0 && lane == 0 && a.err) atomicOr(a.err, err_bits);
@@ -562,7 +627,7 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
 
   // W > 1: merge the waves' states in LDS.
   constexpr int STRIDE = DL + 4;  // floats per lane record (padded)
-  float* m_lds = smem + (KV == KV_FP4 ? kQLds + W * kSide : 0);
+  float* m_lds = smem + (KV == KV_FP4 ? kQLds + W * (kSide + kIdsLds) : 0);
   float* l_lds = m_lds + 16 * 8;
   float* acc_lds = l_lds + 16 * 8;  // [W][64][STRIDE]
   if (kg == 0) {
@@ -607,9 +672,26 @@ __global__ __launch_bounds__(512) PA_DECODE_ATTR void k_decode(DecodeArgs a) {
   }
 }
 
+// 16-bit and FP8 pools: one tile in flight per wave, occupancy left to the register count
+// (5 waves per SIMD for FP8 at head_dim 128).
+template <int KV, int D, bool QBF, int GP>
+__global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
+  decode_body<KV, D, QBF, GP, false>(a);
+}
+
+// FP4 pools: a tile is half the bytes of an FP8 one, so one tile per wave leaves too little
+// in flight; the double-buffered loop, held to at least 4 waves per SIMD (128 registers),
+// keeps about twice as much.
+template <int D, bool QBF, int GP>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_fp4(
+    DecodeArgs a) {
+  decode_body<KV_FP4, D, QBF, GP, true>(a);
+}
+
 template <int KV, int D, int GP>
 static size_t decode_lds_bytes(int waves) {
-  size_t f = KV == KV_FP4 ? fp4_qlds_floats<D, GP>() + (size_t)waves * fp4_side_floats<D, GP>()
+  size_t f = KV == KV_FP4 ? fp4_qlds_floats<D, GP>() +
+                                (size_t)waves * (fp4_side_floats<D, GP>() + kIdsLds)
                           : 0;
   if (waves > 1) f += 2 * 16 * 8 + (size_t)waves * 64 * (D / 4 + 4);  // the wave merge
   return f * sizeof(float);
@@ -631,8 +713,10 @@ static int launch_one(const DecodeArgs& a, int waves, hipStream_t st) {
 #else
   const dim3 grid(P, a.num_kv_heads, a.num_seqs);
 #endif
-  hipLaunchKernelGGL((k_decode<KV, D, QBF, GP>), grid,
-                     dim3(64 * waves), lds, st, a);
+  if constexpr (KV == KV_FP4)
+    hipLaunchKernelGGL((k_decode_fp4<D, QBF, GP>), grid, dim3(64 * waves), lds, st, a);
+  else
+    hipLaunchKernelGGL((k_decode<KV, D, QBF, GP>), grid, dim3(64 * waves), lds, st, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -216,6 +216,7 @@ __global__ __launch_bounds__(256) void k_fp4_mark(Fp4Args a) {
 
 // One wave per (row, head, K|V); only block leaders do work.
 constexpr int kRowsPerWg = 4;  // FP4 calibrate / encode: one wave per row, 4 rows per workgroup
+static_assert(kRowsPerWg == 4, "the FP4 encode merges the V codes of a four of tokens");
 
 template <bool BF16, int D>
 __global__ __launch_bounds__(64 * kRowsPerWg) void k_fp4_calibrate(Fp4Args a) {
@@ -315,65 +316,114 @@ __global__ __launch_bounds__(64 * kRowsPerWg) void k_fp4_calibrate(Fp4Args a) {
 template <bool BF16, int D>
 __global__ __launch_bounds__(64 * kRowsPerWg) void k_fp4_encode(Fp4Args a) {
   using TL = Fp4Tile<D>;
-  const int i = blockIdx.x * kRowsPerWg + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = blockIdx.x * kRowsPerWg + wave;
   const int h = blockIdx.y;
+  const bool vside = blockIdx.z == 1;
   const Fp4Side& sd = a.side[blockIdx.z];
   const int lane = threadIdx.x & 63;
-  if (i >= a.num_tokens) return;
-  const int64_t slot = a.slots[i];
-  if (slot < 0 || slot >= a.nslots) return;
-  const int64_t bh = (slot >> 4) * a.hkv + h;
-  const int off = (int)(slot & 15);
-  uint8_t* tile = sd.tiles + bh * TL::kBytes;
-  uint8_t* rec = tile + TL::kRecord;
-  const uint4 r4 = *reinterpret_cast<const uint4*>(rec);  // bytes 12..15 ignored
-  const uint32_t rw[3] = {r4.x, r4.y, r4.z};
-  int count = (int)(rw[0] & 0xFFu);
-  if (count == 0xFF) {  // never calibrated: cannot happen after the calibrate launch
-    if (lane == 0) flag(a.err, PA_DEVERR_UNCALIBRATED);
-    return;
+  __shared__ int64_t wg_slot[kRowsPerWg];
+  __shared__ uint32_t wg_bits[kRowsPerWg][64];
+
+  int64_t slot = -1;  // -1: this wave stores nothing
+  if (i < a.num_tokens) {
+    slot = a.slots[i];
+    if (slot >= a.nslots) slot = -1;
   }
-  if (count > a.cap) count = a.cap;
-  const bool active = lane < D / 2;
-  const int c0 = 2 * lane, c1 = c0 + 1;
-  float x0 = 0.0f, x1 = 0.0f;
-  if (active) {
-    const uint32_t pair = *reinterpret_cast<const uint32_t*>(sd.rows + ((int64_t)i * a.hkv + h) * D + c0);
-    x0 = act_to_f32<BF16>(pair & 0xFFFFu);
-    x1 = act_to_f32<BF16>(pair >> 16);
-  }
-  bool out0 = false, out1 = false;
-  for (int j = 0; j < count; ++j) {
-    const int pos = 1 + j;
-    const int c = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
-    out0 |= (c == c0);
-    out1 |= (c == c1);
-  }
-  const float a0 = (active && !out0) ? __builtin_fabsf(x0) : 0.0f;
-  const float a1 = (active && !out1) ? __builtin_fabsf(x1) : 0.0f;
-  const float amax = wave_max(fmaxf(a0, a1));
-  const float s = amax / 6.0f;
-  uint32_t q0 = 0u, q1 = 0u;
-  if (s != 0.0f) {
-    q0 = out0 ? 0u : encode_e2m1(x0 / s);
-    q1 = out1 ? 0u : encode_e2m1(x1 / s);
-  }
-  if (active) tile[off * (D / 2) + lane] = (uint8_t)(q0 | (q1 << 4));
-  for (int j = 0; j < count; ++j) {
-    const int pos = 1 + j;
-    const int c = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
-    if (active && (c >> 1) == lane) {
-      const float xv = (c & 1) ? x1 : x0;
-      const uint16_t hv = bitcast<uint16_t>((_Float16)xv);
-      if (j == 0)
-        reinterpret_cast<uint16_t*>(tile + TL::kSlot0)[off] = hv;
-      else
-        sd.out_val[(bh * (a.cap - 1) + (j - 1)) * kBlock + off] = hv;
+  uint32_t* vword = nullptr;  // V: this lane's code word and its bits for this token
+  uint32_t vbits = 0u, vmask = 0u;
+  if (slot >= 0) {
+    const int64_t bh = (slot >> 4) * a.hkv + h;
+    const int off = (int)(slot & 15);
+    uint8_t* tile = sd.tiles + bh * TL::kBytes;
+    uint8_t* rec = tile + TL::kRecord;
+    const uint4 r4 = *reinterpret_cast<const uint4*>(rec);  // bytes 12..15 ignored
+    const uint32_t rw[3] = {r4.x, r4.y, r4.z};
+    int count = (int)(rw[0] & 0xFFu);
+    if (count == 0xFF) {  // never calibrated: cannot happen after the calibrate launch
+      if (lane == 0) flag(a.err, PA_DEVERR_UNCALIBRATED);
+      slot = -1;
+    } else {
+      if (count > a.cap) count = a.cap;
+      const bool active = lane < D / 2;
+      const int c0 = 2 * lane, c1 = c0 + 1;
+      float x0 = 0.0f, x1 = 0.0f;
+      if (active) {
+        const uint32_t pair =
+            *reinterpret_cast<const uint32_t*>(sd.rows + ((int64_t)i * a.hkv + h) * D + c0);
+        x0 = act_to_f32<BF16>(pair & 0xFFFFu);
+        x1 = act_to_f32<BF16>(pair >> 16);
+      }
+      bool out0 = false, out1 = false;
+      for (int j = 0; j < count; ++j) {
+        const int pos = 1 + j;
+        const int c = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
+        out0 |= (c == c0);
+        out1 |= (c == c1);
+      }
+      const float a0 = (active && !out0) ? __builtin_fabsf(x0) : 0.0f;
+      const float a1 = (active && !out1) ? __builtin_fabsf(x1) : 0.0f;
+      const float amax = wave_max(fmaxf(a0, a1));
+      const float sc = amax / 6.0f;
+      uint32_t q0 = 0u, q1 = 0u;
+      if (sc != 0.0f) {
+        q0 = out0 ? 0u : encode_e2m1(x0 / sc);
+        q1 = out1 ? 0u : encode_e2m1(x1 / sc);
+      }
+      if (active) {
+        if (!vside) {
+          tile[off * (D / 2) + lane] = (uint8_t)(q0 | (q1 << 4));  // K: token rows
+        } else {
+          // V: channels 2 lane and 2 lane + 1 sit in word lane % 4 of chunk
+          // (lane / 4) * 4 + off / 4, at bit 8 ((off % 4) / 2) + 4 (off % 2) and 16 above
+          const int sh = 8 * ((off & 3) >> 1) + 4 * (off & 1);
+          vword = reinterpret_cast<uint32_t*>(tile) +
+                  (((lane >> 2) * 4 + (off >> 2)) * 4 + (lane & 3));
+          vbits = (q0 << sh) | (q1 << (sh + 16));
+          vmask = (0xFu << sh) | (0xFu << (sh + 16));
+        }
+      }
+      for (int j = 0; j < count; ++j) {
+        const int pos = 1 + j;
+        const int c = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
+        if (active && (c >> 1) == lane) {
+          const float xv = (c & 1) ? x1 : x0;
+          const uint16_t hv = bitcast<uint16_t>((_Float16)xv);
+          if (j == 0)
+            reinterpret_cast<uint16_t*>(tile + TL::kSlot0)[off] = hv;
+          else
+            sd.out_val[(bh * (a.cap - 1) + (j - 1)) * kBlock + off] = hv;
+        }
+      }
+      if (lane == 0) {
+        reinterpret_cast<float*>(tile + TL::kScale)[off] = sc;
+        *reinterpret_cast<uint32_t*>(rec + 12) = 0xFFFFFFFFu;
+      }
     }
   }
-  if (lane == 0) {
-    reinterpret_cast<float*>(tile + TL::kScale)[off] = s;
-    *reinterpret_cast<uint32_t*>(rec + 12) = 0xFFFFFFFFu;
+  if (!vside) return;  // uniform over the workgroup
+
+  // V codes of four tokens share each 32-bit word. When this workgroup's rows are a whole
+  // aligned four of one block (the usual case in prefill), wave 0 stores the merged words;
+  // otherwise other calls' or workgroups' rows may share the words, and each lane merges
+  // its nibbles with atomics on disjoint bits (clear, then set).
+  if (lane == 0) wg_slot[wave] = slot;
+  wg_bits[wave][lane] = vbits;
+  __syncthreads();
+  const int64_t s0 = wg_slot[0];
+  bool full = s0 >= 0 && (s0 & 3) == 0;
+#pragma unroll
+  for (int w = 1; w < kRowsPerWg; ++w) full = full && wg_slot[w] == s0 + w;
+  if (full) {
+    if (wave == 0 && vword) {
+      uint32_t word = 0u;
+#pragma unroll
+      for (int w = 0; w < kRowsPerWg; ++w) word |= wg_bits[w][lane];
+      *vword = word;
+    }
+  } else if (vword) {
+    atomicAnd(vword, ~vmask);
+    atomicOr(vword, vbits);
   }
 }
 

@@ -190,7 +190,8 @@ def test_fp4_calibrates_once_per_block_and_reuses():
     assert np.array_equal(kd[:, 0, 9], xall[:, 0, 9])
     # untouched offsets (codes, scales, first-outlier values), the unused outlier slots
     # and the tile's padding keep their sentinel bytes
-    assert np.all(C.fp4_codes(pool, "k")[2, 0, 8:] == 0xA5)
+    byte, shift = C.fp4_code_map("k", d)
+    assert np.array_equal(C.fp4_get_codes(pool, "k")[2, 0, 8:], (0xA5 >> shift[8:]) & 0xF)
     assert np.all(C.fp4_scales(pool, "k")[2, 0, 8:].view(np.uint8) == 0xA5)
     assert np.all(C.fp4_slot0(pool, "k")[2, 0, 8:] == 0xA5A5)
     assert np.all(pool.arrays["k_out_val"][2, 0].view(np.uint8) == 0xA5)
@@ -228,3 +229,50 @@ def test_fp8_code_is_e4m3_of_the_fp32_quotient():
     row[0, 0, 0] = _bf16_bits(np.array([x]))[0]
     C.cache_write(pool, row, row, "bf16", np.array([0]), k_scale=np.array([s]), v_scale=np.array([s]))
     assert pool.arrays["k"][0, 0, 0, 0] == 0x7A
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("kv", ["k", "v"])
+def test_fp4_code_map_is_a_bijection_onto_the_code_bytes(kv, d):
+    """Every (token, channel) code owns its own nibble of the 8 d code bytes, and every
+    nibble belongs to one code."""
+    byte, shift = C.fp4_code_map(kv, d)
+    nib = (byte * 2 + shift // 4).ravel()
+    assert nib.min() == 0 and nib.max() == 16 * d - 1
+    assert len(np.unique(nib)) == 16 * d
+
+
+def test_fp4_v_chunks_hold_a_channel_group_of_four_tokens():
+    """V chunk (g, j): 16 bytes holding channels 8 g .. 8 g + 7 of tokens 4 j .. 4 j + 3,
+    two tokens per byte (one channel), so a converter taking a byte yields a token pair."""
+    d = 128
+    byte, shift = C.fp4_code_map("v", d)
+    for g in range(d // 8):
+        for j in range(4):
+            chunk = g * 4 + j
+            t = np.arange(4 * j, 4 * j + 4)[:, None]
+            ch = np.arange(8 * g, 8 * g + 8)[None, :]
+            b = byte[t, ch]
+            assert np.all(b // 16 == chunk)
+            # one byte = one channel, two consecutive tokens (even token low)
+            for c in range(8):
+                col = b[:, c]
+                assert col[0] == col[1] and col[2] == col[3] and col[0] + 1 == col[2]
+                assert list(shift[t[:, 0], ch[0, c]]) == [0, 4, 0, 4]
+
+
+def test_fp4_put_codes_keeps_the_other_nibbles():
+    d = 128
+    for kv in ("k", "v"):
+        pool = C.Pool.filled("fp4", 2, 1, d)
+        rng = np.random.default_rng(3)
+        want = np.full((16, d), -1)
+        for t in rng.permutation(16)[:7]:
+            codes = rng.integers(0, 16, d).astype(np.uint8)
+            C.fp4_put_codes(pool, kv, 1, 0, int(t), codes)
+            want[t] = codes
+        got = C.fp4_get_codes(pool, kv)[1, 0]
+        byte, shift = C.fp4_code_map(kv, d)
+        sentinel = (0xA5 >> shift) & 0xF
+        assert np.array_equal(got, np.where(want >= 0, want, sentinel))
+        assert np.all(C.fp4_code_bytes(pool, kv)[0] == 0xA5)

@@ -371,3 +371,40 @@ def test_fp8_write_every_input(act, d):
                for b, h, r, c in bad[:8]]
         assert len(bad) == 0, f"{len(bad)} codes differ:\n" + "\n".join(msg)
     assert_pool_equal(got, opool)
+
+
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+def test_fp4_write_scattered_slots(act):
+    """FP4 writes whose rows arrive in scrambled slot order, in calls that cover parts of
+    4-token groups (V codes of four tokens share each word), mixed with whole aligned
+    groups, over several calls: the pool must match the oracle byte for byte."""
+    from oracle import cache as C
+    from paged_quantized_kv_reshape_amd import KVPool, pa_cache_write
+    rng = np.random.default_rng(11)
+    d, hkv, nb = 128, 2, 24
+    x = rng.standard_normal((nb * 16, hkv, d)).astype(np.float32)
+    x[:, :, 5] *= 20.0  # one planted outlier channel
+    bits = (x.astype(np.float16).view(np.uint16) if act == "f16" else
+            ((x.view(np.uint32) + 0x7FFF + ((x.view(np.uint32) >> 16) & 1)) >> 16).astype(np.uint16))
+    order = rng.permutation(nb * 16)
+    # call 1: whole aligned fours of blocks 0..7, rows shuffled within the call
+    quads = [np.arange(4 * q, 4 * q + 4) for q in range(32)]
+    call1 = np.concatenate([quads[q] for q in rng.permutation(32)])
+    rest = np.setdiff1d(order, call1, assume_unique=False)
+    rest = rest[rng.permutation(len(rest))]
+    calls = [call1] + list(np.array_split(rest, 5))  # scattered slots, partial fours
+    opool = C.Pool.filled("fp4", nb, hkv, d)
+    pool = KVPool("fp4", nb, hkv, d, fill=0xA5)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tdt = torch.bfloat16 if act == "bf16" else torch.float16
+    for ci, slots in enumerate(calls):
+        slots = np.asarray(slots, dtype=np.int64)
+        rows = np.ascontiguousarray(bits[slots])
+        C.cache_write(opool, rows, rows[::-1].copy(), act, slots)
+        rt = torch.from_numpy(rows.view(np.int16)).cuda().view(tdt)
+        rv = torch.from_numpy(rows[::-1].copy().view(np.int16)).cuda().view(tdt)
+        _say(f"[fp4 scattered] act={act} call {ci}: {len(slots)} rows")
+        pa_cache_write(pool, rt, rv, torch.from_numpy(slots).cuda(), err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert_pool_equal(pool.numpy(), opool)
