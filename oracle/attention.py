@@ -13,6 +13,13 @@ module writes that definition out directly (no online softmax, no blocking):
   * split-KV ("Flash-Decoding", same page and its cited sources): the context is cut into
     fixed partitions, each gives (o_p, lse_p), and the log-sum-exp merge recombines them.
 Query head h reads kv head h // (Hq / Hkv) (grouped-query attention, contiguous groups).
+
+Multi-token queries over the same cache (chunked prefill: a long prompt processed in
+chunks, dailyaiworld.com, "vLLM 0.7 Ships Unified KV Cache Compression", engine diagram
+with 512-token chunks, and inferensys glossary "vLLM", chunked prefill entry; draft
+verification: the target model checks several proposed tokens at once, inferensys glossary
+"vLLM", speculative decoding entry): the n queries of a sequence are its last n positions,
+already written to the cache, and each attends causally to every position up to its own.
 """
 from __future__ import annotations
 
@@ -86,4 +93,28 @@ def paged_decode(q_bits, act: str, pool: Pool, block_tables, context_lens, sm_sc
     for s in (range(q.shape[0]) if seqs is None else seqs):
         k_seq, v_seq = gather_sequence(pool, block_tables[s], context_lens[s], k_scale, v_scale)
         res[s] = decode_dense(q[s], k_seq, v_seq, float(sm_scale), partition_size)
+    return res
+
+
+def paged_prefill(q_bits, act: str, pool: Pool, block_tables, context_lens, query_start,
+                  sm_scale: float, k_scale=None, v_scale=None, seqs=None):
+    """Multi-token queries for every sequence (or the listed ones) of a batch.
+
+    q_bits [T, Hq, D] raw 16-bit bits, sequence s owning rows query_start[s] ..
+    query_start[s + 1] - 1. With n = query_start[s + 1] - query_start[s] and L =
+    context_lens[s], query i sits at position L - n + i and attends to positions
+    0 .. L - n + i. Returns dict seq -> out [n, Hq, D]."""
+    q = act_decode(q_bits, act)
+    res = {}
+    for s in (range(len(context_lens)) if seqs is None else seqs):
+        L = int(context_lens[s])
+        q0, q1 = int(query_start[s]), int(query_start[s + 1])
+        n = q1 - q0
+        k_seq, v_seq = gather_sequence(pool, block_tables[s], L, k_scale, v_scale)
+        out = np.zeros((n, q.shape[1], q.shape[2]))
+        for i in range(n):
+            pos = L - n + i
+            out[i], _ = decode_dense(q[q0 + i], k_seq[:pos + 1], v_seq[:pos + 1],
+                                     float(sm_scale))
+        res[s] = out
     return res

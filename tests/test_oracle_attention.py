@@ -175,3 +175,62 @@ def test_merge_of_split_equals_unsplit(ps):
     l_pad = np.concatenate([l, np.full((8, 1), -np.inf)], axis=1)
     mp, lp = A.merge(o_pad, l_pad)
     assert np.allclose(mp, out, rtol=1e-12, atol=1e-13) and np.allclose(lp, lse, rtol=1e-13)
+
+
+def _prefill_setup(seed, lens, ns, hq, hkv, d):
+    rng = np.random.default_rng(seed)
+    nb = sum(-(-L // 16) for L in lens) + 3
+    pool, bt, rows = _pool_with_sequences(rng, lens, hkv, d, nb)
+    qs = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    q = _f16_rows(rng, (int(qs[-1]), hq, d))
+    return pool, bt, rows, qs, q
+
+
+def test_prefill_single_query_is_decode():
+    lens, ns, hq, hkv, d = [37, 50, 16], [1, 1, 1], 8, 2, 64
+    pool, bt, rows, qs, q = _prefill_setup(1, lens, ns, hq, hkv, d)
+    pre = A.paged_prefill(q, "f16", pool, bt, lens, qs, 0.125)
+    dec = A.paged_decode(q, "f16", pool, bt, lens, 0.125)
+    for s in range(len(lens)):
+        assert np.array_equal(pre[s][0], dec[s][0])
+
+
+def test_prefill_matches_masked_dense_brute_force():
+    """Independent route: the whole causal score matrix of each sequence from its
+    contiguous rows (no block table), masked with -inf, softmax over rows."""
+    lens, ns, hq, hkv, d = [23, 40], [7, 17], 4, 1, 32
+    pool, bt, rows, qs, q = _prefill_setup(2, lens, ns, hq, hkv, d)
+    sc = 0.2
+    pre = A.paged_prefill(q, "f16", pool, bt, lens, qs, sc)
+    qv = F.f16_decode(q)
+    for s, (L, n) in enumerate(zip(lens, ns)):
+        k = F.f16_decode(rows[s][0])[:, 0, :]  # [L, D], one kv head
+        v = F.f16_decode(rows[s][1])[:, 0, :]
+        for h in range(hq):
+            Q = qv[qs[s]:qs[s + 1], h, :]  # [n, D]
+            z = sc * Q @ k.T  # [n, L]
+            pos = L - n + np.arange(n)
+            z = np.where(np.arange(L)[None, :] <= pos[:, None], z, -np.inf)
+            w = np.exp(z - z.max(axis=1, keepdims=True))
+            ref = (w @ v) / w.sum(axis=1, keepdims=True)
+            assert np.allclose(pre[s][:, h, :], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_is_causal_and_ends_at_decode():
+    """A query ignores cache positions after its own (they are overwritten with other
+    values), and the chunk's last query equals decode over the whole context."""
+    lens, ns, hq, hkv, d = [45], [12], 8, 2, 64
+    pool, bt, rows, qs, q = _prefill_setup(3, lens, ns, hq, hkv, d)
+    pre = A.paged_prefill(q, "f16", pool, bt, lens, qs, 0.125)
+    L, n = lens[0], ns[0]
+    rng = np.random.default_rng(9)
+    t = np.arange(L - n + 5, L)  # positions after query 4 of the chunk
+    junk = _f16_rows(rng, (len(t), hkv, d), scale=5.0)
+    pool2 = C.Pool(pool.kind, pool.num_blocks, pool.num_kv_heads, pool.head_dim,
+                   {k: a.copy() for k, a in pool.arrays.items()})
+    C.cache_write(pool2, junk, junk, "f16", bt[0, t // 16].astype(np.int64) * 16 + t % 16)
+    pre2 = A.paged_prefill(q, "f16", pool2, bt, lens, qs, 0.125)
+    assert np.array_equal(pre[0][:5], pre2[0][:5])
+    assert not np.allclose(pre[0][5:], pre2[0][5:])
+    last = A.paged_decode(q[qs[1] - 1:qs[1]], "f16", pool, bt, lens, 0.125)
+    assert np.array_equal(pre[0][n - 1], last[0][0])
