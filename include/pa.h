@@ -216,6 +216,34 @@ int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
               float* part_out, float* part_lse, int32_t* dev_err, void* stream);
 
 /*
+ * Paged attention for several query tokens per sequence, over the same pool: a chunk of a
+ * long prompt processed after its keys and values were written (chunked prefill,
+ * dailyaiworld.com, "vLLM 0.7 Ships Unified KV Cache Compression", engine diagram with
+ * 512-token chunks; inferensys glossary "vLLM", chunked prefill entry), or the tokens a
+ * draft model proposed, checked in one pass (inferensys glossary "vLLM", speculative
+ * decoding entry).
+ *   q             [num_queries, num_q_heads, head_dim], dtype q_dtype; sequence s owns
+ *                 rows query_start[s] .. query_start[s + 1] - 1
+ *   query_start   [num_seqs + 1] int32, device memory: row offsets into q and out
+ *   max_query_len an upper bound on every sequence's query count n_s (sizes the grid)
+ *   block_tables, context_lens, sm_scale as for pa_decode; context_lens[s] = L_s counts
+ *                 the sequence's tokens including its n_s queries, whose keys and values
+ *                 must already be in the pool
+ *   out           [num_queries, num_q_heads, head_dim] fp32: query i of sequence s
+ *                 (position L_s - n_s + i) attends causally to positions 0 .. L_s - n_s + i
+ * The query group Hq / Hkv must divide 16. A sequence with n_s < 0, n_s > L_s,
+ * n_s > max_query_len, rows outside [0, num_queries) or an invalid L_s is flagged
+ * (PA_DEVERR_BAD_CONTEXT) and not read; its rows are zeroed when they lie inside
+ * [0, num_queries) and n_s <= max_query_len. Asynchronous on `stream`.
+ */
+int pa_prefill(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+               int32_t num_queries, const int32_t* query_start, int32_t max_query_len,
+               const pa_kv_pool* pool,
+               const int32_t* block_tables, int32_t max_blocks_per_seq,
+               const int32_t* context_lens, float sm_scale, float* out, int32_t* dev_err,
+               void* stream);
+
+/*
  * Log-sum-exp merge of pa_decode partitions: for each (s, h), over p < ceil(L_s / ps),
  * M = max lse_p, w_p = exp(lse_p - M), out = sum w_p o_p / sum w_p and, if lse_out is
  * not NULL, lse_out[s, h] = M + ln sum w_p. Shapes as in pa_decode; out [num_seqs,

@@ -68,6 +68,8 @@ def lib():
             "pa_reset_blocks": (ctypes.c_int, [pool_p, vp, i32, vp]),
             "pa_decode": (ctypes.c_int, [vp, i32, i32, i32, pool_p, vp, i32, vp, f32, i32, vp, vp,
                                          vp, vp, vp]),
+            "pa_prefill": (ctypes.c_int, [vp, i32, i32, i32, i32, vp, i32, pool_p, vp, i32, vp,
+                                          f32, vp, vp, vp]),
             "pa_merge": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]),
             "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "pa_read_device_error": (ctypes.c_int, [vp, vp, vp]),
@@ -193,6 +195,23 @@ def pa_decode(q, pool: KVPool, block_tables, context_lens, sm_scale, partition_s
         _ptr(q), ACT_DTYPES[q.dtype], S, Hq, ctypes.byref(s), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), float(sm_scale), partition_size, _ptr(out),
         _ptr(part_out), _ptr(part_lse), _ptr(dev_err), _stream()))
+
+
+def pa_prefill(q, query_start, max_query_len, pool: KVPool, block_tables, context_lens,
+               sm_scale, out, dev_err=None):
+    """q [T, Hq, D]; query_start [S + 1] int32 (sequence s owns rows query_start[s] ..
+    query_start[s + 1] - 1, its last positions); fills out [T, Hq, D] fp32."""
+    assert q.dtype in ACT_DTYPES and block_tables.dtype == torch.int32
+    assert context_lens.dtype == torch.int32 and query_start.dtype == torch.int32
+    S = context_lens.shape[0]
+    assert query_start.shape[0] == S + 1
+    T, Hq, _ = q.shape
+    assert out.shape[0] == T
+    s = pool.struct()
+    _check("pa_prefill", lib().pa_prefill(
+        _ptr(q), ACT_DTYPES[q.dtype], S, Hq, T, _ptr(query_start), int(max_query_len),
+        ctypes.byref(s), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        float(sm_scale), _ptr(out), _ptr(dev_err), _stream()))
 
 
 def pa_merge(part_out, part_lse, context_lens, partition_size, out, lse_out=None):

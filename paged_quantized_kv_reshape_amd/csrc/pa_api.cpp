@@ -176,7 +176,7 @@ int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
       !aligned(dev_err, 4))
     return PA_ERR_ALIGN;
 
-  pa::DecodeArgs a;
+  pa::DecodeArgs a{};
   a.q = q;
   a.k = pool->k;
   a.v = pool->v;
@@ -220,6 +220,59 @@ int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
   if (forced == 1 || forced == 2 || forced == 4 || forced == 8) waves = forced;
   return pa::launch_decode(a, pool->dtype, q_dtype == PA_ACT_BF16, pool->head_dim, waves,
                            (hipStream_t)stream);
+}
+
+int pa_prefill(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+               int32_t num_queries, const int32_t* query_start, int32_t max_query_len,
+               const pa_kv_pool* pool,
+               const int32_t* block_tables, int32_t max_blocks_per_seq,
+               const int32_t* context_lens, float sm_scale, float* out, int32_t* dev_err,
+               void* stream) {
+  int st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (!act_ok(q_dtype) || !act_matches_pool(q_dtype, pool->dtype)) return PA_ERR_DTYPE;
+  if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_q_heads < 1) return PA_ERR_SHAPE;
+  if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_SHAPE;
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (16 % group != 0) return PA_ERR_SHAPE;  // a wave's 16 columns hold whole queries
+  if (max_query_len < 0 || num_queries < 0) return PA_ERR_SHAPE;
+  if (max_blocks_per_seq < 1 || (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE > INT32_MAX)
+    return PA_ERR_CONTEXT;
+  if (num_seqs == 0 || max_query_len == 0 || num_queries == 0) return PA_OK;
+  if (!q || !query_start || !block_tables || !context_lens || !out) return PA_ERR_NULL;
+  // the grid's x dimension counts (query tile, kv head) pairs
+  if ((int64_t)max_query_len * pool->num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(query_start, 4) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(dev_err, 4))
+    return PA_ERR_ALIGN;
+
+  pa::DecodeArgs a{};
+  a.q = q;
+  a.k = pool->k;
+  a.v = pool->v;
+  a.k_out_val = pool->k_out_val;
+  a.v_out_val = pool->v_out_val;
+  a.k_scale = pool->k_scale;
+  a.v_scale = pool->v_scale;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.err = dev_err;
+  a.query_start = query_start;
+  a.max_query_len = max_query_len;
+  a.num_queries = num_queries;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.group = group;
+  a.num_blocks = pool->num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.partition_size = 0;
+  a.max_partitions = 1;
+  a.cap = pa::outlier_capacity(pool->head_dim);
+  a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  return pa::launch_prefill(a, pool->dtype, q_dtype == PA_ACT_BF16, pool->head_dim,
+                            (hipStream_t)stream);
 }
 
 int pa_merge(const float* part_out, const float* part_lse, const int32_t* context_lens,

@@ -44,13 +44,6 @@ namespace pa {
 enum { KV_F16 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_FP4 = 3 };
 
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
-#ifndef PA_GRID_HEAD_FAST
-#define PA_GRID_HEAD_FAST 1
-#endif
-#ifndef PA_DECODE_CONTIG
-#define PA_DECODE_CONTIG 0
-#endif
-
 
 template <int KV, int D>
 struct Geo {
@@ -205,7 +198,10 @@ __device__ __forceinline__ void v_fragments(const Tile<KV, D>& T, uint2 (&vf)[Ge
 // (the next tile is loaded after the current one is consumed; the other waves of the
 // compute unit cover the latency), true double-buffers (the next tile's loads are issued
 // before the current tile's math, so each wave keeps a tile in flight while it computes).
-template <int KV, int D, bool QBF, int GP, bool DB>
+// MQ selects multi-token queries (chunked prefill, draft verification): each wave owns 16
+// MFMA columns, one per (query, head), and walks every block up to its last query's
+// position with causal masks; there is no split and no merge.
+template <int KV, int D, bool QBF, int GP, bool DB, bool MQ>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   using G_ = Geo<KV, D>;
   constexpr int KS = G_::KS, NT = G_::NT, DL = G_::DL;
@@ -216,6 +212,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   constexpr int kQLds = fp4_qlds_floats<D, GP>();  // floats of the FP4 q copy
   constexpr int kSide = fp4_side_floats<D, GP>();  // floats of one wave's side accumulator
   static_assert(!DB || KV == KV_FP4, "the double-buffered loop is the FP4 kernel's");
+  static_assert(!MQ || (GP == 16 && !DB), "multi-token queries fill all 16 columns");
   static_assert(kQLds == (D + D / DL) * GP && kSide == (D + (GP < 16 ? DL : 0)) * GP,
                 "FP4 LDS layout");
   constexpr bool PVB = QBF || KV == KV_FP4;  // PV MFMA in bf16 (else fp16)
@@ -227,62 +224,89 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   const int W = blockDim.x >> 6;
   const int c = lane & 15;  // MFMA column: query head (QK, PV); K row token; V channel group
   const int kg = lane >> 4;
-#if PA_GRID_HEAD_FAST
-  // grid.x = kv head fastest, then partition: the workgroups of one block's kv heads run
-  // side by side and read neighbouring tiles ([block][kv head][16][D] is contiguous)
+  // grid.x = kv head fastest, then partition (MQ: query tile): the workgroups of one
+  // block's kv heads run side by side and read neighbouring tiles ([block][kv head][16][D]
+  // is contiguous); grid.y = sequence
   const int kvh = (int)(blockIdx.x % (unsigned)a.num_kv_heads);
   const int p = (int)(blockIdx.x / (unsigned)a.num_kv_heads);
   const int s = blockIdx.y;
-#else
-  const int p = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
-#endif
   const int G = a.group;
   const int Hq = a.num_q_heads;
 
   const int L = a.context_lens[s];
   const int cap_tokens = a.max_blocks * kBlock;
-  const bool split = a.partition_size > 0;
-  if (L < 1 || L > cap_tokens) {
-    if (threadIdx.x == 0 && p == 0 && kvh == 0 && a.err) atomicOr(a.err, PA_DEVERR_BAD_CONTEXT);
-    if (!split && p == 0) {
-      for (int i = threadIdx.x; i < G * D; i += blockDim.x)
-        a.out[((int64_t)s * Hq + kvh * G) * D + i] = 0.0f;
+  // MQ: sequence s's queries are rows q0 .. q0 + nq - 1 at positions L - nq .. L - 1;
+  // wave w of query tile p takes QPW = 16 / G consecutive queries
+  int q0 = 0, nq = 1;
+  if constexpr (MQ) {
+    q0 = a.query_start[s];
+    nq = a.query_start[s + 1] - q0;
+  }
+  const int QPW = MQ ? kBlock / G : 1;
+  const int j0 = MQ ? (p * W + wave) * QPW : 0;  // first query of this wave
+  const bool split = !MQ && a.partition_size > 0;
+  const bool rows_ok = !MQ || (q0 >= 0 && nq >= 0 && (int64_t)q0 + nq <= a.num_queries);
+  const bool bad_q = MQ && (!rows_ok || nq > L || nq > a.max_query_len);
+  if (L < 1 || L > cap_tokens || bad_q) {
+    if constexpr (MQ) {
+      if (lane == 0 && wave == 0 && p == 0 && kvh == 0 && a.err)
+        atomicOr(a.err, PA_DEVERR_BAD_CONTEXT);
+      if (rows_ok && nq <= a.max_query_len)  // zero this wave's rows
+        for (int j = j0; j < min(j0 + QPW, nq); ++j)
+          for (int i = lane; i < G * D; i += 64)
+            a.out[((int64_t)(q0 + j) * Hq + kvh * G) * D + i] = 0.0f;
+    } else {
+      if (threadIdx.x == 0 && p == 0 && kvh == 0 && a.err) atomicOr(a.err, PA_DEVERR_BAD_CONTEXT);
+      if (!split && p == 0) {
+        for (int i = threadIdx.x; i < G * D; i += blockDim.x)
+          a.out[((int64_t)s * Hq + kvh * G) * D + i] = 0.0f;
+      }
     }
     return;
   }
-  const int start = split ? p * a.partition_size : 0;
-  if (start >= L) return;  // empty partition: not written, the merge skips it
-  const int end = split ? min(start + a.partition_size, L) : L;
+  if (MQ && j0 >= nq) return;  // no query for this wave
+  // the blocks this wave reads: its share of the partition (decode, blocks w, w + W, ...),
+  // or every block up to its last query's position (MQ)
+  int start, end;
+  if constexpr (MQ) {
+    start = 0;
+    end = L - nq + min(j0 + QPW, nq);
+  } else {
+    start = split ? p * a.partition_size : 0;
+    if (start >= L) return;  // empty partition: not written, the merge skips it
+    end = split ? min(start + a.partition_size, L) : L;
+  }
   const int jb0 = start / kBlock;
   const int nblk = (end + kBlock - 1) / kBlock - jb0;
-#if PA_DECODE_CONTIG
-  // wave w takes the contiguous run of blocks [w * nblk / W, (w + 1) * nblk / W)
-  const int my_lo = (int)((int64_t)wave * nblk / W);
-  const int my_n = (int)((int64_t)(wave + 1) * nblk / W) - my_lo;
-  constexpr int kStep = 1;
-#else
-  // wave w takes blocks w, w + W, w + 2W, ...
-  const int my_lo = wave;
-  const int my_n = wave < nblk ? (nblk - wave + W - 1) / W : 0;
-  const int kStep = W;
-#endif
+  const int my_lo = MQ ? 0 : wave;
+  const int my_n = MQ ? nblk : (wave < nblk ? (nblk - wave + W - 1) / W : 0);
+  const int kStep = MQ ? 1 : W;
+  // this lane's column: MQ query jc (head c % G), whose keys end at position L - nq + jc;
+  // blocks wholly at or before the wave's first query position need no masks (MQ)
+  const int jc = MQ ? j0 + c / G : 0;
+  const int col_end = MQ ? (jc < nq ? L - nq + jc + 1 : 0) : end;
+  const int nfull = MQ ? (L - nq + j0 + 1) / kBlock : 0;
 
   // ---- query fragments (B operand of S^T = K Q^T), zero for padded heads ----
   uint4 qf[KS];
   {
+    const int64_t qr = MQ ? (int64_t)(q0 + jc) : (int64_t)s;
+    const int qhead = MQ ? c % G : c;
+    const bool qok = MQ ? jc < nq : c < G;
     const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
-                          (((int64_t)s * Hq + kvh * G + c) * D + DL * kg) * 2;
+                          ((qr * Hq + kvh * G + qhead) * D + DL * kg) * 2;
 #pragma unroll
     for (int t = 0; t < KS; ++t)
-      qf[t] = c < G ? reinterpret_cast<const uint4*>(qrow)[t] : make_uint4(0, 0, 0, 0);
+      qf[t] = qok ? reinterpret_cast<const uint4*>(qrow)[t] : make_uint4(0, 0, 0, 0);
   }
   // FP4 only: q in fp32 for the K-outlier term, channel-major: head c of channel ch at
   // (ch + ch / DL) * 16 + c. A column's 16 heads are 16 consecutive words (one read per
   // outlier is conflict-free) and the pad of 16 words after each DL channels puts the
   // four lane groups of a write on different banks.
-  float* q_lds = smem;
+  // (MQ: each wave has its own q copy and side accumulator, [q][side] per wave)
+  float* q_lds = MQ ? smem + (int64_t)wave * (kQLds + kSide) : smem;
   if constexpr (KV == KV_FP4) {
-    if (wave == 0) {
+    if (MQ || wave == 0) {
 #pragma unroll
       for (int t = 0; t < KS; ++t) {
         const uint32_t w[4] = {qf[t].x, qf[t].y, qf[t].z, qf[t].w};
@@ -293,14 +317,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
         }
       }
     }
-    __syncthreads();
+    if constexpr (!MQ) __syncthreads();
   }
   // FP4 only: this wave's side accumulator of the V-outlier terms, [D channels][GP heads]
   // fp32 (plus the spare row). The outlier channel of a block is known only at run time, and a run-time
   // index into the accumulator registers would cost a copy of all of them per case; so
   // the terms are summed here and folded into the registers at the end (and before a
   // rescale, which must scale both).
-  float* side = smem + kQLds + (int64_t)wave * kSide;
+  float* side = MQ ? q_lds + kQLds : smem + kQLds + (int64_t)wave * kSide;
   // this lane's entry for channel ch (a spare row for a padding head)
   auto side_at = [&](int ch) -> float* {
     return side + (c < GP ? ch * GP + c : D * GP + (c - GP));
@@ -435,14 +459,18 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     const int tok0 = T.jb * kBlock + 4 * kg;
     bool valid[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) valid[r] = FULL || (T.ok && (tok0 + r < end));
-    // V bytes of tokens past the context are arbitrary: zeroed, as a NaN code times p = 0
-    // would still be NaN (E2M1 has no NaN, and FP4's p already carries the mask)
+    for (int r = 0; r < 4; ++r) valid[r] = FULL || (T.ok && (tok0 + r < col_end));
+    // V bytes of tokens past the wave's last key are arbitrary: zeroed, as a NaN code
+    // times p = 0 would still be NaN (E2M1 has no NaN). The bound is the wave's, uniform
+    // over columns: a lane's V registers hold one channel group of these tokens for every
+    // column of the PV product, so per-column causal limits (MQ) act through p alone.
     if constexpr (!FULL && KV != KV_FP4) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < 4; ++r) {
+        const bool keep = T.ok && tok0 + r < end;
 #pragma unroll
-        for (int i = 0; i < G_::VW; ++i) T.v[r][i] = valid[r] ? T.v[r][i] : 0u;
+        for (int i = 0; i < G_::VW; ++i) T.v[r][i] = keep ? T.v[r][i] : 0u;
+      }
     }
 
     // logits S^T[token 4 kg + r][head c]
@@ -594,6 +622,19 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     } else if (my_n > 0 && ta.ok) {
       compute(ta, std::false_type{});
     }
+  } else if constexpr (MQ) {
+    // full blocks, then the (at most two) blocks that reach past the wave's first query
+    Tile<KV, D> tile;
+    if (my_n > 0) load_tile(tile, 0);
+    int i = 0;
+    for (; i + 1 < my_n && i < nfull; ++i) {
+      if (tile.ok) compute(tile, std::true_type{});
+      load_tile(tile, i + 1);
+    }
+    for (; i < my_n; ++i) {
+      if (tile.ok) compute(tile, std::false_type{});
+      if (i + 1 < my_n) load_tile(tile, i + 1);
+    }
   } else {
     Tile<KV, D> tile;
     if (my_n > 0) load_tile(tile, 0);
@@ -610,16 +651,17 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   const float lt = group4_sum(l);
   const float vscale = KV == KV_FP8 ? a.v_scale[kvh] : 1.0f;
   const int h = kvh * G + c;
-  if (W == 1) {
-    if (c < G) {
+  if (W == 1 || MQ) {
+    if (MQ ? jc < nq : c < G) {
       const float inv = lt > 0.0f ? vscale / lt : 0.0f;  // 0: every block id was bad
-      float* dst = split ? a.part_out + (((int64_t)s * Hq + h) * a.max_partitions + p) * D
-                         : a.out + ((int64_t)s * Hq + h) * D;
+      float* dst = MQ ? a.out + ((int64_t)(q0 + jc) * Hq + kvh * G + c % G) * D
+                   : split ? a.part_out + (((int64_t)s * Hq + h) * a.max_partitions + p) * D
+                           : a.out + ((int64_t)s * Hq + h) * D;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int n = 0; n < NT; ++n) dst[DL * kg + NT * r + n] = acc[n][r] * inv;
-      if (split && kg == 0)
+      if (!MQ && split && kg == 0)
         a.part_lse[((int64_t)s * Hq + h) * a.max_partitions + p] = (m + __log2f(lt)) * kLn2;
     }
     return;
@@ -676,7 +718,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 // (5 waves per SIMD for FP8 at head_dim 128).
 template <int KV, int D, bool QBF, int GP>
 __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
-  decode_body<KV, D, QBF, GP, false>(a);
+  decode_body<KV, D, QBF, GP, false, false>(a);
 }
 
 // FP4 pools: a tile is half the bytes of an FP8 one, so one tile per wave leaves too little
@@ -685,7 +727,14 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
 template <int D, bool QBF, int GP>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_fp4(
     DecodeArgs a) {
-  decode_body<KV_FP4, D, QBF, GP, true>(a);
+  decode_body<KV_FP4, D, QBF, GP, true, false>(a);
+}
+
+// Multi-token queries: 4 waves of 16 (query, head) columns each; single-buffered.
+constexpr int kPrefillWaves = 4;
+template <int KV, int D, bool QBF>
+__global__ __launch_bounds__(64 * kPrefillWaves) void k_prefill(DecodeArgs a) {
+  decode_body<KV, D, QBF, 16, false, true>(a);
 }
 
 template <int KV, int D, int GP>
@@ -708,16 +757,51 @@ static int launch_one(const DecodeArgs& a, int waves, hipStream_t st) {
     max_lds = 65536;
   while (waves > 1 && decode_lds_bytes<KV, D, GP>(waves) > (size_t)max_lds) waves /= 2;
   const size_t lds = decode_lds_bytes<KV, D, GP>(waves);
-#if PA_GRID_HEAD_FAST
   const dim3 grid((unsigned)((int64_t)P * a.num_kv_heads), (unsigned)a.num_seqs, 1);
-#else
-  const dim3 grid(P, a.num_kv_heads, a.num_seqs);
-#endif
   if constexpr (KV == KV_FP4)
     hipLaunchKernelGGL((k_decode_fp4<D, QBF, GP>), grid, dim3(64 * waves), lds, st, a);
   else
     hipLaunchKernelGGL((k_decode<KV, D, QBF, GP>), grid, dim3(64 * waves), lds, st, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+template <int KV, int D, bool QBF>
+static int launch_prefill_one(const DecodeArgs& a, hipStream_t st) {
+  const int qpw = kBlock / a.group;  // queries per wave
+  const int per_wg = kPrefillWaves * qpw;
+  const int tiles = (a.max_query_len + per_wg - 1) / per_wg;
+  if (tiles == 0 || a.num_seqs == 0) return PA_OK;
+  const size_t lds =
+      KV == KV_FP4
+          ? (size_t)kPrefillWaves * (fp4_qlds_floats<D, 16>() + fp4_side_floats<D, 16>()) * 4
+          : 0;
+  const dim3 grid((unsigned)((int64_t)tiles * a.num_kv_heads), (unsigned)a.num_seqs, 1);
+  hipLaunchKernelGGL((k_prefill<KV, D, QBF>), grid, dim3(64 * kPrefillWaves), lds, st, a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int launch_prefill(const DecodeArgs& a, int kv, bool qbf, int D, hipStream_t st) {
+  if (D == 128) {
+    switch (kv) {
+      case KV_F16: return launch_prefill_one<KV_F16, 128, false>(a, st);
+      case KV_BF16: return launch_prefill_one<KV_BF16, 128, true>(a, st);
+      case KV_FP8:
+        return qbf ? launch_prefill_one<KV_FP8, 128, true>(a, st)
+                   : launch_prefill_one<KV_FP8, 128, false>(a, st);
+      case KV_FP4:
+        return qbf ? launch_prefill_one<KV_FP4, 128, true>(a, st)
+                   : launch_prefill_one<KV_FP4, 128, false>(a, st);
+    }
+  } else {
+    switch (kv) {
+      case KV_F16: return launch_prefill_one<KV_F16, 64, false>(a, st);
+      case KV_BF16: return launch_prefill_one<KV_BF16, 64, true>(a, st);
+      case KV_FP8:
+        return qbf ? launch_prefill_one<KV_FP8, 64, true>(a, st)
+                   : launch_prefill_one<KV_FP8, 64, false>(a, st);
+    }
+  }
+  return PA_ERR_DTYPE;
 }
 
 int launch_decode(const DecodeArgs& a, int kv, bool qbf, int D, int waves, hipStream_t st) {

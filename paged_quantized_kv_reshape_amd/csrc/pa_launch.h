@@ -34,6 +34,8 @@ struct DecodeArgs {
   float* part_out;  // [S, Hq, P, D] otherwise
   float* part_lse;  // [S, Hq, P]
   int32_t* err;
+  const int32_t* query_start;  // multi-token queries: [S + 1] row offsets of q and out
+  int32_t max_query_len, num_queries;
   int32_t num_seqs, num_q_heads, num_kv_heads, group, num_blocks, max_blocks, partition_size,
       max_partitions, cap;
   float sm_scale_log2;  // sm_scale * log2(e)
@@ -41,6 +43,7 @@ struct DecodeArgs {
 
 int launch_decode(const DecodeArgs& a, int kv_dtype, bool q_bf16, int head_dim, int waves,
                   hipStream_t st);
+int launch_prefill(const DecodeArgs& a, int kv_dtype, bool q_bf16, int head_dim, hipStream_t st);
 
 int launch_merge(const float* part_out, const float* part_lse, const int32_t* context_lens,
                  int32_t S, int32_t Hq, int32_t D, int32_t P, int32_t ps, float* out,

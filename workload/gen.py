@@ -194,6 +194,19 @@ def make_workload(name, seed, num_seqs, num_q_heads, num_kv_heads, head_dim, kv,
     return w
 
 
+def prefill_queries(w: Workload, n: int):
+    """Multi-token queries for w: the last n_s = min(n, L_s) positions of every sequence.
+
+    Returns (q bits [sum n_s, Hq, D] uint16, query_start [S + 1] int32). The rows are
+    N(0, 1) in fp32 rounded to the activation dtype, drawn from the fifth child of the
+    workload's root SeedSequence (the first four are structure, Q, K, V)."""
+    ns = np.minimum(np.int64(n), w.context_lens.astype(np.int64))
+    qs = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    st = np.random.SeedSequence(w.seed).spawn(5)[4]
+    q = _normal_rows(st, int(qs[-1]), w.num_q_heads, w.head_dim, w.act)
+    return q, qs
+
+
 # The five workloads, full size. c1 is the tiny fp16 case; c2/c3 the 8B-shaped layer
 # (32 q heads over 8 kv heads, head_dim 128, 64 sequences of 1k-8k tokens); c4 the 70B
 # one-GPU tensor-parallel share (8 q heads over 1 kv head, 256 x 8192 tokens, FP8);
