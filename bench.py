@@ -165,6 +165,120 @@ def cpu_baseline(w, budget_s: float, decode_b_per_token: float):
                        f"(+ partitions) of the sequences; bytes counted as for the GPU step")}
 
 
+def prefill_flops(w, qs) -> int:
+    """Algorithmic flops of multi-token attention: query i of sequence s (position
+    L - n + i) does 2 D flops per key for QK and 2 D for PV over L - n + i + 1 keys."""
+    tot = 0
+    for s in range(w.num_seqs):
+        L, n = int(w.context_lens[s]), int(qs[s + 1] - qs[s])
+        keys = n * (L - n) + n * (n + 1) // 2
+        tot += 4 * w.head_dim * w.num_q_heads * keys
+    return tot
+
+
+def prefill_main(args, config, DESCRIPTIONS):
+    """Chunked-prefill attention (pa_prefill) on the chosen workload: every sequence's last
+    CHUNK positions are queries over its whole paged context."""
+    import numpy as np
+    import torch
+
+    from oracle import attention as A
+    from oracle import cache as C
+    from paged_quantized_kv_reshape_amd import harness as H
+    from paged_quantized_kv_reshape_amd import pa_prefill
+    from workload import prefill_queries
+
+    print(f"[bench] generating {args.config} (prefill chunk {args.prefill})", file=sys.stderr,
+          flush=True)
+    w = config(args.config)
+    run = H.DeviceRun(w, device="cuda", partition_size=0, pool_copies=1)
+    run.prepare()
+    torch.cuda.synchronize()
+    q_bits, qs = prefill_queries(w, args.prefill)
+    tdt = torch.bfloat16 if w.act == "bf16" else torch.float16
+    q = torch.from_numpy(q_bits.view(np.int16)).cuda().view(tdt)
+    qs_t = torch.from_numpy(qs).cuda()
+    out = torch.empty((q.shape[0], w.num_q_heads, w.head_dim), dtype=torch.float32,
+                      device="cuda")
+    nmax = int(np.diff(qs).max())
+    flops = prefill_flops(w, qs)
+
+    def launch():
+        pa_prefill(q, qs_t, nmax, run.pool, run.block_tables, run.context_lens, w.sm_scale,
+                   out, run.dev_err)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    if run.device_error():
+        raise SystemExit(f"device error: {run.device_error()}")
+    stream = torch.cuda.current_stream().cuda_stream
+    timer = HipTimer()
+    a, b = timer.event(), timer.event()
+    t0 = time.perf_counter()
+    timer.record(a, stream)
+    for _ in range(args.steps):
+        launch()
+    timer.record(b, stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    t = timer.ms(a, b) * 1e-3 / args.steps
+    timer.close()
+    tflops = flops / t / 1e12
+    res = {
+        "metric": "paged multi-token (chunked prefill) attention: achieved TFLOP/s",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.act, "data": "synthetic",
+        "config": {"workload": f"{args.config}: {DESCRIPTIONS[args.config]}",
+                   "prefill_chunk": args.prefill, "queries": int(qs[-1]),
+                   "kv_cache_dtype": w.kv, "num_seqs": w.num_seqs,
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim},
+        "algorithmic_flops": flops,
+        "wall_ms_per_step": round(wall * 1e3, 4),
+        "roofline": {"kernel": "k_prefill", "bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": 2500.0, "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+        print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
+        with threadpool_limits(limits=1):
+            ks = vs = None
+            if w.kv == "fp8":
+                ks = C.fp8_head_scale(w.k_rows, w.act)
+                vs = C.fp8_head_scale(w.v_rows, w.act)
+            pool = C.Pool.filled(w.kv, w.num_blocks, w.num_kv_heads, w.head_dim)
+            s0 = 0
+            n0 = -(-int(w.context_lens[s0]) // 16)
+            keep = np.asarray(sorted(int(b) for b in w.block_tables[s0, :n0]))
+            for c in list(w.setup_calls) + [w.step_call]:
+                sel = np.isin(c.slots // 16, keep)
+                if sel.any():
+                    C.cache_write(pool, w.k_rows[c.rows[sel]], w.v_rows[c.rows[sel]], w.act,
+                                  c.slots[sel], ks, vs)
+            # a bounded sample: the first queries of sequence 0's chunk, about 10 s
+            n_s = int(qs[1] - qs[0])
+            t0 = time.perf_counter()
+            done = 0
+            while done < n_s and time.perf_counter() - t0 < args.cpu_seconds * 0.7:
+                sub = np.array([0, 1], dtype=np.int32)  # one query at position L_sub - 1
+                L_sub = np.array([int(w.context_lens[s0]) - n_s + done + 1], dtype=np.int32)
+                A.paged_prefill(q_bits[done:done + 1], w.act, pool, w.block_tables[:1], L_sub,
+                                sub, w.sm_scale, ks, vs)
+                done += 1
+            dt = time.perf_counter() - t0
+        L0 = int(w.context_lens[s0])
+        keys = sum(L0 - n_s + i + 1 for i in range(done))
+        f = 4 * w.head_dim * w.num_q_heads * keys
+        res["cpu_baseline"] = {"value": round(f / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                               "kind": "oracle", "seconds": round(dt, 2),
+                               "sample": f"{done} queries of sequence 0's chunk (all heads), "
+                                         f"exact fp64, flops counted as for the GPU"}
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +292,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
+    ap.add_argument("--prefill", type=int, default=0, metavar="CHUNK",
+                    help="time pa_prefill instead: the last CHUNK positions of every sequence "
+                         "as queries (chunked prefill), reported in TFLOP/s")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -196,6 +313,10 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.prefill > 0:
+        prefill_main(args, config, DESCRIPTIONS)
+        return
 
     print(f"[bench] generating {args.config}", file=sys.stderr, flush=True)
     w = config(args.config)
