@@ -58,6 +58,9 @@ from .formats import (
     e4m3_decode,
     e4m3_encode,
     f16_decode,
+    fp8_decode,
+    fp8_encode,
+    fp8_max,
     f16_encode,
     f32_quotient,
     f32_round,
@@ -77,9 +80,15 @@ def outlier_capacity(head_dim: int) -> int:
     return int(np.floor(head_dim / (1.0 + OUTLIER_SIGMAS ** 2)))
 
 
+# FP8 pool kinds: code format and where the scale lives ("head": a per-(layer, kv head)
+# input; "token": computed per (token, kv head, K|V) at write time, stored in the run)
+FP8_KINDS = {"fp8": ("e4m3", "head"), "bf8": ("e5m2", "head"),
+             "fp8t": ("e4m3", "token"), "bf8t": ("e5m2", "token")}
+
+
 @dataclass
 class Pool:
-    kind: str  # "f16" | "bf16" | "fp8" | "fp4"
+    kind: str  # "f16" | "bf16" | "fp8" | "bf8" | "fp8t" | "bf8t" | "fp4"
     num_blocks: int
     num_kv_heads: int
     head_dim: int
@@ -89,8 +98,11 @@ class Pool:
     def shapes(kind, nb, hkv, d):
         if kind in ("f16", "bf16"):
             return {"k": ((nb, hkv, 16, d), np.uint16), "v": ((nb, hkv, 16, d), np.uint16)}
-        if kind == "fp8":
+        if kind in ("fp8", "bf8"):
             return {"k": ((nb, hkv, 16, d), np.uint8), "v": ((nb, hkv, 16, d), np.uint8)}
+        if kind in ("fp8t", "bf8t"):
+            return {"k": ((nb, hkv, fp8t_run_bytes(d)), np.uint8),
+                    "v": ((nb, hkv, fp8t_run_bytes(d)), np.uint8)}
         if kind == "fp4":
             cap = outlier_capacity(d)
             out = {}
@@ -117,6 +129,25 @@ class Pool:
 # ----------------------------------------------------------------------------------
 # FP4 tile regions (views into a pool's k / v byte arrays)
 # ----------------------------------------------------------------------------------
+
+
+def fp8t_run_bytes(head_dim: int) -> int:
+    """Bytes of one per-token-scaled FP8 (block, head) run: the 16 x D code bytes (token
+    rows), then the 16 fp32 token scales, rounded up to a multiple of 128 bytes."""
+    return -(-(16 * head_dim + 64) // 128) * 128
+
+
+def fp8t_codes(pool: Pool, kv: str) -> np.ndarray:
+    """Codes of a per-token-scaled FP8 pool, a view [NB, Hkv, 16, D] uint8."""
+    d = pool.head_dim
+    a = pool.arrays[kv]
+    return a[..., :16 * d].reshape(a.shape[0], a.shape[1], 16, d)
+
+
+def fp8t_scales(pool: Pool, kv: str) -> np.ndarray:
+    """Per-token scales of a per-token-scaled FP8 pool, a view [NB, Hkv, 16] fp32."""
+    d = pool.head_dim
+    return pool.arrays[kv][..., 16 * d:16 * d + 64].view(np.float32)
 
 
 def fp4_tile_bytes(head_dim: int) -> int:
@@ -206,14 +237,22 @@ def fp4_outlier_values(pool: Pool, kv: str, blk, h) -> np.ndarray:
 # ----------------------------------------------------------------------------------
 
 
-def fp8_head_scale(rows_bits: np.ndarray, act: str) -> np.ndarray:
-    """Per-kv-head fp32 scale fp32(absmax_h / 448) over rows [T, Hkv, D] (the rows are
-    visited in slices only to bound memory; a maximum does not depend on order)."""
+def fp8_head_scale(rows_bits: np.ndarray, act: str, fmt: str = "e4m3") -> np.ndarray:
+    """Per-kv-head fp32 scale fp32(absmax_h / max) over rows [T, Hkv, D], max = 448 (E4M3)
+    or 57344 (E5M2) (the rows are visited in slices only to bound memory; a maximum does
+    not depend on order)."""
     absmax = np.zeros(rows_bits.shape[1])
     for lo in range(0, rows_bits.shape[0], 1 << 16):
         x = act_decode(rows_bits[lo:lo + (1 << 16)], act)
         absmax = np.maximum(absmax, np.abs(x).max(axis=(0, 2)))
-    return f32_quotient(absmax, E4M3_MAX).astype(np.float32)
+    return f32_quotient(absmax, fp8_max(fmt)).astype(np.float32)
+
+
+def fp8_token_scale(x: np.ndarray, fmt: str) -> np.ndarray:
+    """Per-row fp32 scale fp32(max_c |x_c| / max) of rows x [..., D] (fp64 of the input
+    values): the scale each token's row is quantized with when it is written (dynamic,
+    per token, the FP8 counterpart of the 4-bit path's per-token scale)."""
+    return f32_quotient(np.abs(x).max(axis=-1), fp8_max(fmt))
 
 
 # ----------------------------------------------------------------------------------
@@ -292,13 +331,21 @@ def cache_write(pool: Pool, k_rows, v_rows, act: str, slots, k_scale=None, v_sca
         A["k"][blk, :, off, :] = np.asarray(k_rows)[live]
         A["v"][blk, :, off, :] = np.asarray(v_rows)[live]
         return
-    if pool.kind == "fp8":
+    if pool.kind in FP8_KINDS:
+        fmt, where = FP8_KINDS[pool.kind]
         for name, rows, sc in (("k", k_rows, k_scale), ("v", v_rows, v_scale)):
             x = act_decode(np.asarray(rows)[live], act)  # [n, Hkv, D]
-            s = np.asarray(sc, dtype=np.float32).astype(np.float64)[None, :, None]
+            if where == "head":
+                s = np.asarray(sc, dtype=np.float32).astype(np.float64)[None, :, None]
+            else:
+                s = fp8_token_scale(x, fmt)[..., None]  # [n, Hkv, 1]
             q = f32_quotient(x, s)
-            codes = e4m3_encode(np.where(s == 0.0, 0.0, q))
-            A[name][blk, :, off, :] = codes
+            codes = fp8_encode(np.where(s == 0.0, 0.0, q), fmt)
+            if where == "head":
+                A[name][blk, :, off, :] = codes
+            else:
+                fp8t_codes(pool, name)[blk, :, off, :] = codes
+                fp8t_scales(pool, name)[blk, :, off] = s[..., 0].astype(np.float32)
         return
     if pool.kind == "fp4":
         hkv = pool.num_kv_heads
@@ -354,9 +401,14 @@ def dequant_slot_rows(pool: Pool, blk, off, k_scale=None, v_scale=None):
             out.append(act_decode(A[name][blk, :, off, :], "bf16"))
         elif pool.kind == "f16":
             out.append(f16_decode(A[name][blk, :, off, :]))
-        elif pool.kind == "fp8":
-            s = np.asarray(sc, dtype=np.float32).astype(np.float64)[None, :, None]
-            out.append(e4m3_decode(A[name][blk, :, off, :]) * s)
+        elif pool.kind in FP8_KINDS:
+            fmt, where = FP8_KINDS[pool.kind]
+            if where == "head":
+                s = np.asarray(sc, dtype=np.float32).astype(np.float64)[None, :, None]
+                out.append(fp8_decode(A[name][blk, :, off, :], fmt) * s)
+            else:
+                s = fp8t_scales(pool, name)[blk, :, off].astype(np.float64)[..., None]
+                out.append(fp8_decode(fp8t_codes(pool, name)[blk, :, off, :], fmt) * s)
         elif pool.kind == "fp4":
             codes = fp4_get_codes(pool, name)[blk, :, off, :]  # [n, Hkv, D]
             n, hkv = codes.shape[:2]
@@ -392,6 +444,7 @@ __all__ = [
     "fp4_tile_bytes", "fp4_code_map", "fp4_code_bytes", "fp4_get_codes", "fp4_put_codes",
     "fp4_scales", "fp4_records", "fp4_slot0",
     "fp4_outlier_values",
+    "FP8_KINDS", "fp8t_run_bytes", "fp8t_codes", "fp8t_scales", "fp8_token_scale",
     "fp8_head_scale", "fp4_calibrate", "fp4_calibration_margin", "fp4_encode_row",
     "cache_write", "dequant_slot_rows", "gather_sequence", "f32_round",
 ]

@@ -9,6 +9,9 @@ Formats used by the pages:
     v0.7.2 Architecture"; inferensys glossary "vLLM", KV cache quantization entry).
     The variant is the OCP "E4M3FN" one: exponent bias 7, subnormals m*2^-9, largest
     finite value 448 (S.1111.110), NaN = S.1111.111, no infinities.
+  * FP8 E5M2 KV cache (same report and section: "FP8 (E4M3 and E5M2)"). OCP E5M2:
+    exponent bias 15, subnormals m*2^-16, largest finite value 57344 (S.11110.11),
+    infinities S.11111.00, NaN S.11111.xx with xx != 0.
   * 4-bit float KV cache (dailyaiworld.com, "vLLM 0.7 Ships Unified KV Cache
     Compression", section "Technical Breakdown: Dynamic Quantization with Outlier
     Retention", step 3). Read as OCP E2M1: bias 1, magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6.
@@ -133,6 +136,62 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
     idx = _nearest_even_index(a, _E4M3_MAGS).astype(np.uint8)
     idx = np.where(nan, np.uint8(0x7F), idx)
     return (idx | sign).astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------------
+# OCP FP8 E5M2
+# ----------------------------------------------------------------------------------
+
+E5M2_MAX = 57344.0
+
+
+def e5m2_magnitudes() -> np.ndarray:
+    """Magnitudes of the 124 finite non-negative E5M2 codes 0x00..0x7B, by code."""
+    out = np.empty(124, dtype=np.float64)
+    for code in range(124):
+        e, m = code >> 2, code & 3
+        if e == 0:
+            out[code] = m * 2.0 ** -16  # subnormal: (m/4) * 2^(1-15)
+        else:
+            out[code] = (1.0 + m / 4.0) * 2.0 ** (e - 15)
+    return out
+
+
+_E5M2_MAGS = e5m2_magnitudes()
+
+
+def e5m2_decode(codes: np.ndarray) -> np.ndarray:
+    """E5M2 byte codes -> fp64 (+-inf for S.11111.00, NaN for S.11111.xx, xx != 0)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    mag_bits = c & 0x7F
+    val = np.where(mag_bits == 0x7C, np.inf,
+                   np.where(mag_bits > 0x7C, np.nan, _E5M2_MAGS[np.minimum(mag_bits, 123)]))
+    return np.where(c & 0x80, -val, val)
+
+
+def e5m2_encode(v: np.ndarray) -> np.ndarray:
+    """fp64 -> E5M2 byte codes: nearest, ties to even, saturating to +-57344 (infinities
+    included, as for E4M3), sign of zero kept, NaN -> S.11111.11."""
+    v = np.asarray(v, dtype=np.float64)
+    sign = np.signbit(v).astype(np.uint8) << np.uint8(7)
+    nan = np.isnan(v)
+    a = np.minimum(np.abs(np.where(nan, 0.0, v)), E5M2_MAX)
+    idx = _nearest_even_index(a, _E5M2_MAGS).astype(np.uint8)
+    idx = np.where(nan, np.uint8(0x7F), idx)
+    return (idx | sign).astype(np.uint8)
+
+
+def fp8_encode(v: np.ndarray, fmt: str) -> np.ndarray:
+    """fmt "e4m3" or "e5m2"."""
+    return e4m3_encode(v) if fmt == "e4m3" else e5m2_encode(v)
+
+
+def fp8_decode(codes: np.ndarray, fmt: str) -> np.ndarray:
+    return e4m3_decode(codes) if fmt == "e4m3" else e5m2_decode(codes)
+
+
+def fp8_max(fmt: str) -> float:
+    return E4M3_MAX if fmt == "e4m3" else E5M2_MAX
 
 
 # ----------------------------------------------------------------------------------

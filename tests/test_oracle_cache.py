@@ -276,3 +276,53 @@ def test_fp4_put_codes_keeps_the_other_nibbles():
         sentinel = (0xA5 >> shift) & 0xF
         assert np.array_equal(got, np.where(want >= 0, want, sentinel))
         assert np.all(C.fp4_code_bytes(pool, kv)[0] == 0xA5)
+
+
+@pytest.mark.parametrize("kind", ["fp8t", "bf8t"])
+def test_fp8_token_scale_pool_invariants(kind):
+    """Per-token FP8: every written row's largest magnitude encodes to the format's largest
+    code, dequantized values are within half a grid step (times the scale) of the input,
+    and every byte of unwritten rows keeps its sentinel."""
+    fmt = C.FP8_KINDS[kind][0]
+    top = 0x7E if fmt == "e4m3" else 0x7B
+    rng = np.random.default_rng(4)
+    d, hkv, nb = 128, 2, 4
+    x = rng.standard_normal((10, hkv, d)).astype(np.float32) * 3
+    x[:, 0, 7] *= 20
+    bits = ((x.view(np.uint32) + 0x7FFF + ((x.view(np.uint32) >> 16) & 1)) >> 16).astype(np.uint16)
+    pool = C.Pool.filled(kind, nb, hkv, d)
+    slots = np.array([16 + 3, 16 + 9, 48, 49, 50, 51, 52, 53, 54, 55], dtype=np.int64)
+    C.cache_write(pool, bits, bits, "bf16", slots)
+    xv = F.bf16_decode(bits)
+    codes = C.fp8t_codes(pool, "k")
+    sc = C.fp8t_scales(pool, "k")
+    blk, off = slots // 16, slots % 16
+    for i in range(len(slots)):
+        for h in range(hkv):
+            c = codes[blk[i], h, off[i]]
+            j = int(np.argmax(np.abs(xv[i, h])))
+            assert (int(c[j]) & 0x7F) == top
+            assert sc[blk[i], h, off[i]] == np.float32(np.abs(xv[i, h]).max() / F.fp8_max(fmt))
+    kd, vd = C.dequant_slot_rows(pool, blk, off)
+    mags = F.e4m3_magnitudes() if fmt == "e4m3" else F.e5m2_magnitudes()
+    step = np.max(np.diff(mags) / np.maximum(mags[1:], 1e-300))  # relative grid step bound
+    s = sc[blk, :, off][..., None].astype(np.float64)
+    assert np.all(np.abs(kd - xv) <= np.maximum(np.abs(xv) * step, s * mags[1]) + 1e-12)
+    # untouched rows: offsets other than the written ones, and block 0 / 3 entirely
+    raw = pool.arrays["k"]
+    assert np.all(raw[[0, 2]] == 0xA5)
+    assert np.all(codes[1, :, [o for o in range(16) if o not in (3, 9)]] == 0xA5)
+    assert np.all(raw[3, :, 16 * d + 64:] == 0xA5)  # padding
+
+
+def test_fp8_head_scale_e5m2_invariant():
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal((50, 3, 64)) * 7).astype(np.float16).view(np.uint16)
+    s = C.fp8_head_scale(x, "f16", "e5m2")
+    pool = C.Pool.filled("bf8", 4, 3, 64)
+    C.cache_write(pool, x[:16], x[:16], "f16", np.arange(16, 32), s, s)
+    xv = F.f16_decode(x[:16])
+    for h in range(3):
+        if np.abs(xv[:, h]).max() == np.abs(F.f16_decode(x)[:, h]).max():
+            j = np.unravel_index(np.argmax(np.abs(xv[:, h])), xv[:, h].shape)
+            assert int(pool.arrays["k"][1, h, j[0], j[1]]) & 0x7F == 0x7B

@@ -132,3 +132,67 @@ def test_f32_quotient_is_correctly_rounded():
         up, dn = np.nextafter(r32, np.float32(np.inf)), np.nextafter(r32, np.float32(-np.inf))
         d = abs(Fraction(float(r32)) - exact)
         assert d <= abs(Fraction(float(up)) - exact) and d <= abs(Fraction(float(dn)) - exact)
+
+
+def _fval(s):
+    return {"nan": float("nan"), "inf": float("inf"), "-inf": float("-inf")}.get(s, None) \
+        if s in ("nan", "inf", "-inf") else float(s)
+
+
+def test_e5m2_table_matches_ocp_spec():
+    for code_s, val_s in read_golden("e5m2_values.txt"):
+        code = int(code_s, 16)
+        got = F.e5m2_decode(np.array([code], dtype=np.uint8))[0]
+        want = _fval(val_s)
+        if np.isnan(want):
+            assert np.isnan(got), code_s
+        else:
+            assert got == want and np.signbit(got) == np.signbit(want), (code_s, got, want)
+
+
+def test_e5m2_all_finite_codes_round_trip():
+    codes = np.array([c for c in range(256) if (c & 0x7F) < 0x7C], dtype=np.uint8)
+    assert len(codes) == 248
+    assert np.array_equal(F.e5m2_encode(F.e5m2_decode(codes)), codes)  # includes -0 -> 0x80
+
+
+def test_e5m2_midpoints_go_to_even_code():
+    mags = F.e5m2_magnitudes()
+    assert np.all(np.diff(mags) > 0) and mags[-1] == F.E5M2_MAX
+    mids = (mags[:-1] + mags[1:]) / 2
+    lo = np.arange(len(mags) - 1)
+    assert np.array_equal(F.e5m2_encode(mids).astype(np.int64), np.where(lo % 2 == 0, lo, lo + 1))
+    eps = np.diff(mags) * 1e-6
+    assert np.array_equal(F.e5m2_encode(mids - eps).astype(np.int64), lo)
+    assert np.array_equal(F.e5m2_encode(mids + eps).astype(np.int64), lo + 1)
+
+
+def test_e5m2_saturation_nan_and_signed_zero():
+    v = np.array([57344.0, 60000.0, 61440.0, 1e30, np.inf, -7e4, -np.inf, 0.0, -0.0, np.nan])
+    got = F.e5m2_encode(v).tolist()
+    assert got[:7] == [0x7B, 0x7B, 0x7B, 0x7B, 0x7B, 0xFB, 0xFB]
+    assert got[7:9] == [0x00, 0x80]
+    assert got[9] & 0x7F == 0x7F
+
+
+def test_e5m2_matches_torch_cast_on_clamped_fp32():
+    rng = np.random.default_rng(321)
+    mags = F.e5m2_magnitudes()
+    parts = [rng.standard_normal(20000) * 3000, rng.standard_normal(20000) * 2.0 ** -15,
+             (mags[:-1] + mags[1:]) / 2, rng.uniform(-57344, 57344, 20000)]
+    x = np.clip(np.concatenate(parts), -57344, 57344).astype(np.float32)
+    x = np.concatenate([x, -x])
+    want = torch.from_numpy(x).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(F.e5m2_encode(x.astype(np.float64)), want)
+
+
+def test_e5m2_error_bound_closed_form():
+    rng = np.random.default_rng(6)
+    x = rng.uniform(-57344, 57344, 50000)
+    x = np.concatenate([x, rng.standard_normal(50000) * 2.0 ** -14])
+    err = np.abs(x - F.e5m2_decode(F.e5m2_encode(x)))
+    a = np.abs(x)
+    # spacing: 2^-16 below 2^-14, else 2^(floor(log2 a) - 2)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
+    spacing = 2.0 ** (e - 2)
+    assert np.all(err <= spacing / 2 + 1e-300)
