@@ -126,9 +126,10 @@ def cpu_baseline(w, budget_s: float, decode_b_per_token: float):
 
     with threadpool_limits(limits=1):
         ks = vs = None
-        if w.kv == "fp8":  # inputs of the method (per-head scales), not timed
-            ks = C.fp8_head_scale(w.k_rows, w.act)
-            vs = C.fp8_head_scale(w.v_rows, w.act)
+        if w.kv in ("fp8", "bf8"):  # inputs of the method (per-head scales), not timed
+            fmt = C.FP8_KINDS[w.kv][0]
+            ks = C.fp8_head_scale(w.k_rows, w.act, fmt)
+            vs = C.fp8_head_scale(w.v_rows, w.act, fmt)
         pool = C.Pool.filled(w.kv, w.num_blocks, w.num_kv_heads, w.head_dim)
         calls = list(w.setup_calls) + [w.step_call]
         blk_of_call = [c.slots // 16 for c in calls]
@@ -246,9 +247,10 @@ def prefill_main(args, config, DESCRIPTIONS):
         print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
         with threadpool_limits(limits=1):
             ks = vs = None
-            if w.kv == "fp8":
-                ks = C.fp8_head_scale(w.k_rows, w.act)
-                vs = C.fp8_head_scale(w.v_rows, w.act)
+            if w.kv in ("fp8", "bf8"):
+                fmt = C.FP8_KINDS[w.kv][0]
+                ks = C.fp8_head_scale(w.k_rows, w.act, fmt)
+                vs = C.fp8_head_scale(w.v_rows, w.act, fmt)
             pool = C.Pool.filled(w.kv, w.num_blocks, w.num_kv_heads, w.head_dim)
             s0 = 0
             n0 = -(-int(w.context_lens[s0]) // 16)

@@ -50,7 +50,10 @@ typedef enum {
   PA_KV_F16 = 0,            /* fp16 copy, no quantization                              */
   PA_KV_BF16 = 1,           /* bf16 copy, no quantization                              */
   PA_KV_FP8_E4M3 = 2,       /* OCP E4M3FN codes, one fp32 scale per kv head (K and V)  */
-  PA_KV_FP4_E2M1_OUTL = 3   /* E2M1 codes + per-token fp32 scale + fp16 outlier buffer */
+  PA_KV_FP4_E2M1_OUTL = 3,  /* E2M1 codes + per-token fp32 scale + fp16 outlier buffer */
+  PA_KV_FP8_E5M2 = 4,       /* OCP E5M2 codes, one fp32 scale per kv head (K and V)    */
+  PA_KV_FP8_E4M3_TOKEN = 5, /* E4M3FN codes + a per-token fp32 scale set at write time */
+  PA_KV_FP8_E5M2_TOKEN = 6  /* E5M2 codes + a per-token fp32 scale set at write time   */
 } pa_kv_dtype;
 
 /* Activation (query and new K/V row) dtypes. */
@@ -77,10 +80,23 @@ typedef enum {
  * The paged KV pool (passed by host pointer; the arrays it points to are device memory).
  *
  *   PA_KV_F16 / PA_KV_BF16 : k, v   [num_blocks, num_kv_heads, 16, head_dim] 16-bit values
- *   PA_KV_FP8_E4M3         : k, v   [num_blocks, num_kv_heads, 16, head_dim] uint8 codes
+ *   PA_KV_FP8_E4M3 / _E5M2 : k, v   [num_blocks, num_kv_heads, 16, head_dim] uint8 codes
  *                            k_scale, v_scale [num_kv_heads] fp32 (inputs, read-only):
  *                            the stored value is code * scale (per layer and kv head;
- *                            see pa_fp8_head_scales).
+ *                            see pa_fp8_head_scales). Both OCP FP8 formats are the pages'
+ *                            ("FP8 (E4M3 and E5M2)", xonoai.com field report,
+ *                            "Deconstructing the v0.7.2 Architecture").
+ *   PA_KV_FP8_E4M3_TOKEN / _E5M2_TOKEN :
+ *                            k, v   [num_blocks, num_kv_heads, PA_FP8T_TILE_BYTES(head_dim)]
+ *                                   bytes, one run per (block, kv head): codes
+ *                                   [16 tokens][head_dim], then at PA_FP8T_SCALE_OFF the 16
+ *                                   per-token fp32 scales, padding to a multiple of 128.
+ *                            The scale of a token row is fp32(max |x| / 448) (E4M3) or
+ *                            fp32(max |x| / 57344) (E5M2), set when the row is written:
+ *                            quantization on the fly (dailyaiworld.com, "vLLM 0.7 Ships
+ *                            Unified KV Cache Compression", opening section), with no
+ *                            per-head calibration to drift (xonoai.com report, closing
+ *                            section). No scale arrays are needed.
  *   PA_KV_FP4_E2M1_OUTL    : k, v   [num_blocks, num_kv_heads, PA_FP4_TILE_BYTES(head_dim)]
  *                                   bytes: one contiguous run per (block, kv head) holding
  *                                   everything a decode reads for that block, so it is
@@ -114,6 +130,9 @@ typedef enum {
 #define PA_FP4_RECORD_OFF(head_dim) (8 * (head_dim) + 64)
 #define PA_FP4_SLOT0_OFF(head_dim) (8 * (head_dim) + 80)
 #define PA_FP4_TILE_BYTES(head_dim) ((8 * (head_dim) + 112 + 127) / 128 * 128)
+/* per-token-scaled FP8 run: token scales after the 16 x head_dim code bytes */
+#define PA_FP8T_SCALE_OFF(head_dim) (16 * (head_dim))
+#define PA_FP8T_TILE_BYTES(head_dim) ((16 * (head_dim) + 64 + 127) / 128 * 128)
 
 typedef struct pa_kv_pool {
   int32_t dtype;          /* pa_kv_dtype */
@@ -173,14 +192,15 @@ int pa_cache_write(const pa_kv_pool* pool, const void* k_new, const void* v_new,
 
 /*
  * Per-kv-head FP8 scale of a tensor x [num_rows, num_kv_heads, head_dim] (activation dtype
- * `act`): scale_out[h] = fp32(max |x[:, h, :]| / 448), the per-(layer, kv head) fp32 scale
- * that maps each head's largest magnitude onto the largest E4M3FN value (xonoai.com
- * report, "Deconstructing the v0.7.2 Architecture" and "Field Observations", on FP8
- * calibration). scale_out [num_kv_heads] fp32 is overwritten. Call once for K and once
- * for V. Asynchronous on `stream`.
+ * `act`) for a pool of dtype kv_dtype (PA_KV_FP8_E4M3 or PA_KV_FP8_E5M2):
+ * scale_out[h] = fp32(max |x[:, h, :]| / M), M = 448 (E4M3) or 57344 (E5M2), the
+ * per-(layer, kv head) fp32 scale that maps each head's largest magnitude onto the
+ * format's largest value (xonoai.com report, "Deconstructing the v0.7.2 Architecture" and
+ * "Field Observations", on FP8 calibration). scale_out [num_kv_heads] fp32 is overwritten.
+ * Call once for K and once for V. Asynchronous on `stream`.
  */
-int pa_fp8_head_scales(const void* x, int32_t act, int64_t num_rows, int32_t num_kv_heads,
-                       int32_t head_dim, float* scale_out, void* stream);
+int pa_fp8_head_scales(const void* x, int32_t act, int32_t kv_dtype, int64_t num_rows,
+                       int32_t num_kv_heads, int32_t head_dim, float* scale_out, void* stream);
 
 /*
  * Mark the listed physical blocks as never written (FP4 records set to 0xFF), so the next

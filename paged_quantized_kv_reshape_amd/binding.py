@@ -14,7 +14,9 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 _lib = None
 
-KV_DTYPES = {"f16": 0, "bf16": 1, "fp8": 2, "fp4": 3}
+KV_DTYPES = {"f16": 0, "bf16": 1, "fp8": 2, "fp4": 3, "bf8": 4, "fp8t": 5, "bf8t": 6}
+# pool formats with one fp32 scale per kv head (inputs: k_scale / v_scale)
+HEAD_SCALED = ("fp8", "bf8")
 ACT_DTYPES = {torch.float16: 0, torch.bfloat16: 1}
 BLOCK_SIZE = 16
 DEVERR_BITS = {1: "bad block id", 2: "bad slot", 4: "bad context length",
@@ -64,7 +66,7 @@ def lib():
             "pa_pool_layout": (ctypes.c_int, [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]),
             "pa_outlier_capacity": (ctypes.c_int, [i32]),
             "pa_cache_write": (ctypes.c_int, [pool_p, vp, vp, i32, i32, vp, vp, vp]),
-            "pa_fp8_head_scales": (ctypes.c_int, [vp, i32, i64, i32, i32, vp, vp]),
+            "pa_fp8_head_scales": (ctypes.c_int, [vp, i32, i32, i64, i32, i32, vp, vp]),
             "pa_reset_blocks": (ctypes.c_int, [pool_p, vp, i32, vp]),
             "pa_decode": (ctypes.c_int, [vp, i32, i32, i32, pool_p, vp, i32, vp, f32, i32, vp, vp,
                                          vp, vp, vp]),
@@ -127,8 +129,8 @@ class KVPool:
             if n:
                 self.bytes[name] = torch.full((n,), fill, dtype=torch.uint8, device=device)
         self.k_scale, self.v_scale = k_scale, v_scale
-        if kv_dtype == "fp8" and (k_scale is None or v_scale is None):
-            raise ValueError("an fp8 pool needs k_scale and v_scale")
+        if kv_dtype in HEAD_SCALED and (k_scale is None or v_scale is None):
+            raise ValueError(f"a {kv_dtype} pool needs k_scale and v_scale")
         if kv_dtype == "fp4":
             pa_reset_blocks(self, torch.arange(num_blocks, dtype=torch.int32, device=device))
 
@@ -164,12 +166,13 @@ def pa_cache_write(pool: KVPool, k_new, v_new, slot_mapping, dev_err=None):
         _ptr(slot_mapping), _ptr(dev_err), _stream()))
 
 
-def pa_fp8_head_scales(x, scale_out):
-    """x [rows, Hkv, D] fp16/bf16 -> scale_out [Hkv] fp32 (overwritten)."""
+def pa_fp8_head_scales(x, scale_out, kv_dtype="fp8"):
+    """x [rows, Hkv, D] fp16/bf16 -> scale_out [Hkv] fp32 (overwritten) for a pool of
+    kv_dtype "fp8" (E4M3, absmax / 448) or "bf8" (E5M2, absmax / 57344)."""
     assert x.dtype in ACT_DTYPES and scale_out.dtype == torch.float32
     _check("pa_fp8_head_scales", lib().pa_fp8_head_scales(
-        _ptr(x), ACT_DTYPES[x.dtype], x.shape[0], x.shape[1], x.shape[2], _ptr(scale_out),
-        _stream()))
+        _ptr(x), ACT_DTYPES[x.dtype], KV_DTYPES[kv_dtype], x.shape[0], x.shape[1], x.shape[2],
+        _ptr(scale_out), _stream()))
 
 
 def pa_reset_blocks(pool: KVPool, block_ids):

@@ -16,7 +16,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int check_pool(const pa_kv_pool* p) {
   if (!p) return PA_ERR_NULL;
-  if (p->dtype < PA_KV_F16 || p->dtype > PA_KV_FP4_E2M1_OUTL) return PA_ERR_DTYPE;
+  if (p->dtype < PA_KV_F16 || p->dtype > PA_KV_FP8_E5M2_TOKEN) return PA_ERR_DTYPE;
   if (p->block_size != PA_BLOCK_SIZE) return PA_ERR_BLOCK_SIZE;
   if (p->num_blocks < 1 || p->num_kv_heads < 1 || p->num_kv_heads > kMaxGridYZ)
     return PA_ERR_SHAPE;
@@ -24,7 +24,7 @@ int check_pool(const pa_kv_pool* p) {
   if ((int64_t)p->num_blocks * PA_BLOCK_SIZE > INT64_C(0x3FFFFFFFFFFFFFFF)) return PA_ERR_SHAPE;
   if (!p->k || !p->v) return PA_ERR_NULL;
   if (!aligned(p->k, 16) || !aligned(p->v, 16)) return PA_ERR_ALIGN;
-  if (p->dtype == PA_KV_FP8_E4M3) {
+  if (p->dtype == PA_KV_FP8_E4M3 || p->dtype == PA_KV_FP8_E5M2) {
     if (!p->k_scale || !p->v_scale) return PA_ERR_NULL;
     if (!aligned(p->k_scale, 4) || !aligned(p->v_scale, 4)) return PA_ERR_ALIGN;
   }
@@ -87,7 +87,7 @@ int pa_outlier_capacity(int32_t head_dim) {
 int pa_pool_layout(int32_t dtype, int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
                    size_t bytes_out[4]) {
   if (!bytes_out) return PA_ERR_NULL;
-  if (dtype < PA_KV_F16 || dtype > PA_KV_FP4_E2M1_OUTL) return PA_ERR_DTYPE;
+  if (dtype < PA_KV_F16 || dtype > PA_KV_FP8_E5M2_TOKEN) return PA_ERR_DTYPE;
   if (num_blocks < 1 || num_kv_heads < 1 || (head_dim != 64 && head_dim != 128))
     return PA_ERR_SHAPE;
   if (dtype == PA_KV_FP4_E2M1_OUTL && head_dim != 128) return PA_ERR_SHAPE;
@@ -97,7 +97,12 @@ int pa_pool_layout(int32_t dtype, int32_t num_blocks, int32_t num_kv_heads, int3
   switch (dtype) {
     case PA_KV_F16:
     case PA_KV_BF16: bytes_out[0] = bytes_out[1] = rows * head_dim * 2; break;
-    case PA_KV_FP8_E4M3: bytes_out[0] = bytes_out[1] = rows * head_dim; break;
+    case PA_KV_FP8_E4M3:
+    case PA_KV_FP8_E5M2: bytes_out[0] = bytes_out[1] = rows * head_dim; break;
+    case PA_KV_FP8_E4M3_TOKEN:
+    case PA_KV_FP8_E5M2_TOKEN:
+      bytes_out[0] = bytes_out[1] = bh * (size_t)PA_FP8T_TILE_BYTES(head_dim);
+      break;
     default:
       bytes_out[0] = bytes_out[1] = bh * (size_t)PA_FP4_TILE_BYTES(head_dim);
       bytes_out[2] = bytes_out[3] = bh * (size_t)(pa::outlier_capacity(head_dim) - 1) *
@@ -122,16 +127,17 @@ int pa_cache_write(const pa_kv_pool* pool, const void* k_new, const void* v_new,
                           dev_err, (hipStream_t)stream);
 }
 
-int pa_fp8_head_scales(const void* x, int32_t act, int64_t num_rows, int32_t num_kv_heads,
-                       int32_t head_dim, float* scale_out, void* stream) {
+int pa_fp8_head_scales(const void* x, int32_t act, int32_t kv_dtype, int64_t num_rows,
+                       int32_t num_kv_heads, int32_t head_dim, float* scale_out, void* stream) {
   if (!act_ok(act)) return PA_ERR_DTYPE;
+  if (kv_dtype != PA_KV_FP8_E4M3 && kv_dtype != PA_KV_FP8_E5M2) return PA_ERR_DTYPE;
   if (num_rows < 0 || num_kv_heads < 1 || num_kv_heads > 256 ||
       (head_dim != 64 && head_dim != 128))
     return PA_ERR_SHAPE;
   if (!scale_out || (num_rows > 0 && !x)) return PA_ERR_NULL;
   if (!aligned(x, 16) || !aligned(scale_out, 4)) return PA_ERR_ALIGN;
-  return pa::launch_fp8_scales(x, act == PA_ACT_BF16, num_rows, num_kv_heads, head_dim, scale_out,
-                               (hipStream_t)stream);
+  return pa::launch_fp8_scales(x, act == PA_ACT_BF16, kv_dtype == PA_KV_FP8_E5M2, num_rows,
+                               num_kv_heads, head_dim, scale_out, (hipStream_t)stream);
 }
 
 int pa_reset_blocks(const pa_kv_pool* pool, const int32_t* block_ids, int32_t n, void* stream) {

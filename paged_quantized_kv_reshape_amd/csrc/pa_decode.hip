@@ -41,7 +41,13 @@
 
 namespace pa {
 
-enum { KV_F16 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_FP4 = 3 };
+// pool formats (the pa_kv_dtype values)
+enum { KV_F16 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_FP4 = 3, KV_BF8 = 4, KV_FP8T = 5, KV_BF8T = 6 };
+constexpr bool is_f8(int kv) { return kv == KV_FP8 || kv == KV_BF8 || kv == KV_FP8T || kv == KV_BF8T; }
+constexpr bool f8_e5(int kv) { return kv == KV_BF8 || kv == KV_BF8T; }        // E5M2 codes
+constexpr bool f8_tok(int kv) { return kv == KV_FP8T || kv == KV_BF8T; }      // per-token scales
+constexpr bool head_scaled(int kv) { return kv == KV_FP8 || kv == KV_BF8; }  // per-head scales
+constexpr bool tok_scaled(int kv) { return kv == KV_FP4 || f8_tok(kv); }
 
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
 
@@ -50,11 +56,13 @@ struct Geo {
   static constexpr int KS = D / 32;  // QK MFMA steps (k = 32 channels each)
   static constexpr int NT = D / 16;  // PV MFMA tiles (16 output channels each)
   static constexpr int DL = D / 4;   // channels per lane in K fragments and outputs
-  static constexpr int EBITS = KV == KV_FP8 ? 8 : KV == KV_FP4 ? 4 : 16;
+  static constexpr int EBITS = is_f8(KV) ? 8 : KV == KV_FP4 ? 4 : 16;
   static constexpr int ROWB = D * EBITS / 8;       // bytes of one token row
   // bytes between consecutive (block, head) tiles; an FP4 tile also holds its per-token
   // scales, its outlier record and its first outlier slot after the codes
-  static constexpr int TILEB = KV == KV_FP4 ? PA_FP4_TILE_BYTES(D) : kBlock * ROWB;
+  static constexpr int TILEB = KV == KV_FP4   ? PA_FP4_TILE_BYTES(D)
+                               : f8_tok(KV) ? PA_FP8T_TILE_BYTES(D)
+                                            : kBlock * ROWB;
   static constexpr int KW = DL * EBITS / 32;       // K words per lane
   static constexpr int VW = NT * EBITS / 32;       // V words per lane per token
   static constexpr int KLANEB = DL * EBITS / 8;    // K bytes per lane
@@ -94,12 +102,18 @@ __device__ __forceinline__ void load_words(uint32_t (&w)[N], const uint8_t* p) {
 
 // Hardware conversions (scale 1.0, so exact: every E4M3 and E2M1 value is a bf16 and an
 // fp16 value). SEL picks the 16-bit half (FP8) or the byte (FP4) of the source word.
-template <bool BF, int SEL>
+template <bool BF, int SEL, bool E5 = false>
 __device__ __forceinline__ uint32_t cvt_fp8x2(uint32_t w) {
-  if constexpr (BF)
+  if constexpr (E5) {  // E5M2 ("bf8")
+    if constexpr (BF)
+      return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, SEL != 0));
+    else
+      return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, SEL != 0));
+  } else if constexpr (BF) {
     return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, SEL != 0));
-  else
+  } else {
     return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, SEL != 0));
+  }
 }
 template <bool BF, int SEL>
 __device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t w) {
@@ -128,10 +142,11 @@ template <int KV, int D, bool QBF>
 __device__ __forceinline__ uint4 k_fragment(const Tile<KV, D>& T, int t) {
   if constexpr (KV == KV_F16 || KV == KV_BF16) {
     return make_uint4(T.k[4 * t], T.k[4 * t + 1], T.k[4 * t + 2], T.k[4 * t + 3]);
-  } else if constexpr (KV == KV_FP8) {
+  } else if constexpr (is_f8(KV)) {
+    constexpr bool E5 = f8_e5(KV);
     const uint32_t a = T.k[2 * t], b = T.k[2 * t + 1];
-    return make_uint4(cvt_fp8x2<QBF, 0>(a), cvt_fp8x2<QBF, 1>(a), cvt_fp8x2<QBF, 0>(b),
-                      cvt_fp8x2<QBF, 1>(b));
+    return make_uint4(cvt_fp8x2<QBF, 0, E5>(a), cvt_fp8x2<QBF, 1, E5>(a),
+                      cvt_fp8x2<QBF, 0, E5>(b), cvt_fp8x2<QBF, 1, E5>(b));
   } else {
     const uint32_t a = T.k[t];
     return make_uint4(cvt_fp4x2<QBF, 0>(a), cvt_fp4x2<QBF, 1>(a), cvt_fp4x2<QBF, 2>(a),
@@ -186,8 +201,8 @@ __device__ __forceinline__ void v_fragments(const Tile<KV, D>& T, uint2 (&vf)[Ge
           __builtin_amdgcn_perm(w1, u1, 0x07060302u)}; // channel 3
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        vf[4 * wi + c].x = cvt_fp8x2<PVB, 0>(t[c]);
-        vf[4 * wi + c].y = cvt_fp8x2<PVB, 1>(t[c]);
+        vf[4 * wi + c].x = cvt_fp8x2<PVB, 0, f8_e5(KV)>(t[c]);
+        vf[4 * wi + c].y = cvt_fp8x2<PVB, 1, f8_e5(KV)>(t[c]);
       }
     }
   }
@@ -341,7 +356,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 
   // ---- scale of the logits (base 2) ----
   float cz = a.sm_scale_log2;
-  if constexpr (KV == KV_FP8) cz *= a.k_scale[kvh];
+  if constexpr (head_scaled(KV)) cz *= a.k_scale[kvh];
 
   // ---- block ids ----
   // Single buffer: 64 of this wave's block ids per register, one register ahead, read
@@ -409,6 +424,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         load_words(T.v[r], vpool + T.tile * G_::TILEB + v_lane_off + r * G_::ROWB);
+    }
+    if constexpr (f8_tok(KV)) {  // per-token scales of tokens 4 kg .. 4 kg + 3
+      T.sk = reinterpret_cast<const float4*>(kpool + T.tile * G_::TILEB + PA_FP8T_SCALE_OFF(D))[kg];
+      T.sv = reinterpret_cast<const float4*>(vpool + T.tile * G_::TILEB + PA_FP8T_SCALE_OFF(D))[kg];
     }
     if constexpr (KV == KV_FP4) {
       const uint8_t* kt = kpool + T.tile * G_::TILEB;
@@ -512,6 +531,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         z[r] = valid[r] ? __builtin_fmaf(sacc[r], sk[r], ok[r]) * cz : -INFINITY;
+    } else if constexpr (f8_tok(KV)) {
+      const float sk[4] = {T.sk.x, T.sk.y, T.sk.z, T.sk.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) z[r] = valid[r] ? sacc[r] * sk[r] * cz : -INFINITY;
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r) z[r] = valid[r] ? sacc[r] * cz : -INFINITY;
@@ -538,9 +561,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
       l += pr[r];
     }
 
-    // P^T operand: hi + lo 16-bit pairs (FP4: p * s_t, the V per-token scale)
+    // P^T operand: hi + lo 16-bit pairs (per-token formats: p * s_t, the V token scale)
     float pv[4];
-    if constexpr (KV == KV_FP4) {
+    if constexpr (tok_scaled(KV)) {
       const float sv[4] = {T.sv.x, T.sv.y, T.sv.z, T.sv.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) pv[r] = valid[r] ? pr[r] * sv[r] : 0.0f;
@@ -649,7 +672,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   if (err_bits != 0 && lane == 0 && a.err) atomicOr(a.err, err_bits);
   fold_side(false);
   const float lt = group4_sum(l);
-  const float vscale = KV == KV_FP8 ? a.v_scale[kvh] : 1.0f;
+  const float vscale = head_scaled(KV) ? a.v_scale[kvh] : 1.0f;
   const int h = kvh * G + c;
   if (W == 1 || MQ) {
     if (MQ ? jc < nq : c < G) {
@@ -788,6 +811,15 @@ int launch_prefill(const DecodeArgs& a, int kv, bool qbf, int D, hipStream_t st)
       case KV_FP8:
         return qbf ? launch_prefill_one<KV_FP8, 128, true>(a, st)
                    : launch_prefill_one<KV_FP8, 128, false>(a, st);
+      case KV_BF8:
+        return qbf ? launch_prefill_one<KV_BF8, 128, true>(a, st)
+                   : launch_prefill_one<KV_BF8, 128, false>(a, st);
+      case KV_FP8T:
+        return qbf ? launch_prefill_one<KV_FP8T, 128, true>(a, st)
+                   : launch_prefill_one<KV_FP8T, 128, false>(a, st);
+      case KV_BF8T:
+        return qbf ? launch_prefill_one<KV_BF8T, 128, true>(a, st)
+                   : launch_prefill_one<KV_BF8T, 128, false>(a, st);
       case KV_FP4:
         return qbf ? launch_prefill_one<KV_FP4, 128, true>(a, st)
                    : launch_prefill_one<KV_FP4, 128, false>(a, st);
@@ -799,6 +831,15 @@ int launch_prefill(const DecodeArgs& a, int kv, bool qbf, int D, hipStream_t st)
       case KV_FP8:
         return qbf ? launch_prefill_one<KV_FP8, 64, true>(a, st)
                    : launch_prefill_one<KV_FP8, 64, false>(a, st);
+      case KV_BF8:
+        return qbf ? launch_prefill_one<KV_BF8, 64, true>(a, st)
+                   : launch_prefill_one<KV_BF8, 64, false>(a, st);
+      case KV_FP8T:
+        return qbf ? launch_prefill_one<KV_FP8T, 64, true>(a, st)
+                   : launch_prefill_one<KV_FP8T, 64, false>(a, st);
+      case KV_BF8T:
+        return qbf ? launch_prefill_one<KV_BF8T, 64, true>(a, st)
+                   : launch_prefill_one<KV_BF8T, 64, false>(a, st);
     }
   }
   return PA_ERR_DTYPE;
@@ -812,6 +853,15 @@ int launch_decode(const DecodeArgs& a, int kv, bool qbf, int D, int waves, hipSt
       case KV_FP8:
         return qbf ? launch_one<KV_FP8, 128, true>(a, waves, st)
                    : launch_one<KV_FP8, 128, false>(a, waves, st);
+      case KV_BF8:
+        return qbf ? launch_one<KV_BF8, 128, true>(a, waves, st)
+                   : launch_one<KV_BF8, 128, false>(a, waves, st);
+      case KV_FP8T:
+        return qbf ? launch_one<KV_FP8T, 128, true>(a, waves, st)
+                   : launch_one<KV_FP8T, 128, false>(a, waves, st);
+      case KV_BF8T:
+        return qbf ? launch_one<KV_BF8T, 128, true>(a, waves, st)
+                   : launch_one<KV_BF8T, 128, false>(a, waves, st);
       case KV_FP4:
         if (a.group <= 8)
           return qbf ? launch_one<KV_FP4, 128, true, 8>(a, waves, st)
@@ -826,6 +876,15 @@ int launch_decode(const DecodeArgs& a, int kv, bool qbf, int D, int waves, hipSt
       case KV_FP8:
         return qbf ? launch_one<KV_FP8, 64, true>(a, waves, st)
                    : launch_one<KV_FP8, 64, false>(a, waves, st);
+      case KV_BF8:
+        return qbf ? launch_one<KV_BF8, 64, true>(a, waves, st)
+                   : launch_one<KV_BF8, 64, false>(a, waves, st);
+      case KV_FP8T:
+        return qbf ? launch_one<KV_FP8T, 64, true>(a, waves, st)
+                   : launch_one<KV_FP8T, 64, false>(a, waves, st);
+      case KV_BF8T:
+        return qbf ? launch_one<KV_BF8T, 64, true>(a, waves, st)
+                   : launch_one<KV_BF8T, 64, false>(a, waves, st);
     }
   }
   return PA_ERR_DTYPE;

@@ -79,6 +79,28 @@ __device__ __forceinline__ uint32_t encode_e4m3(float v) {
   return sign | code;
 }
 
+// fp32 -> E5M2 byte (OCP: bias 15, two mantissa bits, largest finite 57344): nearest, ties
+// to even, saturating to +-57344, sign of zero kept, NaN -> S.11111.11.
+__device__ __forceinline__ uint32_t encode_e5m2(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  if (__builtin_isnan(v)) return sign | 0x7Fu;
+  const float a = fminf(__builtin_fabsf(v), 57344.0f);
+  uint32_t code;
+  if (a < 0x1p-14f) {
+    // subnormal range: value = m * 2^-16, m = a * 65536 rounded to nearest even (0..4;
+    // 4 is the smallest normal, code 0x04). Scaling by 65536 is exact.
+    code = (uint32_t)__builtin_rintf(a * 65536.0f);
+  } else {
+    // normal: round the 23-bit fp32 mantissa to 2 bits (nearest, ties even); a carry
+    // moves into the exponent, which is rebiased from 127 to 15.
+    uint32_t b = __float_as_uint(a);
+    b += 0xFFFFFu + ((b >> 21) & 1u);
+    code = (b >> 21) - (112u << 2);
+  }
+  return sign | code;
+}
+
 // fp32 -> E2M1 nibble. Thresholds are the midpoints of the grid 0 .5 1 1.5 2 3 4 6; at an
 // exact midpoint the comparison (> or >=) sends the value to the even code.
 __device__ __forceinline__ uint32_t encode_e2m1(float v) {

@@ -16,7 +16,7 @@ inline int outlier_capacity(int head_dim) {
 
 int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool bf16, int32_t T,
                  const int64_t* slots, int32_t* err, hipStream_t st);
-int launch_fp8_scales(const void* x, bool bf16, int64_t rows, int32_t hkv, int32_t D,
+int launch_fp8_scales(const void* x, bool bf16, bool e5m2, int64_t rows, int32_t hkv, int32_t D,
                       float* scale_out, hipStream_t st);
 int launch_reset(const pa_kv_pool& p, const int32_t* ids, int32_t n, hipStream_t st);
 

@@ -62,8 +62,8 @@ __global__ __launch_bounds__(256) void k_write_copy(const uint4* __restrict__ k_
   v_pool[dst] = v_new[src];
 }
 
-// FP8 E4M3, 16 values per thread: code = E4M3(fp32(x / s_h)), with the fp32 quotient
-// correctly rounded.
+// FP8 (E4M3 or E5M2), 16 values per thread: code = FP8(fp32(x / s)), with the fp32 quotient
+// correctly rounded; s is the kv head's scale, or the row's own (per-token pools).
 //
 // The quotient x / |s| comes from y = fp32(1 / |s|) (correctly rounded, once per thread)
 // and two correction steps: q <- q - (|s| q - x) y, each remainder |s| q - x formed by one
@@ -72,15 +72,17 @@ __global__ __launch_bounds__(256) void k_write_copy(const uint4* __restrict__ k_
 // ulp, and from there one step with a correctly rounded reciprocal gives the correctly
 // rounded quotient (Markstein's theorem on fma-based division), so the fast form is
 // exact, not a guess with a fallback. It needs no overflow and no underflow of the
-// remainder where the code is decided: x is first clamped to +-fp32(440 |s|) (any
-// |x / s| > 440 saturates to the code of 448 either way, and the clamped quotient stays
-// inside the E4M3 range), and 2^-80 <= |s| <= 2^100 keeps every remainder of a quotient
+// remainder where the code is decided: x is first clamped to +-fp32(B |s|), B = 440
+// (E4M3) or 56000 (E5M2), past the last rounding midpoint below the largest value (432,
+// 53248), so any larger |x / s| saturates either way and the clamped quotient stays inside
+// the format's range, and 2^-80 <= |s| <= 2^100 keeps every remainder of a quotient
 // above 2^-20 exact (smaller quotients encode as a signed zero, and the steps keep the
 // quotient's sign, that of zero included, as y > 0). Other scales, and NaN inputs, take
 // the IEEE division and the software encoder.
 //
-// gfx950's fp32 -> E4M3 conversion (v_cvt_pk_fp8_f32: nearest, ties to even) gives the
-// same byte as the software encoder for every non-NaN fp32 input in [-448, 448].
+// gfx950's fp32 -> FP8 conversions (v_cvt_pk_fp8_f32 for E4M3, v_cvt_pk_bf8_f32 for E5M2:
+// nearest, ties to even) give the same byte as the software encoders for every non-NaN
+// fp32 input inside the format's range.
 template <bool BF16>
 __device__ __forceinline__ uint32_t act_nan_pair(uint32_t u) {
   // nonzero when a 16-bit half is a NaN: |bits| above the infinity pattern (0x7F80 bf16,
@@ -88,10 +90,10 @@ __device__ __forceinline__ uint32_t act_nan_pair(uint32_t u) {
   return ((u & 0x7FFF7FFFu) + (BF16 ? 0x007F007Fu : 0x03FF03FFu)) & 0x80008000u;
 }
 
-template <bool BF16>
+template <bool BF16, bool E5>
 __device__ __forceinline__ uint4 fp8_encode16(const uint4 lo, const uint4 hi, float s, bool fast) {
   const float sa = __builtin_fabsf(s);
-  const float y = 1.0f / sa, bound = 440.0f * sa;
+  const float y = 1.0f / sa, bound = (E5 ? 56000.0f : 440.0f) * sa;
   const uint32_t flip = s < 0.0f ? 0x80808080u : 0u;
   const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   float x[16], q[16];
@@ -112,23 +114,32 @@ __device__ __forceinline__ uint4 fp8_encode16(const uint4 lo, const uint4 hi, fl
   uint32_t out[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    out[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[4 * i], q[4 * i + 1], 0, false);
-    out[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[4 * i + 2], q[4 * i + 3], (int)out[i],
-                                                       true) ^ flip;
+    if constexpr (E5) {
+      out[i] = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(q[4 * i], q[4 * i + 1], 0, false);
+      out[i] = (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(q[4 * i + 2], q[4 * i + 3],
+                                                         (int)out[i], true) ^ flip;
+    } else {
+      out[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[4 * i], q[4 * i + 1], 0, false);
+      out[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[4 * i + 2], q[4 * i + 3],
+                                                         (int)out[i], true) ^ flip;
+    }
   }
   if (!fast || nan != 0u) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       out[i] = 0u;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) out[i] |= encode_e4m3(x[4 * i + j] / s) << (8 * j);
+      for (int j = 0; j < 4; ++j) {
+        const float t = x[4 * i + j] / s;
+        out[i] |= (E5 ? encode_e5m2(t) : encode_e4m3(t)) << (8 * j);
+      }
     }
   }
   if (s == 0.0f) out[0] = out[1] = out[2] = out[3] = 0u;  // a zero scale stores zero codes
   return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
-template <bool BF16, int CH>
+template <bool BF16, int CH, bool E5>
 __global__ __launch_bounds__(256) void k_write_fp8(const uint4* __restrict__ k_new,
                                                    const uint4* __restrict__ v_new,
                                                    uint4* __restrict__ k_pool,
@@ -146,8 +157,66 @@ __global__ __launch_bounds__(256) void k_write_fp8(const uint4* __restrict__ k_n
   const bool fv = __builtin_fabsf(sv) >= 0x1p-80f && __builtin_fabsf(sv) <= 0x1p100f;
   const uint4 k0 = k_new[2 * src], k1 = k_new[2 * src + 1];
   const uint4 v0 = v_new[2 * src], v1 = v_new[2 * src + 1];
-  k_pool[dst] = fp8_encode16<BF16>(k0, k1, sk, fk);
-  v_pool[dst] = fp8_encode16<BF16>(v0, v1, sv, fv);
+  k_pool[dst] = fp8_encode16<BF16, E5>(k0, k1, sk, fk);
+  v_pool[dst] = fp8_encode16<BF16, E5>(v0, v1, sv, fv);
+}
+
+// Per-token-scaled FP8: the row's scale is fp32(max |x| / M) (M = 448 or 57344), computed
+// here by the row's CH threads (consecutive lanes of one wave: CH divides 64 and every row
+// starts on a multiple of CH), then the codes as above; the run holds the 16 code rows and
+// then the 16 scales.
+template <bool BF16, int CH, bool E5>
+__global__ __launch_bounds__(256) void k_write_fp8_tok(const uint4* __restrict__ k_new,
+                                                       const uint4* __restrict__ v_new,
+                                                       uint8_t* __restrict__ k_pool,
+                                                       uint8_t* __restrict__ v_pool,
+                                                       const int64_t* __restrict__ slots,
+                                                       int32_t T, int32_t hkv, int64_t nslots,
+                                                       int32_t* err) {
+  constexpr int D = CH * 16;
+  constexpr int64_t TB = PA_FP8T_TILE_BYTES(D);
+  constexpr float FMAX = E5 ? 57344.0f : 448.0f;
+  const uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t per_tok = (uint32_t)hkv * CH;
+  const uint32_t i = idx / per_tok;
+  const uint32_t rem = idx - i * per_tok;
+  const int c = (int)(rem & (CH - 1));
+  const int h = (int)(rem / CH);
+  if (i >= (uint32_t)T) return;  // (a whole row's lanes leave together)
+  const int64_t slot = slots[i];
+  if (slot < 0) return;
+  if (slot >= nslots) {
+    if (c == 0) flag(err, PA_DEVERR_BAD_SLOT);
+    return;
+  }
+  const int64_t src = ((int64_t)i * hkv + h) * CH + c;
+  const uint4 k0 = k_new[2 * src], k1 = k_new[2 * src + 1];
+  const uint4 v0 = v_new[2 * src], v1 = v_new[2 * src + 1];
+  auto absmax16 = [](const uint4 a, const uint4 b) {
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      m = fmaxf(m, __builtin_fabsf(act_to_f32<BF16>((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu)));
+    return m;
+  };
+  float mk = absmax16(k0, k1), mv = absmax16(v0, v1);
+#pragma unroll
+  for (int o = CH / 2; o >= 1; o >>= 1) {
+    mk = fmaxf(mk, __shfl_xor(mk, o));
+    mv = fmaxf(mv, __shfl_xor(mv, o));
+  }
+  const float sk = mk / FMAX, sv = mv / FMAX;
+  const bool fk = sk >= 0x1p-80f && sk <= 0x1p100f;
+  const bool fv = sv >= 0x1p-80f && sv <= 0x1p100f;
+  const int64_t run = ((slot >> 4) * hkv + h) * TB;
+  const int off = (int)(slot & 15);
+  *reinterpret_cast<uint4*>(k_pool + run + off * D + 16 * c) = fp8_encode16<BF16, E5>(k0, k1, sk, fk);
+  *reinterpret_cast<uint4*>(v_pool + run + off * D + 16 * c) = fp8_encode16<BF16, E5>(v0, v1, sv, fv);
+  if (c == 0) {
+    reinterpret_cast<float*>(k_pool + run + PA_FP8T_SCALE_OFF(D))[off] = sk;
+    reinterpret_cast<float*>(v_pool + run + PA_FP8T_SCALE_OFF(D))[off] = sv;
+  }
 }
 
 // ---------------------------------------------------------------------------------
@@ -457,11 +526,11 @@ __global__ __launch_bounds__(256) void k_absmax(const uint4* __restrict__ x, int
   if ((threadIdx.x & 63) == 0) atomicMax(bits + h, __float_as_uint(m));
 }
 
-__global__ void k_scale_finish(uint32_t* bits, int32_t hkv) {
+__global__ void k_scale_finish(uint32_t* bits, int32_t hkv, float fmax) {
   const int t = threadIdx.x;
   if (t < hkv) {
     const float a = __uint_as_float(bits[t]);
-    reinterpret_cast<float*>(bits)[t] = a / 448.0f;
+    reinterpret_cast<float*>(bits)[t] = a / fmax;
   }
 }
 
@@ -490,8 +559,10 @@ int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool
   const int64_t nslots = (int64_t)p.num_blocks * kBlock;
   const int D = p.head_dim, hkv = p.num_kv_heads;
   if (T == 0) return PA_OK;
-  if (p.dtype == PA_KV_F16 || p.dtype == PA_KV_BF16 || p.dtype == PA_KV_FP8_E4M3) {
-    const bool fp8 = p.dtype == PA_KV_FP8_E4M3;
+  if (p.dtype != PA_KV_FP4_E2M1_OUTL) {
+    const bool fp8 = p.dtype != PA_KV_F16 && p.dtype != PA_KV_BF16;
+    const bool e5 = p.dtype == PA_KV_FP8_E5M2 || p.dtype == PA_KV_FP8_E5M2_TOKEN;
+    const bool tok = p.dtype == PA_KV_FP8_E4M3_TOKEN || p.dtype == PA_KV_FP8_E5M2_TOKEN;
     // threads per (token, head) row: 16-byte chunks of the copy, 16 values for FP8
     const int ch = fp8 ? D / 16 : D * 2 / 16;
     const int64_t per_tok = (int64_t)hkv * ch;
@@ -506,11 +577,26 @@ int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool
         auto kern = D == 128 ? k_write_copy<16> : k_write_copy<8>;
         hipLaunchKernelGGL(kern, g, dim3(256), 0, st, kn, vn, (uint4*)p.k, (uint4*)p.v,
                            slots + t0, n, hkv, nslots, err);
+      } else if (tok) {
+        // kernel table: [bf16][D == 128][e5]
+        void (*const tab[2][2][2])(const uint4*, const uint4*, uint8_t*, uint8_t*,
+                                   const int64_t*, int32_t, int32_t, int64_t, int32_t*) = {
+            {{k_write_fp8_tok<false, 4, false>, k_write_fp8_tok<false, 4, true>},
+             {k_write_fp8_tok<false, 8, false>, k_write_fp8_tok<false, 8, true>}},
+            {{k_write_fp8_tok<true, 4, false>, k_write_fp8_tok<true, 4, true>},
+             {k_write_fp8_tok<true, 8, false>, k_write_fp8_tok<true, 8, true>}}};
+        hipLaunchKernelGGL(tab[bf16][D == 128][e5], g, dim3(256), 0, st, kn, vn,
+                           (uint8_t*)p.k, (uint8_t*)p.v, slots + t0, n, hkv, nslots, err);
       } else {
-        auto kern = bf16 ? (D == 128 ? k_write_fp8<true, 8> : k_write_fp8<true, 4>)
-                         : (D == 128 ? k_write_fp8<false, 8> : k_write_fp8<false, 4>);
-        hipLaunchKernelGGL(kern, g, dim3(256), 0, st, kn, vn, (uint4*)p.k, (uint4*)p.v,
-                           p.k_scale, p.v_scale, slots + t0, n, hkv, nslots, err);
+        void (*const tab[2][2][2])(const uint4*, const uint4*, uint4*, uint4*, const float*,
+                                   const float*, const int64_t*, int32_t, int32_t, int64_t,
+                                   int32_t*) = {
+            {{k_write_fp8<false, 4, false>, k_write_fp8<false, 4, true>},
+             {k_write_fp8<false, 8, false>, k_write_fp8<false, 8, true>}},
+            {{k_write_fp8<true, 4, false>, k_write_fp8<true, 4, true>},
+             {k_write_fp8<true, 8, false>, k_write_fp8<true, 8, true>}}};
+        hipLaunchKernelGGL(tab[bf16][D == 128][e5], g, dim3(256), 0, st, kn, vn, (uint4*)p.k,
+                           (uint4*)p.v, p.k_scale, p.v_scale, slots + t0, n, hkv, nslots, err);
       }
     }
   } else {
@@ -537,7 +623,7 @@ int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
-int launch_fp8_scales(const void* x, bool bf16, int64_t rows, int32_t hkv, int32_t D,
+int launch_fp8_scales(const void* x, bool bf16, bool e5m2, int64_t rows, int32_t hkv, int32_t D,
                       float* scale_out, hipStream_t st) {
   uint32_t* bits = reinterpret_cast<uint32_t*>(scale_out);
   hipLaunchKernelGGL(k_scale_init, dim3(1), dim3(256), 0, st, bits, hkv);
@@ -550,7 +636,8 @@ int launch_fp8_scales(const void* x, bool bf16, int64_t rows, int32_t hkv, int32
     hipLaunchKernelGGL(kern, dim3(gx, hkv), dim3(256), 0, st, (const uint4*)x, rows, hkv, chunks,
                        bits);
   }
-  hipLaunchKernelGGL(k_scale_finish, dim3(1), dim3(256), 0, st, bits, hkv);
+  hipLaunchKernelGGL(k_scale_finish, dim3(1), dim3(256), 0, st, bits, hkv,
+                     e5m2 ? 57344.0f : 448.0f);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -31,11 +31,11 @@ class DeviceRun:
         self.context_lens = torch.from_numpy(w.context_lens.astype(np.int32)).to(device)
         self.dev_err = torch.zeros(1, dtype=torch.int32, device=device)
         self.k_scale = self.v_scale = None
-        if w.kv == "fp8":
+        if w.kv in B.HEAD_SCALED:
             self.k_scale = torch.empty(w.num_kv_heads, dtype=torch.float32, device=device)
             self.v_scale = torch.empty(w.num_kv_heads, dtype=torch.float32, device=device)
-            B.pa_fp8_head_scales(self.k_rows, self.k_scale)
-            B.pa_fp8_head_scales(self.v_rows, self.v_scale)
+            B.pa_fp8_head_scales(self.k_rows, self.k_scale, w.kv)
+            B.pa_fp8_head_scales(self.v_rows, self.v_scale, w.kv)
         self.pools = [B.KVPool(w.kv, w.num_blocks, w.num_kv_heads, w.head_dim, device=device,
                                fill=fill, k_scale=self.k_scale, v_scale=self.v_scale)
                       for _ in range(pool_copies)]
@@ -98,7 +98,7 @@ class DeviceRun:
 # ---------------------------------------------------------------------------------
 # Algorithmic bytes: what the method itself must move, not what a kernel happens to fetch.
 # ---------------------------------------------------------------------------------
-_KV_ELEM_BITS = {"f16": 16, "bf16": 16, "fp8": 8, "fp4": 4}
+_KV_ELEM_BITS = {"f16": 16, "bf16": 16, "fp8": 8, "fp4": 4, "bf8": 8, "fp8t": 8, "bf8t": 8}
 
 
 def outlier_counts(run) -> dict:
@@ -127,8 +127,10 @@ def decode_bytes(w, outliers=None) -> dict:
         extra += 2 * blocks * hkv * 16        # outlier records
         if outliers is not None:              # fp16 values of every outlier channel
             extra += (outliers["k"] + outliers["v"]) * 16 * 2
-    if w.kv == "fp8":
+    if w.kv in ("fp8", "bf8"):
         extra += 2 * hkv * 4                  # per-head scales
+    if w.kv in ("fp8t", "bf8t"):
+        extra += 2 * tok * hkv * 4            # per-token fp32 scales, K and V
     meta = blocks * 4 + S * 4
     io = S * hq * d * 2 + S * hq * d * 4
     return {"kv": kv + extra, "meta": meta, "io": io, "total": kv + extra + meta + io,
@@ -141,6 +143,6 @@ def write_bytes(w, num_tokens: int) -> int:
     hkv, d = w.num_kv_heads, w.head_dim
     rd = num_tokens * (2 * hkv * d * 2 + 8)
     wr = 2 * num_tokens * hkv * d * _KV_ELEM_BITS[w.kv] // 8
-    if w.kv == "fp4":
+    if w.kv in ("fp4", "fp8t", "bf8t"):
         wr += 2 * num_tokens * hkv * 4
     return rd + wr

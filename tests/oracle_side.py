@@ -18,9 +18,10 @@ def replay(w, only_blocks=None):
     """Oracle pool after every write call of the workload (setup, then step)."""
     pool = C.Pool.filled(w.kv, w.num_blocks, w.num_kv_heads, w.head_dim)
     ks = vs = None
-    if w.kv == "fp8":
-        ks = C.fp8_head_scale(w.k_rows, w.act)
-        vs = C.fp8_head_scale(w.v_rows, w.act)
+    if w.kv in ("fp8", "bf8"):
+        fmt = C.FP8_KINDS[w.kv][0]
+        ks = C.fp8_head_scale(w.k_rows, w.act, fmt)
+        vs = C.fp8_head_scale(w.v_rows, w.act, fmt)
     log = []
     keep = None if only_blocks is None else np.asarray(sorted(only_blocks))
     for call in list(w.setup_calls) + [w.step_call]:

@@ -45,6 +45,10 @@ def test_status_strings():
     # FP4: per (block, head) 1024 code bytes + 64 scale bytes + 16 record bytes + 32 bytes of
     # the first outlier, padded to 1152; then 10 more outlier slots of 16 fp16 values
     ("fp4", 128, [10 * 3 * 1152] * 2 + [10 * 3 * 10 * 16 * 2] * 2),
+    ("bf8", 128, [10 * 3 * 16 * 128] * 2 + [0] * 2),
+    # per-token FP8: 16 x D code bytes + 16 fp32 scales per (block, head), padded to 128
+    ("fp8t", 128, [10 * 3 * 2176] * 2 + [0] * 2),
+    ("bf8t", 64, [10 * 3 * 1152] * 2 + [0] * 2),
 ])
 def test_pool_layout_sizes(kv, d, expect):
     assert B.pa_pool_layout(kv, 10, 3, d) == expect
@@ -54,6 +58,7 @@ def test_pool_layout_rejects():
     lib = B.lib()
     out = (ctypes.c_size_t * 4)()
     assert lib.pa_pool_layout(9, 10, 1, 128, out) == DTYPE
+    assert lib.pa_pool_layout(7, 10, 1, 128, out) == DTYPE
     assert lib.pa_pool_layout(0, 0, 1, 128, out) == SHAPE
     assert lib.pa_pool_layout(0, 10, 1, 96, out) == SHAPE
     assert lib.pa_pool_layout(3, 10, 1, 64, out) == SHAPE  # FP4 needs head_dim 128
@@ -141,10 +146,11 @@ def test_merge_and_scale_and_reset_reject():
     assert m(out=None) == NULL and m(po=None) == NULL
     assert m(po=FAKE + 4) == ALIGN
     assert m(S=0) == PA_OK
-    f = lambda **k: lib.pa_fp8_head_scales(k.get("x", FAKE), k.get("act", 1), k.get("rows", 5),
-                                           k.get("hkv", 1), k.get("d", 128), k.get("out", FAKE),
-                                           None)
+    f = lambda **k: lib.pa_fp8_head_scales(k.get("x", FAKE), k.get("act", 1), k.get("kv", 2),
+                                           k.get("rows", 5), k.get("hkv", 1), k.get("d", 128),
+                                           k.get("out", FAKE), None)
     assert f(act=2) == DTYPE and f(hkv=0) == SHAPE and f(d=32) == SHAPE and f(rows=-1) == SHAPE
+    assert f(kv=1) == DTYPE and f(kv=3) == DTYPE and f(kv=5) == DTYPE
     assert f(out=None) == NULL and f(x=None) == NULL and f(x=FAKE + 2) == ALIGN
     p = _pool(dtype=3)
     assert lib.pa_reset_blocks(ctypes.byref(p), None, 3, None) == NULL
