@@ -166,6 +166,24 @@ def cpu_baseline(w, budget_s: float, decode_b_per_token: float):
                        f"(+ partitions) of the sequences; bytes counted as for the GPU step")}
 
 
+def workload_of(args, config):
+    """The named workload, with its KV-cache format replaced when --kv is given (fp4 needs
+    head_dim 128; 16-bit pools store the activation dtype, so --kv f16 also makes the
+    activations fp16)."""
+    if args.kv is None:
+        return config(args.config)
+    over = dict(kv=args.kv)
+    if args.kv in ("f16", "bf16"):
+        over["act"] = args.kv
+    return config(args.config, **over)
+
+
+def profile_label(args) -> str:
+    """Workload label of the committed profiles: the config name, plus the KV format when
+    it was overridden."""
+    return args.config if args.kv is None else f"{args.config}_{args.kv}"
+
+
 def prefill_flops(w, qs) -> int:
     """Algorithmic flops of multi-token attention: query i of sequence s (position
     L - n + i) does 2 D flops per key for QK and 2 D for PV over L - n + i + 1 keys."""
@@ -191,7 +209,7 @@ def prefill_main(args, config, DESCRIPTIONS):
 
     print(f"[bench] generating {args.config} (prefill chunk {args.prefill})", file=sys.stderr,
           flush=True)
-    w = config(args.config)
+    w = workload_of(args, config)
     run = H.DeviceRun(w, device="cuda", partition_size=0, pool_copies=1)
     run.prepare()
     torch.cuda.synchronize()
@@ -231,7 +249,8 @@ def prefill_main(args, config, DESCRIPTIONS):
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(t * 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.act, "data": "synthetic",
-        "config": {"workload": f"{args.config}: {DESCRIPTIONS[args.config]}",
+        "config": {"workload": f"{args.config}: {DESCRIPTIONS[args.config]}"
+                               + (f" (KV cache as {w.kv})" if args.kv else ""),
                    "prefill_chunk": args.prefill, "queries": int(qs[-1]),
                    "kv_cache_dtype": w.kv, "num_seqs": w.num_seqs,
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
@@ -294,6 +313,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
+    ap.add_argument("--kv", default=None,
+                    choices=["f16", "bf16", "fp8", "bf8", "fp8t", "bf8t", "fp4"],
+                    help="override the workload's KV-cache format (same shapes and inputs)")
     ap.add_argument("--prefill", type=int, default=0, metavar="CHUNK",
                     help="time pa_prefill instead: the last CHUNK positions of every sequence "
                          "as queries (chunked prefill), reported in TFLOP/s")
@@ -321,7 +343,7 @@ def main():
         return
 
     print(f"[bench] generating {args.config}", file=sys.stderr, flush=True)
-    w = config(args.config)
+    w = workload_of(args, config)
     ps = w.partition_size if args.partition_size is None else args.partition_size
     w.partition_size = ps
     run = H.DeviceRun(w, device="cuda", partition_size=ps, pool_copies=args.copies)
@@ -406,7 +428,7 @@ def main():
     t_step = wall / K
     dec_gbs = dec["total"] / t_dec / 1e9
     value = step_bytes / t_step / 1e9
-    traffic = counter_traffic(decode_kernel_name(w.kv), args.config, ps)
+    traffic = counter_traffic(decode_kernel_name(w.kv), profile_label(args), ps)
 
     res = {
         "metric": METRIC,
@@ -421,7 +443,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.config}: {DESCRIPTIONS[args.config]}",
+        "config": {"workload": f"{args.config}: {DESCRIPTIONS[args.config]}"
+                               + (f" (KV cache as {w.kv})" if args.kv else ""),
                    "kv_cache_dtype": w.kv, "num_seqs": w.num_seqs,
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": 16, "kv_tokens": dec["tokens"],
