@@ -10,10 +10,11 @@ Modules:
   cache      - pool layout, cache-write replay (copy, FP8, FP4 + outlier calibration),
                dequantization and block-table gather
   attention  - exact softmax decode, partition split and log-sum-exp merge
+  blocks     - whole-block copies within a pool and between pools (copy on write, swap)
 
 Parity status: every function is pinned by a `-m "not gpu"` test against closed forms,
 format tables, library routines or brute force, except the FP4 calibration granularity
 (which tokens a block's outlier set is computed over), a reading of the pages that is
 checked only for self-consistency: parity unpinned for that choice.
 """
-from . import attention, cache, formats  # noqa: F401
+from . import attention, blocks, cache, formats  # noqa: F401
