@@ -184,6 +184,112 @@ def profile_label(args) -> str:
     return args.config if args.kv is None else f"{args.config}_{args.kv}"
 
 
+PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16 host link, per direction, published
+
+
+def blocks_main(args, config, DESCRIPTIONS):
+    """Whole-block copies on the workload's pool geometry: N block copies inside the pool
+    (HBM-bound: each block's bytes are read and written once), N blocks swapped out to a
+    pool in pinned host memory and back (bound by the host link), and torch's DMA copies of
+    one contiguous buffer of the same size as the attainable link rate."""
+    import numpy as np
+    import torch
+
+    from paged_quantized_kv_reshape_amd import KVPool, pa_copy_blocks, pa_pool_layout
+
+    w = workload_of(args, config)
+    nb, hkv, d, kv = w.num_blocks, w.num_kv_heads, w.head_dim, w.kv
+    N = args.blocks
+    if 2 * N > nb:
+        raise SystemExit(f"--blocks {N}: the pool has {nb} blocks, at most {nb // 2} copies")
+    per_block = sum(pa_pool_layout(kv, 1, hkv, d))
+    ones = torch.ones(hkv, dtype=torch.float32, device="cuda")
+    pool = KVPool(kv, nb, hkv, d, fill=0x5A, k_scale=ones, v_scale=ones)
+    host = KVPool(kv, N, hkv, d, device="cpu", fill=0)
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(nb).astype(np.int32)
+    cow = torch.from_numpy(np.stack([perm[:N], perm[N:2 * N]], 1).copy()).cuda()
+    out_p = torch.from_numpy(np.stack([perm[:N], np.arange(N, dtype=np.int32)], 1).copy()).cuda()
+    in_p = torch.from_numpy(np.stack([np.arange(N, dtype=np.int32), perm[N:2 * N]], 1).copy()).cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dev_buf = torch.empty(N * per_block, dtype=torch.uint8, device="cuda")
+    host_buf = torch.empty(N * per_block, dtype=torch.uint8, pin_memory=True)
+    stream = torch.cuda.current_stream().cuda_stream
+    timer = HipTimer()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = timer.event(), timer.event()
+        timer.record(a, stream)
+        for _ in range(args.steps):
+            fn()
+        timer.record(b, stream)
+        torch.cuda.synchronize()
+        return timer.ms(a, b) * 1e-3 / args.steps
+
+    print(f"[bench] {kv} pool of {nb} blocks ({per_block} B each), {N} blocks per call",
+          file=sys.stderr, flush=True)
+    t_cow = timed(lambda: pa_copy_blocks(pool, pool, cow, err))
+    t_out = timed(lambda: pa_copy_blocks(pool, host, out_p, err))
+    t_in = timed(lambda: pa_copy_blocks(host, pool, in_p, err))
+    t_d2h = timed(lambda: host_buf.copy_(dev_buf, non_blocking=True))
+    t_h2d = timed(lambda: dev_buf.copy_(host_buf, non_blocking=True))
+    dev_buf2 = torch.empty_like(dev_buf)
+    t_d2d = timed(lambda: dev_buf2.copy_(dev_buf))
+    one = cow[:1].contiguous()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(200):
+        pa_copy_blocks(pool, pool, one, err)
+    host_us = (time.perf_counter() - t0) / 200 * 1e6
+    torch.cuda.synchronize()
+    timer.close()
+    if int(err.item()):
+        raise SystemExit(f"device error {int(err.item())}")
+    moved = N * per_block
+    cow_gbs = 2 * moved / t_cow / 1e9
+    res = {
+        "metric": "whole-block copy (copy on write) and swap: achieved GB/s",
+        "value": round(cow_gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t_cow * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": f"{args.config}: {DESCRIPTIONS[args.config]}"
+                               + (f" (KV cache as {kv})" if args.kv else ""),
+                   "kv_cache_dtype": kv, "pool_blocks": nb, "bytes_per_block": per_block,
+                   "blocks_per_call": N},
+        "roofline": {"kernel": "k_copy_blocks", "bound": "hbm", "achieved": round(cow_gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(cow_gbs / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes": 2 * moved, "traffic": None},
+        "contiguous_d2d_copy_GBs": round(2 * moved / t_d2d / 1e9, 2),
+        "swap": {"out_GBs": round(moved / t_out / 1e9, 2), "in_GBs": round(moved / t_in / 1e9, 2),
+                 "out_ms": round(t_out * 1e3, 4), "in_ms": round(t_in * 1e3, 4),
+                 "dma_contiguous_d2h_GBs": round(moved / t_d2h / 1e9, 2),
+                 "dma_contiguous_h2d_GBs": round(moved / t_h2d / 1e9, 2),
+                 "link_peak_GBs": PCIE_PEAK_GBS,
+                 "out_frac_of_link": round(moved / t_out / 1e9 / PCIE_PEAK_GBS, 4),
+                 "in_frac_of_link": round(moved / t_in / 1e9 / PCIE_PEAK_GBS, 4)},
+        "host_us_per_call": round(host_us, 2),
+    }
+    if not args.no_cpu_baseline:
+        from oracle import blocks as OB
+        from oracle import cache as C
+        print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
+        opool = C.Pool.filled(kv, nb, hkv, d)
+        pairs = cow.cpu().numpy()
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 10.0) or reps == 0:
+            OB.copy_blocks(opool, opool, pairs)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        res["cpu_baseline"] = {"value": round(2 * moved / dt / 1e9, 4), "unit": "GB/s",
+                               "cores": 1, "kind": "oracle", "seconds": round(dt * reps, 2),
+                               "sample": f"{reps} x the same {N} in-pool copies (NumPy fancy "
+                                         f"indexing), bytes counted as for the GPU"}
+    print(json.dumps(res), flush=True)
+
+
 def prefill_flops(w, qs) -> int:
     """Algorithmic flops of multi-token attention: query i of sequence s (position
     L - n + i) does 2 D flops per key for QK and 2 D for PV over L - n + i + 1 keys."""
@@ -316,6 +422,10 @@ def main():
     ap.add_argument("--kv", default=None,
                     choices=["f16", "bf16", "fp8", "bf8", "fp8t", "bf8t", "fp4"],
                     help="override the workload's KV-cache format (same shapes and inputs)")
+    ap.add_argument("--blocks", type=int, default=0, metavar="N",
+                    help="time pa_copy_blocks instead: N copies inside the workload's pool "
+                         "(copy on write), N blocks out to a pinned host pool and back "
+                         "(swap), beside plain DMA copies of the same bytes")
     ap.add_argument("--prefill", type=int, default=0, metavar="CHUNK",
                     help="time pa_prefill instead: the last CHUNK positions of every sequence "
                          "as queries (chunked prefill), reported in TFLOP/s")
@@ -340,6 +450,9 @@ def main():
 
     if args.prefill > 0:
         prefill_main(args, config, DESCRIPTIONS)
+        return
+    if args.blocks > 0:
+        blocks_main(args, config, DESCRIPTIONS)
         return
 
     print(f"[bench] generating {args.config}", file=sys.stderr, flush=True)

@@ -16,8 +16,9 @@
  *
  * Conventions shared by every entry point
  *   - Pointers are device pointers unless stated otherwise. The caller owns all memory;
- *     the library allocates nothing and keeps no mutable global state, so calls from
- *     several host threads or streams are safe if their buffers do not overlap.
+ *     the library allocates no device memory and keeps no mutable global state, so calls
+ *     from several host threads or streams are safe if their buffers do not overlap. (The
+ *     host-side block allocator below is an object the caller creates and destroys.)
  *   - Arguments are validated on the host before anything is launched; a failed check
  *     returns a negative pa_status and launches nothing. Work is queued asynchronously
  *     on `stream` (a hipStream_t; NULL = the default stream). Device-side faults surface
@@ -68,10 +69,13 @@ typedef enum {
   PA_ERR_CONTEXT = -5,     /* max_blocks_per_seq out of range                           */
   PA_ERR_PARTITION = -6,   /* partition_size not 0 and not a positive multiple of 16    */
   PA_ERR_LAUNCH = -7,      /* the HIP runtime refused a launch                          */
-  PA_ERR_ALIGN = -8        /* a pointer is not 16-byte aligned                          */
+  PA_ERR_ALIGN = -8,       /* a pointer is not 16-byte aligned                          */
+  PA_ERR_MEMORY = -9,      /* a pointer is not memory this GPU can access               */
+  PA_ERR_EXHAUSTED = -10,  /* the block allocator has fewer free blocks than requested  */
+  PA_ERR_STATE = -11       /* the block allocator was asked about a block not in use    */
 } pa_status;
 
-#define PA_DEVERR_BAD_BLOCK 1        /* block table entry outside [0, num_blocks)        */
+#define PA_DEVERR_BAD_BLOCK 1        /* block table / copy pair id outside its pool      */
 #define PA_DEVERR_BAD_SLOT 2         /* slot_mapping entry outside [0, num_blocks * 16)   */
 #define PA_DEVERR_BAD_CONTEXT 4      /* context_lens entry outside [1, MB * 16]           */
 #define PA_DEVERR_UNCALIBRATED 8     /* decode read an FP4 block whose record is unset    */
@@ -210,6 +214,69 @@ int pa_fp8_head_scales(const void* x, int32_t act, int32_t kv_dtype, int64_t num
  * No-op (PA_OK) for formats without records.
  */
 int pa_reset_blocks(const pa_kv_pool* pool, const int32_t* block_ids, int32_t n, void* stream);
+
+/*
+ * Copy whole physical blocks from pool `src` to pool `dst`: for i < num_pairs, block
+ * pairs[2 i + 1] of dst becomes a byte-for-byte copy of block pairs[2 i] of src in every
+ * array the format uses (codes, the per-token scales and FP4 records inside the runs, the
+ * FP4 outlier slots). Per-head FP8 scales are not block data and are not touched.
+ *   - Copy on write: src == dst duplicates a block that several sequences share before
+ *     one of them extends it (inferensys glossary "vLLM", PagedAttention entry: blocks
+ *     shared across sequences for beam search, parallel sampling and prefix caching).
+ *   - Swap: a second pool of the same format whose arrays are pinned host memory
+ *     (hipHostMalloc) holds a preempted sequence's blocks; copying device -> host swaps
+ *     them out, host -> device back in (inferensys glossary "vLLM", preemption by
+ *     swapping KV blocks to CPU RAM, and CPU offloading). The GPU reads and writes the
+ *     host pool in place.
+ * The two pools must have the same dtype, num_kv_heads and head_dim (num_blocks may
+ * differ; k_scale / v_scale are ignored). pairs [num_pairs][2] int32 (source, destination),
+ * 8-byte aligned. Every pool array, pairs and dev_err must be device memory of the current
+ * GPU or pinned host memory. When the pools' arrays differ (a swap) each pointer is looked
+ * up first and anything else (pageable host memory) returns PA_ERR_MEMORY before any
+ * launch; within one pool nothing is looked up (a few microseconds saved per call). Destinations must be distinct and, within one pool, not also sources
+ * in the same call; otherwise the bytes of the affected blocks are unspecified (every
+ * access still stays inside the pools). A pair naming a block outside its pool is skipped
+ * and flagged (PA_DEVERR_BAD_BLOCK). A copied FP4 block keeps its calibration record, so
+ * writes into the copy reuse the source's outlier set. Asynchronous on `stream`.
+ */
+int pa_copy_blocks(const pa_kv_pool* src, const pa_kv_pool* dst, const int32_t* pairs,
+                   int32_t num_pairs, int32_t* dev_err, void* stream);
+
+/*
+ * Host-only reference-counted allocator of a pool's physical block ids (inferensys
+ * glossary "vLLM": finished sequences return their blocks to the pool at once, continuous
+ * batching entry; blocks shared across sequences, PagedAttention entry). It holds no
+ * device memory and launches nothing; every call is O(number of ids named) and
+ * serialized by an internal lock. Ids are 0 .. num_blocks - 1.
+ *   create     a handle with every block free; free blocks are handed out most recently
+ *              freed first, initially in ascending order. destroy releases the handle.
+ *   alloc      n blocks with reference count 1 into ids_out[n], all or nothing
+ *              (PA_ERR_EXHAUSTED, nothing changed, when fewer than n are free).
+ *   share      one more reference to each listed block (an id may repeat); every id must
+ *              be in use (PA_ERR_STATE, nothing changed).
+ *   release    drop one reference per listed occurrence; blocks that reach zero return to
+ *              the free list and are written to freed_out (capacity n, may be NULL) with
+ *              their count in *num_freed (may be NULL). Fails with PA_ERR_STATE, nothing
+ *              changed, if a block would go below zero. Freed FP4 blocks must be re-armed
+ *              with pa_reset_blocks before their next first write.
+ *   writable   copy on write for block `id` (in use): if it has one reference, *id_out = id
+ *              and the call returns 0; otherwise a new block is allocated, id loses one
+ *              reference, *id_out = the new block and the call returns 1: the caller then
+ *              copies id -> *id_out with pa_copy_blocks. PA_ERR_EXHAUSTED if none is free.
+ *   refcount   the block's reference count (0 when free), or PA_ERR_SHAPE out of range.
+ *   num_free   the number of free blocks.
+ * Out-of-range ids give PA_ERR_SHAPE, NULL pointers PA_ERR_NULL.
+ */
+typedef struct pa_block_allocator pa_block_allocator;
+int pa_allocator_create(int32_t num_blocks, pa_block_allocator** out);
+int pa_allocator_destroy(pa_block_allocator* a);
+int pa_allocator_alloc(pa_block_allocator* a, int32_t n, int32_t* ids_out);
+int pa_allocator_share(pa_block_allocator* a, const int32_t* ids, int32_t n);
+int pa_allocator_release(pa_block_allocator* a, const int32_t* ids, int32_t n,
+                         int32_t* freed_out, int32_t* num_freed);
+int pa_allocator_writable(pa_block_allocator* a, int32_t id, int32_t* id_out);
+int pa_allocator_refcount(pa_block_allocator* a, int32_t id);
+int pa_allocator_num_free(pa_block_allocator* a);
 
 /*
  * Paged decode for one query token per sequence.

@@ -75,6 +75,15 @@ def lib():
             "pa_merge": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]),
             "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "pa_read_device_error": (ctypes.c_int, [vp, vp, vp]),
+            "pa_copy_blocks": (ctypes.c_int, [pool_p, pool_p, vp, i32, vp, vp]),
+            "pa_allocator_create": (ctypes.c_int, [i32, ctypes.POINTER(vp)]),
+            "pa_allocator_destroy": (ctypes.c_int, [vp]),
+            "pa_allocator_alloc": (ctypes.c_int, [vp, i32, vp]),
+            "pa_allocator_share": (ctypes.c_int, [vp, vp, i32]),
+            "pa_allocator_release": (ctypes.c_int, [vp, vp, i32, vp, vp]),
+            "pa_allocator_writable": (ctypes.c_int, [vp, i32, ctypes.POINTER(i32)]),
+            "pa_allocator_refcount": (ctypes.c_int, [vp, i32]),
+            "pa_allocator_num_free": (ctypes.c_int, [vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -111,11 +120,12 @@ def pa_outlier_capacity(head_dim: int) -> int:
 
 
 class KVPool:
-    """Device arrays of one paged pool (caller-owned memory, as the ABI requires).
+    """Arrays of one paged pool (caller-owned memory, as the ABI requires).
 
-    `fill` is the byte every array starts with; FP4 outlier records are then reset to
-    0xFF (never written) with pa_reset_blocks. FP8 pools need k_scale / v_scale [Hkv] fp32
-    device tensors."""
+    `fill` is the byte every array starts with; FP4 outlier records are then set to 0xFF
+    (never written): with pa_reset_blocks on the GPU, or directly for a pool in pinned
+    host memory (device="cpu", the destination of swaps). Per-head FP8 pools on the GPU
+    need k_scale / v_scale [Hkv] fp32 device tensors."""
 
     NAMES = ["k", "v", "k_out_val", "v_out_val"]
 
@@ -124,15 +134,24 @@ class KVPool:
         self.kv_dtype, self.num_blocks = kv_dtype, num_blocks
         self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
         sizes = pa_pool_layout(kv_dtype, num_blocks, num_kv_heads, head_dim)
+        self.host = torch.device(device).type == "cpu"
         self.bytes = {}
         for name, n in zip(self.NAMES, sizes):
             if n:
-                self.bytes[name] = torch.full((n,), fill, dtype=torch.uint8, device=device)
+                if self.host:  # pinned (hipHostMalloc), so the GPU can reach it in place
+                    t = torch.empty((n,), dtype=torch.uint8, pin_memory=True)
+                    self.bytes[name] = t.fill_(fill)
+                else:
+                    self.bytes[name] = torch.full((n,), fill, dtype=torch.uint8, device=device)
         self.k_scale, self.v_scale = k_scale, v_scale
-        if kv_dtype in HEAD_SCALED and (k_scale is None or v_scale is None):
+        if kv_dtype in HEAD_SCALED and not self.host and (k_scale is None or v_scale is None):
             raise ValueError(f"a {kv_dtype} pool needs k_scale and v_scale")
         if kv_dtype == "fp4":
-            pa_reset_blocks(self, torch.arange(num_blocks, dtype=torch.int32, device=device))
+            if self.host:
+                for side in ("k", "v"):
+                    self.fp4_records(side).fill_(0xFF)
+            else:
+                pa_reset_blocks(self, torch.arange(num_blocks, dtype=torch.int32, device=device))
 
     def fp4_records(self, side: str):
         """FP4 only: the 16-byte outlier records [NB, Hkv, 16] (a view of the k or v tiles)."""
@@ -180,6 +199,80 @@ def pa_reset_blocks(pool: KVPool, block_ids):
     s = pool.struct()
     _check("pa_reset_blocks", lib().pa_reset_blocks(ctypes.byref(s), _ptr(block_ids),
                                                     block_ids.numel(), _stream()))
+
+
+def pa_copy_blocks(src: KVPool, dst: KVPool, pairs, dev_err=None):
+    """pairs [n, 2] int32 (source block of src, destination block of dst), on the GPU or
+    in pinned host memory; src may be dst (copy on write) or either may be a host pool
+    (swap)."""
+    assert pairs.dtype == torch.int32 and pairs.dim() == 2 and pairs.shape[1] == 2
+    assert pairs.is_contiguous()
+    s, d = src.struct(), dst.struct()
+    _check("pa_copy_blocks", lib().pa_copy_blocks(ctypes.byref(s), ctypes.byref(d),
+                                                  _ptr(pairs), pairs.shape[0], _ptr(dev_err),
+                                                  _stream()))
+
+
+class BlockAllocator:
+    """The library's host-side reference-counted block allocator (pa_allocator_*)."""
+
+    def __init__(self, num_blocks: int):
+        h = ctypes.c_void_p()
+        _check("pa_allocator_create", lib().pa_allocator_create(num_blocks, ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = num_blocks
+
+    def close(self):
+        if self._h:
+            lib().pa_allocator_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _ids(ids):
+        arr = (ctypes.c_int32 * max(len(ids), 1))(*[int(i) for i in ids])
+        return arr, len(ids)
+
+    def alloc(self, n: int) -> list:
+        out = (ctypes.c_int32 * max(n, 1))()
+        _check("pa_allocator_alloc", lib().pa_allocator_alloc(self._h, n, out))
+        return list(out)[:n]
+
+    def share(self, ids):
+        arr, n = self._ids(ids)
+        _check("pa_allocator_share", lib().pa_allocator_share(self._h, arr, n))
+
+    def release(self, ids) -> list:
+        """Drop one reference per listed id; returns the ids that became free."""
+        arr, n = self._ids(ids)
+        freed = (ctypes.c_int32 * max(n, 1))()
+        k = ctypes.c_int32()
+        _check("pa_allocator_release", lib().pa_allocator_release(self._h, arr, n, freed,
+                                                                 ctypes.byref(k)))
+        return list(freed)[:k.value]
+
+    def writable(self, block_id: int):
+        """(id to write into, whether the caller must copy block_id there first)."""
+        out = ctypes.c_int32()
+        r = lib().pa_allocator_writable(self._h, block_id, ctypes.byref(out))
+        if r < 0:
+            raise PAError("pa_allocator_writable", r)
+        return out.value, r == 1
+
+    def refcount(self, block_id: int) -> int:
+        r = lib().pa_allocator_refcount(self._h, block_id)
+        if r < 0:
+            raise PAError("pa_allocator_refcount", r)
+        return r
+
+    @property
+    def num_free(self) -> int:
+        return lib().pa_allocator_num_free(self._h)
 
 
 def max_partitions(max_blocks_per_seq: int, partition_size: int) -> int:

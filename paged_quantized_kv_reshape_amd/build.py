@@ -16,7 +16,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpa.so")
-SOURCES = ["pa_api.cpp", "pa_write.hip", "pa_decode.hip", "pa_merge.hip"]
+SOURCES = ["pa_api.cpp", "pa_alloc.cpp", "pa_write.hip", "pa_decode.hip", "pa_merge.hip",
+           "pa_blocks.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -14,7 +14,8 @@ constexpr int64_t kMaxGridYZ = 65535;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-int check_pool(const pa_kv_pool* p) {
+// Format, shape, block arrays and their alignment; not the per-head scales.
+int check_pool_arrays(const pa_kv_pool* p) {
   if (!p) return PA_ERR_NULL;
   if (p->dtype < PA_KV_F16 || p->dtype > PA_KV_FP8_E5M2_TOKEN) return PA_ERR_DTYPE;
   if (p->block_size != PA_BLOCK_SIZE) return PA_ERR_BLOCK_SIZE;
@@ -24,16 +25,42 @@ int check_pool(const pa_kv_pool* p) {
   if ((int64_t)p->num_blocks * PA_BLOCK_SIZE > INT64_C(0x3FFFFFFFFFFFFFFF)) return PA_ERR_SHAPE;
   if (!p->k || !p->v) return PA_ERR_NULL;
   if (!aligned(p->k, 16) || !aligned(p->v, 16)) return PA_ERR_ALIGN;
-  if (p->dtype == PA_KV_FP8_E4M3 || p->dtype == PA_KV_FP8_E5M2) {
-    if (!p->k_scale || !p->v_scale) return PA_ERR_NULL;
-    if (!aligned(p->k_scale, 4) || !aligned(p->v_scale, 4)) return PA_ERR_ALIGN;
-  }
   if (p->dtype == PA_KV_FP4_E2M1_OUTL) {
     if (p->head_dim != 128) return PA_ERR_SHAPE;  // 4-bit format: head_dim 128 only
     if (!p->k_out_val || !p->v_out_val) return PA_ERR_NULL;
     if (!aligned(p->k_out_val, 8) || !aligned(p->v_out_val, 8)) return PA_ERR_ALIGN;
   }
   return PA_OK;
+}
+
+int check_pool(const pa_kv_pool* p) {
+  const int st = check_pool_arrays(p);
+  if (st != PA_OK) return st;
+  if (p->dtype == PA_KV_FP8_E4M3 || p->dtype == PA_KV_FP8_E5M2) {
+    if (!p->k_scale || !p->v_scale) return PA_ERR_NULL;
+    if (!aligned(p->k_scale, 4) || !aligned(p->v_scale, 4)) return PA_ERR_ALIGN;
+  }
+  return PA_OK;
+}
+
+// True when the current GPU can dereference p at address p: its own device memory, or
+// pinned host memory mapped at the same address. Pageable host memory, which the runtime
+// does not know, is refused (a kernel touching it would fault).
+bool gpu_accessible(const void* p) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();  // leave no error behind for the next launch check
+    return false;
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (at.type == hipMemoryTypeDevice) return at.device == dev;
+  if (at.type == hipMemoryTypeHost || at.type == hipMemoryTypeManaged)
+    return at.devicePointer == p;
+  return false;
 }
 
 bool act_ok(int32_t act) { return act == PA_ACT_F16 || act == PA_ACT_BF16; }
@@ -75,6 +102,9 @@ const char* pa_status_string(int status) {
     case PA_ERR_PARTITION: return "PA_ERR_PARTITION: partition_size must be 0 or a positive multiple of 16";
     case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: the HIP runtime refused a launch";
     case PA_ERR_ALIGN: return "PA_ERR_ALIGN: a pointer is not suitably aligned";
+    case PA_ERR_MEMORY: return "PA_ERR_MEMORY: a pointer is not memory this GPU can access";
+    case PA_ERR_EXHAUSTED: return "PA_ERR_EXHAUSTED: not enough free blocks";
+    case PA_ERR_STATE: return "PA_ERR_STATE: the block is not in use";
     default: return "unknown pa_status";
   }
 }
@@ -148,6 +178,56 @@ int pa_reset_blocks(const pa_kv_pool* pool, const int32_t* block_ids, int32_t n,
   if (!block_ids) return PA_ERR_NULL;
   if (!aligned(block_ids, 4)) return PA_ERR_ALIGN;
   return pa::launch_reset(*pool, block_ids, n, (hipStream_t)stream);
+}
+
+int pa_copy_blocks(const pa_kv_pool* src, const pa_kv_pool* dst, const int32_t* pairs,
+                   int32_t num_pairs, int32_t* dev_err, void* stream) {
+  int st = check_pool_arrays(src);
+  if (st != PA_OK) return st;
+  if ((st = check_pool_arrays(dst)) != PA_OK) return st;
+  if (src->dtype != dst->dtype) return PA_ERR_DTYPE;
+  if (src->num_kv_heads != dst->num_kv_heads || src->head_dim != dst->head_dim)
+    return PA_ERR_SHAPE;
+  if (num_pairs < 0) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!pairs) return PA_ERR_NULL;
+  if (!aligned(pairs, 8) || !aligned(dev_err, 4)) return PA_ERR_ALIGN;
+  size_t sb[4], db[4];
+  if ((st = pa_pool_layout(src->dtype, src->num_blocks, src->num_kv_heads, src->head_dim, sb)) !=
+      PA_OK)
+    return st;
+  if ((st = pa_pool_layout(dst->dtype, dst->num_blocks, dst->num_kv_heads, dst->head_dim, db)) !=
+      PA_OK)
+    return st;
+  pa::CopyArgs a{};
+  const void* sp[4] = {src->k, src->v, src->k_out_val, src->v_out_val};
+  void* dp[4] = {dst->k, dst->v, dst->k_out_val, dst->v_out_val};
+  for (int j = 0; j < 4; ++j) {
+    if (sb[j] == 0) continue;
+    const size_t per_block = sb[j] / (size_t)src->num_blocks;
+    if (per_block % 16 != 0 || per_block / 16 > UINT32_MAX) return PA_ERR_SHAPE;
+    if (!aligned(sp[j], 16) || !aligned(dp[j], 16)) return PA_ERR_ALIGN;
+    a.src[a.num_arrays] = sp[j];
+    a.dst[a.num_arrays] = dp[j];
+    a.vecs_per_block[a.num_arrays] = (uint32_t)(per_block / 16);
+    ++a.num_arrays;
+  }
+  // A swap names memory on the host: check that the GPU can reach every pointer. Within
+  // one pool (copy on write) the arrays are the decode's own device memory and, as for
+  // the other entry points, are not looked up.
+  bool same = true;
+  for (int j = 0; j < a.num_arrays; ++j) same = same && a.src[j] == a.dst[j];
+  if (!same) {
+    for (int j = 0; j < a.num_arrays; ++j)
+      if (!gpu_accessible(a.src[j]) || !gpu_accessible(a.dst[j])) return PA_ERR_MEMORY;
+    if (!gpu_accessible(pairs) || (dev_err && !gpu_accessible(dev_err))) return PA_ERR_MEMORY;
+  }
+  a.pairs = pairs;
+  a.num_pairs = num_pairs;
+  a.src_blocks = src->num_blocks;
+  a.dst_blocks = dst->num_blocks;
+  a.err = dev_err;
+  return pa::launch_copy_blocks(a, (hipStream_t)stream);
 }
 
 int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,

@@ -45,6 +45,17 @@ int launch_decode(const DecodeArgs& a, int kv_dtype, bool q_bf16, int head_dim, 
                   hipStream_t st);
 int launch_prefill(const DecodeArgs& a, int kv_dtype, bool q_bf16, int head_dim, hipStream_t st);
 
+// Whole-block copy: array j of the pool has vecs_per_block[j] 16-byte vectors per block.
+struct CopyArgs {
+  const void* src[4];
+  void* dst[4];
+  uint32_t vecs_per_block[4];
+  const int32_t* pairs;  // [num_pairs][2] (source, destination)
+  int32_t num_pairs, num_arrays, src_blocks, dst_blocks;
+  int32_t* err;
+};
+int launch_copy_blocks(const CopyArgs& a, hipStream_t st);
+
 int launch_merge(const float* part_out, const float* part_lse, const int32_t* context_lens,
                  int32_t S, int32_t Hq, int32_t D, int32_t P, int32_t ps, float* out,
                  float* lse_out, hipStream_t st);

@@ -14,6 +14,7 @@ from conftest import ROOT
 B = pytest.importorskip("paged_quantized_kv_reshape_amd.binding")
 
 PA_OK, NULL, SHAPE, DTYPE, BLOCK, CONTEXT, PART, LAUNCH, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7, -8
+MEMORY, EXHAUSTED, STATE = -9, -10, -11
 FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
 
 
@@ -32,7 +33,8 @@ def test_library_exports_every_declared_entry_point():
 
 def test_status_strings():
     lib = B.lib()
-    for code in (PA_OK, NULL, SHAPE, DTYPE, BLOCK, CONTEXT, PART, LAUNCH, ALIGN):
+    for code in (PA_OK, NULL, SHAPE, DTYPE, BLOCK, CONTEXT, PART, LAUNCH, ALIGN, MEMORY,
+                 EXHAUSTED, STATE):
         s = lib.pa_status_string(code).decode()
         assert s.startswith("PA_"), s
     assert "unknown" in lib.pa_status_string(-99).decode()
@@ -67,10 +69,10 @@ def test_pool_layout_rejects():
     assert lib.pa_outlier_capacity(80) == SHAPE
 
 
-def _pool(dtype=2, nb=8, hkv=1, d=128, bs=16, scales=True, fp4=True):
+def _pool(dtype=2, nb=8, hkv=1, d=128, bs=16, scales=True, fp4=True, base=FAKE):
     s = B.pa_kv_pool()
     s.dtype, s.num_blocks, s.block_size, s.num_kv_heads, s.head_dim = dtype, nb, bs, hkv, d
-    s.k = s.v = FAKE
+    s.k = s.v = base
     if scales:
         s.k_scale = s.v_scale = FAKE
     if fp4:
@@ -157,6 +159,34 @@ def test_merge_and_scale_and_reset_reject():
     assert lib.pa_reset_blocks(ctypes.byref(p), FAKE, -1, None) == SHAPE
     assert lib.pa_reset_blocks(ctypes.byref(_pool(dtype=2)), FAKE, 3, None) == PA_OK  # no records
     assert lib.pa_read_device_error(None, None, None) == NULL
+
+
+def test_copy_blocks_rejects():
+    """Every check of pa_copy_blocks runs before a launch. With no GPU here, no pointer is
+    memory a GPU can access, so well-formed calls between two pools (their arrays at
+    different addresses) stop at the memory check. A well-formed call within one pool
+    would launch, so none is made here."""
+    lib = B.lib()
+    c = lambda a, b, pairs=FAKE, n=3, err=None: lib.pa_copy_blocks(
+        None if a is None else ctypes.byref(a), None if b is None else ctypes.byref(b),
+        pairs, n, err, None)
+    a = _pool(nb=8)
+    assert c(None, a) == NULL and c(a, None) == NULL
+    assert c(a, _pool(dtype=4)) == DTYPE                 # E4M3 -> E5M2
+    assert c(a, _pool(hkv=2)) == SHAPE and c(a, _pool(d=64)) == SHAPE
+    assert c(a, _pool(bs=32)) == BLOCK
+    assert c(a, a, n=-1) == SHAPE
+    assert c(a, a, n=0) == PA_OK                         # nothing to copy
+    assert c(a, a, pairs=None) == NULL
+    assert c(a, a, pairs=FAKE + 4) == ALIGN and c(a, a, err=FAKE + 2) == ALIGN
+    s = _pool(dtype=3)
+    s.k_out_val = FAKE + 8                               # outlier slots need 16 bytes here
+    assert c(s, _pool(dtype=3)) == ALIGN
+    assert c(_pool(dtype=3, fp4=False), _pool(dtype=3)) == NULL
+    other = FAKE + (1 << 30)
+    assert c(_pool(scales=False), _pool(nb=4, scales=False, base=other)) == MEMORY  # no scales
+    for kv in range(7):
+        assert c(_pool(dtype=kv), _pool(dtype=kv, nb=3, base=other)) == MEMORY
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
