@@ -184,6 +184,20 @@ def profile_label(args) -> str:
     return args.config if args.kv is None else f"{args.config}_{args.kv}"
 
 
+def copy_probe(mib: int):
+    """One plain elementwise kernel over mib MiB (n bytes read, n written): the known
+    traffic that calibrates the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    print(f"[bench] copy probe: {n} bytes read + {n} written", file=sys.stderr, flush=True)
+    del src, dst
+
+
 PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16 host link, per direction, published
 
 
@@ -231,6 +245,8 @@ def blocks_main(args, config, DESCRIPTIONS):
 
     print(f"[bench] {kv} pool of {nb} blocks ({per_block} B each), {N} blocks per call",
           file=sys.stderr, flush=True)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
     t_cow = timed(lambda: pa_copy_blocks(pool, pool, cow, err))
     t_out = timed(lambda: pa_copy_blocks(pool, host, out_p, err))
     t_in = timed(lambda: pa_copy_blocks(host, pool, in_p, err))
@@ -473,14 +489,7 @@ def main():
           f"{dec['total']}, write bytes {wr}", file=sys.stderr, flush=True)
 
     if args.copy_probe_mib:
-        n = args.copy_probe_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.bitwise_not(src, out=dst)  # one elementwise kernel: n bytes read, n written
-        torch.cuda.synchronize()
-        print(f"[bench] copy probe: {n} bytes read + {n} written", file=sys.stderr, flush=True)
-        del src, dst
+        copy_probe(args.copy_probe_mib)
 
     # every libpa call goes on torch's current stream; the events are recorded on it too
     stream = torch.cuda.current_stream().cuda_stream
