@@ -25,6 +25,10 @@ Readings where the pages are silent (each listed in the design notes):
     The per-channel norm is the RMS over those tokens; mu and sigma are the mean and
     population standard deviation of the D norms; outliers are the channels with
     norm >= mu + 3.2 sigma, ascending; sigma = 0 means no outliers.
+    The variant closest to the pages' wording ("per-channel norms ... during the prefill
+    phase") computes one set per (sequence, kv-head, K|V) from the sequence's first
+    prefill chunk and gives it to every block the sequence opens (fp4_sequence_records,
+    cache_write's seq_records).
   * FP4 scale: one fp32 scale per (token, kv-head, K|V), fp32(inlier absmax / 6); inlier
     codes are E2M1(fp32(x / s_t)); outlier positions hold code +0; s_t = 0 gives +0 codes;
     two codes per byte, even channel in the low nibble; outliers are stored as fp16(x).
@@ -285,6 +289,33 @@ def fp4_calibration_margin(x: np.ndarray) -> float:
     return float(np.min(np.abs(r - thr)) / thr)
 
 
+def fp4_sequence_records(k_rows, v_rows, act: str, row_start) -> tuple:
+    """Per-sequence outlier sets (the calibration read literally: the per-channel norms of
+    the key and value vectors a sequence's prefill produces, here its first prefill chunk).
+
+    k_rows, v_rows [R, Hkv, D] raw 16-bit bits; sequence s owns rows row_start[s] ..
+    row_start[s + 1] - 1. Returns (records [S, 2, Hkv, 16] uint8 in the block record format
+    - count, ascending channel ids, 0xFF padding; side 0 = K, 1 = V - and margins [S, 2, Hkv]
+    as in fp4_calibration_margin). A sequence with no rows gets an empty set."""
+    row_start = np.asarray(row_start, dtype=np.int64)
+    S = len(row_start) - 1
+    hkv = np.asarray(k_rows).shape[1]
+    recs = np.full((S, 2, hkv, 16), UNCALIBRATED, dtype=np.uint8)
+    margins = np.full((S, 2, hkv), np.inf)
+    for side, rows in enumerate((k_rows, v_rows)):
+        for sq in range(S):
+            x = act_decode(np.asarray(rows)[row_start[sq]:row_start[sq + 1]], act)  # [n, Hkv, D]
+            for h in range(hkv):
+                if x.shape[0] == 0:
+                    recs[sq, side, h, 0] = 0
+                    continue
+                o = fp4_calibrate(x[:, h, :])
+                margins[sq, side, h] = fp4_calibration_margin(x[:, h, :])
+                recs[sq, side, h, 0] = len(o)
+                recs[sq, side, h, 1:1 + len(o)] = o
+    return recs, margins
+
+
 def fp4_encode_row(x: np.ndarray, outliers: np.ndarray):
     """One token row x [D] (fp64 of the input values) with its block's outlier set.
 
@@ -307,7 +338,7 @@ def fp4_encode_row(x: np.ndarray, outliers: np.ndarray):
 
 
 def cache_write(pool: Pool, k_rows, v_rows, act: str, slots, k_scale=None, v_scale=None,
-                only_blocks=None, calib_log=None):
+                only_blocks=None, calib_log=None, seq_records=None, token_seq=None):
     """Replay one cache-write call: row i of k_rows/v_rows [T, Hkv, D] (raw 16-bit bits)
     goes to slot slots[i] = physical_block * 16 + offset; negative slots are skipped.
 
@@ -315,7 +346,12 @@ def cache_write(pool: Pool, k_rows, v_rows, act: str, slots, k_scale=None, v_sca
     those physical blocks are replayed (each block's contents depend only on the calls
     that write into it, so sampled replays are exact). If calib_log is a list, every FP4
     calibration appends (name, block, head, margin) with margin as in
-    fp4_calibration_margin."""
+    fp4_calibration_margin.
+
+    FP4 per-sequence calibration: with seq_records [S, 2, Hkv, 16] (fp4_sequence_records)
+    and token_seq [T] (the sequence of each row), a block this call opens takes the record
+    of the sequence of its lowest-offset row in the call instead of calibrating on the
+    call's rows; blocks already calibrated keep their record either way."""
     slots = np.asarray(slots, dtype=np.int64)
     live = np.nonzero(slots >= 0)[0]
     assert len(np.unique(slots[live])) == len(live), "slots within one call must be distinct"
@@ -355,10 +391,18 @@ def cache_write(pool: Pool, k_rows, v_rows, act: str, slots, k_scale=None, v_sca
             scale_arr = fp4_scales(pool, name)
             slot0_arr, val_arr = fp4_slot0(pool, name), A[name + "_out_val"]
             # step 1-2: calibrate blocks this call opens, on this call's tokens
+            side = 0 if name == "k" else 1
             for b in np.unique(blk):
                 rows_in_b = np.nonzero(blk == b)[0]
                 for h in range(hkv):
                     if idx_arr[b, h, 0] != UNCALIBRATED:
+                        continue
+                    if seq_records is not None:
+                        lead = rows_in_b[np.argmin(off[rows_in_b])]
+                        sq = int(np.asarray(token_seq)[live[lead]])
+                        rec = np.asarray(seq_records)[sq, side, h].copy()
+                        rec[1 + rec[0]:] = UNCALIBRATED
+                        idx_arr[b, h, :] = rec
                         continue
                     o = fp4_calibrate(x_all[rows_in_b, h, :])
                     if calib_log is not None:
