@@ -207,6 +207,42 @@ int pa_fp8_head_scales(const void* x, int32_t act, int32_t kv_dtype, int64_t num
                        int32_t num_kv_heads, int32_t head_dim, float* scale_out, void* stream);
 
 /*
+ * FP4 per-sequence calibration, the pages' wording taken literally: the per-channel norms
+ * of the key and value vectors a sequence's prefill produces decide its outlier channels
+ * (dailyaiworld.com, "Technical Breakdown: Dynamic Quantization with Outlier Retention",
+ * steps 1-2), here once per (sequence, kv head, K|V) instead of once per block.
+ *   k_rows, v_rows [num_rows, num_kv_heads, head_dim], activation dtype `act`: the rows
+ *                 the sets come from (typically each sequence's first prefill chunk);
+ *                 sequence s owns rows row_start[s] .. row_start[s + 1] - 1
+ *   row_start     [num_seqs + 1] int32
+ *   seq_records   [num_seqs, 2, num_kv_heads, 16] uint8 (written): K (index 0) and V (1)
+ *                 sets in the block record format (count, ascending channel ids, 0xFF)
+ * Same statistics as the per-block calibration: per-channel RMS over the rows, channels at
+ * or above mean + 3.2 population sigma of the head_dim norms. head_dim 128. A sequence with
+ * no rows gets an empty set; one whose range is not inside [0, num_rows) too, flagged
+ * PA_DEVERR_BAD_CONTEXT. Asynchronous on `stream`.
+ */
+int pa_fp4_sequence_outliers(const void* k_rows, const void* v_rows, int32_t act,
+                             int64_t num_rows, int32_t num_kv_heads, int32_t head_dim,
+                             const int32_t* row_start, int32_t num_seqs, uint8_t* seq_records,
+                             int32_t* dev_err, void* stream);
+
+/*
+ * pa_cache_write into an FP4 pool with per-sequence calibration: a block the call opens
+ * takes the outlier set of its sequence from seq_records (pa_fp4_sequence_outliers) rather
+ * than one computed from the call's rows in it, so a decode token that starts a block
+ * encodes with the sequence's set. The sequence of a block is that of its lowest-offset
+ * row in the call; blocks already written keep their set. token_seq [num_tokens] int32:
+ * the sequence of each row; a row naming a sequence outside [0, num_seqs) opens its block
+ * with no outliers and is flagged (PA_DEVERR_BAD_CONTEXT). The pool must be
+ * PA_KV_FP4_E2M1_OUTL. Everything else as pa_cache_write. Asynchronous on `stream`.
+ */
+int pa_cache_write_seq_outliers(const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                                int32_t act, int32_t num_tokens, const int64_t* slot_mapping,
+                                const int32_t* token_seq, const uint8_t* seq_records,
+                                int32_t num_seqs, int32_t* dev_err, void* stream);
+
+/*
  * Mark the listed physical blocks as never written (FP4 records set to 0xFF), so the next
  * write into each one calibrates it afresh: call it once for every block of a new pool,
  * and when the engine hands a freed block to a new sequence (inferensys glossary "vLLM", continuous batching entry: finished

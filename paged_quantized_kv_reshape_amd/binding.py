@@ -76,6 +76,10 @@ def lib():
             "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "pa_read_device_error": (ctypes.c_int, [vp, vp, vp]),
             "pa_copy_blocks": (ctypes.c_int, [pool_p, pool_p, vp, i32, vp, vp]),
+            "pa_fp4_sequence_outliers": (ctypes.c_int, [vp, vp, i32, i64, i32, i32, vp, i32, vp,
+                                                        vp, vp]),
+            "pa_cache_write_seq_outliers": (ctypes.c_int, [pool_p, vp, vp, i32, i32, vp, vp, vp,
+                                                           i32, vp, vp]),
             "pa_allocator_create": (ctypes.c_int, [i32, ctypes.POINTER(vp)]),
             "pa_allocator_destroy": (ctypes.c_int, [vp]),
             "pa_allocator_alloc": (ctypes.c_int, [vp, i32, vp]),
@@ -183,6 +187,31 @@ def pa_cache_write(pool: KVPool, k_new, v_new, slot_mapping, dev_err=None):
     _check("pa_cache_write", lib().pa_cache_write(
         ctypes.byref(s), _ptr(k_new), _ptr(v_new), ACT_DTYPES[k_new.dtype], T,
         _ptr(slot_mapping), _ptr(dev_err), _stream()))
+
+
+def pa_fp4_sequence_outliers(k_rows, v_rows, row_start, seq_records, dev_err=None):
+    """k_rows, v_rows [R, Hkv, 128] fp16/bf16; row_start [S + 1] int32; seq_records
+    [S, 2, Hkv, 16] uint8 (written)."""
+    assert k_rows.dtype in ACT_DTYPES and v_rows.dtype == k_rows.dtype
+    assert k_rows.shape == v_rows.shape and row_start.dtype == torch.int32
+    assert seq_records.dtype == torch.uint8
+    S = row_start.numel() - 1
+    assert tuple(seq_records.shape) == (S, 2, k_rows.shape[1], 16)
+    _check("pa_fp4_sequence_outliers", lib().pa_fp4_sequence_outliers(
+        _ptr(k_rows), _ptr(v_rows), ACT_DTYPES[k_rows.dtype], k_rows.shape[0], k_rows.shape[1],
+        k_rows.shape[2], _ptr(row_start), S, _ptr(seq_records), _ptr(dev_err), _stream()))
+
+
+def pa_cache_write_seq_outliers(pool: KVPool, k_new, v_new, slot_mapping, token_seq,
+                                seq_records, dev_err=None):
+    assert k_new.dtype in ACT_DTYPES and v_new.dtype == k_new.dtype
+    assert slot_mapping.dtype == torch.int64 and token_seq.dtype == torch.int32
+    assert seq_records.dtype == torch.uint8
+    s = pool.struct()
+    _check("pa_cache_write_seq_outliers", lib().pa_cache_write_seq_outliers(
+        ctypes.byref(s), _ptr(k_new), _ptr(v_new), ACT_DTYPES[k_new.dtype], k_new.shape[0],
+        _ptr(slot_mapping), _ptr(token_seq), _ptr(seq_records), seq_records.shape[0],
+        _ptr(dev_err), _stream()))
 
 
 def pa_fp8_head_scales(x, scale_out, kv_dtype="fp8"):

@@ -170,6 +170,41 @@ int pa_fp8_head_scales(const void* x, int32_t act, int32_t kv_dtype, int64_t num
                                num_kv_heads, head_dim, scale_out, (hipStream_t)stream);
 }
 
+int pa_fp4_sequence_outliers(const void* k_rows, const void* v_rows, int32_t act,
+                             int64_t num_rows, int32_t num_kv_heads, int32_t head_dim,
+                             const int32_t* row_start, int32_t num_seqs, uint8_t* seq_records,
+                             int32_t* dev_err, void* stream) {
+  if (!act_ok(act)) return PA_ERR_DTYPE;
+  if (head_dim != 128 || num_rows < 0 || num_seqs < 0 || num_kv_heads < 1 ||
+      num_kv_heads > kMaxGridYZ)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!row_start || !seq_records || (num_rows > 0 && (!k_rows || !v_rows))) return PA_ERR_NULL;
+  if (!aligned(k_rows, 16) || !aligned(v_rows, 16) || !aligned(row_start, 4) ||
+      !aligned(seq_records, 16) || !aligned(dev_err, 4))
+    return PA_ERR_ALIGN;
+  return pa::launch_fp4_seq_outliers(k_rows, v_rows, act == PA_ACT_BF16, num_rows, num_kv_heads,
+                                     head_dim, row_start, num_seqs, seq_records, dev_err,
+                                     (hipStream_t)stream);
+}
+
+int pa_cache_write_seq_outliers(const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                                int32_t act, int32_t num_tokens, const int64_t* slot_mapping,
+                                const int32_t* token_seq, const uint8_t* seq_records,
+                                int32_t num_seqs, int32_t* dev_err, void* stream) {
+  int st = check_pool(pool);
+  if (st != PA_OK) return st;
+  if (pool->dtype != PA_KV_FP4_E2M1_OUTL || !act_ok(act)) return PA_ERR_DTYPE;
+  if (num_tokens < 0 || num_seqs < 0) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !token_seq || !seq_records) return PA_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slot_mapping, 8) ||
+      !aligned(token_seq, 4) || !aligned(seq_records, 16) || !aligned(dev_err, 4))
+    return PA_ERR_ALIGN;
+  return pa::launch_write(*pool, k_new, v_new, act == PA_ACT_BF16, num_tokens, slot_mapping,
+                          dev_err, (hipStream_t)stream, token_seq, seq_records, num_seqs);
+}
+
 int pa_reset_blocks(const pa_kv_pool* pool, const int32_t* block_ids, int32_t n, void* stream) {
   int st = check_pool(pool);
   if (st != PA_OK) return st;

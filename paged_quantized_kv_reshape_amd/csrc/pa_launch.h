@@ -14,8 +14,15 @@ inline int outlier_capacity(int head_dim) {
   return head_dim == 128 ? 11 : head_dim == 64 ? 5 : -1;
 }
 
+// token_seq / seq_records / num_seqs: FP4 per-sequence calibration (blocks the call opens
+// take their sequence's outlier set); nullptr / 0 for the per-block calibration.
 int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool bf16, int32_t T,
-                 const int64_t* slots, int32_t* err, hipStream_t st);
+                 const int64_t* slots, int32_t* err, hipStream_t st,
+                 const int32_t* token_seq = nullptr, const uint8_t* seq_records = nullptr,
+                 int32_t num_seqs = 0);
+int launch_fp4_seq_outliers(const void* k_rows, const void* v_rows, bool bf16, int64_t num_rows,
+                           int32_t hkv, int32_t D, const int32_t* row_start, int32_t num_seqs,
+                           uint8_t* records, int32_t* err, hipStream_t st);
 int launch_fp8_scales(const void* x, bool bf16, bool e5m2, int64_t rows, int32_t hkv, int32_t D,
                       float* scale_out, hipStream_t st);
 int launch_reset(const pa_kv_pool& p, const int32_t* ids, int32_t n, hipStream_t st);

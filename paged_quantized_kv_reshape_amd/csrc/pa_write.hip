@@ -258,6 +258,20 @@ struct Fp4Args {
   int32_t num_tokens, hkv, head_dim, cap;
   int64_t nslots;
   int32_t* err;
+  // per-sequence calibration (k_fp4_adopt): row i belongs to sequence token_seq[i], whose
+  // record for (K|V, head h) is seq_records[((seq * 2 + side) * hkv + h) * 16 ...]
+  const int32_t* token_seq;
+  const uint8_t* seq_records;
+  int32_t num_seqs;
+};
+struct SeqOutlierArgs {
+  const uint16_t* k_rows;  // [num_rows, hkv, D] activation bits
+  const uint16_t* v_rows;
+  const int32_t* row_start;  // [S + 1]
+  int64_t num_rows;
+  int32_t hkv, cap;
+  uint8_t* records;  // [S, 2, hkv, 16]
+  int32_t* err;
 };
 
 template <int D>
@@ -281,6 +295,44 @@ __global__ __launch_bounds__(256) void k_fp4_mark(Fp4Args a) {
   if (rec[0] != 0xFF) return;  // already calibrated: reuse its channel set
   atomicAnd(reinterpret_cast<unsigned int*>(rec + 12), ~(1u << off));
   reinterpret_cast<int32_t*>(tile + TL::kScale)[off] = (int32_t)i;
+}
+
+// The outlier set from per-channel RMS norms r (channel lane + 64 k in r[k]) of one wave:
+// mu and population sigma over the D norms, channels with r >= mu + 3.2 sigma (none when
+// sigma = 0), ascending, at most cap of them; returned as record bytes 0..11 (count, ids,
+// 0xFF padding) in three words.
+template <int D>
+__device__ __forceinline__ void record_from_norms(const float (&r)[D / 64], int cap,
+                                                  uint32_t (&bytes)[3]) {
+  constexpr int CPL = D / 64;
+  float part = 0.0f;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) part += r[k];
+  const float mu = wave_sum(part) / (float)D;
+  float dev = 0.0f;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) dev += (r[k] - mu) * (r[k] - mu);
+  const float sigma = __builtin_sqrtf(wave_sum(dev) / (float)D);
+  const float thr = mu + kOutlierSigmas * sigma;
+  bytes[0] = bytes[1] = bytes[2] = 0xFFFFFFFFu;
+  int count = 0;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) {
+    const bool hit = sigma != 0.0f && r[k] >= thr;
+    uint64_t mask = __ballot(hit);
+    while (mask) {
+      const int c = __builtin_ctzll(mask) + 64 * k;
+      mask &= mask - 1;
+      if (count < cap) {
+        const int pos = 1 + count;  // byte position in the record
+        bytes[pos >> 2] &= ~(0xFFu << ((pos & 3) * 8));
+        bytes[pos >> 2] |= (uint32_t)c << ((pos & 3) * 8);
+      }
+      ++count;
+    }
+  }
+  const int stored = count < cap ? count : cap;
+  bytes[0] = (bytes[0] & ~0xFFu) | (uint32_t)stored;
 }
 
 // One wave per (row, head, K|V); only block leaders do work.
@@ -340,44 +392,100 @@ __global__ __launch_bounds__(64 * kRowsPerWg) void k_fp4_calibrate(Fp4Args a) {
 #pragma unroll
     for (int o = 0; o < kBlock; ++o) ss[k] = __builtin_fmaf(xv[o][k], xv[o][k], ss[k]);  // +0 for absent rows
   }
-  float r[CPL], part = 0.0f;
+  float r[CPL];
 #pragma unroll
-  for (int k = 0; k < CPL; ++k) {
-    r[k] = __builtin_sqrtf(ss[k] / (float)n);
-    part += r[k];
-  }
-  const float mu = wave_sum(part) / (float)D;
-  float dev = 0.0f;
-#pragma unroll
-  for (int k = 0; k < CPL; ++k) dev += (r[k] - mu) * (r[k] - mu);
-  const float sigma = __builtin_sqrtf(wave_sum(dev) / (float)D);
-  const float thr = mu + kOutlierSigmas * sigma;
-
-  // Ascending channel list via ballots (channel lane + 64 k).
-  uint32_t bytes[3] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
-  int count = 0;
-#pragma unroll
-  for (int k = 0; k < CPL; ++k) {
-    const bool hit = sigma != 0.0f && r[k] >= thr;
-    uint64_t mask = __ballot(hit);
-    while (mask) {
-      const int c = __builtin_ctzll(mask) + 64 * k;
-      mask &= mask - 1;
-      if (count < a.cap) {
-        const int pos = 1 + count;  // byte position in the record
-        bytes[pos >> 2] &= ~(0xFFu << ((pos & 3) * 8));
-        bytes[pos >> 2] |= (uint32_t)c << ((pos & 3) * 8);
-      }
-      ++count;
-    }
-  }
+  for (int k = 0; k < CPL; ++k) r[k] = __builtin_sqrtf(ss[k] / (float)n);
+  uint32_t bytes[3];
+  record_from_norms<D>(r, a.cap, bytes);
   if (lane == 0) {
-    const int stored = count < a.cap ? count : a.cap;
-    bytes[0] = (bytes[0] & ~0xFFu) | (uint32_t)stored;
     uint32_t* w = reinterpret_cast<uint32_t*>(rec);
     w[0] = bytes[0];
     w[1] = bytes[1];
     w[2] = bytes[2];
+  }
+}
+
+// Per-sequence calibration, second launch: a block this call opens takes the outlier set
+// of its leader row's sequence (the record bytes 0..11 of seq_records) instead of one
+// computed from the call's rows. One thread per (row, head, K|V).
+template <int D>
+__global__ __launch_bounds__(256) void k_fp4_adopt(Fp4Args a) {
+  using TL = Fp4Tile<D>;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)a.num_tokens * a.hkv) return;
+  const int64_t i = idx / a.hkv, h = idx - i * a.hkv;
+  const int64_t slot = a.slots[i];
+  if (slot < 0 || slot >= a.nslots) return;
+  const int64_t bh = (slot >> 4) * a.hkv + h;
+  const int off = (int)(slot & 15);
+  uint8_t* rec = a.side[blockIdx.z].tiles + bh * TL::kBytes + TL::kRecord;
+  const uint32_t pending = ~*reinterpret_cast<const volatile uint32_t*>(rec + 12) & 0xFFFFu;
+  if (!(pending & (1u << off)) || off != __builtin_ctz(pending)) return;  // not the leader
+  const int32_t sq = a.token_seq[i];
+  uint32_t w0 = 0xFFFFFF00u, w1 = 0xFFFFFFFFu, w2 = 0xFFFFFFFFu;  // no outliers
+  if (sq < 0 || sq >= a.num_seqs) {
+    flag(a.err, PA_DEVERR_BAD_CONTEXT);
+  } else {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(
+        a.seq_records + (((int64_t)sq * 2 + blockIdx.z) * a.hkv + h) * 16);
+    w0 = src[0];
+    w1 = src[1];
+    w2 = src[2];
+  }
+  uint32_t* w = reinterpret_cast<uint32_t*>(rec);
+  w[0] = w0;
+  w[1] = w1;
+  w[2] = w2;
+}
+
+// Per-sequence outlier sets: one workgroup (4 waves) per (sequence, head, K|V) sums the
+// squares of the sequence's rows per channel (wave w takes rows w, w + 4, ...; the four
+// partial sums are added in a fixed order), then wave 0 forms the record.
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void k_fp4_seq_outliers(SeqOutlierArgs a) {
+  constexpr int CPL = D / 64;
+  const int sq = blockIdx.x, h = blockIdx.y, side = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint16_t* rows = side ? a.v_rows : a.k_rows;
+  const int64_t r0 = a.row_start[sq], r1 = a.row_start[sq + 1];
+  const bool bad = r0 < 0 || r1 < r0 || r1 > a.num_rows;
+  __shared__ float part[4][D];
+  float ss[CPL];
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) ss[k] = 0.0f;
+  if (!bad) {
+    for (int64_t r = r0 + wave; r < r1; r += 4) {
+      const uint16_t* x = rows + (r * a.hkv + h) * D;
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        const float v = act_to_f32<BF16>(x[lane + 64 * k]);
+        ss[k] = __builtin_fmaf(v, v, ss[k]);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) part[wave][lane + 64 * k] = ss[k];
+  __syncthreads();
+  if (wave != 0) return;
+  uint32_t* out = reinterpret_cast<uint32_t*>(a.records + (((int64_t)sq * 2 + side) * a.hkv + h) * 16);
+  const int64_t n = bad ? 0 : r1 - r0;
+  uint32_t bytes[3] = {0xFFFFFF00u, 0xFFFFFFFFu, 0xFFFFFFFFu};  // no outliers
+  if (n > 0) {
+    float r[CPL];
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const int c = lane + 64 * k;
+      const float tot = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
+      r[k] = __builtin_sqrtf(tot / (float)n);
+    }
+    record_from_norms<D>(r, a.cap, bytes);
+  }
+  if (lane == 0) {
+    if (bad) flag(a.err, PA_DEVERR_BAD_CONTEXT);
+    out[0] = bytes[0];
+    out[1] = bytes[1];
+    out[2] = bytes[2];
+    out[3] = 0xFFFFFFFFu;
   }
 }
 
@@ -555,7 +663,8 @@ __global__ __launch_bounds__(256) void k_reset_records(uint8_t* tiles_k, uint8_t
 static inline unsigned grid1(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
 
 int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool bf16,
-                 int32_t T, const int64_t* slots, int32_t* err, hipStream_t st) {
+                 int32_t T, const int64_t* slots, int32_t* err, hipStream_t st,
+                 const int32_t* token_seq, const uint8_t* seq_records, int32_t num_seqs) {
   const int64_t nslots = (int64_t)p.num_blocks * kBlock;
   const int D = p.head_dim, hkv = p.num_kv_heads;
   if (T == 0) return PA_OK;
@@ -612,14 +721,40 @@ int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool
     a.cap = outlier_capacity(D);
     a.nslots = nslots;
     a.err = err;
-    hipLaunchKernelGGL(k_fp4_mark<128>, dim3(grid1((int64_t)T * hkv, 256), 1, 2), dim3(256), 0,
-                       st, a);
+    a.token_seq = token_seq;
+    a.seq_records = seq_records;
+    a.num_seqs = num_seqs;
+    const dim3 gt(grid1((int64_t)T * hkv, 256), 1, 2);
+    hipLaunchKernelGGL(k_fp4_mark<128>, gt, dim3(256), 0, st, a);
     const dim3 g((unsigned)((T + kRowsPerWg - 1) / kRowsPerWg), hkv, 2);
-    auto cal = bf16 ? k_fp4_calibrate<true, 128> : k_fp4_calibrate<false, 128>;
+    if (seq_records) {
+      hipLaunchKernelGGL(k_fp4_adopt<128>, gt, dim3(256), 0, st, a);
+    } else {
+      auto cal = bf16 ? k_fp4_calibrate<true, 128> : k_fp4_calibrate<false, 128>;
+      hipLaunchKernelGGL(cal, g, dim3(64 * kRowsPerWg), 0, st, a);
+    }
     auto enc = bf16 ? k_fp4_encode<true, 128> : k_fp4_encode<false, 128>;
-    hipLaunchKernelGGL(cal, g, dim3(64 * kRowsPerWg), 0, st, a);
     hipLaunchKernelGGL(enc, g, dim3(64 * kRowsPerWg), 0, st, a);
   }
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int launch_fp4_seq_outliers(const void* k_rows, const void* v_rows, bool bf16, int64_t num_rows,
+                           int32_t hkv, int32_t D, const int32_t* row_start, int32_t num_seqs,
+                           uint8_t* records, int32_t* err, hipStream_t st) {
+  if (D != 128) return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  SeqOutlierArgs a;
+  a.k_rows = (const uint16_t*)k_rows;
+  a.v_rows = (const uint16_t*)v_rows;
+  a.row_start = row_start;
+  a.num_rows = num_rows;
+  a.hkv = hkv;
+  a.cap = outlier_capacity(D);
+  a.records = records;
+  a.err = err;
+  auto kern = bf16 ? k_fp4_seq_outliers<true, 128> : k_fp4_seq_outliers<false, 128>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)num_seqs, hkv, 2), dim3(256), 0, st, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

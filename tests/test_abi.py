@@ -189,6 +189,28 @@ def test_copy_blocks_rejects():
         assert c(_pool(dtype=kv), _pool(dtype=kv, nb=3, base=other)) == MEMORY
 
 
+def test_fp4_sequence_calls_reject():
+    lib = B.lib()
+    f = lambda **k: lib.pa_fp4_sequence_outliers(
+        k.get("k", FAKE), k.get("v", FAKE), k.get("act", 1), k.get("rows", 10), k.get("hkv", 1),
+        k.get("d", 128), k.get("rs", FAKE), k.get("S", 2), k.get("out", FAKE), k.get("err"), None)
+    assert f(act=3) == DTYPE
+    assert f(d=64) == SHAPE and f(rows=-1) == SHAPE and f(S=-1) == SHAPE and f(hkv=0) == SHAPE
+    assert f(S=0) == PA_OK
+    assert f(rs=None) == NULL and f(out=None) == NULL and f(k=None) == NULL
+    assert f(out=FAKE + 4) == ALIGN and f(k=FAKE + 2) == ALIGN and f(err=FAKE + 1) == ALIGN
+    w = lambda pool=None, **k: lib.pa_cache_write_seq_outliers(
+        ctypes.byref(pool if pool is not None else _pool(dtype=3)), FAKE, FAKE, k.get("act", 1),
+        k.get("T", 4), k.get("slots", FAKE), k.get("ts", FAKE), k.get("recs", FAKE),
+        k.get("S", 2), None, None)
+    assert w(pool=_pool(dtype=2)) == DTYPE  # FP4 pools only
+    assert w(act=2) == DTYPE and w(T=-1) == SHAPE and w(S=-1) == SHAPE
+    assert w(T=0) == PA_OK
+    assert w(ts=None) == NULL and w(recs=None) == NULL and w(slots=None) == NULL
+    assert w(recs=FAKE + 4) == ALIGN and w(ts=FAKE + 2) == ALIGN
+    assert w(pool=_pool(dtype=3, fp4=False)) == NULL
+
+
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     monkeypatch.setattr(B, "_LIB_PATH", str(tmp_path / "missing.so"))
