@@ -180,8 +180,9 @@ def workload_of(args, config):
 
 def profile_label(args) -> str:
     """Workload label of the committed profiles: the config name, plus the KV format when
-    it was overridden."""
-    return args.config if args.kv is None else f"{args.config}_{args.kv}"
+    it was overridden and the FP4 calibration when it is per sequence."""
+    label = args.config if args.kv is None else f"{args.config}_{args.kv}"
+    return label + ("_seqcal" if getattr(args, "fp4_calibration", "block") == "sequence" else "")
 
 
 def copy_probe(mib: int):
@@ -438,6 +439,9 @@ def main():
     ap.add_argument("--kv", default=None,
                     choices=["f16", "bf16", "fp8", "bf8", "fp8t", "bf8t", "fp4"],
                     help="override the workload's KV-cache format (same shapes and inputs)")
+    ap.add_argument("--fp4-calibration", default="block", choices=["block", "sequence"],
+                    help="FP4 pools: outlier sets per block (first write) or per sequence "
+                         "(first 512-token prefill chunk)")
     ap.add_argument("--blocks", type=int, default=0, metavar="N",
                     help="time pa_copy_blocks instead: N copies inside the workload's pool "
                          "(copy on write), N blocks out to a pinned host pool and back "
@@ -475,7 +479,8 @@ def main():
     w = workload_of(args, config)
     ps = w.partition_size if args.partition_size is None else args.partition_size
     w.partition_size = ps
-    run = H.DeviceRun(w, device="cuda", partition_size=ps, pool_copies=args.copies)
+    run = H.DeviceRun(w, device="cuda", partition_size=ps, pool_copies=args.copies,
+                      fp4_calibration=args.fp4_calibration)
     run.prepare()
     torch.cuda.synchronize()
     if run.device_error():
@@ -571,7 +576,8 @@ def main():
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": 16, "kv_tokens": dec["tokens"],
                    "partition_size": ps, "step_write_tokens": step_tokens,
-                   "pool_copies": args.copies},
+                   "pool_copies": args.copies}
+                  | ({"fp4_calibration": args.fp4_calibration} if w.kv == "fp4" else {}),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "seq_tokens_per_s": round(dec["tokens"] / t_step, 1),
         "decode_tokens_per_s": round(w.num_seqs / t_step, 1),

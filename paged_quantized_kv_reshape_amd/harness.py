@@ -20,8 +20,19 @@ def _dev_bits(a: np.ndarray, act: str, device) -> torch.Tensor:
 
 
 class DeviceRun:
-    def __init__(self, w, device="cuda", partition_size=None, fill=0xA5, pool_copies=1):
+    """fp4_calibration: "block" (each block's outlier set from its first write) or
+    "sequence" (one set per sequence from its first 512-token prefill chunk, computed on
+    the device with pa_fp4_sequence_outliers; writes go through
+    pa_cache_write_seq_outliers)."""
+
+    SEQ_CHUNK = 512
+
+    def __init__(self, w, device="cuda", partition_size=None, fill=0xA5, pool_copies=1,
+                 fp4_calibration="block"):
+        assert fp4_calibration in ("block", "sequence")
+        assert fp4_calibration == "block" or w.kv == "fp4"
         self.w = w
+        self.fp4_calibration = fp4_calibration
         self.device = device
         self.ps = w.partition_size if partition_size is None else partition_size
         self.q = _dev_bits(w.q, w.act, device)
@@ -45,6 +56,19 @@ class DeviceRun:
         self.step_k = self.k_rows.index_select(0, idx).contiguous()
         self.step_v = self.v_rows.index_select(0, idx).contiguous()
         self.step_slots = torch.from_numpy(sc.slots).to(device)
+        self.seq_records = None
+        if fp4_calibration == "sequence":
+            n = np.minimum(self.SEQ_CHUNK, np.maximum(w.context_lens.astype(np.int64) - 1, 0))
+            rows = np.concatenate([w.seq_start[s] + np.arange(n[s]) for s in range(w.num_seqs)])
+            starts = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+            idx = torch.from_numpy(rows.astype(np.int64)).to(device)
+            self.seq_records = torch.empty((w.num_seqs, 2, w.num_kv_heads, 16), dtype=torch.uint8,
+                                           device=device)
+            B.pa_fp4_sequence_outliers(self.k_rows.index_select(0, idx),
+                                       self.v_rows.index_select(0, idx),
+                                       torch.from_numpy(starts).to(device), self.seq_records,
+                                       self.dev_err)
+            self.step_seq = self._token_seq(sc.rows)
         S, Hq, D = w.q.shape
         self.out = torch.empty((S, Hq, D), dtype=torch.float32, device=device)
         self.lse = torch.empty((S, Hq), dtype=torch.float32, device=device)
@@ -55,17 +79,29 @@ class DeviceRun:
             self.part_lse = torch.empty((S, Hq, P), dtype=torch.float32, device=device)
 
     # -- writes ---------------------------------------------------------------------
+    def _token_seq(self, rows):
+        ts = np.searchsorted(self.w.seq_start, rows, side="right") - 1
+        return torch.from_numpy(ts.astype(np.int32)).to(self.device)
+
+    def _write(self, pool, k, v, slots, token_seq):
+        if self.seq_records is None:
+            B.pa_cache_write(pool, k, v, slots, self.dev_err)
+        else:
+            B.pa_cache_write_seq_outliers(pool, k, v, slots, token_seq, self.seq_records,
+                                          self.dev_err)
+
     def setup_writes(self, pool=None):
         pool = pool or self.pool
         for call in self.w.setup_calls:
             idx = torch.from_numpy(call.rows).to(self.device)
             slots = torch.from_numpy(call.slots).to(self.device)
-            B.pa_cache_write(pool, self.k_rows.index_select(0, idx),
-                             self.v_rows.index_select(0, idx), slots, self.dev_err)
+            ts = self._token_seq(call.rows) if self.seq_records is not None else None
+            self._write(pool, self.k_rows.index_select(0, idx), self.v_rows.index_select(0, idx),
+                        slots, ts)
 
     def step_write(self, pool=None):
-        B.pa_cache_write(pool or self.pool, self.step_k, self.step_v, self.step_slots,
-                         self.dev_err)
+        self._write(pool or self.pool, self.step_k, self.step_v, self.step_slots,
+                    getattr(self, "step_seq", None))
 
     def prepare(self):
         for p in self.pools:
