@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "paged decode attention: achieved KV-read GB/s (% HBM peak) + seq-tokens/s"
 KERNEL_SOURCES = ["paged_quantized_kv_reshape_amd/csrc/pa_decode.hip",
+                  "paged_quantized_kv_reshape_amd/csrc/pa_tile.h",
                   "paged_quantized_kv_reshape_amd/csrc/pa_device.h"]
 
 
@@ -380,7 +381,8 @@ def prefill_main(args, config, DESCRIPTIONS):
                    "head_dim": w.head_dim},
         "algorithmic_flops": flops,
         "wall_ms_per_step": round(wall * 1e3, 4),
-        "roofline": {"kernel": "k_prefill", "bound": "mfma", "achieved": round(tflops, 2),
+        "roofline": {"kernel": "k_prefill" if w.kv == "fp4" else "k_prefill_mt", "bound": "mfma",
+                     "achieved": round(tflops, 2),
                      "peak": 2500.0, "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4),
                      "traffic": None},
     }

@@ -1,0 +1,387 @@
+// pa_prefill.hip - multi-token paged attention on gfx950 for 16-bit and FP8 pools: the
+// queries of a prompt chunk processed after their keys and values were written (chunked
+// prefill, dailyaiworld.com, "vLLM 0.7 Ships Unified KV Cache Compression", engine diagram
+// with 512-token chunks), or the tokens a draft model proposed (inferensys glossary
+// "vLLM", speculative decoding entry). Query i of a sequence with n queries and context L
+// sits at position L - n + i and attends causally to positions 0 .. L - n + i.
+//
+// Work decomposition
+//   grid (query tile x kv head, sequence), 4 waves per workgroup. A wave owns NCT tiles of
+//   16 MFMA columns; a column is one (query, head) pair, the G heads of a query side by
+//   side, so a wave takes 16 NCT / G consecutive queries. It walks the sequence's blocks
+//   two at a time, up to its last query's position, and every tile it loads and converts
+//   feeds all NCT column tiles.
+//
+// Per pair of 16-token blocks A, B (lane l: c = l % 16, kg = l / 16):
+//   S^T = K Q^T   one 16x16x32 MFMA per 32 channels, block and column tile; lane (c, kg)
+//                 then holds column c's logits of tokens 4 kg .. 4 kg + 3 of A and of B;
+//   softmax       per column, base 2, running max and sum, lazy rescale, causal limits
+//                 per column (blocks wholly before the wave's first query need none);
+//   O^T += V^T P^T one 16x16x32 MFMA per 16 output channels and column tile, the k index
+//                 running over the 32 tokens of the pair: k = 8 kg + i holds token
+//                 4 kg + i of A (i < 4) or 4 kg + i - 4 of B (i >= 4) - the order in which
+//                 the lane already holds both its probabilities and its V^T values. P
+//                 enters as a hi + lo pair of 16-bit values (about 16 significant bits).
+#include <type_traits>
+
+#include "pa_device.h"
+#include "pa_launch.h"
+#include "pa_tile.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold, log2 units
+
+// q fragments of one wave in LDS: [NCT][KS][64 lanes] x 16 bytes
+template <int D, int NCT>
+constexpr int q_lds_bytes() { return NCT * (D / 32) * 64 * 16; }
+
+// at least 2 waves per SIMD (256 registers per lane)
+template <int KV, int D, bool QBF, int NCT>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void k_prefill_mt(DecodeArgs a) {
+  using G_ = Geo<KV, D>;
+  constexpr int KS = G_::KS, NT = G_::NT, DL = G_::DL;
+  constexpr bool PVB = QBF;  // PV MFMA type: the query's (FP8 codes are exact in both)
+  static_assert(KV != KV_FP4, "FP4 pools use the decode kernel's multi-query mode");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, kg = lane >> 4;
+  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin by linear id, so
+  // linear id w runs on XCD w % 8; renumbering it xcd * (its share) + w / 8 gives each
+  // XCD a contiguous range of (sequence, query tile) work, and all query tiles of a
+  // sequence meet in one XCD's L2, where its K/V (2 MB at 8192 FP8 tokens) stays resident.
+  unsigned xw, yw;
+  {
+    const unsigned X = gridDim.x, N = X * gridDim.y;
+    const unsigned w = blockIdx.y * X + blockIdx.x;
+    const unsigned per = N / 8, rem = N % 8, xcd = w % 8, k = w / 8;
+    const unsigned wr = xcd < rem ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
+    xw = wr % X;
+    yw = wr / X;
+  }
+  const int kvh = (int)(xw % (unsigned)a.num_kv_heads);
+  const int qt = (int)(xw / (unsigned)a.num_kv_heads);
+  const int s = (int)yw;
+  const int G = a.group, Hq = a.num_q_heads;
+  const int QPW = 16 * NCT / G;  // queries per wave
+
+  const int L = a.context_lens[s];
+  const int q0 = a.query_start[s];
+  const int nq = a.query_start[s + 1] - q0;
+  const int j0 = (qt * kWaves + wave) * QPW;  // first query of this wave
+  const bool rows_ok = q0 >= 0 && nq >= 0 && (int64_t)q0 + nq <= a.num_queries;
+  if (L < 1 || L > a.max_blocks * kBlock || !rows_ok || nq > L || nq > a.max_query_len) {
+    if (lane == 0 && wave == 0 && qt == 0 && kvh == 0 && a.err)
+      atomicOr(a.err, PA_DEVERR_BAD_CONTEXT);
+    if (rows_ok && nq <= a.max_query_len)  // zero this wave's rows
+      for (int j = j0; j < min(j0 + QPW, nq); ++j)
+        for (int i = lane; i < G * D; i += 64)
+          a.out[((int64_t)(q0 + j) * Hq + kvh * G) * D + i] = 0.0f;
+    return;
+  }
+  if (j0 >= nq) return;  // no query for this wave
+
+  // keys [0, end) cover the wave's last query; blocks below nfull precede its first one
+  const int end = L - nq + min(j0 + QPW, nq);
+  const int nblk = (end + kBlock - 1) / kBlock;
+  const int nfull = (L - nq + j0 + 1) / kBlock;
+
+  // ---- this lane's columns: query jq[ct] (head col % G), keys below col_end[ct] ----
+  // The q fragments wait in LDS, each lane reading back only what it wrote (no barrier):
+  // registers go to the accumulators of more column tiles instead.
+  extern __shared__ uint4 q_lds_all[];
+  uint4* const q_lds = q_lds_all + (int64_t)wave * NCT * KS * 64 + lane;
+  int col_end[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int col = 16 * ct + c;
+    const int jq = j0 + col / G;
+    const bool qok = jq < nq;
+    col_end[ct] = qok ? L - nq + jq + 1 : 0;
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
+                          (((int64_t)(q0 + (qok ? jq : 0)) * Hq + kvh * G + col % G) * D +
+                           DL * kg) * 2;
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+      q_lds[(ct * KS + t) * 64] =
+          qok ? reinterpret_cast<const uint4*>(qrow)[t] : make_uint4(0, 0, 0, 0);
+  }
+  float cz = a.sm_scale_log2;
+  if constexpr (head_scaled(KV)) cz *= a.k_scale[kvh];
+
+  // ---- block ids: 64 per register, read with readlane ----
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks;
+  auto load_ids = [&](int chunk) -> int {
+    const int x = chunk * 64 + lane;
+    return x < nblk ? bt[x] : 0;
+  };
+  int ids_a = load_ids(0), ids_b = load_ids(1);
+  const uint8_t* kpool = reinterpret_cast<const uint8_t*>(a.k);
+  const uint8_t* vpool = reinterpret_cast<const uint8_t*>(a.v);
+  const int k_lane_off = c * G_::ROWB + kg * G_::KLANEB;
+  const int v_lane_off = 4 * kg * G_::ROWB + c * G_::VLANEB;
+  int err_bits = 0;
+
+  // block x of the sequence (x < nblk); ids are consumed in order, so the register pair
+  // slides by one chunk when x reaches a multiple of 64
+  auto load_tile = [&](Tile<KV, D>& T, int x) {
+    if (x > 0 && (x & 63) == 0) {
+      ids_a = ids_b;
+      ids_b = load_ids((x >> 6) + 1);
+    }
+    const int b_raw = __builtin_amdgcn_readlane(ids_a, x & 63);
+    T.jb = x;
+    T.ok = (unsigned)b_raw < (unsigned)a.num_blocks;
+    err_bits |= T.ok ? 0 : PA_DEVERR_BAD_BLOCK;
+    T.tile = (int64_t)(T.ok ? b_raw : 0) * a.num_kv_heads + kvh;
+    load_words(T.k, kpool + T.tile * G_::TILEB + k_lane_off);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      load_words(T.v[r], vpool + T.tile * G_::TILEB + v_lane_off + r * G_::ROWB);
+    if constexpr (f8_tok(KV)) {
+      T.sk = reinterpret_cast<const float4*>(kpool + T.tile * G_::TILEB + PA_FP8T_SCALE_OFF(D))[kg];
+      T.sv = reinterpret_cast<const float4*>(vpool + T.tile * G_::TILEB + PA_FP8T_SCALE_OFF(D))[kg];
+    }
+  };
+  // the second block of a last, odd pair: no bytes, every token invalid
+  auto empty_tile = [&](Tile<KV, D>& T, int x) {
+#pragma unroll
+    for (int i = 0; i < G_::KW; ++i) T.k[i] = 0u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < G_::VW; ++i) T.v[r][i] = 0u;
+    T.sk = T.sv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    T.jb = x;
+    T.ok = false;
+    T.tile = 0;
+  };
+
+  // ---- online softmax state, per column tile ----
+  float m[NCT], l[NCT];
+  f32x4 acc[NCT][NT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    m[ct] = -INFINITY;
+    l[ct] = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[ct][n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  bool started = false;  // wave-uniform
+
+  auto compute = [&](Tile<KV, D>& TA, Tile<KV, D>& TB, auto kFull) {
+    constexpr bool FULL = decltype(kFull)::value;
+    if constexpr (!FULL) {
+      // V bytes of tokens past the wave's last key are arbitrary (a NaN code times p = 0
+      // is still NaN): zeroed, with the wave's bound, which holds for every column
+      auto mask_v = [&](Tile<KV, D>& T) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool keep = T.ok && T.jb * kBlock + 4 * kg + r < end;
+#pragma unroll
+          for (int i = 0; i < G_::VW; ++i) T.v[r][i] = keep ? T.v[r][i] : 0u;
+        }
+      };
+      mask_v(TA);
+      mask_v(TB);
+    }
+    // logits of tokens 4 kg .. 4 kg + 3 of one block for column tile ct, masked
+    auto logits = [&](const Tile<KV, D>& T, const f32x4& sa, int ct, float* z) {
+      const int tok0 = T.jb * kBlock + 4 * kg;
+      float sk[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+      if constexpr (f8_tok(KV)) {
+        sk[0] = T.sk.x;
+        sk[1] = T.sk.y;
+        sk[2] = T.sk.z;
+        sk[3] = T.sk.w;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool valid = FULL || (T.ok && tok0 + r < col_end[ct]);
+        z[r] = valid ? sa[r] * sk[r] * cz : -INFINITY;
+      }
+    };
+    // logits of both blocks for every column tile; each K fragment feeds NCT MFMAs
+    f32x4 sacc[2][NCT];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) sacc[b][ct] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      const uint4 ka = k_fragment<KV, D, QBF>(TA, t);
+      const uint4 kb = k_fragment<KV, D, QBF>(TB, t);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const uint4 qf = q_lds[(ct * KS + t) * 64];
+        sacc[0][ct] = mfma_k32(ka, qf, sacc[0][ct], QBF);
+        sacc[1][ct] = mfma_k32(kb, qf, sacc[1][ct], QBF);
+      }
+    }
+    // V^T fragments of both blocks, converted while the QK MFMAs run (no dependence)
+    uint2 vfa[NT], vfb[NT];
+    v_fragments<KV, D, PVB>(TA, vfa);
+    v_fragments<KV, D, PVB>(TB, vfb);
+
+    // masked logits and block maxima of every column tile, then one wave-uniform
+    // decision for a (rare, lazy) rescale of them all
+    float z[NCT][8], mb[NCT];
+    bool grow = false;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      logits(TA, sacc[0][ct], ct, z[ct]);
+      logits(TB, sacc[1][ct], ct, z[ct] + 4);
+      float x = fmaxf(fmaxf(fmaxf(z[ct][0], z[ct][1]), fmaxf(z[ct][2], z[ct][3])),
+                      fmaxf(fmaxf(z[ct][4], z[ct][5]), fmaxf(z[ct][6], z[ct][7])));
+      mb[ct] = group4_max(x);
+      grow = grow || mb[ct] > m[ct] + kRescaleLog2;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const float mn = fmaxf(m[ct], mb[ct]);
+        if (started) {
+          // (-inf - -inf for a column with nothing unmasked yet: its l and acc are 0 and
+          // are left alone)
+          const float alpha = m[ct] == mn ? 1.0f : __builtin_amdgcn_exp2f(m[ct] - mn);
+          l[ct] *= alpha;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) acc[ct][n] *= alpha;
+        }
+        m[ct] = mn;
+      }
+    }
+    started = true;
+
+    uint4 ph[NCT], pl[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // (masked logits are -inf: exp2(-inf - m) = 0 once m is finite; m is -inf only
+        // while every logit of the column so far is masked)
+        const float p = FULL ? __builtin_amdgcn_exp2f(z[ct][i] - m[ct])
+                             : (z[ct][i] == -INFINITY ? 0.0f
+                                                      : __builtin_amdgcn_exp2f(z[ct][i] - m[ct]));
+        l[ct] += p;
+        pv[i] = p;
+      }
+      if constexpr (f8_tok(KV)) {  // PV runs on the codes: p times the V token scale
+        pv[0] *= TA.sv.x;
+        pv[1] *= TA.sv.y;
+        pv[2] *= TA.sv.z;
+        pv[3] *= TA.sv.w;
+        pv[4] *= TB.sv.x;
+        pv[5] *= TB.sv.y;
+        pv[6] *= TB.sv.z;
+        pv[7] *= TB.sv.w;
+      }
+      uint32_t h[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h[i] = pack2(pv[2 * i], pv[2 * i + 1], PVB);
+        lo[i] = pack2(pv[2 * i] - lo16_to_f32(h[i], PVB), pv[2 * i + 1] - hi16_to_f32(h[i], PVB),
+                      PVB);
+      }
+      ph[ct] = make_uint4(h[0], h[1], h[2], h[3]);
+      pl[ct] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const uint4 vop = make_uint4(vfa[n].x, vfa[n].y, vfb[n].x, vfb[n].y);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        acc[ct][n] = mfma_k32(vop, ph[ct], acc[ct][n], PVB);
+        acc[ct][n] = mfma_k32(vop, pl[ct], acc[ct][n], PVB);
+      }
+    }
+  };
+
+  // ---- pairs of blocks: unmasked ones, then the rest (at most two pairs) ----
+  Tile<KV, D> ta, tb;
+  const int npair = (nblk + 1) / 2;
+  auto load_pair = [&](int pi) {
+    load_tile(ta, 2 * pi);
+    if (2 * pi + 1 < nblk)
+      load_tile(tb, 2 * pi + 1);
+    else
+      empty_tile(tb, 2 * pi + 1);
+  };
+  load_pair(0);
+  int pi = 0;
+  for (; pi + 1 < npair && 2 * pi + 2 <= nfull; ++pi) {
+    compute(ta, tb, std::true_type{});
+    load_pair(pi + 1);
+  }
+  for (; pi < npair; ++pi) {
+    compute(ta, tb, std::false_type{});
+    if (pi + 1 < npair) load_pair(pi + 1);
+  }
+
+  // ---- epilogue ----
+  if (err_bits != 0 && lane == 0 && a.err) atomicOr(a.err, err_bits);
+  const float vscale = head_scaled(KV) ? a.v_scale[kvh] : 1.0f;
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int col = 16 * ct + c;
+    const int jq = j0 + col / G;
+    const float lt = group4_sum(l[ct]);
+    if (jq < nq) {
+      const float inv = lt > 0.0f ? vscale / lt : 0.0f;  // 0: every block id was bad
+      float* dst = a.out + ((int64_t)(q0 + jq) * Hq + kvh * G + col % G) * D;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) dst[DL * kg + NT * r + n] = acc[ct][n][r] * inv;
+    }
+  }
+}
+
+template <int KV, int D, bool QBF, int NCT>
+int launch_mt(const DecodeArgs& a, hipStream_t st) {
+  const int qpw = 16 * NCT / a.group;
+  const int per_wg = kWaves * qpw;
+  const int tiles = (a.max_query_len + per_wg - 1) / per_wg;
+  if (tiles == 0 || a.num_seqs == 0) return PA_OK;
+  const dim3 grid((unsigned)((int64_t)tiles * a.num_kv_heads), (unsigned)a.num_seqs, 1);
+  const size_t lds = (size_t)kWaves * q_lds_bytes<D, NCT>();
+  hipLaunchKernelGGL((k_prefill_mt<KV, D, QBF, NCT>), grid, dim3(64 * kWaves), lds, st, a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+template <int KV, int D, bool QBF>
+int launch_kv(const DecodeArgs& a, int nct, hipStream_t st) {
+  return nct == 2 ? launch_mt<KV, D, QBF, 2>(a, st) : launch_mt<KV, D, QBF, 3>(a, st);
+}
+
+template <int D>
+int launch_d(const DecodeArgs& a, int kv, bool qbf, int nct, hipStream_t st) {
+  switch (kv) {
+    case KV_F16: return launch_kv<KV_F16, D, false>(a, nct, st);
+    case KV_BF16: return launch_kv<KV_BF16, D, true>(a, nct, st);
+    case KV_FP8:
+      return qbf ? launch_kv<KV_FP8, D, true>(a, nct, st) : launch_kv<KV_FP8, D, false>(a, nct, st);
+    case KV_BF8:
+      return qbf ? launch_kv<KV_BF8, D, true>(a, nct, st) : launch_kv<KV_BF8, D, false>(a, nct, st);
+    case KV_FP8T:
+      return qbf ? launch_kv<KV_FP8T, D, true>(a, nct, st) : launch_kv<KV_FP8T, D, false>(a, nct, st);
+    case KV_BF8T:
+      return qbf ? launch_kv<KV_BF8T, D, true>(a, nct, st) : launch_kv<KV_BF8T, D, false>(a, nct, st);
+  }
+  return PA_ERR_DTYPE;
+}
+
+}  // namespace
+
+int launch_prefill_mt(const DecodeArgs& a, int kv, bool qbf, int D, int nct, hipStream_t st) {
+  if (kv == KV_FP4) return PA_ERR_DTYPE;
+  return D == 128 ? launch_d<128>(a, kv, qbf, nct, st) : launch_d<64>(a, kv, qbf, nct, st);
+}
+
+}  // namespace pa

@@ -1,0 +1,206 @@
+// pa_tile.h - the paged K/V tile as the attention kernels read it on gfx950: pool formats,
+// per-lane tile geometry, the 16-byte loads of one (block, kv head) tile and the exact
+// conversions of its codes into the 16-bit MFMA operands (internal to libpa).
+//
+// Lane l of a wave (c = l % 16, kg = l / 16) holds, of a 16-token block:
+//   K  token c's channels [D/4 kg, D/4 (kg + 1)) - the A operand of S^T = K Q^T, one
+//      16x16x32 MFMA per 32 channels (k_fragment);
+//   V  tokens 4 kg .. 4 kg + 3 of channels NT c .. NT c + NT - 1 - after an in-register
+//      transpose, the A operand of O^T += V^T P^T (v_fragments).
+#pragma once
+
+#include "../../include/pa.h"
+#include "pa_device.h"
+
+namespace pa {
+
+// pool formats (the pa_kv_dtype values)
+enum { KV_F16 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_FP4 = 3, KV_BF8 = 4, KV_FP8T = 5, KV_BF8T = 6 };
+constexpr bool is_f8(int kv) { return kv == KV_FP8 || kv == KV_BF8 || kv == KV_FP8T || kv == KV_BF8T; }
+constexpr bool f8_e5(int kv) { return kv == KV_BF8 || kv == KV_BF8T; }        // E5M2 codes
+constexpr bool f8_tok(int kv) { return kv == KV_FP8T || kv == KV_BF8T; }      // per-token scales
+constexpr bool head_scaled(int kv) { return kv == KV_FP8 || kv == KV_BF8; }  // per-head scales
+constexpr bool tok_scaled(int kv) { return kv == KV_FP4 || f8_tok(kv); }
+
+template <int KV, int D>
+struct Geo {
+  static constexpr int KS = D / 32;  // QK MFMA steps (k = 32 channels each)
+  static constexpr int NT = D / 16;  // PV MFMA tiles (16 output channels each)
+  static constexpr int DL = D / 4;   // channels per lane in K fragments and outputs
+  static constexpr int EBITS = is_f8(KV) ? 8 : KV == KV_FP4 ? 4 : 16;
+  static constexpr int ROWB = D * EBITS / 8;       // bytes of one token row
+  // bytes between consecutive (block, head) tiles; an FP4 tile also holds its per-token
+  // scales, its outlier record and its first outlier slot after the codes
+  static constexpr int TILEB = KV == KV_FP4   ? PA_FP4_TILE_BYTES(D)
+                               : f8_tok(KV) ? PA_FP8T_TILE_BYTES(D)
+                                            : kBlock * ROWB;
+  static constexpr int KW = DL * EBITS / 32;       // K words per lane
+  static constexpr int VW = NT * EBITS / 32;       // V words per lane per token
+  static constexpr int KLANEB = DL * EBITS / 8;    // K bytes per lane
+  static constexpr int VLANEB = NT * EBITS / 8;    // V bytes per lane per token
+};
+
+template <int N>
+__device__ __forceinline__ void load_words(uint32_t (&w)[N], const uint8_t* p) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const uint4 x = reinterpret_cast<const uint4*>(p)[i];
+      w[4 * i] = x.x;
+      w[4 * i + 1] = x.y;
+      w[4 * i + 2] = x.z;
+      w[4 * i + 3] = x.w;
+    }
+  } else if constexpr (N == 2) {
+    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    w[0] = x.x;
+    w[1] = x.y;
+  } else {
+    static_assert(N == 1, "word count");
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+
+// Hardware conversions (scale 1.0, so exact: every E4M3 and E2M1 value is a bf16 and an
+// fp16 value). SEL picks the 16-bit half (FP8) or the byte (FP4) of the source word.
+template <bool BF, int SEL, bool E5 = false>
+__device__ __forceinline__ uint32_t cvt_fp8x2(uint32_t w) {
+  if constexpr (E5) {  // E5M2 ("bf8")
+    if constexpr (BF)
+      return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, SEL != 0));
+    else
+      return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, SEL != 0));
+  } else if constexpr (BF) {
+    return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, SEL != 0));
+  } else {
+    return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, SEL != 0));
+  }
+}
+template <bool BF, int SEL>
+__device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t w) {
+  if constexpr (BF)
+    return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
+  else
+    return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL));
+}
+
+template <int KV, int D>
+struct Tile {
+  using G_ = Geo<KV, D>;
+  uint32_t k[G_::KW];
+  uint32_t v[4][G_::VW];  // token rows 4 kg .. 4 kg + 3 (FP4: words of one channel chunk)
+  float4 sk, sv;  // FP4 per-token scales of tokens 4 kg .. 4 kg + 3
+  uint32_t r0;    // FP4: first word of the K (lanes 0-31) and V (lanes 32-63) records
+  uint2 k_o0, v_o0;  // FP4 outlier slot 0 of tokens 4 kg .. 4 kg + 3 (fp16), fetched with
+                     // the tile since a full block usually holds exactly one outlier
+  int64_t tile;   // b * Hkv + kv head
+  int jb;         // logical block index in the sequence
+  bool ok;        // block id in range
+};
+
+// 16-bit K fragment for step t: 8 values of channels D/4 kg + 8 t + (0..7).
+template <int KV, int D, bool QBF>
+__device__ __forceinline__ uint4 k_fragment(const Tile<KV, D>& T, int t) {
+  if constexpr (KV == KV_F16 || KV == KV_BF16) {
+    return make_uint4(T.k[4 * t], T.k[4 * t + 1], T.k[4 * t + 2], T.k[4 * t + 3]);
+  } else if constexpr (is_f8(KV)) {
+    constexpr bool E5 = f8_e5(KV);
+    const uint32_t a = T.k[2 * t], b = T.k[2 * t + 1];
+    return make_uint4(cvt_fp8x2<QBF, 0, E5>(a), cvt_fp8x2<QBF, 1, E5>(a),
+                      cvt_fp8x2<QBF, 0, E5>(b), cvt_fp8x2<QBF, 1, E5>(b));
+  } else {
+    const uint32_t a = T.k[t];
+    return make_uint4(cvt_fp4x2<QBF, 0>(a), cvt_fp4x2<QBF, 1>(a), cvt_fp4x2<QBF, 2>(a),
+                      cvt_fp4x2<QBF, 3>(a));
+  }
+}
+
+// V^T fragments: vf[n] = channel NT c + n of tokens 4 kg .. 4 kg + 3 as four 16-bit values
+// (tokens 0,1 in the low word, 2,3 in the high word).
+template <int KV, int D, bool PVB>
+__device__ __forceinline__ void v_fragments(const Tile<KV, D>& T, uint2 (&vf)[Geo<KV, D>::NT]) {
+  constexpr int NT = Geo<KV, D>::NT;
+  if constexpr (KV == KV_FP4) {
+    // V is stored by channel: word w of the lane's chunk holds channels 2w, 2w+1, each as
+    // two bytes of token pairs (4 kg, 4 kg + 1) and (4 kg + 2, 4 kg + 3); one conversion
+    // per byte gives a fragment half directly
+#pragma unroll
+    for (int w = 0; w < NT / 2; ++w) {
+      vf[2 * w].x = cvt_fp4x2<true, 0>(T.v[w][0]);
+      vf[2 * w].y = cvt_fp4x2<true, 1>(T.v[w][0]);
+      vf[2 * w + 1].x = cvt_fp4x2<true, 2>(T.v[w][0]);
+      vf[2 * w + 1].y = cvt_fp4x2<true, 3>(T.v[w][0]);
+    }
+  } else if constexpr (KV == KV_F16 || KV == KV_BF16) {
+    // pairs[r][i] = 16-bit channels (2i, 2i+1) of token r
+    uint32_t pairs[4][NT / 2];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int i = 0; i < NT / 2; ++i) pairs[r][i] = T.v[r][i];
+    }
+#pragma unroll
+    for (int i = 0; i < NT / 2; ++i) {
+      vf[2 * i].x = __builtin_amdgcn_perm(pairs[1][i], pairs[0][i], 0x05040100u);
+      vf[2 * i].y = __builtin_amdgcn_perm(pairs[3][i], pairs[2][i], 0x05040100u);
+      vf[2 * i + 1].x = __builtin_amdgcn_perm(pairs[1][i], pairs[0][i], 0x07060302u);
+      vf[2 * i + 1].y = __builtin_amdgcn_perm(pairs[3][i], pairs[2][i], 0x07060302u);
+    }
+  } else {
+    // FP8: 4x4 byte transposes, then one conversion per token pair.
+#pragma unroll
+    for (int wi = 0; wi < Geo<KV, D>::VW; ++wi) {
+      const uint32_t x0 = T.v[0][wi], x1 = T.v[1][wi], x2 = T.v[2][wi], x3 = T.v[3][wi];
+      const uint32_t u0 = __builtin_amdgcn_perm(x1, x0, 0x05010400u);  // x0b0 x1b0 x0b1 x1b1
+      const uint32_t u1 = __builtin_amdgcn_perm(x1, x0, 0x07030602u);  // x0b2 x1b2 x0b3 x1b3
+      const uint32_t w0 = __builtin_amdgcn_perm(x3, x2, 0x05010400u);
+      const uint32_t w1 = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
+      const uint32_t t[4] = {
+          __builtin_amdgcn_perm(w0, u0, 0x05040100u),  // channel 0 of tokens 0..3
+          __builtin_amdgcn_perm(w0, u0, 0x07060302u),  // channel 1
+          __builtin_amdgcn_perm(w1, u1, 0x05040100u),  // channel 2
+          __builtin_amdgcn_perm(w1, u1, 0x07060302u)}; // channel 3
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        vf[4 * wi + c].x = cvt_fp8x2<PVB, 0, f8_e5(KV)>(t[c]);
+        vf[4 * wi + c].y = cvt_fp8x2<PVB, 1, f8_e5(KV)>(t[c]);
+      }
+    }
+  }
+}
+
+
+
+// V^T fragments of one channel group, for kernels that consume V a group at a time:
+// group g of a 16-bit tile gives vf[j] = v_fragments' vf[2 g + j] (j < 2), of an FP8 tile
+// vf[j] = vf[4 g + j] (j < 4). kVGroup is the group size.
+template <int KV>
+constexpr int kVGroup = is_f8(KV) ? 4 : 2;
+template <int KV, int D, bool PVB, int GI>
+__device__ __forceinline__ void v_fragments_group(const Tile<KV, D>& T, uint2 (&vf)[kVGroup<KV>]) {
+  static_assert(KV != KV_FP4, "FP4 V fragments come from channel chunks");
+  if constexpr (KV == KV_F16 || KV == KV_BF16) {
+    const uint32_t p0 = T.v[0][GI], p1 = T.v[1][GI], p2 = T.v[2][GI], p3 = T.v[3][GI];
+    vf[0].x = __builtin_amdgcn_perm(p1, p0, 0x05040100u);
+    vf[0].y = __builtin_amdgcn_perm(p3, p2, 0x05040100u);
+    vf[1].x = __builtin_amdgcn_perm(p1, p0, 0x07060302u);
+    vf[1].y = __builtin_amdgcn_perm(p3, p2, 0x07060302u);
+  } else {
+    const uint32_t x0 = T.v[0][GI], x1 = T.v[1][GI], x2 = T.v[2][GI], x3 = T.v[3][GI];
+    const uint32_t u0 = __builtin_amdgcn_perm(x1, x0, 0x05010400u);
+    const uint32_t u1 = __builtin_amdgcn_perm(x1, x0, 0x07030602u);
+    const uint32_t w0 = __builtin_amdgcn_perm(x3, x2, 0x05010400u);
+    const uint32_t w1 = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
+    const uint32_t t[4] = {__builtin_amdgcn_perm(w0, u0, 0x05040100u),
+                           __builtin_amdgcn_perm(w0, u0, 0x07060302u),
+                           __builtin_amdgcn_perm(w1, u1, 0x05040100u),
+                           __builtin_amdgcn_perm(w1, u1, 0x07060302u)};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      vf[c].x = cvt_fp8x2<PVB, 0, f8_e5(KV)>(t[c]);
+      vf[c].y = cvt_fp8x2<PVB, 1, f8_e5(KV)>(t[c]);
+    }
+  }
+}
+
+}  // namespace pa
