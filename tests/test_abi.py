@@ -138,6 +138,28 @@ def test_decode_rejects():
     assert _decode(S=0) == PA_OK  # empty batch: nothing to launch
 
 
+def _prefill(pool=None, q=FAKE, qd=1, S=2, Hq=8, T=10, qs=FAKE, mq=5, bt=FAKE, MB=4,
+             cl=FAKE, out=FAKE):
+    pool = pool if pool is not None else _pool()
+    return B.lib().pa_prefill(q, qd, S, Hq, T, qs, mq, ctypes.byref(pool), bt, MB, cl, 0.1, out,
+                              None, None)
+
+
+def test_prefill_rejects():
+    assert _prefill(pool=_pool(bs=32)) == BLOCK
+    assert _prefill(qd=3) == DTYPE
+    assert _prefill(pool=_pool(dtype=0), qd=1) == DTYPE
+    assert _prefill(pool=_pool(hkv=1), Hq=3) == SHAPE      # group 3 does not divide 16
+    assert _prefill(pool=_pool(hkv=1), Hq=32) == SHAPE     # group 32 > 16
+    assert _prefill(pool=_pool(hkv=3), Hq=8) == SHAPE      # Hq % Hkv != 0
+    assert _prefill(S=-1) == SHAPE and _prefill(T=-1) == SHAPE and _prefill(mq=-1) == SHAPE
+    assert _prefill(MB=0) == CONTEXT
+    assert _prefill(q=None) == NULL and _prefill(qs=None) == NULL and _prefill(out=None) == NULL
+    assert _prefill(bt=None) == NULL and _prefill(cl=None) == NULL
+    assert _prefill(q=FAKE + 4) == ALIGN and _prefill(out=FAKE + 4) == ALIGN
+    assert _prefill(S=0) == PA_OK  # nothing to launch
+
+
 def test_merge_and_scale_and_reset_reject():
     lib = B.lib()
     m = lambda **k: lib.pa_merge(k.get("po", FAKE), k.get("pl", FAKE), k.get("cl", FAKE),

@@ -238,6 +238,33 @@ def test_gqa_group_sizes(kv, hq, ps):
 
 
 @pytest.mark.parametrize("ps", [0, 128])
+@pytest.mark.parametrize("hq,hkv", [(6, 2), (5, 1), (24, 2)])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "fp8t", "fp4"])
+def test_gqa_groups_not_powers_of_two(kv, hq, hkv, ps):
+    """Query-head groups of 3, 5 and 12: the MFMA column tile holds G real heads and
+    16 - G padding columns (the FP4 kernel's 8-column LDS layout for G <= 8, 16 above)."""
+    from paged_quantized_kv_reshape_amd.harness import DeviceRun
+    base = "c5" if kv == "fp4" else "c4"
+    over = dict(num_seqs=3, lens=[300, 77, 16], num_q_heads=hq, num_kv_heads=hkv)
+    if kv == "bf16":
+        over.update(kv="bf16", planted=False)
+    elif kv == "fp8t":
+        over.update(kv="fp8t")
+    w = config(base, **over)
+    _say(f"[gqa odd] {kv} Hq={hq} Hkv={hkv} ps={ps}")
+    run = DeviceRun(w, partition_size=ps)
+    run.prepare()
+    run.decode()
+    torch.cuda.synchronize()
+    assert run.device_error() == 0
+    pool, ks, vs, near = replay(w)
+    assert_pool_equal(run.pool.numpy(), pool, near=near)
+    ref = oracle_decode(w, pool, ks, vs, range(w.num_seqs))
+    assert_close(run.out.cpu().numpy(), np.stack([ref[s][0] for s in range(w.num_seqs)]),
+                 f"{kv} Hq={hq} Hkv={hkv} ps={ps}")
+
+
+@pytest.mark.parametrize("ps", [0, 128])
 @pytest.mark.parametrize("kv,act,d", [("fp8", "f16", 128), ("fp4", "f16", 128),
                                       ("fp8", "bf16", 64), ("fp8", "f16", 64),
                                       ("f16", "f16", 128), ("bf16", "bf16", 64)])
