@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Bench: one step of the paged, quantized KV-cache hot path on one MI355X.
 
-A step is the whole path over one batch of synthetic input: the step's cache write
-(pa_cache_write of the new K/V rows), the paged decode (pa_decode) and, when the context
-is split into partitions, the log-sum-exp merge (pa_merge). The default workload is the
+A step is the whole path over one batch of synthetic input: the step's cache write of the
+new K/V rows, the paged decode and, when the context is split into partitions, the
+log-sum-exp merge (pa_merge). Where one new token per sequence goes to its last position
+in a 16-bit or FP8 pool, the write and the decode run as one pa_append_decode launch;
+otherwise (FP4 pools, or --separate-write) as pa_cache_write + pa_decode. The default workload is the
 Llama-3.1-70B tensor-parallel one-GPU share: 256 sequences of 8192 tokens, 8 query heads
 over 1 kv head, head_dim 128, FP8 E4M3 KV cache (xonoai.com field report on vLLM v0.7.2,
 "Comparative Inference Engine Performance": 256 concurrent 8k-token streams of the 70B
@@ -12,7 +14,7 @@ several copies, rotated step by step, so that no step finds its KV in the 256 MB
 Infinity Cache left warm by the step before.
 
 Prints one JSON line: value = algorithmic bytes of the step / step time (GB/s), plus the
-decode kernel's roofline (its algorithmic bytes / its average launch time from HIP events
+dominant kernel's roofline (its algorithmic bytes / its average launch time from HIP events
 on the launch stream) and the oracle's rate on the host cores (cpu_baseline).
 
     python bench.py [--steps K] [--warmup W] [--config c4] [--partition-size PS]
@@ -96,9 +98,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def decode_kernel_name(kv: str) -> str:
-    """The decode kernel that runs for a pool format (FP4 has its own entry point)."""
-    return "k_decode_fp4" if kv == "fp4" else "k_decode"
+def decode_kernel_name(kv: str, fused: bool = False) -> str:
+    """The decode kernel that runs for a pool format (FP4 has its own entry point); with
+    the step fused into one launch (pa_append_decode) its append variant."""
+    return "k_decode_fp4" if kv == "fp4" else "k_decode_append" if fused else "k_decode"
 
 
 def counter_traffic(kernel: str, cfg: str, ps: int):
@@ -441,6 +444,9 @@ def main():
     ap.add_argument("--kv", default=None,
                     choices=["f16", "bf16", "fp8", "bf8", "fp8t", "bf8t", "fp4"],
                     help="override the workload's KV-cache format (same shapes and inputs)")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="run the step as pa_cache_write + pa_decode even where one "
+                         "pa_append_decode launch can do both")
     ap.add_argument("--fp4-calibration", default="block", choices=["block", "sequence"],
                     help="FP4 pools: outlier sets per block (first write) or per sequence "
                          "(first 512-token prefill chunk)")
@@ -498,10 +504,15 @@ def main():
     if args.copy_probe_mib:
         copy_probe(args.copy_probe_mib)
 
+    # The step: one pa_append_decode launch (+ merge) where the pool format and the step's
+    # write allow it (one new token per sequence, at its last position), else
+    # pa_cache_write + pa_decode (+ merge).
+    fused = run.can_append and not args.separate_write
+    step = run.step_fused if fused else run.step
     # every libpa call goes on torch's current stream; the events are recorded on it too
     stream = torch.cuda.current_stream().cuda_stream
     for i in range(args.warmup):
-        run.step(run.pools[i % args.copies])
+        step(run.pools[i % args.copies])
     torch.cuda.synchronize()
 
     K = args.steps
@@ -510,17 +521,18 @@ def main():
     def pool_of(i):
         return run.pools[(args.warmup + i) % args.copies]
 
-    # (1) the timed region: K whole steps, events only at step boundaries
-    bounds = [timer.event() for _ in range(K + 1)]
+    # (1) the timed region: K whole steps back to back, one event pair around all of them
+    # (a marker between steps would sit between the kernels and add its own latency)
+    bounds = [timer.event(), timer.event()]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    timer.record(bounds[0], stream)
     for i in range(K):
-        timer.record(bounds[i], stream)
-        run.step(pool_of(i))
-    timer.record(bounds[K], stream)
+        step(pool_of(i))
+    timer.record(bounds[1], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_step_ev = timer.ms(bounds[0], bounds[K]) * 1e-3 / K
+    t_step_ev = timer.ms(bounds[0], bounds[1]) * 1e-3 / K
     err = run.device_error()
     out = run.out.cpu().numpy()
     if err or not np.isfinite(out).all():
@@ -528,22 +540,31 @@ def main():
 
     # (2) per-kernel attribution: the same K steps with an event around every kernel (each
     # bracket also holds the runtime's dispatch latency, a few microseconds)
+    # (fused: no write kernel, the first bracket is empty)
     ev = [[timer.event() for _ in range(4)] for _ in range(K)]
     for i in range(K):
         e = ev[i]
         timer.record(e[0], stream)
-        run.step_write(pool_of(i))
+        if not fused:
+            run.step_write(pool_of(i))
         timer.record(e[1], stream)
-        run.decode(pool_of(i), merge=False)
+        if fused:
+            run.append_decode(pool_of(i), merge=False)
+        else:
+            run.decode(pool_of(i), merge=False)
         timer.record(e[2], stream)
         run.merge()
         timer.record(e[3], stream)
-    # (3) the dominant kernel's launch duration: K decode launches back to back (same
-    # pools, same stream) between one pair of events, so no marker sits between them
+    # (3) the dominant kernel's launch duration: K launches back to back (same pools, same
+    # stream) between one pair of events, so no marker sits between them (fused: each
+    # launch writes the same rows again, then decodes)
     burst = [timer.event(), timer.event()]
     timer.record(burst[0], stream)
     for i in range(K):
-        run.decode(pool_of(i), merge=False)
+        if fused:
+            run.append_decode(pool_of(i), merge=False)
+        else:
+            run.decode(pool_of(i), merge=False)
     timer.record(burst[1], stream)
     torch.cuda.synchronize()
     t_write = float(np.mean([timer.ms(e[0], e[1]) for e in ev])) * 1e-3
@@ -555,9 +576,10 @@ def main():
         raise SystemExit(f"device error during timing: {run.device_error()}")
 
     t_step = wall / K
-    dec_gbs = dec["total"] / t_dec / 1e9
+    kernel_bytes = step_bytes if fused else dec["total"]  # the fused kernel also writes
+    dec_gbs = kernel_bytes / t_dec / 1e9
     value = step_bytes / t_step / 1e9
-    traffic = counter_traffic(decode_kernel_name(w.kv), profile_label(args), ps)
+    traffic = counter_traffic(decode_kernel_name(w.kv, fused), profile_label(args), ps)
 
     res = {
         "metric": METRIC,
@@ -578,6 +600,8 @@ def main():
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": 16, "kv_tokens": dec["tokens"],
                    "partition_size": ps, "step_write_tokens": step_tokens,
+                   "step": ("pa_append_decode (write + decode, one launch)" if fused
+                            else "pa_cache_write + pa_decode") + (" + pa_merge" if ps else ""),
                    "pool_copies": args.copies}
                   | ({"fp4_calibration": args.fp4_calibration} if w.kv == "fp4" else {}),
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
@@ -585,14 +609,15 @@ def main():
         "decode_tokens_per_s": round(w.num_seqs / t_step, 1),
         "step_bytes": step_bytes,
         "kernel_ms": {"decode": round(t_dec * 1e3, 4),
-                      "bracketed": {"cache_write": round(t_write * 1e3, 4),
+                      "bracketed": {"cache_write": round(t_write * 1e3, 4) if not fused else 0.0,
                                     "decode": round(t_dec_br * 1e3, 4),
                                     "merge": round(t_merge * 1e3, 4)},
                       "step_events": round(t_step_ev * 1e3, 4)},
-        "roofline": {"kernel": decode_kernel_name(w.kv), "bound": "hbm", "achieved": round(dec_gbs, 2),
+        "roofline": {"kernel": decode_kernel_name(w.kv, fused), "bound": "hbm",
+                     "achieved": round(dec_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "algorithmic_bytes": dec["total"],
+                     "algorithmic_bytes": kernel_bytes,
                      "traffic": traffic},
     }
     if not args.no_cpu_baseline:

@@ -339,6 +339,26 @@ int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
               float* part_out, float* part_lse, int32_t* dev_err, void* stream);
 
 /*
+ * One decode step in one launch: sequence s's new key and value rows, k_new[s] and v_new[s]
+ * ([num_seqs, num_kv_heads, head_dim], q_dtype), are stored at its last position
+ * L_s - 1 (slot block_tables[s][(L_s - 1) / 16] * 16 + (L_s - 1) % 16), byte for byte as
+ * pa_cache_write stores them, and the sequence then attends over its L_s tokens exactly as
+ * pa_decode. The cache write and the decode of a serving step (dailyaiworld.com, engine
+ * diagram: new tokens go to the cache, then Flash-Decoding reads it) without a second
+ * launch: the workgroup that reads position L_s - 1 writes it first. Pools: 16-bit and the
+ * four FP8 formats; an FP4 pool returns PA_ERR_DTYPE (its first write into a block
+ * calibrates over all rows a call puts there: use pa_cache_write, then pa_decode). A
+ * block id outside the pool at that position is flagged and nothing is written there.
+ * All other arguments, shapes and rules as pa_decode. Asynchronous on `stream`.
+ */
+int pa_append_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                     const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, float sm_scale, int32_t partition_size,
+                     float* out, float* part_out, float* part_lse, int32_t* dev_err,
+                     void* stream);
+
+/*
  * Paged attention for several query tokens per sequence, over the same pool: a chunk of a
  * long prompt processed after its keys and values were written (chunked prefill,
  * dailyaiworld.com, "vLLM 0.7 Ships Unified KV Cache Compression", engine diagram with

@@ -76,6 +76,8 @@ def lib():
             "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
             "pa_read_device_error": (ctypes.c_int, [vp, vp, vp]),
             "pa_copy_blocks": (ctypes.c_int, [pool_p, pool_p, vp, i32, vp, vp]),
+            "pa_append_decode": (ctypes.c_int, [vp, i32, i32, i32, pool_p, vp, vp, vp, i32, vp,
+                                                f32, i32, vp, vp, vp, vp, vp]),
             "pa_fp4_sequence_outliers": (ctypes.c_int, [vp, vp, i32, i64, i32, i32, vp, i32, vp,
                                                         vp, vp]),
             "pa_cache_write_seq_outliers": (ctypes.c_int, [pool_p, vp, vp, i32, i32, vp, vp, vp,
@@ -320,6 +322,21 @@ def pa_decode(q, pool: KVPool, block_tables, context_lens, sm_scale, partition_s
         _ptr(q), ACT_DTYPES[q.dtype], S, Hq, ctypes.byref(s), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), float(sm_scale), partition_size, _ptr(out),
         _ptr(part_out), _ptr(part_lse), _ptr(dev_err), _stream()))
+
+
+def pa_append_decode(q, pool: KVPool, k_new, v_new, block_tables, context_lens, sm_scale,
+                     partition_size=0, out=None, part_out=None, part_lse=None, dev_err=None):
+    """pa_decode after writing each sequence's new row k_new[s] / v_new[s] ([S, Hkv, D],
+    q's dtype) at its last position, in one launch (16-bit and FP8 pools)."""
+    assert q.dtype in ACT_DTYPES and k_new.dtype == q.dtype and v_new.dtype == q.dtype
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    assert k_new.is_contiguous() and v_new.is_contiguous()
+    S, Hq, _ = q.shape
+    s = pool.struct()
+    _check("pa_append_decode", lib().pa_append_decode(
+        _ptr(q), ACT_DTYPES[q.dtype], S, Hq, ctypes.byref(s), _ptr(k_new), _ptr(v_new),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), float(sm_scale),
+        partition_size, _ptr(out), _ptr(part_out), _ptr(part_lse), _ptr(dev_err), _stream()))
 
 
 def pa_prefill(q, query_start, max_query_len, pool: KVPool, block_tables, context_lens,

@@ -265,10 +265,16 @@ int pa_copy_blocks(const pa_kv_pool* src, const pa_kv_pool* dst, const int32_t* 
   return pa::launch_copy_blocks(a, (hipStream_t)stream);
 }
 
-int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
-              const pa_kv_pool* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
-              const int32_t* context_lens, float sm_scale, int32_t partition_size, float* out,
-              float* part_out, float* part_lse, int32_t* dev_err, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// pa_decode and pa_append_decode: k_new / v_new NULL for the former
+int decode_call(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                const int32_t* context_lens, float sm_scale, int32_t partition_size, float* out,
+                float* part_out, float* part_lse, int32_t* dev_err, void* stream) {
   int st = check_pool(pool);
   if (st != PA_OK) return st;
   if (!act_ok(q_dtype) || !act_matches_pool(q_dtype, pool->dtype)) return PA_ERR_DTYPE;
@@ -294,11 +300,13 @@ int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
     if (!aligned(part_out, 16) || !aligned(part_lse, 4)) return PA_ERR_ALIGN;
   }
   if (!aligned(q, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
-      !aligned(dev_err, 4))
+      !aligned(dev_err, 4) || !aligned(k_new, 16) || !aligned(v_new, 16))
     return PA_ERR_ALIGN;
 
   pa::DecodeArgs a{};
   a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.k = pool->k;
   a.v = pool->v;
   a.k_out_val = pool->k_out_val;
@@ -341,6 +349,32 @@ int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
   if (forced == 1 || forced == 2 || forced == 4 || forced == 8) waves = forced;
   return pa::launch_decode(a, pool->dtype, q_dtype == PA_ACT_BF16, pool->head_dim, waves,
                            (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+              const pa_kv_pool* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, float sm_scale, int32_t partition_size, float* out,
+              float* part_out, float* part_lse, int32_t* dev_err, void* stream) {
+  return decode_call(q, q_dtype, num_seqs, num_q_heads, pool, nullptr, nullptr, block_tables,
+                     max_blocks_per_seq, context_lens, sm_scale, partition_size, out, part_out,
+                     part_lse, dev_err, stream);
+}
+
+int pa_append_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                     const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, float sm_scale, int32_t partition_size,
+                     float* out, float* part_out, float* part_lse, int32_t* dev_err,
+                     void* stream) {
+  if (pool && pool->dtype == PA_KV_FP4_E2M1_OUTL) return PA_ERR_DTYPE;
+  if (num_seqs > 0 && (!k_new || !v_new)) return PA_ERR_NULL;
+  return decode_call(q, q_dtype, num_seqs, num_q_heads, pool, k_new, v_new, block_tables,
+                     max_blocks_per_seq, context_lens, sm_scale, partition_size, out, part_out,
+                     part_lse, dev_err, stream);
 }
 
 int pa_prefill(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,

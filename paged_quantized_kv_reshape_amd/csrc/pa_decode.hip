@@ -39,6 +39,7 @@
 #include <type_traits>
 
 #include "pa_device.h"
+#include "pa_encode.h"
 #include "pa_launch.h"
 #include "pa_tile.h"
 
@@ -57,6 +58,48 @@ template <int D, int GP>
 constexpr int fp4_side_floats() { return (D + (GP < 16 ? D / 4 : 0)) * GP; }
 
 
+// pa_append_decode: the workgroup that reads sequence s's last position writes the
+// sequence's new row there first, for its kv head, exactly as the cache-write kernels
+// store it (16-bit copy, FP8 with the head's scale, FP8 with the row's own scale). K uses
+// lanes [0, R) and V lanes [R, 2R) of one wave, R lanes per row.
+template <int KV, int D, bool QBF>
+__device__ __forceinline__ void append_row(const DecodeArgs& a, int s, int kvh, int b, int off) {
+  using G_ = Geo<KV, D>;
+  constexpr int R = is_f8(KV) ? D / 16 : D * 2 / 16;  // lanes per row
+  static_assert(2 * R <= 64, "one wave writes the row");
+  const int t = threadIdx.x & 63;
+  if (t >= 2 * R) return;
+  const bool vside = t >= R;
+  const int c = t - (vside ? R : 0);
+  const uint4* src = reinterpret_cast<const uint4*>(vside ? a.v_new : a.k_new) +
+                     ((int64_t)s * a.num_kv_heads + kvh) * (D * 2 / 16);
+  uint8_t* tile = reinterpret_cast<uint8_t*>(const_cast<void*>(vside ? a.v : a.k)) +
+                  ((int64_t)b * a.num_kv_heads + kvh) * G_::TILEB;
+  if constexpr (KV == KV_F16 || KV == KV_BF16) {
+    reinterpret_cast<uint4*>(tile + off * G_::ROWB)[c] = src[c];
+  } else {
+    constexpr bool E5 = f8_e5(KV);
+    const uint4 lo = src[2 * c], hi = src[2 * c + 1];
+    float sc;
+    if constexpr (f8_tok(KV)) {
+      // the row's absmax over its R threads (consecutive lanes, R divides 64)
+      const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      float mx = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        mx = fmaxf(mx, __builtin_fabsf(act_to_f32<QBF>((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu)));
+#pragma unroll
+      for (int o = R / 2; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+      sc = mx / (E5 ? 57344.0f : 448.0f);
+      if (c == 0) reinterpret_cast<float*>(tile + PA_FP8T_SCALE_OFF(D))[off] = sc;
+    } else {
+      sc = vside ? a.v_scale[kvh] : a.k_scale[kvh];
+    }
+    const bool fast = __builtin_fabsf(sc) >= 0x1p-80f && __builtin_fabsf(sc) <= 0x1p100f;
+    *reinterpret_cast<uint4*>(tile + off * D + 16 * c) = fp8_encode16<QBF, E5>(lo, hi, sc, fast);
+  }
+}
+
 // The decode of one workgroup. DB selects the block loop: false keeps one tile in flight
 // (the next tile is loaded after the current one is consumed; the other waves of the
 // compute unit cover the latency), true double-buffers (the next tile's loads are issued
@@ -64,7 +107,7 @@ constexpr int fp4_side_floats() { return (D + (GP < 16 ? D / 4 : 0)) * GP; }
 // MQ selects multi-token queries (chunked prefill, draft verification): each wave owns 16
 // MFMA columns, one per (query, head), and walks every block up to its last query's
 // position with causal masks; there is no split and no merge.
-template <int KV, int D, bool QBF, int GP, bool DB, bool MQ>
+template <int KV, int D, bool QBF, int GP, bool DB, bool MQ, bool APPEND = false>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   using G_ = Geo<KV, D>;
   constexpr int KS = G_::KS, NT = G_::NT, DL = G_::DL;
@@ -128,6 +171,28 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     return;
   }
   if (MQ && j0 >= nq) return;  // no query for this wave
+  if constexpr (APPEND) {
+    static_assert(!MQ && KV != KV_FP4, "append: single-query decode, 16-bit and FP8 pools");
+    // The wave that will read position L - 1 (the partition's blocks go round-robin to
+    // the workgroup's waves) writes the new row there first. No other wave or workgroup
+    // reads that (block, kv head) tile in this launch and this wave has not loaded it
+    // yet, so a fence at workgroup scope is enough: its release waits for the stores to
+    // reach L2, its acquire orders the wave's later loads after them. The other waves do
+    // not wait. (A device-scope fence would also write back and invalidate the XCD's L2:
+    // measured, that cost the c4 decode 60% of its speed.)
+    const int pos = L - 1;
+    const int start_blk = split ? p * (a.partition_size / kBlock) : 0;
+    const bool here = !split || p == pos / a.partition_size;  // uniform over the workgroup
+    if (here && wave == (pos / kBlock - start_blk) % W) {
+      const int32_t b = a.block_tables[(int64_t)s * a.max_blocks + pos / kBlock];
+      if ((unsigned)b < (unsigned)a.num_blocks)
+        append_row<KV, D, QBF>(a, s, kvh, b, pos % kBlock);
+      else if (lane == 0 && a.err)
+        atomicOr(a.err, PA_DEVERR_BAD_BLOCK);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+  }
   // the blocks this wave reads: its share of the partition (decode, blocks w, w + W, ...),
   // or every block up to its last query's position (MQ)
   int start, end;
@@ -587,9 +652,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 
 // 16-bit and FP8 pools: one tile in flight per wave, occupancy left to the register count
 // (5 waves per SIMD for FP8 at head_dim 128).
-template <int KV, int D, bool QBF, int GP>
+template <int KV, int D, bool QBF, int GP, bool APPEND = false>
 __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
-  decode_body<KV, D, QBF, GP, false, false>(a);
+  decode_body<KV, D, QBF, GP, false, false, APPEND>(a);
 }
 
 // FP4 pools: a tile is half the bytes of an FP8 one, so one tile per wave leaves too little
@@ -629,10 +694,14 @@ static int launch_one(const DecodeArgs& a, int waves, hipStream_t st) {
   while (waves > 1 && decode_lds_bytes<KV, D, GP>(waves) > (size_t)max_lds) waves /= 2;
   const size_t lds = decode_lds_bytes<KV, D, GP>(waves);
   const dim3 grid((unsigned)((int64_t)P * a.num_kv_heads), (unsigned)a.num_seqs, 1);
-  if constexpr (KV == KV_FP4)
+  if constexpr (KV == KV_FP4) {
+    if (a.k_new) return PA_ERR_DTYPE;  // no append for FP4 pools
     hipLaunchKernelGGL((k_decode_fp4<D, QBF, GP>), grid, dim3(64 * waves), lds, st, a);
-  else
-    hipLaunchKernelGGL((k_decode<KV, D, QBF, GP>), grid, dim3(64 * waves), lds, st, a);
+  } else if (a.k_new) {
+    hipLaunchKernelGGL((k_decode<KV, D, QBF, GP, true>), grid, dim3(64 * waves), lds, st, a);
+  } else {
+    hipLaunchKernelGGL((k_decode<KV, D, QBF, GP, false>), grid, dim3(64 * waves), lds, st, a);
+  }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

@@ -41,6 +41,10 @@ struct DecodeArgs {
   float* part_out;  // [S, Hq, P, D] otherwise
   float* part_lse;  // [S, Hq, P]
   int32_t* err;
+  // decode with append (pa_append_decode): sequence s's new K/V row [Hkv, D] at k_new /
+  // v_new + s * Hkv * D (activation dtype of q), written at position L_s - 1 first
+  const void* k_new;
+  const void* v_new;
   const int32_t* query_start;  // multi-token queries: [S + 1] row offsets of q and out
   int32_t max_query_len, num_queries;
   int32_t num_seqs, num_q_heads, num_kv_heads, group, num_blocks, max_blocks, partition_size,

@@ -127,6 +127,27 @@ class DeviceRun:
         self.step_write(pool)
         self.decode(pool)
 
+    @property
+    def can_append(self) -> bool:
+        """The step can run as one pa_append_decode launch: one new token per sequence, at
+        its last position, in a 16-bit or FP8 pool."""
+        w = self.w
+        last = w.seq_start + w.context_lens.astype(np.int64) - 1
+        return (w.kv != "fp4" and self.seq_records is None and len(w.step_call.rows) == w.num_seqs
+                and np.array_equal(w.step_call.rows, last))
+
+    def append_decode(self, pool=None, merge=True):
+        B.pa_append_decode(self.q, pool or self.pool, self.step_k, self.step_v, self.block_tables,
+                           self.context_lens, self.w.sm_scale, self.ps, out=self.out,
+                           part_out=self.part_out, part_lse=self.part_lse, dev_err=self.dev_err)
+        if merge:
+            self.merge()
+
+    def step_fused(self, pool=None):
+        """The same step in one launch (+ merge): each sequence's new row is written by the
+        decode workgroup that reads it."""
+        self.append_decode(pool)
+
     def device_error(self) -> int:
         return B.pa_read_device_error(self.dev_err)
 

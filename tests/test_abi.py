@@ -138,6 +138,19 @@ def test_decode_rejects():
     assert _decode(S=0) == PA_OK  # empty batch: nothing to launch
 
 
+def test_append_decode_rejects():
+    lib = B.lib()
+    f = lambda pool=None, kn=FAKE, vn=FAKE, **k: lib.pa_append_decode(
+        FAKE, 1, k.get("S", 2), 8, ctypes.byref(pool if pool is not None else _pool()), kn, vn,
+        FAKE, 4, FAKE, 0.1, k.get("ps", 0), FAKE, FAKE, FAKE, None, None)
+    assert f(pool=_pool(dtype=3)) == DTYPE           # FP4 pools: write, then decode
+    assert f(kn=None) == NULL and f(vn=None) == NULL
+    assert f(kn=FAKE + 8) == ALIGN
+    assert f(ps=24) == PART
+    assert f(pool=_pool(bs=8)) == BLOCK
+    assert f(S=0) == PA_OK
+
+
 def _prefill(pool=None, q=FAKE, qd=1, S=2, Hq=8, T=10, qs=FAKE, mq=5, bt=FAKE, MB=4,
              cl=FAKE, out=FAKE):
     pool = pool if pool is not None else _pool()
