@@ -343,7 +343,10 @@ int decode_call(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_
   const int64_t wgs = (int64_t)num_seqs * pool->num_kv_heads * max_part;
   const int64_t heads = pool->num_kv_heads < 8 ? pool->num_kv_heads : 8;
   const int64_t target_waves = 8 * heads * (int64_t)device_cus();
-  int waves = 1;
+  // FP4 pools start from 2 waves: a 4-bit tile is half an FP8 one, so a one-wave
+  // workgroup keeps too little in flight, and the FP4 kernel's wave merge reuses its own
+  // LDS, so two waves cost no occupancy (c5: 107 us vs 113 us with one wave).
+  int waves = pool->dtype == PA_KV_FP4_E2M1_OUTL && blocks >= 4 ? 2 : 1;
   while (waves < 8 && wgs * waves < target_waves && blocks >= 2 * waves) waves *= 2;
   const int forced = env_int("PA_DECODE_WAVES", 0);
   if (forced == 1 || forced == 2 || forced == 4 || forced == 8) waves = forced;

@@ -603,9 +603,13 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     return;
   }
 
-  // W > 1: merge the waves' states in LDS.
+  // W > 1: merge the waves' states in LDS. FP4: the merge reuses the LDS of the q copy,
+  // the side accumulators and the id slots, so every wave must be past its block loop
+  // and its fold first (the merge then costs no LDS of its own, and a 2-wave workgroup
+  // keeps the occupancy of two 1-wave ones).
   constexpr int STRIDE = DL + 4;  // floats per lane record (padded)
-  float* m_lds = smem + (KV == KV_FP4 ? kQLds + W * (kSide + kIdsLds) : 0);
+  if constexpr (KV == KV_FP4) __syncthreads();
+  float* m_lds = smem;
   float* l_lds = m_lds + 16 * 8;
   float* acc_lds = l_lds + 16 * 8;  // [W][64][STRIDE]
   if (kg == 0) {
@@ -678,7 +682,9 @@ static size_t decode_lds_bytes(int waves) {
   size_t f = KV == KV_FP4 ? fp4_qlds_floats<D, GP>() +
                                 (size_t)waves * (fp4_side_floats<D, GP>() + kIdsLds)
                           : 0;
-  if (waves > 1) f += 2 * 16 * 8 + (size_t)waves * 64 * (D / 4 + 4);  // the wave merge
+  // the wave merge (FP4: in the same bytes, after the block loops)
+  const size_t merge = waves > 1 ? 2 * 16 * 8 + (size_t)waves * 64 * (D / 4 + 4) : 0;
+  f = KV == KV_FP4 ? (f > merge ? f : merge) : f + merge;
   return f * sizeof(float);
 }
 
