@@ -36,6 +36,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "paged decode attention: achieved KV-read GB/s (% HBM peak) + seq-tokens/s"
 KERNEL_SOURCES = ["paged_quantized_kv_reshape_amd/csrc/pa_decode.hip",
                   "paged_quantized_kv_reshape_amd/csrc/pa_tile.h",
+                  "paged_quantized_kv_reshape_amd/csrc/pa_encode.h",
+                  "paged_quantized_kv_reshape_amd/csrc/pa_fp4.h",
                   "paged_quantized_kv_reshape_amd/csrc/pa_device.h"]
 
 

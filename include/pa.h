@@ -345,10 +345,11 @@ int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
  * pa_cache_write stores them, and the sequence then attends over its L_s tokens exactly as
  * pa_decode. The cache write and the decode of a serving step (dailyaiworld.com, engine
  * diagram: new tokens go to the cache, then Flash-Decoding reads it) without a second
- * launch: the workgroup that reads position L_s - 1 writes it first. Pools: 16-bit and the
- * four FP8 formats; an FP4 pool returns PA_ERR_DTYPE (its first write into a block
- * calibrates over all rows a call puts there: use pa_cache_write, then pa_decode). A
- * block id outside the pool at that position is flagged and nothing is written there.
+ * launch: the wave that reads position L_s - 1 writes it first. Every pool format; in an
+ * FP4 pool a block the new row opens is calibrated on that row, as pa_cache_write does for
+ * a call that puts one row into the block. The block must not be read by another sequence
+ * of the batch (a shared block is copied first, pa_allocator_writable). A block id outside
+ * the pool at that position is flagged and nothing is written there.
  * All other arguments, shapes and rules as pa_decode. Asynchronous on `stream`.
  */
 int pa_append_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,

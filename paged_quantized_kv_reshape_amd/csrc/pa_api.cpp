@@ -373,7 +373,6 @@ int pa_append_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t n
                      const int32_t* context_lens, float sm_scale, int32_t partition_size,
                      float* out, float* part_out, float* part_lse, int32_t* dev_err,
                      void* stream) {
-  if (pool && pool->dtype == PA_KV_FP4_E2M1_OUTL) return PA_ERR_DTYPE;
   if (num_seqs > 0 && (!k_new || !v_new)) return PA_ERR_NULL;
   return decode_call(q, q_dtype, num_seqs, num_q_heads, pool, k_new, v_new, block_tables,
                      max_blocks_per_seq, context_lens, sm_scale, partition_size, out, part_out,

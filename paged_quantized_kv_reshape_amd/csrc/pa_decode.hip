@@ -40,6 +40,7 @@
 
 #include "pa_device.h"
 #include "pa_encode.h"
+#include "pa_fp4.h"
 #include "pa_launch.h"
 #include "pa_tile.h"
 
@@ -97,6 +98,43 @@ __device__ __forceinline__ void append_row(const DecodeArgs& a, int s, int kvh, 
     }
     const bool fast = __builtin_fabsf(sc) >= 0x1p-80f && __builtin_fabsf(sc) <= 0x1p100f;
     *reinterpret_cast<uint4*>(tile + off * D + 16 * c) = fp8_encode16<QBF, E5>(lo, hi, sc, fast);
+  }
+}
+
+// The same for an FP4 pool, by one wave, K then V: a block whose record is still unset gets
+// its outlier set from this row alone (the rows a cache-write call of one token per
+// sequence puts into a block), then the row is encoded with the block's set; the wave is
+// the only writer of the block in this launch, so the V nibbles merge by read-modify-write.
+template <int D, bool QBF>
+__device__ __forceinline__ void append_row_fp4(const DecodeArgs& a, int s, int kvh, int b,
+                                               int off) {
+  using TL = Fp4Tile<D>;
+  const int lane = threadIdx.x & 63;
+  const int64_t bh = (int64_t)b * a.num_kv_heads + kvh;
+#pragma unroll
+  for (int side = 0; side < 2; ++side) {
+    const uint16_t* row = reinterpret_cast<const uint16_t*>(side ? a.v_new : a.k_new) +
+                          ((int64_t)s * a.num_kv_heads + kvh) * D;
+    uint8_t* tile = reinterpret_cast<uint8_t*>(const_cast<void*>(side ? a.v : a.k)) +
+                    bh * TL::kBytes;
+    uint16_t* ov = const_cast<uint16_t*>(side ? a.v_out_val : a.k_out_val) +
+                   bh * (a.cap - 1) * kBlock;
+    const uint4 r4 = *reinterpret_cast<const uint4*>(tile + TL::kRecord);
+    uint32_t rw[3] = {r4.x, r4.y, r4.z};
+    if ((rw[0] & 0xFFu) == 0xFFu) {  // the block's first write (uniform)
+      fp4_calibrate_row<QBF, D>(row, a.cap, rw);
+      if (lane == 0) {
+        uint32_t* w = reinterpret_cast<uint32_t*>(tile + TL::kRecord);
+        w[0] = rw[0];
+        w[1] = rw[1];
+        w[2] = rw[2];
+      }
+    }
+    int count = (int)(rw[0] & 0xFFu);
+    if (count > a.cap) count = a.cap;
+    Fp4VBits vb;
+    fp4_encode_row<QBF, D>(row, tile, ov, off, side == 1, rw, count, vb);
+    if (vb.word) *vb.word = (*vb.word & ~vb.mask) | vb.bits;
   }
 }
 
@@ -172,7 +210,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   }
   if (MQ && j0 >= nq) return;  // no query for this wave
   if constexpr (APPEND) {
-    static_assert(!MQ && KV != KV_FP4, "append: single-query decode, 16-bit and FP8 pools");
+    static_assert(!MQ, "append: single-query decode");
     // The wave that will read position L - 1 (the partition's blocks go round-robin to
     // the workgroup's waves) writes the new row there first. No other wave or workgroup
     // reads that (block, kv head) tile in this launch and this wave has not loaded it
@@ -185,9 +223,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     const bool here = !split || p == pos / a.partition_size;  // uniform over the workgroup
     if (here && wave == (pos / kBlock - start_blk) % W) {
       const int32_t b = a.block_tables[(int64_t)s * a.max_blocks + pos / kBlock];
-      if ((unsigned)b < (unsigned)a.num_blocks)
-        append_row<KV, D, QBF>(a, s, kvh, b, pos % kBlock);
-      else if (lane == 0 && a.err)
+      if ((unsigned)b < (unsigned)a.num_blocks) {
+        if constexpr (KV == KV_FP4)
+          append_row_fp4<D, QBF>(a, s, kvh, b, pos % kBlock);
+        else
+          append_row<KV, D, QBF>(a, s, kvh, b, pos % kBlock);
+      } else if (lane == 0 && a.err)
         atomicOr(a.err, PA_DEVERR_BAD_BLOCK);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -664,10 +705,10 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
 // FP4 pools: a tile is half the bytes of an FP8 one, so one tile per wave leaves too little
 // in flight; the double-buffered loop, held to at least 4 waves per SIMD (128 registers),
 // keeps about twice as much.
-template <int D, bool QBF, int GP>
+template <int D, bool QBF, int GP, bool APPEND = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_fp4(
     DecodeArgs a) {
-  decode_body<KV_FP4, D, QBF, GP, true, false>(a);
+  decode_body<KV_FP4, D, QBF, GP, true, false, APPEND>(a);
 }
 
 // Multi-token queries: 4 waves of 16 (query, head) columns each; single-buffered.
@@ -701,8 +742,10 @@ static int launch_one(const DecodeArgs& a, int waves, hipStream_t st) {
   const size_t lds = decode_lds_bytes<KV, D, GP>(waves);
   const dim3 grid((unsigned)((int64_t)P * a.num_kv_heads), (unsigned)a.num_seqs, 1);
   if constexpr (KV == KV_FP4) {
-    if (a.k_new) return PA_ERR_DTYPE;  // no append for FP4 pools
-    hipLaunchKernelGGL((k_decode_fp4<D, QBF, GP>), grid, dim3(64 * waves), lds, st, a);
+    if (a.k_new)
+      hipLaunchKernelGGL((k_decode_fp4<D, QBF, GP, true>), grid, dim3(64 * waves), lds, st, a);
+    else
+      hipLaunchKernelGGL((k_decode_fp4<D, QBF, GP, false>), grid, dim3(64 * waves), lds, st, a);
   } else if (a.k_new) {
     hipLaunchKernelGGL((k_decode<KV, D, QBF, GP, true>), grid, dim3(64 * waves), lds, st, a);
   } else {

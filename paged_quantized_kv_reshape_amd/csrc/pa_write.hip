@@ -12,6 +12,7 @@
 // contiguous run of head_dim values (head_dim / 2 bytes for FP4).
 #include "pa_device.h"
 #include "pa_encode.h"
+#include "pa_fp4.h"
 #include "pa_launch.h"
 
 namespace pa {
@@ -167,15 +168,6 @@ struct Fp4Side {
   uint16_t* out_val;     // [NB, Hkv, CAP - 1, 16]: outlier slots 1 .. CAP - 1
 };
 
-// Regions of one (block, head) FP4 tile.
-template <int D>
-struct Fp4Tile {
-  static constexpr int kBytes = PA_FP4_TILE_BYTES(D);
-  static constexpr int kScale = PA_FP4_SCALE_OFF(D);
-  static constexpr int kRecord = PA_FP4_RECORD_OFF(D);
-  static constexpr int kSlot0 = PA_FP4_SLOT0_OFF(D);
-  static_assert(kScale % 16 == 0 && kRecord % 16 == 0 && kSlot0 % 8 == 0, "FP4 tile layout");
-};
 struct Fp4Args {
   Fp4Side side[2];
   const int64_t* slots;
@@ -219,44 +211,6 @@ __global__ __launch_bounds__(256) void k_fp4_mark(Fp4Args a) {
   if (rec[0] != 0xFF) return;  // already calibrated: reuse its channel set
   atomicAnd(reinterpret_cast<unsigned int*>(rec + 12), ~(1u << off));
   reinterpret_cast<int32_t*>(tile + TL::kScale)[off] = (int32_t)i;
-}
-
-// The outlier set from per-channel RMS norms r (channel lane + 64 k in r[k]) of one wave:
-// mu and population sigma over the D norms, channels with r >= mu + 3.2 sigma (none when
-// sigma = 0), ascending, at most cap of them; returned as record bytes 0..11 (count, ids,
-// 0xFF padding) in three words.
-template <int D>
-__device__ __forceinline__ void record_from_norms(const float (&r)[D / 64], int cap,
-                                                  uint32_t (&bytes)[3]) {
-  constexpr int CPL = D / 64;
-  float part = 0.0f;
-#pragma unroll
-  for (int k = 0; k < CPL; ++k) part += r[k];
-  const float mu = wave_sum(part) / (float)D;
-  float dev = 0.0f;
-#pragma unroll
-  for (int k = 0; k < CPL; ++k) dev += (r[k] - mu) * (r[k] - mu);
-  const float sigma = __builtin_sqrtf(wave_sum(dev) / (float)D);
-  const float thr = mu + kOutlierSigmas * sigma;
-  bytes[0] = bytes[1] = bytes[2] = 0xFFFFFFFFu;
-  int count = 0;
-#pragma unroll
-  for (int k = 0; k < CPL; ++k) {
-    const bool hit = sigma != 0.0f && r[k] >= thr;
-    uint64_t mask = __ballot(hit);
-    while (mask) {
-      const int c = __builtin_ctzll(mask) + 64 * k;
-      mask &= mask - 1;
-      if (count < cap) {
-        const int pos = 1 + count;  // byte position in the record
-        bytes[pos >> 2] &= ~(0xFFu << ((pos & 3) * 8));
-        bytes[pos >> 2] |= (uint32_t)c << ((pos & 3) * 8);
-      }
-      ++count;
-    }
-  }
-  const int stored = count < cap ? count : cap;
-  bytes[0] = (bytes[0] & ~0xFFu) | (uint32_t)stored;
 }
 
 // One wave per (row, head, K|V); only block leaders do work.
@@ -431,8 +385,7 @@ __global__ __launch_bounds__(64 * kRowsPerWg) void k_fp4_encode(Fp4Args a) {
     slot = a.slots[i];
     if (slot >= a.nslots) slot = -1;
   }
-  uint32_t* vword = nullptr;  // V: this lane's code word and its bits for this token
-  uint32_t vbits = 0u, vmask = 0u;
+  Fp4VBits vb;  // V: this lane's code word and its bits for this token
   if (slot >= 0) {
     const int64_t bh = (slot >> 4) * a.hkv + h;
     const int off = (int)(slot & 15);
@@ -446,60 +399,8 @@ __global__ __launch_bounds__(64 * kRowsPerWg) void k_fp4_encode(Fp4Args a) {
       slot = -1;
     } else {
       if (count > a.cap) count = a.cap;
-      const bool active = lane < D / 2;
-      const int c0 = 2 * lane, c1 = c0 + 1;
-      float x0 = 0.0f, x1 = 0.0f;
-      if (active) {
-        const uint32_t pair =
-            *reinterpret_cast<const uint32_t*>(sd.rows + ((int64_t)i * a.hkv + h) * D + c0);
-        x0 = act_to_f32<BF16>(pair & 0xFFFFu);
-        x1 = act_to_f32<BF16>(pair >> 16);
-      }
-      bool out0 = false, out1 = false;
-      for (int j = 0; j < count; ++j) {
-        const int pos = 1 + j;
-        const int c = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
-        out0 |= (c == c0);
-        out1 |= (c == c1);
-      }
-      const float a0 = (active && !out0) ? __builtin_fabsf(x0) : 0.0f;
-      const float a1 = (active && !out1) ? __builtin_fabsf(x1) : 0.0f;
-      const float amax = wave_max(fmaxf(a0, a1));
-      const float sc = amax / 6.0f;
-      uint32_t q0 = 0u, q1 = 0u;
-      if (sc != 0.0f) {
-        q0 = out0 ? 0u : encode_e2m1(x0 / sc);
-        q1 = out1 ? 0u : encode_e2m1(x1 / sc);
-      }
-      if (active) {
-        if (!vside) {
-          tile[off * (D / 2) + lane] = (uint8_t)(q0 | (q1 << 4));  // K: token rows
-        } else {
-          // V: channels 2 lane and 2 lane + 1 sit in word lane % 4 of chunk
-          // (lane / 4) * 4 + off / 4, at bit 8 ((off % 4) / 2) + 4 (off % 2) and 16 above
-          const int sh = 8 * ((off & 3) >> 1) + 4 * (off & 1);
-          vword = reinterpret_cast<uint32_t*>(tile) +
-                  (((lane >> 2) * 4 + (off >> 2)) * 4 + (lane & 3));
-          vbits = (q0 << sh) | (q1 << (sh + 16));
-          vmask = (0xFu << sh) | (0xFu << (sh + 16));
-        }
-      }
-      for (int j = 0; j < count; ++j) {
-        const int pos = 1 + j;
-        const int c = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
-        if (active && (c >> 1) == lane) {
-          const float xv = (c & 1) ? x1 : x0;
-          const uint16_t hv = bitcast<uint16_t>((_Float16)xv);
-          if (j == 0)
-            reinterpret_cast<uint16_t*>(tile + TL::kSlot0)[off] = hv;
-          else
-            sd.out_val[(bh * (a.cap - 1) + (j - 1)) * kBlock + off] = hv;
-        }
-      }
-      if (lane == 0) {
-        reinterpret_cast<float*>(tile + TL::kScale)[off] = sc;
-        *reinterpret_cast<uint32_t*>(rec + 12) = 0xFFFFFFFFu;
-      }
+      fp4_encode_row<BF16, D>(sd.rows + ((int64_t)i * a.hkv + h) * D, tile,
+                              sd.out_val + bh * (a.cap - 1) * kBlock, off, vside, rw, count, vb);
     }
   }
   if (!vside) return;  // uniform over the workgroup
@@ -509,22 +410,22 @@ __global__ __launch_bounds__(64 * kRowsPerWg) void k_fp4_encode(Fp4Args a) {
   // otherwise other calls' or workgroups' rows may share the words, and each lane merges
   // its nibbles with atomics on disjoint bits (clear, then set).
   if (lane == 0) wg_slot[wave] = slot;
-  wg_bits[wave][lane] = vbits;
+  wg_bits[wave][lane] = vb.bits;
   __syncthreads();
   const int64_t s0 = wg_slot[0];
   bool full = s0 >= 0 && (s0 & 3) == 0;
 #pragma unroll
   for (int w = 1; w < kRowsPerWg; ++w) full = full && wg_slot[w] == s0 + w;
   if (full) {
-    if (wave == 0 && vword) {
+    if (wave == 0 && vb.word) {
       uint32_t word = 0u;
 #pragma unroll
       for (int w = 0; w < kRowsPerWg; ++w) word |= wg_bits[w][lane];
-      *vword = word;
+      *vb.word = word;
     }
-  } else if (vword) {
-    atomicAnd(vword, ~vmask);
-    atomicOr(vword, vbits);
+  } else if (vb.word) {
+    atomicAnd(vb.word, ~vb.mask);
+    atomicOr(vb.word, vb.bits);
   }
 }
 

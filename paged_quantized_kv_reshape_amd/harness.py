@@ -130,10 +130,11 @@ class DeviceRun:
     @property
     def can_append(self) -> bool:
         """The step can run as one pa_append_decode launch: one new token per sequence, at
-        its last position, in a 16-bit or FP8 pool."""
+        its last position (per-block FP4 calibration; the per-sequence mode writes through
+        its own entry point)."""
         w = self.w
         last = w.seq_start + w.context_lens.astype(np.int64) - 1
-        return (w.kv != "fp4" and self.seq_records is None and len(w.step_call.rows) == w.num_seqs
+        return (self.seq_records is None and len(w.step_call.rows) == w.num_seqs
                 and np.array_equal(w.step_call.rows, last))
 
     def append_decode(self, pool=None, merge=True):

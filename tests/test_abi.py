@@ -143,7 +143,7 @@ def test_append_decode_rejects():
     f = lambda pool=None, kn=FAKE, vn=FAKE, **k: lib.pa_append_decode(
         FAKE, 1, k.get("S", 2), 8, ctypes.byref(pool if pool is not None else _pool()), kn, vn,
         FAKE, 4, FAKE, 0.1, k.get("ps", 0), FAKE, FAKE, FAKE, None, None)
-    assert f(pool=_pool(dtype=3)) == DTYPE           # FP4 pools: write, then decode
+    assert f(pool=_pool(dtype=3, fp4=False)) == NULL  # FP4 without its outlier arrays
     assert f(kn=None) == NULL and f(vn=None) == NULL
     assert f(kn=FAKE + 8) == ALIGN
     assert f(ps=24) == PART

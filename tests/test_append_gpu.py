@@ -1,10 +1,11 @@
 """GPU parity of pa_append_decode (each sequence's new row written at its last position by
 the decode launch itself) against the oracle's cache write followed by its exact decode.
 
-Pools bit-exact after the step (every format it takes: fp16, bf16, FP8 E4M3 / E5M2 with
-per-head or per-token scales); outputs within max-abs 2e-3 and relative L2 1e-2, single
-pass and split (with pa_merge), 1 and 4 waves per workgroup; and bit for bit the output of
-pa_cache_write followed by pa_decode on the same inputs."""
+Pools bit-exact after the step in every format (fp16, bf16, FP8 E4M3 / E5M2 with per-head
+or per-token scales, FP4 with outliers, including blocks the new row opens and calibrates);
+outputs within max-abs 2e-3 and relative L2 1e-2, single pass and split (with pa_merge),
+1 and 4 waves per workgroup; and bit for bit the output of pa_cache_write followed by
+pa_decode on the same inputs."""
 import os
 
 import numpy as np
@@ -28,6 +29,11 @@ CASES = {
     "fp8t": ("c4", dict(num_seqs=3, lens=[300, 77, 17], kv="fp8t")),
     "bf8t": ("c4", dict(num_seqs=3, lens=[300, 64, 16], kv="bf8t", head_dim=64,
                         num_kv_heads=2)),
+    # FP4: last positions 299 (inside a calibrated block), 976, 32 and 16 (each the first
+    # row of a fresh block, calibrated on that row alone, as the separate write does)
+    "fp4": ("c5", dict(num_seqs=4, lens=[300, 977, 33, 17])),
+    "fp4-2kv": ("c5", dict(num_seqs=3, lens=[129, 50, 1], num_kv_heads=2, num_q_heads=16,
+                           act="f16")),
 }
 
 
