@@ -569,6 +569,10 @@ def main():
             run.decode(pool_of(i), merge=False)
     timer.record(burst[1], stream)
     torch.cuda.synchronize()
+    # per-step spread, from the attribution pass (its markers add their own latency, so
+    # these run a few microseconds above the timed region's mean)
+    step_ms = np.array([timer.ms(e[0], e[3]) for e in ev])
+    dec_ms = np.array([timer.ms(e[1], e[2]) for e in ev])
     t_write = float(np.mean([timer.ms(e[0], e[1]) for e in ev])) * 1e-3
     t_dec_br = float(np.mean([timer.ms(e[1], e[2]) for e in ev])) * 1e-3
     t_merge = float(np.mean([timer.ms(e[2], e[3]) for e in ev])) * 1e-3
@@ -614,7 +618,11 @@ def main():
                       "bracketed": {"cache_write": round(t_write * 1e3, 4) if not fused else 0.0,
                                     "decode": round(t_dec_br * 1e3, 4),
                                     "merge": round(t_merge * 1e3, 4)},
-                      "step_events": round(t_step_ev * 1e3, 4)},
+                      "step_events": round(t_step_ev * 1e3, 4),
+                      "bracketed_step_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4)
+                                                     for q in (10, 50, 90)],
+                      "bracketed_decode_p10_p50_p90": [round(float(np.percentile(dec_ms, q)), 4)
+                                                       for q in (10, 50, 90)]},
         "roofline": {"kernel": decode_kernel_name(w.kv, fused), "bound": "hbm",
                      "achieved": round(dec_gbs, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
