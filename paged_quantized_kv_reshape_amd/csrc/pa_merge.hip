@@ -6,27 +6,35 @@
 // merge is exact: out = sum_p exp(lse_p - M) o_p / sum_p exp(lse_p - M), M = max_p lse_p,
 // and the merged lse = M + ln sum_p exp(lse_p - M).
 //
-// One workgroup of W waves per (sequence, query head). Wave w folds partitions w, w + W,
-// ... into (M_w, sum_w, acc_w) with its own maximum M_w (lane l owns channels D/64 l ..
-// D/64 (l + 1) - 1, so each partition's row is one coalesced read); the W partial states
-// are then combined through LDS. A long context (hundreds of partitions) is thus read by W waves
-// in parallel instead of one, which keeps the merge bandwidth-bound.
+// One workgroup of W waves per (sequence, query head). The partitions go to the waves in
+// batches of 16: wave w takes partitions 16 w .. 16 w + 15, then 16 (w + W) .. and so on.
+// A batch costs one trip to memory: lane j loads lse of the batch's partition j and the
+// wave loads the batch's 16 rows (lane l holds channels D/64 l .. D/64 (l + 1) - 1 of each,
+// so a row is one coalesced read, a batch 16 consecutive rows), all before any of them is
+// used. Slots past the last partition re-read the last row (in range, and cached) with
+// weight 0. A wave rescales its running state (M_w, weight sum, acc_w) when a batch raises
+// its maximum; the W states are then combined through LDS. The merge is bound by the
+// latency of that one trip, not by the bytes: a context of a few hundred partitions is read
+// by every wave of the workgroup at once.
+#include <algorithm>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
 namespace pa {
 
+constexpr int kMergeBatch = 16;  // partitions per wave and trip
+constexpr int kMergeMaxWaves = 16;
+
 template <int D>
-__global__ __launch_bounds__(1024) void k_merge(const float* __restrict__ po,
-                                                const float* __restrict__ pl,
-                                                const int32_t* __restrict__ cl, int32_t Hq,
-                                                int32_t P, int32_t ps,
-                                                float* __restrict__ out,
-                                                float* __restrict__ lse_out) {
+__global__ __launch_bounds__(64 * kMergeMaxWaves) void k_merge(
+    const float* __restrict__ po, const float* __restrict__ pl, const int32_t* __restrict__ cl,
+    int32_t Hq, int32_t P, int32_t ps, float* __restrict__ out, float* __restrict__ lse_out) {
   constexpr int CPL = D / 64;  // channels per lane: lane l owns [CPL l, CPL (l + 1))
+  constexpr int B = kMergeBatch;
   typedef float vec_t __attribute__((ext_vector_type(CPL)));
-  __shared__ float s_m[16], s_w[16];
-  __shared__ vec_t s_acc[16][64];
+  __shared__ float s_m[kMergeMaxWaves], s_w[kMergeMaxWaves];
+  __shared__ vec_t s_acc[kMergeMaxWaves][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
@@ -43,19 +51,30 @@ __global__ __launch_bounds__(1024) void k_merge(const float* __restrict__ po,
     return;
   }
   const float* lse = pl + sh * P;
-  float m = -INFINITY;
-  for (int p = wave + W * lane; p < np; p += 64 * W) m = fmaxf(m, lse[p]);
-  m = wave_max(m);
+  const vec_t* rows = reinterpret_cast<const vec_t*>(po + sh * (int64_t)P * D) + lane;
+  float m = -INFINITY;  // this wave's running maximum (wave-uniform)
+  float wl = 0.0f;      // this lane's share of the weight sum
   vec_t acc = vec_t(0.0f);
-  float wsum = 0.0f;
-  const vec_t* base = reinterpret_cast<const vec_t*>(po + sh * (int64_t)P * D) + lane;
-#pragma unroll 8
-  for (int p = wave; p < np; p += W) {
-    const float x = lse[p];
-    const float w = x == -INFINITY ? 0.0f : __expf(x - m);
-    wsum += w;
-    acc += w * base[(int64_t)p * (D / CPL)];
+  for (int b0 = wave * B; b0 < np; b0 += W * B) {
+    const float x = lane < B && b0 + lane < np ? lse[b0 + lane] : -INFINITY;
+    vec_t r[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) r[j] = rows[(int64_t)min(b0 + j, np - 1) * (D / CPL)];
+    const float mn = fmaxf(m, wave_max(x));
+    if (mn == -INFINITY) continue;  // no finite lse yet: the state is still all zero
+    if (mn > m) {
+      const float f = m == -INFINITY ? 0.0f : __expf(m - mn);
+      acc *= f;
+      wl *= f;
+      m = mn;
+    }
+    const float wx = x == -INFINITY ? 0.0f : __expf(x - m);
+    wl += wx;
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+      acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wx), j)) * r[j];
   }
+  const float wsum = wave_sum(wl);
   if (W == 1) {
     const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
     o[lane] = acc * inv;
@@ -88,9 +107,10 @@ int launch_merge(const float* part_out, const float* part_lse, const int32_t* co
                  float* lse_out, hipStream_t st) {
   const int64_t pairs = (int64_t)S * Hq;
   if (pairs == 0) return PA_OK;
-  // about 8 partitions per wave, 1..16 waves
-  int waves = 1;
-  while (waves < 16 && P > 8 * waves) waves *= 2;
+  // one batch of partitions per wave where that takes at most 16 waves
+  const int waves = (int)std::min<int64_t>(kMergeMaxWaves,
+                                           std::max<int64_t>(1, ((int64_t)P + kMergeBatch - 1) /
+                                                                    kMergeBatch));
   const dim3 grid((unsigned)pairs);
   if (D == 128)
     hipLaunchKernelGGL(k_merge<128>, grid, dim3(64 * waves), 0, st, part_out, part_lse,
