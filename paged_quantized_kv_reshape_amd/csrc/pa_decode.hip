@@ -209,15 +209,19 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     return;
   }
   if (MQ && j0 >= nq) return;  // no query for this wave
+  // APPEND: whether this wave wrote the new row (and so fences before loading its tile)
+  bool wrote = false;
   if constexpr (APPEND) {
     static_assert(!MQ, "append: single-query decode");
     // The wave that will read position L - 1 (the partition's blocks go round-robin to
     // the workgroup's waves) writes the new row there first. No other wave or workgroup
-    // reads that (block, kv head) tile in this launch and this wave has not loaded it
-    // yet, so a fence at workgroup scope is enough: its release waits for the stores to
-    // reach L2, its acquire orders the wave's later loads after them. The other waves do
-    // not wait. (A device-scope fence would also write back and invalidate the XCD's L2:
-    // measured, that cost the c4 decode 60% of its speed.)
+    // reads that (block, kv head) tile in this launch, and the block is the last of the
+    // partition, so it is this wave's last tile: a fence at workgroup scope just before
+    // that tile's loads is enough (its release waits for the stores to reach L2, its
+    // acquire orders the later loads after them), and by then the stores have long
+    // completed, so the wait costs nothing. The other waves do not wait. (A device-scope
+    // fence would also write back and invalidate the XCD's L2: measured, that cost the c4
+    // decode 60% of its speed.)
     const int pos = L - 1;
     const int start_blk = split ? p * (a.partition_size / kBlock) : 0;
     const bool here = !split || p == pos / a.partition_size;  // uniform over the workgroup
@@ -230,8 +234,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
           append_row<KV, D, QBF>(a, s, kvh, b, pos % kBlock);
       } else if (lane == 0 && a.err)
         atomicOr(a.err, PA_DEVERR_BAD_BLOCK);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      wrote = true;
     }
   }
   // the blocks this wave reads: its share of the partition (decode, blocks w, w + W, ...),
@@ -345,6 +348,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   // registers, and wait for every scalar load as soon as it is issued.
   int err_bits = 0;
   auto load_tile = [&](Tile<KV, D>& T, int x) {
+    if constexpr (APPEND) {
+      if (wrote && x == my_n - 1) {  // the tile holding the row this wave wrote
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      }
+    }
     int b_raw;
     if constexpr (DB) {
       b_raw = __builtin_amdgcn_readfirstlane(nid_v);
