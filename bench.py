@@ -17,7 +17,7 @@ Prints one JSON line: value = algorithmic bytes of the step / step time (GB/s), 
 dominant kernel's roofline (its algorithmic bytes / its average launch time from HIP events
 on the launch stream) and the oracle's rate on the host cores (cpu_baseline).
 
-    python bench.py [--steps K] [--warmup W] [--config c4] [--partition-size PS]
+    python bench.py [--steps K (300)] [--warmup W (50)] [--config c4] [--partition-size PS]
 """
 from __future__ import annotations
 
@@ -433,8 +433,8 @@ def prefill_main(args, config, DESCRIPTIONS):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="c4", choices=["c2", "c3", "c4", "c5"])
     ap.add_argument("--partition-size", type=int, default=None,
                     help="override the workload's split (0 = one pass per sequence)")
