@@ -49,8 +49,9 @@ namespace pa {
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
 
 // LDS of the FP4 kernel, in floats, for GP head columns (shared by the kernel and its
-// launch): the q copy ([D + D/DL rows][GP], DL = D / 4) and each wave's side accumulator
-// ([D rows][GP], plus DL spare rows that take the entries of padding heads when GP < 16).
+// launch): the q copy ([D + D/DL rows][GP], DL = D / 4) and, for multi-token queries, each
+// wave's side accumulator ([D rows][GP], plus DL spare rows that take the entries of
+// padding heads when GP < 16).
 template <int D, int GP>
 constexpr int fp4_qlds_floats() { return (D + 4) * GP; }
 // words of one wave's block-id slot (FP4 kernel)
@@ -145,6 +146,21 @@ __device__ __forceinline__ void append_row_fp4(const DecodeArgs& a, int s, int k
 // MQ selects multi-token queries (chunked prefill, draft verification): each wave owns 16
 // MFMA columns, one per (query, head), and walks every block up to its last query's
 // position with causal masks; there is no split and no merge.
+// acc[n][r] += x for the entry e = NT r + n (wave-uniform) of a lane's output channels. The
+// accumulators are viewed as one register vector, so the uniform index becomes the
+// hardware's register indexing (s_set_gpr_idx) on the registers in place: no copy of the
+// accumulators and no trip through memory.
+template <int NT>
+__device__ __forceinline__ void add_entry(f32x4 (&acc)[NT], int e, float x) {
+  typedef float flat_t __attribute__((ext_vector_type(4 * NT)));
+  flat_t w;
+#pragma unroll
+  for (int t = 0; t < 4 * NT; ++t) w[t] = acc[t / 4][t % 4];
+  w[__builtin_amdgcn_readfirstlane(4 * (e % NT) + e / NT)] += x;  // acc[n][r] at 4 n + r
+#pragma unroll
+  for (int t = 0; t < 4 * NT; ++t) acc[t / 4][t % 4] = w[t];
+}
+
 template <int KV, int D, bool QBF, int GP, bool DB, bool MQ, bool APPEND = false>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   using G_ = Geo<KV, D>;
@@ -154,10 +170,13 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   // (c >= GP) use instead of real entries (so every lane's entries sit at one base
   // address plus compile-time offsets).
   constexpr int kQLds = fp4_qlds_floats<D, GP>();  // floats of the FP4 q copy
-  constexpr int kSide = fp4_side_floats<D, GP>();  // floats of one wave's side accumulator
+  // floats of one wave's side accumulator (multi-token queries; decode adds the V-outlier
+  // terms into its registers)
+  constexpr int kSide = MQ ? fp4_side_floats<D, GP>() : 0;
   static_assert(!DB || KV == KV_FP4, "the double-buffered loop is the FP4 kernel's");
   static_assert(!MQ || (GP == 16 && !DB), "multi-token queries fill all 16 columns");
-  static_assert(kQLds == (D + D / DL) * GP && kSide == (D + (GP < 16 ? DL : 0)) * GP,
+  static_assert(kQLds == (D + D / DL) * GP &&
+                    kSide == (MQ ? (D + (GP < 16 ? DL : 0)) * GP : 0),
                 "FP4 LDS layout");
   constexpr bool PVB = QBF || KV == KV_FP4;  // PV MFMA in bf16 (else fp16)
   extern __shared__ float smem[];
@@ -291,11 +310,11 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     }
     if constexpr (!MQ) __syncthreads();
   }
-  // FP4 only: this wave's side accumulator of the V-outlier terms, [D channels][GP heads]
-  // fp32 (plus the spare row). The outlier channel of a block is known only at run time, and a run-time
-  // index into the accumulator registers would cost a copy of all of them per case; so
-  // the terms are summed here and folded into the registers at the end (and before a
-  // rescale, which must scale both).
+  // FP4 multi-token queries only: this wave's side accumulator of the V-outlier terms,
+  // [D channels][GP heads] fp32 (plus the spare row). The outlier channel of a block is
+  // known only at run time; the terms are summed here and folded into the registers at the
+  // end (and before a rescale, which must scale both). (Decode adds them into the
+  // registers directly, add_entry; it has no side accumulator, kSide = 0.)
   float* side = MQ ? q_lds + kQLds : smem + kQLds + (int64_t)wave * kSide;
   // this lane's entry for channel ch (a spare row for a padding head)
   auto side_at = [&](int ch) -> float* {
@@ -539,17 +558,13 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     const uint32_t l23 = pack2(pv[2] - lo16_to_f32(h23, PVB), pv[3] - hi16_to_f32(h23, PVB), PVB);
     const uint2 ph = make_uint2(h01, h23), pl = make_uint2(l01, l23);
 
-    uint2 vf[NT];
-    v_fragments<KV, D, PVB>(T, vf);
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      acc[n] = mfma_k16(vf[n], ph, acc[n], PVB);
-      acc[n] = mfma_k16(vf[n], pl, acc[n], PVB);
-    }
-
-    if constexpr (KV == KV_FP4) {
-      // V outliers: out[c][ch] += sum_t p_t * o_t,ch (fp16 values, unscaled p); ch is
-      // wave-uniform (the record sits in scalar registers).
+    // FP4 V outliers: out[c][ch] += sum_t p_t * o_t,ch (fp16 values, unscaled p); ch is
+    // wave-uniform (the record sits in scalar registers). Decode adds each term straight
+    // into its accumulator register, before this block's PV MFMAs, so the indexed register
+    // read waits only for the previous block's. Multi-token queries sum the terms in the
+    // LDS side accumulator instead, after the MFMAs (measured: the register form cost that
+    // loop 11%).
+    auto v_outliers = [&]() {
       uint32_t rw[3] = {(uint32_t)__builtin_amdgcn_readlane((int)T.r0, 32), 0u, 0u};
       int nv = (int)(rw[0] & 0xFFu);
       if (nv > 3 && nv != 0xFF) {
@@ -578,12 +593,27 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) part = __builtin_fmaf(pr[r], o4[r], part);
         part = group4_sum(part);
-        // the four lanes of column c hold the same reduced term and read the same old
-        // value, so they all write the same sum: no lane branch is needed
-        *side_at(ch) += part;
-        side_used = true;
+        if constexpr (MQ) {
+          // the four lanes of column c hold the same reduced term and read the same old
+          // value, so they all write the same sum: no lane branch is needed
+          *side_at(ch) += part;
+          side_used = true;
+        } else {
+          // channel ch is entry ch % DL = NT r + n, in acc[n][r], of the lanes with
+          // kg = ch / DL
+          add_entry<NT>(acc, ch % DL, kg == ch / DL ? part : 0.0f);
+        }
       }
+    };
+    if constexpr (KV == KV_FP4 && !MQ) v_outliers();
+    uint2 vf[NT];
+    v_fragments<KV, D, PVB>(T, vf);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      acc[n] = mfma_k16(vf[n], ph, acc[n], PVB);
+      acc[n] = mfma_k16(vf[n], pl, acc[n], PVB);
     }
+    if constexpr (KV == KV_FP4 && MQ) v_outliers();
   };
 
   // ---- block loop (single or double buffered, see DB) ----
@@ -730,7 +760,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) void k_prefill(DecodeArgs a) {
 template <int KV, int D, int GP>
 static size_t decode_lds_bytes(int waves) {
   size_t f = KV == KV_FP4 ? fp4_qlds_floats<D, GP>() +
-                                (size_t)waves * (fp4_side_floats<D, GP>() + kIdsLds)
+                                (size_t)waves * kIdsLds
                           : 0;
   // the wave merge (FP4: in the same bytes, after the block loops)
   const size_t merge = waves > 1 ? 2 * 16 * 8 + (size_t)waves * 64 * (D / 4 + 4) : 0;
