@@ -49,15 +49,11 @@ namespace pa {
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
 
 // LDS of the FP4 kernel, in floats, for GP head columns (shared by the kernel and its
-// launch): the q copy ([D + D/DL rows][GP], DL = D / 4) and, for multi-token queries, each
-// wave's side accumulator ([D rows][GP], plus DL spare rows that take the entries of
-// padding heads when GP < 16).
+// launch): the q copy ([D + D/DL rows][GP], DL = D / 4).
 template <int D, int GP>
 constexpr int fp4_qlds_floats() { return (D + 4) * GP; }
 // words of one wave's block-id slot (FP4 kernel)
 constexpr int kIdsLds = 64;
-template <int D, int GP>
-constexpr int fp4_side_floats() { return (D + (GP < 16 ? D / 4 : 0)) * GP; }
 
 
 // pa_append_decode: the workgroup that reads sequence s's last position writes the
@@ -143,41 +139,14 @@ __device__ __forceinline__ void append_row_fp4(const DecodeArgs& a, int s, int k
 // (the next tile is loaded after the current one is consumed; the other waves of the
 // compute unit cover the latency), true double-buffers (the next tile's loads are issued
 // before the current tile's math, so each wave keeps a tile in flight while it computes).
-// MQ selects multi-token queries (chunked prefill, draft verification): each wave owns 16
-// MFMA columns, one per (query, head), and walks every block up to its last query's
-// position with causal masks; there is no split and no merge.
-// acc[n][r] += x for the entry e = NT r + n (wave-uniform) of a lane's output channels. The
-// accumulators are viewed as one register vector, so the uniform index becomes the
-// hardware's register indexing (s_set_gpr_idx) on the registers in place: no copy of the
-// accumulators and no trip through memory.
-template <int NT>
-__device__ __forceinline__ void add_entry(f32x4 (&acc)[NT], int e, float x) {
-  typedef float flat_t __attribute__((ext_vector_type(4 * NT)));
-  flat_t w;
-#pragma unroll
-  for (int t = 0; t < 4 * NT; ++t) w[t] = acc[t / 4][t % 4];
-  w[__builtin_amdgcn_readfirstlane(4 * (e % NT) + e / NT)] += x;  // acc[n][r] at 4 n + r
-#pragma unroll
-  for (int t = 0; t < 4 * NT; ++t) acc[t / 4][t % 4] = w[t];
-}
-
-template <int KV, int D, bool QBF, int GP, bool DB, bool MQ, bool APPEND = false>
+template <int KV, int D, bool QBF, int GP, bool DB, bool APPEND = false>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   using G_ = Geo<KV, D>;
   constexpr int KS = G_::KS, NT = G_::NT, DL = G_::DL;
-  // FP4 LDS buffers hold GP head columns (GP = 8 or 16 >= the GQA group): the q copy and
-  // each wave's side accumulator, which has DL spare rows that lanes of padding heads
-  // (c >= GP) use instead of real entries (so every lane's entries sit at one base
-  // address plus compile-time offsets).
-  constexpr int kQLds = fp4_qlds_floats<D, GP>();  // floats of the FP4 q copy
-  // floats of one wave's side accumulator (multi-token queries; decode adds the V-outlier
-  // terms into its registers)
-  constexpr int kSide = MQ ? fp4_side_floats<D, GP>() : 0;
+  // the FP4 q copy holds GP head columns (GP = 8 or 16 >= the GQA group)
+  constexpr int kQLds = fp4_qlds_floats<D, GP>();
   static_assert(!DB || KV == KV_FP4, "the double-buffered loop is the FP4 kernel's");
-  static_assert(!MQ || (GP == 16 && !DB), "multi-token queries fill all 16 columns");
-  static_assert(kQLds == (D + D / DL) * GP &&
-                    kSide == (MQ ? (D + (GP < 16 ? DL : 0)) * GP : 0),
-                "FP4 LDS layout");
+  static_assert(kQLds == (D + D / DL) * GP, "FP4 LDS layout");
   constexpr bool PVB = QBF || KV == KV_FP4;  // PV MFMA in bf16 (else fp16)
   extern __shared__ float smem[];
 
@@ -187,7 +156,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   const int W = blockDim.x >> 6;
   const int c = lane & 15;  // MFMA column: query head (QK, PV); K row token; V channel group
   const int kg = lane >> 4;
-  // grid.x = kv head fastest, then partition (MQ: query tile): the workgroups of one
+  // grid.x = kv head fastest, then partition: the workgroups of one
   // block's kv heads run side by side and read neighbouring tiles ([block][kv head][16][D]
   // is contiguous); grid.y = sequence
   const int kvh = (int)(blockIdx.x % (unsigned)a.num_kv_heads);
@@ -198,40 +167,18 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 
   const int L = a.context_lens[s];
   const int cap_tokens = a.max_blocks * kBlock;
-  // MQ: sequence s's queries are rows q0 .. q0 + nq - 1 at positions L - nq .. L - 1;
-  // wave w of query tile p takes QPW = 16 / G consecutive queries
-  int q0 = 0, nq = 1;
-  if constexpr (MQ) {
-    q0 = a.query_start[s];
-    nq = a.query_start[s + 1] - q0;
-  }
-  const int QPW = MQ ? kBlock / G : 1;
-  const int j0 = MQ ? (p * W + wave) * QPW : 0;  // first query of this wave
-  const bool split = !MQ && a.partition_size > 0;
-  const bool rows_ok = !MQ || (q0 >= 0 && nq >= 0 && (int64_t)q0 + nq <= a.num_queries);
-  const bool bad_q = MQ && (!rows_ok || nq > L || nq > a.max_query_len);
-  if (L < 1 || L > cap_tokens || bad_q) {
-    if constexpr (MQ) {
-      if (lane == 0 && wave == 0 && p == 0 && kvh == 0 && a.err)
-        atomicOr(a.err, PA_DEVERR_BAD_CONTEXT);
-      if (rows_ok && nq <= a.max_query_len)  // zero this wave's rows
-        for (int j = j0; j < min(j0 + QPW, nq); ++j)
-          for (int i = lane; i < G * D; i += 64)
-            a.out[((int64_t)(q0 + j) * Hq + kvh * G) * D + i] = 0.0f;
-    } else {
-      if (threadIdx.x == 0 && p == 0 && kvh == 0 && a.err) atomicOr(a.err, PA_DEVERR_BAD_CONTEXT);
-      if (!split && p == 0) {
-        for (int i = threadIdx.x; i < G * D; i += blockDim.x)
-          a.out[((int64_t)s * Hq + kvh * G) * D + i] = 0.0f;
-      }
+  const bool split = a.partition_size > 0;
+  if (L < 1 || L > cap_tokens) {
+    if (threadIdx.x == 0 && p == 0 && kvh == 0 && a.err) atomicOr(a.err, PA_DEVERR_BAD_CONTEXT);
+    if (!split && p == 0) {
+      for (int i = threadIdx.x; i < G * D; i += blockDim.x)
+        a.out[((int64_t)s * Hq + kvh * G) * D + i] = 0.0f;
     }
     return;
   }
-  if (MQ && j0 >= nq) return;  // no query for this wave
   // APPEND: whether this wave wrote the new row (and so fences before loading its tile)
   bool wrote = false;
   if constexpr (APPEND) {
-    static_assert(!MQ, "append: single-query decode");
     // The wave that will read position L - 1 (the partition's blocks go round-robin to
     // the workgroup's waves) writes the new row there first. No other wave or workgroup
     // reads that (block, kv head) tile in this launch, and the block is the last of the
@@ -256,48 +203,30 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
       wrote = true;
     }
   }
-  // the blocks this wave reads: its share of the partition (decode, blocks w, w + W, ...),
-  // or every block up to its last query's position (MQ)
-  int start, end;
-  if constexpr (MQ) {
-    start = 0;
-    end = L - nq + min(j0 + QPW, nq);
-  } else {
-    start = split ? p * a.partition_size : 0;
-    if (start >= L) return;  // empty partition: not written, the merge skips it
-    end = split ? min(start + a.partition_size, L) : L;
-  }
+  // the blocks this wave reads: its share of the partition, blocks w, w + W, ...
+  const int start = split ? p * a.partition_size : 0;
+  if (start >= L) return;  // empty partition: not written, the merge skips it
+  const int end = split ? min(start + a.partition_size, L) : L;
   const int jb0 = start / kBlock;
   const int nblk = (end + kBlock - 1) / kBlock - jb0;
-  const int my_lo = MQ ? 0 : wave;
-  const int my_n = MQ ? nblk : (wave < nblk ? (nblk - wave + W - 1) / W : 0);
-  const int kStep = MQ ? 1 : W;
-  // this lane's column: MQ query jc (head c % G), whose keys end at position L - nq + jc;
-  // blocks wholly at or before the wave's first query position need no masks (MQ)
-  const int jc = MQ ? j0 + c / G : 0;
-  const int col_end = MQ ? (jc < nq ? L - nq + jc + 1 : 0) : end;
-  const int nfull = MQ ? (L - nq + j0 + 1) / kBlock : 0;
+  const int my_n = wave < nblk ? (nblk - wave + W - 1) / W : 0;
 
   // ---- query fragments (B operand of S^T = K Q^T), zero for padded heads ----
   uint4 qf[KS];
   {
-    const int64_t qr = MQ ? (int64_t)(q0 + jc) : (int64_t)s;
-    const int qhead = MQ ? c % G : c;
-    const bool qok = MQ ? jc < nq : c < G;
     const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
-                          ((qr * Hq + kvh * G + qhead) * D + DL * kg) * 2;
+                          (((int64_t)s * Hq + kvh * G + c) * D + DL * kg) * 2;
 #pragma unroll
     for (int t = 0; t < KS; ++t)
-      qf[t] = qok ? reinterpret_cast<const uint4*>(qrow)[t] : make_uint4(0, 0, 0, 0);
+      qf[t] = c < G ? reinterpret_cast<const uint4*>(qrow)[t] : make_uint4(0, 0, 0, 0);
   }
   // FP4 only: q in fp32 for the K-outlier term, channel-major: head c of channel ch at
-  // (ch + ch / DL) * 16 + c. A column's 16 heads are 16 consecutive words (one read per
-  // outlier is conflict-free) and the pad of 16 words after each DL channels puts the
-  // four lane groups of a write on different banks.
-  // (MQ: each wave has its own q copy and side accumulator, [q][side] per wave)
-  float* q_lds = MQ ? smem + (int64_t)wave * (kQLds + kSide) : smem;
+  // (ch + ch / DL) * GP + c. A column's heads are consecutive words (one read per outlier
+  // is conflict-free) and the pad of GP words after each DL channels puts the four lane
+  // groups of a write on different banks.
+  float* const q_lds = smem;
   if constexpr (KV == KV_FP4) {
-    if (MQ || wave == 0) {
+    if (wave == 0) {
 #pragma unroll
       for (int t = 0; t < KS; ++t) {
         const uint32_t w[4] = {qf[t].x, qf[t].y, qf[t].z, qf[t].w};
@@ -308,26 +237,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
         }
       }
     }
-    if constexpr (!MQ) __syncthreads();
-  }
-  // FP4 multi-token queries only: this wave's side accumulator of the V-outlier terms,
-  // [D channels][GP heads] fp32 (plus the spare row). The outlier channel of a block is
-  // known only at run time; the terms are summed here and folded into the registers at the
-  // end (and before a rescale, which must scale both). (Decode adds them into the
-  // registers directly, add_entry; it has no side accumulator, kSide = 0.)
-  float* side = MQ ? q_lds + kQLds : smem + kQLds + (int64_t)wave * kSide;
-  // this lane's entry for channel ch (a spare row for a padding head)
-  auto side_at = [&](int ch) -> float* {
-    return side + (c < GP ? ch * GP + c : D * GP + (c - GP));
-  };
-  // base of the entries lane (c, kg) folds into its registers: channel DL kg + NT r + n
-  // sits at fold_base + (NT r + n) GP
-  float* const fold_base = side + (c < GP ? DL * kg * GP + c : D * GP + (c - GP));
-  if constexpr (KV == KV_FP4) {
-    static_assert(kSide % 4 == 0, "side accumulator is cleared in float4 units");
-#pragma unroll
-    for (int i = lane; i < kSide / 4; i += 64)
-      reinterpret_cast<float4*>(side)[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    __syncthreads();
   }
 
   // ---- scale of the logits (base 2) ----
@@ -340,13 +250,13 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   // and each id read one block ahead, so that no vector load of ids is pending when the
   // next tile's loads are issued and no scalar load is pending during a block's math (a
   // scalar load may complete out of order, so any wait on LDS would wait for it too).
-  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks + jb0 + my_lo;
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks + jb0 + wave;
   auto load_ids = [&](int chunk) -> int {
     const int x = chunk * 64 + lane;
-    return x < my_n ? bt[(int64_t)x * kStep] : 0;
+    return x < my_n ? bt[(int64_t)x * W] : 0;
   };
   int ids_a = 0, ids_b = 0, nid_v = 0;
-  int* const ids_lds = reinterpret_cast<int*>(smem + kQLds + W * kSide) + wave * kIdsLds;
+  int* const ids_lds = reinterpret_cast<int*>(smem + kQLds) + wave * kIdsLds;
   if constexpr (DB) {
     ids_lds[lane] = load_ids(0);
     ids_b = load_ids(1);
@@ -388,7 +298,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
       }
       b_raw = __builtin_amdgcn_readlane(ids_a, x & 63);
     }
-    T.jb = jb0 + my_lo + x * kStep;
+    T.jb = jb0 + wave + x * W;
     T.ok = (unsigned)b_raw < (unsigned)a.num_blocks;
     err_bits |= T.ok ? 0 : PA_DEVERR_BAD_BLOCK;
     const int b = T.ok ? b_raw : 0;
@@ -433,23 +343,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   f32x4 acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  // add the side accumulator into acc (lane (c, kg) holds channel DL kg + NT r + n of
-  // head c in acc[n][r]) and clear it
-  bool side_used = false;  // wave-uniform: some V-outlier term went to the side buffer
-  auto fold_side = [&](bool clear) {
-    if constexpr (KV == KV_FP4) {
-      if (!side_used) return;
-      side_used = !clear;
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float* e = fold_base + (NT * r + n) * GP;
-          acc[n][r] += *e;
-          if (clear) *e = 0.0f;
-        }
-    }
-  };
   bool started = false;  // wave-uniform: a block has been folded into (m, l, acc)
 
   // One block. kFull (a compile-time tag) says the block is in range and all 16 of its
@@ -460,17 +353,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     const int tok0 = T.jb * kBlock + 4 * kg;
     bool valid[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) valid[r] = FULL || (T.ok && (tok0 + r < col_end));
-    // V bytes of tokens past the wave's last key are arbitrary: zeroed, as a NaN code
-    // times p = 0 would still be NaN (E2M1 has no NaN). The bound is the wave's, uniform
-    // over columns: a lane's V registers hold one channel group of these tokens for every
-    // column of the PV product, so per-column causal limits (MQ) act through p alone.
+    for (int r = 0; r < 4; ++r) valid[r] = FULL || (T.ok && (tok0 + r < end));
+    // V bytes of tokens past the context are arbitrary: zeroed, as a NaN code times p = 0
+    // would still be NaN (E2M1 has no NaN code)
     if constexpr (!FULL && KV != KV_FP4) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool keep = T.ok && tok0 + r < end;
 #pragma unroll
-        for (int i = 0; i < G_::VW; ++i) T.v[r][i] = keep ? T.v[r][i] : 0u;
+        for (int i = 0; i < G_::VW; ++i) T.v[r][i] = valid[r] ? T.v[r][i] : 0u;
       }
     }
 
@@ -526,9 +416,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     const float mb = group4_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
     if (__builtin_amdgcn_ballot_w64(mb > m + kRescale) != 0) {  // wave-uniform
       const float mn = fmaxf(m, mb);
-      if (started) {  // before the first block l, acc and the side buffer are all zero
+      if (started) {  // before the first block l and acc are all zero
         const float alpha = __builtin_amdgcn_exp2f(m - mn);
-        fold_side(true);
         l *= alpha;
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[n] *= alpha;
@@ -558,13 +447,11 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     const uint32_t l23 = pack2(pv[2] - lo16_to_f32(h23, PVB), pv[3] - hi16_to_f32(h23, PVB), PVB);
     const uint2 ph = make_uint2(h01, h23), pl = make_uint2(l01, l23);
 
-    // FP4 V outliers: out[c][ch] += sum_t p_t * o_t,ch (fp16 values, unscaled p); ch is
-    // wave-uniform (the record sits in scalar registers). Decode adds each term straight
-    // into its accumulator register, before this block's PV MFMAs, so the indexed register
-    // read waits only for the previous block's. Multi-token queries sum the terms in the
-    // LDS side accumulator instead, after the MFMAs (measured: the register form cost that
-    // loop 11%).
-    auto v_outliers = [&]() {
+    if constexpr (KV == KV_FP4) {
+      // V outliers: out[c][ch] += sum_t p_t * o_t,ch (fp16 values, unscaled p); ch is
+      // wave-uniform (the record sits in scalar registers). Each term goes straight into
+      // its accumulator register, before this block's PV MFMAs, so the indexed register
+      // read waits only for the previous block's.
       uint32_t rw[3] = {(uint32_t)__builtin_amdgcn_readlane((int)T.r0, 32), 0u, 0u};
       int nv = (int)(rw[0] & 0xFFu);
       if (nv > 3 && nv != 0xFF) {
@@ -593,19 +480,11 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) part = __builtin_fmaf(pr[r], o4[r], part);
         part = group4_sum(part);
-        if constexpr (MQ) {
-          // the four lanes of column c hold the same reduced term and read the same old
-          // value, so they all write the same sum: no lane branch is needed
-          *side_at(ch) += part;
-          side_used = true;
-        } else {
-          // channel ch is entry ch % DL = NT r + n, in acc[n][r], of the lanes with
-          // kg = ch / DL
-          add_entry<NT>(acc, ch % DL, kg == ch / DL ? part : 0.0f);
-        }
+        // channel ch is entry ch % DL = NT r + n, in acc[n][r], of the lanes with
+        // kg = ch / DL
+        add_entry<NT>(acc, ch % DL, kg == ch / DL ? part : 0.0f);
       }
-    };
-    if constexpr (KV == KV_FP4 && !MQ) v_outliers();
+    }
     uint2 vf[NT];
     v_fragments<KV, D, PVB>(T, vf);
 #pragma unroll
@@ -613,7 +492,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
       acc[n] = mfma_k16(vf[n], ph, acc[n], PVB);
       acc[n] = mfma_k16(vf[n], pl, acc[n], PVB);
     }
-    if constexpr (KV == KV_FP4 && MQ) v_outliers();
   };
 
   // ---- block loop (single or double buffered, see DB) ----
@@ -638,19 +516,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     } else if (my_n > 0 && ta.ok) {
       compute(ta, std::false_type{});
     }
-  } else if constexpr (MQ) {
-    // full blocks, then the (at most two) blocks that reach past the wave's first query
-    Tile<KV, D> tile;
-    if (my_n > 0) load_tile(tile, 0);
-    int i = 0;
-    for (; i + 1 < my_n && i < nfull; ++i) {
-      if (tile.ok) compute(tile, std::true_type{});
-      load_tile(tile, i + 1);
-    }
-    for (; i < my_n; ++i) {
-      if (tile.ok) compute(tile, std::false_type{});
-      if (i + 1 < my_n) load_tile(tile, i + 1);
-    }
   } else {
     Tile<KV, D> tile;
     if (my_n > 0) load_tile(tile, 0);
@@ -663,30 +528,27 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 
   // ---- epilogue ----
   if (err_bits != 0 && lane == 0 && a.err) atomicOr(a.err, err_bits);
-  fold_side(false);
   const float lt = group4_sum(l);
   const float vscale = head_scaled(KV) ? a.v_scale[kvh] : 1.0f;
   const int h = kvh * G + c;
-  if (W == 1 || MQ) {
-    if (MQ ? jc < nq : c < G) {
+  if (W == 1) {
+    if (c < G) {
       const float inv = lt > 0.0f ? vscale / lt : 0.0f;  // 0: every block id was bad
-      float* dst = MQ ? a.out + ((int64_t)(q0 + jc) * Hq + kvh * G + c % G) * D
-                   : split ? a.part_out + (((int64_t)s * Hq + h) * a.max_partitions + p) * D
-                           : a.out + ((int64_t)s * Hq + h) * D;
+      float* dst = split ? a.part_out + (((int64_t)s * Hq + h) * a.max_partitions + p) * D
+                         : a.out + ((int64_t)s * Hq + h) * D;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int n = 0; n < NT; ++n) dst[DL * kg + NT * r + n] = acc[n][r] * inv;
-      if (!MQ && split && kg == 0)
+      if (split && kg == 0)
         a.part_lse[((int64_t)s * Hq + h) * a.max_partitions + p] = (m + __log2f(lt)) * kLn2;
     }
     return;
   }
 
-  // W > 1: merge the waves' states in LDS. FP4: the merge reuses the LDS of the q copy,
-  // the side accumulators and the id slots, so every wave must be past its block loop
-  // and its fold first (the merge then costs no LDS of its own, and a 2-wave workgroup
-  // keeps the occupancy of two 1-wave ones).
+  // W > 1: merge the waves' states in LDS. FP4: the merge reuses the LDS of the q copy and
+  // the id slots, so every wave must be past its block loop first (the merge then costs no
+  // LDS of its own, and a 2-wave workgroup keeps the occupancy of two 1-wave ones).
   constexpr int STRIDE = DL + 4;  // floats per lane record (padded)
   if constexpr (KV == KV_FP4) __syncthreads();
   float* m_lds = smem;
@@ -738,7 +600,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 // (5 waves per SIMD for FP8 at head_dim 128).
 template <int KV, int D, bool QBF, int GP, bool APPEND = false>
 __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
-  decode_body<KV, D, QBF, GP, false, false, APPEND>(a);
+  decode_body<KV, D, QBF, GP, false, APPEND>(a);
 }
 
 // FP4 pools: a tile is half the bytes of an FP8 one, so one tile per wave leaves too little
@@ -747,14 +609,7 @@ __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
 template <int D, bool QBF, int GP, bool APPEND = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_fp4(
     DecodeArgs a) {
-  decode_body<KV_FP4, D, QBF, GP, true, false, APPEND>(a);
-}
-
-// Multi-token queries: 4 waves of 16 (query, head) columns each; single-buffered.
-constexpr int kPrefillWaves = 4;
-template <int KV, int D, bool QBF>
-__global__ __launch_bounds__(64 * kPrefillWaves) void k_prefill(DecodeArgs a) {
-  decode_body<KV, D, QBF, 16, false, true>(a);
+  decode_body<KV_FP4, D, QBF, GP, true, APPEND>(a);
 }
 
 template <int KV, int D, int GP>
@@ -791,68 +646,6 @@ static int launch_one(const DecodeArgs& a, int waves, hipStream_t st) {
     hipLaunchKernelGGL((k_decode<KV, D, QBF, GP, false>), grid, dim3(64 * waves), lds, st, a);
   }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
-}
-
-template <int KV, int D, bool QBF>
-static int launch_prefill_one(const DecodeArgs& a, hipStream_t st) {
-  const int qpw = kBlock / a.group;  // queries per wave
-  const int per_wg = kPrefillWaves * qpw;
-  const int tiles = (a.max_query_len + per_wg - 1) / per_wg;
-  if (tiles == 0 || a.num_seqs == 0) return PA_OK;
-  const size_t lds =
-      KV == KV_FP4
-          ? (size_t)kPrefillWaves * (fp4_qlds_floats<D, 16>() + fp4_side_floats<D, 16>()) * 4
-          : 0;
-  const dim3 grid((unsigned)((int64_t)tiles * a.num_kv_heads), (unsigned)a.num_seqs, 1);
-  hipLaunchKernelGGL((k_prefill<KV, D, QBF>), grid, dim3(64 * kPrefillWaves), lds, st, a);
-  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
-}
-
-int launch_prefill(const DecodeArgs& a, int kv, bool qbf, int D, hipStream_t st) {
-  if (kv != KV_FP4) {
-    // column tiles per wave: 3 (2 with PA_PREFILL_NCT=2, for tuning)
-    const char* e = getenv("PA_PREFILL_NCT");
-    return launch_prefill_mt(a, kv, qbf, D, e && *e ? atoi(e) : 3, st);
-  }
-  if (D == 128) {
-    switch (kv) {
-      case KV_F16: return launch_prefill_one<KV_F16, 128, false>(a, st);
-      case KV_BF16: return launch_prefill_one<KV_BF16, 128, true>(a, st);
-      case KV_FP8:
-        return qbf ? launch_prefill_one<KV_FP8, 128, true>(a, st)
-                   : launch_prefill_one<KV_FP8, 128, false>(a, st);
-      case KV_BF8:
-        return qbf ? launch_prefill_one<KV_BF8, 128, true>(a, st)
-                   : launch_prefill_one<KV_BF8, 128, false>(a, st);
-      case KV_FP8T:
-        return qbf ? launch_prefill_one<KV_FP8T, 128, true>(a, st)
-                   : launch_prefill_one<KV_FP8T, 128, false>(a, st);
-      case KV_BF8T:
-        return qbf ? launch_prefill_one<KV_BF8T, 128, true>(a, st)
-                   : launch_prefill_one<KV_BF8T, 128, false>(a, st);
-      case KV_FP4:
-        return qbf ? launch_prefill_one<KV_FP4, 128, true>(a, st)
-                   : launch_prefill_one<KV_FP4, 128, false>(a, st);
-    }
-  } else {
-    switch (kv) {
-      case KV_F16: return launch_prefill_one<KV_F16, 64, false>(a, st);
-      case KV_BF16: return launch_prefill_one<KV_BF16, 64, true>(a, st);
-      case KV_FP8:
-        return qbf ? launch_prefill_one<KV_FP8, 64, true>(a, st)
-                   : launch_prefill_one<KV_FP8, 64, false>(a, st);
-      case KV_BF8:
-        return qbf ? launch_prefill_one<KV_BF8, 64, true>(a, st)
-                   : launch_prefill_one<KV_BF8, 64, false>(a, st);
-      case KV_FP8T:
-        return qbf ? launch_prefill_one<KV_FP8T, 64, true>(a, st)
-                   : launch_prefill_one<KV_FP8T, 64, false>(a, st);
-      case KV_BF8T:
-        return qbf ? launch_prefill_one<KV_BF8T, 64, true>(a, st)
-                   : launch_prefill_one<KV_BF8T, 64, false>(a, st);
-    }
-  }
-  return PA_ERR_DTYPE;
 }
 
 int launch_decode(const DecodeArgs& a, int kv, bool qbf, int D, int waves, hipStream_t st) {

@@ -54,10 +54,8 @@ struct DecodeArgs {
 
 int launch_decode(const DecodeArgs& a, int kv_dtype, bool q_bf16, int head_dim, int waves,
                   hipStream_t st);
+// multi-token queries (pa_prefill): the paired-block kernel, every pool format
 int launch_prefill(const DecodeArgs& a, int kv_dtype, bool q_bf16, int head_dim, hipStream_t st);
-// 16-bit and FP8 pools: the paired-block multi-query kernel, nct column tiles per wave
-int launch_prefill_mt(const DecodeArgs& a, int kv_dtype, bool q_bf16, int head_dim, int nct,
-                      hipStream_t st);
 
 // Whole-block copy: array j of the pool has vecs_per_block[j] 16-byte vectors per block.
 struct CopyArgs {

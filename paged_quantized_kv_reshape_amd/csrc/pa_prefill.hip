@@ -1,4 +1,4 @@
-// pa_prefill.hip - multi-token paged attention on gfx950 for 16-bit and FP8 pools: the
+// pa_prefill.hip - multi-token paged attention on gfx950, every pool format: the
 // queries of a prompt chunk processed after their keys and values were written (chunked
 // prefill, dailyaiworld.com, "vLLM 0.7 Ships Unified KV Cache Compression", engine diagram
 // with 512-token chunks), or the tokens a draft model proposed (inferensys glossary
@@ -22,6 +22,12 @@
 //                 4 kg + i of A (i < 4) or 4 kg + i - 4 of B (i >= 4) - the order in which
 //                 the lane already holds both its probabilities and its V^T values. P
 //                 enters as a hi + lo pair of 16-bit values (about 16 significant bits).
+// FP4 pools (dailyaiworld.com, same page, "Technical Breakdown", step 4): the logits take
+// the token scale and the K outliers' fp16 terms (q from the fragments already in LDS), P
+// takes the V token scale, and each V outlier's term goes straight into the accumulator
+// register of its channel (register indexing with a wave-uniform channel).
+#include <stdlib.h>
+
 #include <type_traits>
 
 #include "pa_device.h"
@@ -44,8 +50,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
 void k_prefill_mt(DecodeArgs a) {
   using G_ = Geo<KV, D>;
   constexpr int KS = G_::KS, NT = G_::NT, DL = G_::DL;
-  constexpr bool PVB = QBF;  // PV MFMA type: the query's (FP8 codes are exact in both)
-  static_assert(KV != KV_FP4, "FP4 pools use the decode kernel's multi-query mode");
+  // PV MFMA type: the query's (FP8 codes are exact in both); FP4 in bf16, since p s_t (the
+  // V token scale folded into p) may leave fp16's range
+  constexpr bool PVB = QBF || KV == KV_FP4;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -94,7 +101,8 @@ void k_prefill_mt(DecodeArgs a) {
   // The q fragments wait in LDS, each lane reading back only what it wrote (no barrier):
   // registers go to the accumulators of more column tiles instead.
   extern __shared__ uint4 q_lds_all[];
-  uint4* const q_lds = q_lds_all + (int64_t)wave * NCT * KS * 64 + lane;
+  uint4* const q_wave = q_lds_all + (int64_t)wave * NCT * KS * 64;
+  uint4* const q_lds = q_wave + lane;
   int col_end[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
@@ -139,9 +147,28 @@ void k_prefill_mt(DecodeArgs a) {
     err_bits |= T.ok ? 0 : PA_DEVERR_BAD_BLOCK;
     T.tile = (int64_t)(T.ok ? b_raw : 0) * a.num_kv_heads + kvh;
     load_words(T.k, kpool + T.tile * G_::TILEB + k_lane_off);
+    if constexpr (KV == KV_FP4) {
+      const uint8_t* kt = kpool + T.tile * G_::TILEB;
+      const uint8_t* vt = vpool + T.tile * G_::TILEB;
+      // V is stored by channel: one 16-byte chunk, channels 8 c .. 8 c + 7 of tokens
+      // 4 kg .. 4 kg + 3
+      const uint4 x = *reinterpret_cast<const uint4*>(vt + (c * 4 + kg) * 16);
+      T.v[0][0] = x.x;
+      T.v[1][0] = x.y;
+      T.v[2][0] = x.z;
+      T.v[3][0] = x.w;
+      // per-token scales, the first word of each outlier record (lanes 0-31 K's, 32-63
+      // V's) and the first outlier slot, which a full block usually fills exactly
+      T.sk = reinterpret_cast<const float4*>(kt + PA_FP4_SCALE_OFF(D))[kg];
+      T.sv = reinterpret_cast<const float4*>(vt + PA_FP4_SCALE_OFF(D))[kg];
+      T.r0 = *reinterpret_cast<const uint32_t*>((lane < 32 ? kt : vt) + PA_FP4_RECORD_OFF(D));
+      T.k_o0 = reinterpret_cast<const uint2*>(kt + PA_FP4_SLOT0_OFF(D))[kg];
+      T.v_o0 = reinterpret_cast<const uint2*>(vt + PA_FP4_SLOT0_OFF(D))[kg];
+    } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      load_words(T.v[r], vpool + T.tile * G_::TILEB + v_lane_off + r * G_::ROWB);
+      for (int r = 0; r < 4; ++r)
+        load_words(T.v[r], vpool + T.tile * G_::TILEB + v_lane_off + r * G_::ROWB);
+    }
     if constexpr (f8_tok(KV)) {
       T.sk = reinterpret_cast<const float4*>(kpool + T.tile * G_::TILEB + PA_FP8T_SCALE_OFF(D))[kg];
       T.sv = reinterpret_cast<const float4*>(vpool + T.tile * G_::TILEB + PA_FP8T_SCALE_OFF(D))[kg];
@@ -156,6 +183,8 @@ void k_prefill_mt(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < G_::VW; ++i) T.v[r][i] = 0u;
     T.sk = T.sv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    T.r0 = 0u;  // no outliers
+    T.k_o0 = T.v_o0 = make_uint2(0u, 0u);
     T.jb = x;
     T.ok = false;
     T.tile = 0;
@@ -175,9 +204,10 @@ void k_prefill_mt(DecodeArgs a) {
 
   auto compute = [&](Tile<KV, D>& TA, Tile<KV, D>& TB, auto kFull) {
     constexpr bool FULL = decltype(kFull)::value;
-    if constexpr (!FULL) {
+    if constexpr (!FULL && KV != KV_FP4) {
       // V bytes of tokens past the wave's last key are arbitrary (a NaN code times p = 0
-      // is still NaN): zeroed, with the wave's bound, which holds for every column
+      // is still NaN): zeroed, with the wave's bound, which holds for every column (E2M1
+      // has no NaN code, so FP4 codes need no zeroing)
       auto mask_v = [&](Tile<KV, D>& T) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -189,20 +219,97 @@ void k_prefill_mt(DecodeArgs a) {
       mask_v(TA);
       mask_v(TB);
     }
+    // FP4 K outliers of one block for column tile ct: ok[r] = sum_j q[ch_j] o_(4 kg + r),ch_j
+    // (fp16 values times the query in fp32). The record sits in scalar registers, so ch is
+    // wave-uniform; column c's query value of channel ch is read from the q fragments in
+    // LDS, where lane (c, ch / DL) stored it (fragment (ch % DL) / 8, element ch % 8).
+    auto k_outliers = [&](const Tile<KV, D>& T, int ct, float* ok) {
+      ok[0] = ok[1] = ok[2] = ok[3] = 0.0f;
+      uint32_t rw[3] = {(uint32_t)__builtin_amdgcn_readlane((int)T.r0, 0), 0u, 0u};
+      int nk = (int)(rw[0] & 0xFFu);
+      if (nk > 3 && nk != 0xFF) {  // more channels than the first word holds (rare)
+        const uint4 r = load_uniform16(kpool + T.tile * G_::TILEB + PA_FP4_RECORD_OFF(D));
+        rw[1] = r.y;
+        rw[2] = r.z;
+      }
+      if (nk == 0xFF) {
+        err_bits |= T.ok ? PA_DEVERR_UNCALIBRATED : 0;
+        nk = 0;
+      }
+      if (nk > a.cap) nk = a.cap;
+      for (int j = 0; j < nk; ++j) {
+        const int pos = 1 + j;
+        const int ch = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
+        const uint16_t* qh = reinterpret_cast<const uint16_t*>(
+            q_wave + (ct * KS + (ch % DL) / 8) * 64 + c + 16 * (ch / DL));
+        const float qv = act_to_f32<QBF>(qh[ch % 8]);
+        const uint2 ov = j == 0 ? T.k_o0
+                                : *reinterpret_cast<const uint2*>(
+                                      a.k_out_val + ((T.tile * (a.cap - 1) + (j - 1)) * kBlock +
+                                                     4 * kg));
+        ok[0] = __builtin_fmaf(qv, f16_bits_to_f32(ov.x & 0xFFFFu), ok[0]);
+        ok[1] = __builtin_fmaf(qv, f16_bits_to_f32(ov.x >> 16), ok[1]);
+        ok[2] = __builtin_fmaf(qv, f16_bits_to_f32(ov.y & 0xFFFFu), ok[2]);
+        ok[3] = __builtin_fmaf(qv, f16_bits_to_f32(ov.y >> 16), ok[3]);
+      }
+    };
+    // FP4 V outliers of one block for column tile ct: out[c][ch] += sum_t p_t o_t,ch with
+    // the unscaled p of the block's tokens 4 kg .. 4 kg + 3 (p4), summed over the four lanes
+    // of the column and added straight into the accumulator register of channel ch
+    auto v_outliers = [&](const Tile<KV, D>& T, int ct, const float* p4) {
+      uint32_t rw[3] = {(uint32_t)__builtin_amdgcn_readlane((int)T.r0, 32), 0u, 0u};
+      int nv = (int)(rw[0] & 0xFFu);
+      if (nv > 3 && nv != 0xFF) {
+        const uint4 r = load_uniform16(vpool + T.tile * G_::TILEB + PA_FP4_RECORD_OFF(D));
+        rw[1] = r.y;
+        rw[2] = r.z;
+      }
+      if (nv == 0xFF) {
+        err_bits |= T.ok ? PA_DEVERR_UNCALIBRATED : 0;
+        nv = 0;
+      }
+      if (nv > a.cap) nv = a.cap;
+      const int tok0 = T.jb * kBlock + 4 * kg;
+      for (int j = 0; j < nv; ++j) {
+        const int pos = 1 + j;
+        const int ch = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
+        const uint2 ov = j == 0 ? T.v_o0
+                                : *reinterpret_cast<const uint2*>(
+                                      a.v_out_val + ((T.tile * (a.cap - 1) + (j - 1)) * kBlock +
+                                                     4 * kg));
+        // slots of tokens past the wave's last key hold arbitrary bits (maybe NaN): masked
+        // with the wave's bound; the causal limits of the columns act through p
+        const uint32_t oh[4] = {ov.x & 0xFFFFu, ov.x >> 16, ov.y & 0xFFFFu, ov.y >> 16};
+        float part = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool keep = FULL || (T.ok && tok0 + r < end);
+          part = __builtin_fmaf(p4[r], keep ? f16_bits_to_f32(oh[r]) : 0.0f, part);
+        }
+        part = group4_sum(part);
+        // channel ch is entry ch % DL = NT r + n, in acc[ct][n][r], of the lanes with
+        // kg = ch / DL
+        add_entry<NT>(acc[ct], ch % DL, kg == ch / DL ? part : 0.0f);
+      }
+    };
     // logits of tokens 4 kg .. 4 kg + 3 of one block for column tile ct, masked
     auto logits = [&](const Tile<KV, D>& T, const f32x4& sa, int ct, float* z) {
       const int tok0 = T.jb * kBlock + 4 * kg;
       float sk[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-      if constexpr (f8_tok(KV)) {
+      if constexpr (tok_scaled(KV)) {
         sk[0] = T.sk.x;
         sk[1] = T.sk.y;
         sk[2] = T.sk.z;
         sk[3] = T.sk.w;
       }
+      float ok[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (KV == KV_FP4) k_outliers(T, ct, ok);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool valid = FULL || (T.ok && tok0 + r < col_end[ct]);
-        z[r] = valid ? sa[r] * sk[r] * cz : -INFINITY;
+        // (sk = 1 folds away; an fma with 1 and 0 would not, as it turns -0 into +0)
+        const float x = KV == KV_FP4 ? __builtin_fmaf(sa[r], sk[r], ok[r]) : sa[r] * sk[r];
+        z[r] = valid ? x * cz : -INFINITY;
       }
     };
     // logits of both blocks for every column tile; each K fragment feeds NCT MFMAs
@@ -271,15 +378,17 @@ void k_prefill_mt(DecodeArgs a) {
         l[ct] += p;
         pv[i] = p;
       }
-      if constexpr (f8_tok(KV)) {  // PV runs on the codes: p times the V token scale
-        pv[0] *= TA.sv.x;
-        pv[1] *= TA.sv.y;
-        pv[2] *= TA.sv.z;
-        pv[3] *= TA.sv.w;
-        pv[4] *= TB.sv.x;
-        pv[5] *= TB.sv.y;
-        pv[6] *= TB.sv.z;
-        pv[7] *= TB.sv.w;
+      if constexpr (KV == KV_FP4) {  // before p takes the V token scale
+        v_outliers(TA, ct, pv);
+        v_outliers(TB, ct, pv + 4);
+      }
+      if constexpr (tok_scaled(KV)) {
+        // PV runs on the codes: p times the V token scale. A masked token's p is 0 and its
+        // scale slot may hold any bits (a NaN times 0 is still NaN), so it stays 0.
+        const float sv[8] = {TA.sv.x, TA.sv.y, TA.sv.z, TA.sv.w,
+                             TB.sv.x, TB.sv.y, TB.sv.z, TB.sv.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pv[i] = FULL || pv[i] != 0.0f ? pv[i] * sv[i] : 0.0f;
       }
       uint32_t h[4], lo[4];
 #pragma unroll
@@ -373,14 +482,22 @@ int launch_d(const DecodeArgs& a, int kv, bool qbf, int nct, hipStream_t st) {
       return qbf ? launch_kv<KV_FP8T, D, true>(a, nct, st) : launch_kv<KV_FP8T, D, false>(a, nct, st);
     case KV_BF8T:
       return qbf ? launch_kv<KV_BF8T, D, true>(a, nct, st) : launch_kv<KV_BF8T, D, false>(a, nct, st);
+    case KV_FP4:
+      if constexpr (D == 128)
+        return qbf ? launch_kv<KV_FP4, D, true>(a, nct, st) : launch_kv<KV_FP4, D, false>(a, nct, st);
+      break;
   }
   return PA_ERR_DTYPE;
 }
 
 }  // namespace
 
-int launch_prefill_mt(const DecodeArgs& a, int kv, bool qbf, int D, int nct, hipStream_t st) {
-  if (kv == KV_FP4) return PA_ERR_DTYPE;
+int launch_prefill(const DecodeArgs& a, int kv, bool qbf, int D, hipStream_t st) {
+  // column tiles per wave: 3, or 2 for FP4 pools, whose tiles carry scales, records and
+  // outlier slots (3 spill there: 258 vs 316 TFLOP/s on the long-context workload);
+  // PA_PREFILL_NCT=2 or 3 overrides, for tuning
+  const char* e = getenv("PA_PREFILL_NCT");
+  const int nct = e && *e ? atoi(e) : kv == KV_FP4 ? 2 : 3;
   return D == 128 ? launch_d<128>(a, kv, qbf, nct, st) : launch_d<64>(a, kv, qbf, nct, st);
 }
 

@@ -203,4 +203,22 @@ __device__ __forceinline__ void v_fragments_group(const Tile<KV, D>& T, uint2 (&
   }
 }
 
+
+// acc[n][r] += x for the entry e = NT r + n (wave-uniform) of a lane's output channels
+// (channel DL kg + NT r + n of the lane's column, DL = 4 NT). The accumulators are viewed as
+// one register vector, so the uniform index becomes the hardware's register indexing
+// (s_set_gpr_idx_on) on the registers in place: no copy of the accumulators and no trip
+// through memory. (A branch tree over the entries instead is merged by the compiler into
+// an indexed store, which moves the accumulators to scratch.)
+template <int NT>
+__device__ __forceinline__ void add_entry(f32x4 (&acc)[NT], int e, float x) {
+  typedef float flat_t __attribute__((ext_vector_type(4 * NT)));
+  flat_t w;
+#pragma unroll
+  for (int t = 0; t < 4 * NT; ++t) w[t] = acc[t / 4][t % 4];
+  w[__builtin_amdgcn_readfirstlane(4 * (e % NT) + e / NT)] += x;  // acc[n][r] at 4 n + r
+#pragma unroll
+  for (int t = 0; t < 4 * NT; ++t) acc[t / 4][t % 4] = w[t];
+}
+
 }  // namespace pa
