@@ -1,0 +1,136 @@
+"""GPU parity of FP4 pools whose blocks hold many outlier channels.
+
+The long-context workload plants one x20 channel, so its blocks mostly record a single
+outlier and the kernels rarely leave the first outlier slot. Here 9 K channels and 6 V
+channels (besides the planted one) are scaled by 30, which puts 3 to 9 outliers into a
+block (dailyaiworld.com, "vLLM 0.7 Ships Unified KV Cache Compression", "Technical
+Breakdown", steps 1-2: channels at or above 3.2 sigma of the channel RMS are kept in fp16).
+That reaches every record word (count and channels 1-3, 4-7, 8-11) and the outlier slots
+past the first one, in the cache write, the decode (single pass and split), the
+write-and-decode launch and multi-token attention. Pools bit-exact; outputs within max-abs
+2e-3 and relative L2 1e-2 of the oracle's exact attention on the same dequantized cache."""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import cache as C
+from oracle_side import assert_close, assert_pool_equal, oracle_decode, replay
+from workload import config, prefill_queries
+from workload.gen import _round_into
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from test_parity_gpu import _say  # noqa: E402
+
+K_CHANNELS = [3, 17, 29, 40, 64, 77, 90, 101, 127]
+V_CHANNELS = [5, 33, 58, 71, 96, 120]
+_cache = {}
+
+
+def _plant(rows, channels, act, scale=30.0):
+    """Scale some channels of 16-bit rows in place (rounded back to the activation dtype)."""
+    if act == "bf16":
+        f = (rows.astype(np.uint32) << 16).view(np.float32)
+    else:
+        f = rows.view(np.float16).astype(np.float32)
+    f = np.ascontiguousarray(f)
+    f[:, :, channels] *= np.float32(scale)
+    _round_into(f, act, rows, np.empty(f.shape, np.uint32))
+
+
+def _workload(act):
+    """Three sequences; the 705-token one writes its last row into a fresh block."""
+    if act not in _cache:
+        w = config("c5", num_seqs=3, lens=[705, 333, 1500], act=act)
+        _plant(w.k_rows, K_CHANNELS, act)
+        _plant(w.v_rows, V_CHANNELS, act)
+        pool, ks, vs, near = replay(w)
+        # the case is what it claims: blocks with 4+ outliers on both sides, 8+ on K
+        counts = {kv: C.fp4_records(pool, kv)[..., 0] for kv in ("k", "v")}
+        used = {kv: c[c != 0xFF] for kv, c in counts.items()}
+        assert (used["k"] >= 8).sum() > 0 and (used["k"] >= 4).mean() > 0.9
+        assert (used["v"] >= 4).mean() > 0.9
+        _cache[act] = (w, pool, ks, vs, near)
+    return _cache[act]
+
+
+@pytest.fixture(autouse=True)
+def _waves_env():
+    old = os.environ.get("PA_DECODE_WAVES")
+    yield
+    if old is None:
+        os.environ.pop("PA_DECODE_WAVES", None)
+    else:
+        os.environ["PA_DECODE_WAVES"] = old
+
+
+@pytest.mark.parametrize("waves", [1, 2])
+@pytest.mark.parametrize("ps", [0, 64, 512])
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+def test_many_outliers_write_and_decode(act, ps, waves):
+    from paged_quantized_kv_reshape_amd.harness import DeviceRun
+    w, pool, ks, vs, near = _workload(act)
+    os.environ["PA_DECODE_WAVES"] = str(waves)
+    _say(f"[fp4 many outliers] {act} ps={ps} W={waves}")
+    run = DeviceRun(w, partition_size=ps)
+    run.prepare()
+    run.decode()
+    torch.cuda.synchronize()
+    assert run.device_error() == 0
+    assert_pool_equal(run.pool.numpy(), pool, near=near)
+    ref = oracle_decode(w, pool, ks, vs, range(w.num_seqs))
+    assert_close(run.out.cpu().numpy(), np.stack([ref[s][0] for s in range(w.num_seqs)]),
+                 f"many outliers {act} ps={ps} W={waves}")
+
+
+@pytest.mark.parametrize("ps", [0, 512])
+def test_many_outliers_append_decode(ps):
+    """The step's row written by the decode launch itself (the fresh block of sequence 0
+    is calibrated on that row): pool bit-exact, output bitwise equal to the separate
+    write and decode."""
+    from paged_quantized_kv_reshape_amd.harness import DeviceRun
+    w, pool, ks, vs, near = _workload("bf16")
+    _say(f"[fp4 many outliers append] ps={ps}")
+    fused = DeviceRun(w, partition_size=ps)
+    fused.setup_writes()
+    fused.append_decode()
+    sep = DeviceRun(w, partition_size=ps)
+    sep.prepare()
+    sep.decode()
+    torch.cuda.synchronize()
+    assert fused.device_error() == 0 and sep.device_error() == 0
+    assert_pool_equal(fused.pool.numpy(), pool, near=near)
+    got = fused.out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), sep.out.cpu().numpy().view(np.uint32))
+    ref = oracle_decode(w, pool, ks, vs, range(w.num_seqs))
+    assert_close(got, np.stack([ref[s][0] for s in range(w.num_seqs)]),
+                 f"many outliers append ps={ps}")
+
+
+@pytest.mark.parametrize("n", [1, 37, 333])
+@pytest.mark.parametrize("act", ["bf16", "f16"])
+def test_many_outliers_prefill(act, n):
+    from paged_quantized_kv_reshape_amd import pa_prefill
+    from paged_quantized_kv_reshape_amd.harness import DeviceRun
+    w, pool, ks, vs, near = _workload(act)
+    _say(f"[fp4 many outliers prefill] {act} n={n}")
+    run = DeviceRun(w, partition_size=0)
+    run.prepare()
+    q_bits, qs = prefill_queries(w, n)
+    tdt = torch.bfloat16 if act == "bf16" else torch.float16
+    q = torch.from_numpy(q_bits.view(np.int16)).cuda().view(tdt)
+    out = torch.full((q.shape[0], w.num_q_heads, w.head_dim), float("nan"),
+                     dtype=torch.float32, device="cuda")
+    run.dev_err.zero_()
+    pa_prefill(q, torch.from_numpy(qs).cuda(), int(np.diff(qs).max()), run.pool,
+               run.block_tables, run.context_lens, w.sm_scale, out, run.dev_err)
+    torch.cuda.synchronize()
+    assert run.device_error() == 0
+    ref = A.paged_prefill(q_bits, w.act, pool, w.block_tables, w.context_lens, qs, w.sm_scale,
+                          ks, vs)
+    assert_close(out.cpu().numpy(), np.concatenate([ref[s] for s in range(w.num_seqs)]),
+                 f"many outliers prefill {act} n={n}")
