@@ -386,7 +386,7 @@ def prefill_main(args, config, DESCRIPTIONS):
                    "head_dim": w.head_dim},
         "algorithmic_flops": flops,
         "wall_ms_per_step": round(wall * 1e3, 4),
-        "roofline": {"kernel": "k_prefill" if w.kv == "fp4" else "k_prefill_mt", "bound": "mfma",
+        "roofline": {"kernel": "k_prefill_mt", "bound": "mfma",
                      "achieved": round(tflops, 2),
                      "peak": 2500.0, "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4),
                      "traffic": None},
