@@ -38,6 +38,17 @@ namespace pa {
 namespace {
 
 constexpr int kWaves = 4;
+
+// An FP4 outlier record in scalar registers: the count (capped) and the channel bytes
+// 1 .. 11 of the record's first three words
+struct Rec {
+  uint32_t w[3];
+  int n;
+  __device__ int channel(int j) const {
+    const int pos = 1 + j;
+    return (int)((w[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
+  }
+};
 constexpr float kRescaleLog2 = 8.0f;  // lazy-rescale threshold, log2 units
 
 // q fragments of one wave in LDS: [NCT][KS][64 lanes] x 16 bytes
@@ -219,27 +230,41 @@ void k_prefill_mt(DecodeArgs a) {
       mask_v(TA);
       mask_v(TB);
     }
+    // FP4 outlier record of one block and side (0: K, from lane 0's word; 1: V, lane 32's),
+    // decoded once per pair and used by every column tile; wave-uniform
+    auto read_rec = [&](const Tile<KV, D>& T, int side) {
+      Rec r;
+      r.w[0] = (uint32_t)__builtin_amdgcn_readlane((int)T.r0, 32 * side);
+      r.w[1] = r.w[2] = 0u;
+      int n = (int)(r.w[0] & 0xFFu);
+      if (n > 3 && n != 0xFF) {  // more channels than the first word holds (rare)
+        const uint4 x = load_uniform16((side ? vpool : kpool) + T.tile * G_::TILEB +
+                                       PA_FP4_RECORD_OFF(D));
+        r.w[1] = x.y;
+        r.w[2] = x.z;
+      }
+      if (n == 0xFF) {
+        err_bits |= T.ok ? PA_DEVERR_UNCALIBRATED : 0;
+        n = 0;
+      }
+      r.n = n > a.cap ? a.cap : n;
+      return r;
+    };
+    Rec rka, rkb, rva, rvb;
+    if constexpr (KV == KV_FP4) {
+      rka = read_rec(TA, 0);
+      rkb = read_rec(TB, 0);
+      rva = read_rec(TA, 1);
+      rvb = read_rec(TB, 1);
+    }
     // FP4 K outliers of one block for column tile ct: ok[r] = sum_j q[ch_j] o_(4 kg + r),ch_j
     // (fp16 values times the query in fp32). The record sits in scalar registers, so ch is
     // wave-uniform; column c's query value of channel ch is read from the q fragments in
     // LDS, where lane (c, ch / DL) stored it (fragment (ch % DL) / 8, element ch % 8).
-    auto k_outliers = [&](const Tile<KV, D>& T, int ct, float* ok) {
+    auto k_outliers = [&](const Tile<KV, D>& T, const Rec& rk, int ct, float* ok) {
       ok[0] = ok[1] = ok[2] = ok[3] = 0.0f;
-      uint32_t rw[3] = {(uint32_t)__builtin_amdgcn_readlane((int)T.r0, 0), 0u, 0u};
-      int nk = (int)(rw[0] & 0xFFu);
-      if (nk > 3 && nk != 0xFF) {  // more channels than the first word holds (rare)
-        const uint4 r = load_uniform16(kpool + T.tile * G_::TILEB + PA_FP4_RECORD_OFF(D));
-        rw[1] = r.y;
-        rw[2] = r.z;
-      }
-      if (nk == 0xFF) {
-        err_bits |= T.ok ? PA_DEVERR_UNCALIBRATED : 0;
-        nk = 0;
-      }
-      if (nk > a.cap) nk = a.cap;
-      for (int j = 0; j < nk; ++j) {
-        const int pos = 1 + j;
-        const int ch = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
+      for (int j = 0; j < rk.n; ++j) {
+        const int ch = rk.channel(j);
         const uint16_t* qh = reinterpret_cast<const uint16_t*>(
             q_wave + (ct * KS + (ch % DL) / 8) * 64 + c + 16 * (ch / DL));
         const float qv = act_to_f32<QBF>(qh[ch % 8]);
@@ -256,23 +281,10 @@ void k_prefill_mt(DecodeArgs a) {
     // FP4 V outliers of one block for column tile ct: out[c][ch] += sum_t p_t o_t,ch with
     // the unscaled p of the block's tokens 4 kg .. 4 kg + 3 (p4), summed over the four lanes
     // of the column and added straight into the accumulator register of channel ch
-    auto v_outliers = [&](const Tile<KV, D>& T, int ct, const float* p4) {
-      uint32_t rw[3] = {(uint32_t)__builtin_amdgcn_readlane((int)T.r0, 32), 0u, 0u};
-      int nv = (int)(rw[0] & 0xFFu);
-      if (nv > 3 && nv != 0xFF) {
-        const uint4 r = load_uniform16(vpool + T.tile * G_::TILEB + PA_FP4_RECORD_OFF(D));
-        rw[1] = r.y;
-        rw[2] = r.z;
-      }
-      if (nv == 0xFF) {
-        err_bits |= T.ok ? PA_DEVERR_UNCALIBRATED : 0;
-        nv = 0;
-      }
-      if (nv > a.cap) nv = a.cap;
+    auto v_outliers = [&](const Tile<KV, D>& T, const Rec& rv, int ct, const float* p4) {
       const int tok0 = T.jb * kBlock + 4 * kg;
-      for (int j = 0; j < nv; ++j) {
-        const int pos = 1 + j;
-        const int ch = (int)((rw[pos >> 2] >> ((pos & 3) * 8)) & 0xFFu);
+      for (int j = 0; j < rv.n; ++j) {
+        const int ch = rv.channel(j);
         const uint2 ov = j == 0 ? T.v_o0
                                 : *reinterpret_cast<const uint2*>(
                                       a.v_out_val + ((T.tile * (a.cap - 1) + (j - 1)) * kBlock +
@@ -293,7 +305,7 @@ void k_prefill_mt(DecodeArgs a) {
       }
     };
     // logits of tokens 4 kg .. 4 kg + 3 of one block for column tile ct, masked
-    auto logits = [&](const Tile<KV, D>& T, const f32x4& sa, int ct, float* z) {
+    auto logits = [&](const Tile<KV, D>& T, const Rec& rk, const f32x4& sa, int ct, float* z) {
       const int tok0 = T.jb * kBlock + 4 * kg;
       float sk[4] = {1.0f, 1.0f, 1.0f, 1.0f};
       if constexpr (tok_scaled(KV)) {
@@ -303,7 +315,7 @@ void k_prefill_mt(DecodeArgs a) {
         sk[3] = T.sk.w;
       }
       float ok[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if constexpr (KV == KV_FP4) k_outliers(T, ct, ok);
+      if constexpr (KV == KV_FP4) k_outliers(T, rk, ct, ok);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool valid = FULL || (T.ok && tok0 + r < col_end[ct]);
@@ -340,8 +352,8 @@ void k_prefill_mt(DecodeArgs a) {
     bool grow = false;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      logits(TA, sacc[0][ct], ct, z[ct]);
-      logits(TB, sacc[1][ct], ct, z[ct] + 4);
+      logits(TA, rka, sacc[0][ct], ct, z[ct]);
+      logits(TB, rkb, sacc[1][ct], ct, z[ct] + 4);
       float x = fmaxf(fmaxf(fmaxf(z[ct][0], z[ct][1]), fmaxf(z[ct][2], z[ct][3])),
                       fmaxf(fmaxf(z[ct][4], z[ct][5]), fmaxf(z[ct][6], z[ct][7])));
       mb[ct] = group4_max(x);
@@ -379,8 +391,8 @@ void k_prefill_mt(DecodeArgs a) {
         pv[i] = p;
       }
       if constexpr (KV == KV_FP4) {  // before p takes the V token scale
-        v_outliers(TA, ct, pv);
-        v_outliers(TB, ct, pv + 4);
+        v_outliers(TA, rva, ct, pv);
+        v_outliers(TB, rvb, ct, pv + 4);
       }
       if constexpr (tok_scaled(KV)) {
         // PV runs on the codes: p times the V token scale. A masked token's p is 0 and its
