@@ -303,19 +303,20 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     err_bits |= T.ok ? 0 : PA_DEVERR_BAD_BLOCK;
     const int b = T.ok ? b_raw : 0;
     T.tile = (int64_t)b * a.num_kv_heads + kvh;
-    load_words(T.k, kpool + T.tile * G_::TILEB + k_lane_off);
+    // each tile is read once per launch: streaming (non-temporal) loads
+    load_words<G_::KW, true>(T.k, kpool + T.tile * G_::TILEB + k_lane_off);
     if constexpr (KV == KV_FP4) {
       // one 16-byte chunk: channels 8 c .. 8 c + 7 of tokens 4 kg .. 4 kg + 3
-      const uint4 x =
-          *reinterpret_cast<const uint4*>(vpool + T.tile * G_::TILEB + (c * 4 + kg) * 16);
-      T.v[0][0] = x.x;
-      T.v[1][0] = x.y;
-      T.v[2][0] = x.z;
-      T.v[3][0] = x.w;
+      uint32_t x[4];
+      load_words<4, true>(x, vpool + T.tile * G_::TILEB + (c * 4 + kg) * 16);
+      T.v[0][0] = x[0];
+      T.v[1][0] = x[1];
+      T.v[2][0] = x[2];
+      T.v[3][0] = x[3];
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        load_words(T.v[r], vpool + T.tile * G_::TILEB + v_lane_off + r * G_::ROWB);
+        load_words<G_::VW, true>(T.v[r], vpool + T.tile * G_::TILEB + v_lane_off + r * G_::ROWB);
     }
     if constexpr (f8_tok(KV)) {  // per-token scales of tokens 4 kg .. 4 kg + 3
       T.sk = reinterpret_cast<const float4*>(kpool + T.tile * G_::TILEB + PA_FP8T_SCALE_OFF(D))[kg];

@@ -40,24 +40,34 @@ struct Geo {
   static constexpr int VLANEB = NT * EBITS / 8;    // V bytes per lane per token
 };
 
-template <int N>
+// N 32-bit words from p (16-byte aligned for N % 4 == 0). NT selects the non-temporal
+// form (the loads carry the streaming hint, so the lines they fill are the first the caches
+// give up): for K/V tiles that a launch reads exactly once, as in decode. Measured on the
+// 70B one-GPU share (FP8, 539 MB per launch): 94.1 -> 89.7 us per decode launch. Loops that
+// re-read tiles out of L2 (multi-token queries) keep the default form.
+template <int N, bool NT = false>
 __device__ __forceinline__ void load_words(uint32_t (&w)[N], const uint8_t* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   if constexpr (N % 4 == 0) {
 #pragma unroll
     for (int i = 0; i < N / 4; ++i) {
-      const uint4 x = reinterpret_cast<const uint4*>(p)[i];
+      const u32x4* q = reinterpret_cast<const u32x4*>(p) + i;
+      const u32x4 x = NT ? __builtin_nontemporal_load(q) : *q;
       w[4 * i] = x.x;
       w[4 * i + 1] = x.y;
       w[4 * i + 2] = x.z;
       w[4 * i + 3] = x.w;
     }
   } else if constexpr (N == 2) {
-    const uint2 x = *reinterpret_cast<const uint2*>(p);
+    const u32x2* q = reinterpret_cast<const u32x2*>(p);
+    const u32x2 x = NT ? __builtin_nontemporal_load(q) : *q;
     w[0] = x.x;
     w[1] = x.y;
   } else {
     static_assert(N == 1, "word count");
-    w[0] = *reinterpret_cast<const uint32_t*>(p);
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+    w[0] = NT ? __builtin_nontemporal_load(q) : *q;
   }
 }
 
