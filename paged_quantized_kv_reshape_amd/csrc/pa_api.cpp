@@ -262,6 +262,10 @@ int pa_copy_blocks(const pa_kv_pool* src, const pa_kv_pool* dst, const int32_t* 
   a.src_blocks = src->num_blocks;
   a.dst_blocks = dst->num_blocks;
   a.err = dev_err;
+  // within one pool both sides are device memory read and written once: streaming loads
+  // and stores (measured: 4.82 -> 5.06 TB/s for 65536 FP8 blocks); a swap touches pinned
+  // host memory, where the hint cost 1% (54.5 -> 54.1 GB/s), so it keeps the plain form
+  a.streaming = same;
   return pa::launch_copy_blocks(a, (hipStream_t)stream);
 }
 

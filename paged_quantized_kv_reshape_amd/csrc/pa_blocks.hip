@@ -27,6 +27,8 @@ constexpr int kSlots = 8;
 // from being promoted out of scratch memory)
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
+// NT: non-temporal loads and stores (each byte is read once and written once)
+template <bool NT>
 __global__ __launch_bounds__(64 * kWaves) void k_copy_blocks(CopyArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t pair = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
@@ -59,14 +61,19 @@ __global__ __launch_bounds__(64 * kWaves) void k_copy_blocks(CopyArgs a) {
       // loads need no branch; only the stores are masked
       const v4u* p = v < e0 || v >= total ? s0 : v < e1 ? s1 : v < e2 ? s2 : s3;
       const uint32_t o = v >= total ? 0u : v - (v < e0 ? 0u : v < e1 ? e0 : v < e2 ? e1 : e2);
-      r[u] = p[o];
+      r[u] = NT ? __builtin_nontemporal_load(p + o) : p[o];
     }
 #pragma unroll
     for (int u = 0; u < kSlots; ++u) {
       const uint32_t v = base + 64u * u + lane;
       v4u* p = v < e0 ? d0 : v < e1 ? d1 : v < e2 ? d2 : d3;
       const uint32_t o = v - (v < e0 ? 0u : v < e1 ? e0 : v < e2 ? e1 : e2);
-      if (v < total) p[o] = r[u];
+      if (v < total) {
+        if constexpr (NT)
+          __builtin_nontemporal_store(r[u], p + o);
+        else
+          p[o] = r[u];
+      }
     }
   }
 }
@@ -76,7 +83,10 @@ __global__ __launch_bounds__(64 * kWaves) void k_copy_blocks(CopyArgs a) {
 int launch_copy_blocks(const CopyArgs& a, hipStream_t st) {
   if (a.num_pairs == 0) return PA_OK;
   const int64_t gx = ((int64_t)a.num_pairs + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL(k_copy_blocks, dim3((unsigned)gx), dim3(64 * kWaves), 0, st, a);
+  if (a.streaming)
+    hipLaunchKernelGGL(k_copy_blocks<true>, dim3((unsigned)gx), dim3(64 * kWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_copy_blocks<false>, dim3((unsigned)gx), dim3(64 * kWaves), 0, st, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

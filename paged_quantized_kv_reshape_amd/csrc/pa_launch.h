@@ -65,6 +65,7 @@ struct CopyArgs {
   const int32_t* pairs;  // [num_pairs][2] (source, destination)
   int32_t num_pairs, num_arrays, src_blocks, dst_blocks;
   int32_t* err;
+  bool streaming;  // non-temporal loads and stores (copies within one device pool)
 };
 int launch_copy_blocks(const CopyArgs& a, hipStream_t st);
 
