@@ -42,9 +42,10 @@ struct Geo {
 
 // N 32-bit words from p (16-byte aligned for N % 4 == 0). NT selects the non-temporal
 // form (the loads carry the streaming hint, so the lines they fill are the first the caches
-// give up): for K/V tiles that a launch reads exactly once, as in decode. Measured on the
-// 70B one-GPU share (FP8, 539 MB per launch): 94.1 -> 89.7 us per decode launch. Loops that
-// re-read tiles out of L2 (multi-token queries) keep the default form.
+// give up): for K/V tiles that a launch reads exactly once, as in the decode of 8- and
+// 4-bit pools (measured on the 70B one-GPU share, FP8, 539 MB per launch: 94.1 -> 89.7 us
+// per decode launch). Loops that re-read tiles out of L2 (multi-token queries) keep the
+// default form.
 template <int N, bool NT = false>
 __device__ __forceinline__ void load_words(uint32_t (&w)[N], const uint8_t* p) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
