@@ -148,7 +148,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   static_assert(!DB || KV == KV_FP4, "the double-buffered loop is the FP4 kernel's");
   static_assert(kQLds == (D + D / DL) * GP, "FP4 LDS layout");
   constexpr bool PVB = QBF || KV == KV_FP4;  // PV MFMA in bf16 (else fp16)
-  constexpr bool kStream = KV != KV_F16 && KV != KV_BF16;  // non-temporal tile loads
+  constexpr bool kStreamK = KV != KV_F16 && KV != KV_BF16;  // non-temporal K tile loads
   extern __shared__ float smem[];
 
   const int lane = threadIdx.x & 63;
@@ -304,15 +304,16 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     err_bits |= T.ok ? 0 : PA_DEVERR_BAD_BLOCK;
     const int b = T.ok ? b_raw : 0;
     T.tile = (int64_t)b * a.num_kv_heads + kvh;
-    // each tile is read once per launch: streaming (non-temporal) loads for the 8- and
-    // 4-bit pools (c4: 94.1 -> 89.7 us). Not for 16-bit pools: a lane reads its 64-byte
-    // row segment in four 16-byte loads, and with the hint a line can leave before the
-    // later loads reach it (the 8B-shaped bf16 workload: 205 -> 274 us).
-    load_words<G_::KW, kStream>(T.k, kpool + T.tile * G_::TILEB + k_lane_off);
+    // each tile is read once per launch: streaming (non-temporal) loads (c4: 94.1 ->
+    // 89.7 us). 16-bit K excepted: a lane reads its 64-byte row segment in four 16-byte
+    // loads, and with the hint a line can leave before the later loads reach it (the
+    // 8B-shaped bf16 workload: 205 -> 274 us); its V loads, each a whole row across 16
+    // lanes, stream (209 -> 195 us).
+    load_words<G_::KW, kStreamK>(T.k, kpool + T.tile * G_::TILEB + k_lane_off);
     if constexpr (KV == KV_FP4) {
       // one 16-byte chunk: channels 8 c .. 8 c + 7 of tokens 4 kg .. 4 kg + 3
       uint32_t x[4];
-      load_words<4, kStream>(x, vpool + T.tile * G_::TILEB + (c * 4 + kg) * 16);
+      load_words<4, true>(x, vpool + T.tile * G_::TILEB + (c * 4 + kg) * 16);
       T.v[0][0] = x[0];
       T.v[1][0] = x[1];
       T.v[2][0] = x[2];
@@ -320,7 +321,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        load_words<G_::VW, kStream>(T.v[r], vpool + T.tile * G_::TILEB + v_lane_off + r * G_::ROWB);
+        load_words<G_::VW, true>(T.v[r], vpool + T.tile * G_::TILEB + v_lane_off + r * G_::ROWB);
     }
     if constexpr (f8_tok(KV)) {  // per-token scales of tokens 4 kg .. 4 kg + 3
       T.sk = reinterpret_cast<const float4*>(kpool + T.tile * G_::TILEB + PA_FP8T_SCALE_OFF(D))[kg];
