@@ -44,7 +44,7 @@ Pool layout (the boundary's layout, row-major, one array per field):
                                    then 0xFF in the unused bytes
                  next 32 bytes     fp16 values of the first outlier, one per token
                  the rest          padding up to a multiple of 128 bytes (TILE = 1152
-                                   for D = 128)
+                                   for D = 128, 640 for D = 64)
                *_out_val     uint16 [NB, Hkv, CAP - 1, 16]  fp16 bits of outliers 1.. CAP-1
 """
 from __future__ import annotations
@@ -171,17 +171,19 @@ def fp4_code_map(kv: str, d: int):
     (byte index [16, d], bit shift [16, d]).
 
     K codes are token rows: byte t * d/2 + ch // 2, the even channel in the low nibble.
-    V codes are grouped for a transposed read: 16-byte chunk (ch // 8) * 4 + t // 4 holds
-    channels 8 g .. 8 g + 7 of tokens 4 j .. 4 j + 3; inside it, channel ch % 8 takes
-    bytes 2 (ch % 8) and 2 (ch % 8) + 1 (tokens 0-1 and 2-3 of the four), the even
-    token in the low nibble."""
+    V codes are grouped for a transposed read, in chunks of nc = d / 16 channels of four
+    tokens (2 nc bytes: 16 for d = 128, 8 for d = 64): chunk (ch // nc) * 4 + t // 4 holds
+    channels nc g .. nc g + nc - 1 of tokens 4 j .. 4 j + 3; inside it, channel ch % nc
+    takes bytes 2 (ch % nc) and 2 (ch % nc) + 1 (tokens 0-1 and 2-3 of the four), the
+    even token in the low nibble."""
     t = np.arange(16)[:, None]
     ch = np.arange(d)[None, :]
+    nc = d // 16
     if kv == "k":
         byte = t * (d // 2) + ch // 2
         shift = 4 * (ch % 2)
     elif kv == "v":
-        byte = ((ch // 8) * 4 + t // 4) * 16 + (ch % 8) * 2 + (t % 4) // 2
+        byte = ((ch // nc) * 4 + t // 4) * (2 * nc) + (ch % nc) * 2 + (t % 4) // 2
         shift = 4 * (t % 2)
     else:
         raise ValueError(kv)

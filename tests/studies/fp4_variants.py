@@ -1,8 +1,9 @@
 """FP4 calibration variants: attention error against exact attention over the unquantized
-inputs, and bytes per token. A study built on the oracle's primitives (test
-infrastructure, run by hand; it never feeds the product path):
+inputs, and bytes per token. A study built on the oracle's primitives, run by hand; it is
+not part of the parity oracle (its variant quantizers - capacity k, fp16 scales, no
+outliers - are measured here, not pinned) and never feeds the product path:
 
-    python -m oracle.fp4_study [--seqs 4] [--tokens 4096] [--decode 64]
+    python tests/studies/fp4_variants.py [--seqs 4] [--tokens 4096] [--decode 64]
 
 Sequences are written as the serving loop writes them: a prompt in 512-token prefill
 chunks, then `decode` generated tokens one call each (dailyaiworld.com, "vLLM 0.7 Ships
@@ -27,13 +28,17 @@ largest absolute difference. Bytes: per token and kv head, K + V, what the pool 
 from __future__ import annotations
 
 import argparse
+import os
+import sys
 
 import numpy as np
 
-from .attention import attend
-from .cache import fp4_calibrate, fp4_encode_row
-from .formats import (E2M1_MAX, E4M3_MAX, act_decode, e2m1_decode, e2m1_encode, e4m3_decode,
-                      e4m3_encode, f16_decode, f16_encode, f32_quotient)
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__)))))
+from oracle.attention import attend  # noqa: E402
+from oracle.cache import fp4_calibrate, fp4_encode_row  # noqa: E402
+from oracle.formats import (E2M1_MAX, E4M3_MAX, act_decode, e2m1_decode,  # noqa: E402
+                            e2m1_encode, e4m3_decode, e4m3_encode, f16_decode, f16_encode,
+                            f32_quotient)
 
 D, HQ, CHUNK, BLOCK = 128, 8, 512, 16
 RUN_BYTES = 1152      # codes + token scales + record + first outlier slot, padded to 128

@@ -242,27 +242,30 @@ def test_fp4_code_map_is_a_bijection_onto_the_code_bytes(kv, d):
     assert len(np.unique(nib)) == 16 * d
 
 
-def test_fp4_v_chunks_hold_a_channel_group_of_four_tokens():
-    """V chunk (g, j): 16 bytes holding channels 8 g .. 8 g + 7 of tokens 4 j .. 4 j + 3,
-    two tokens per byte (one channel), so a converter taking a byte yields a token pair."""
-    d = 128
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp4_v_chunks_hold_a_channel_group_of_four_tokens(d):
+    """V chunk (g, j): 2 nc bytes (nc = d / 16 channels: 16 bytes at d = 128, 8 at d = 64)
+    holding channels nc g .. nc g + nc - 1 of tokens 4 j .. 4 j + 3, two tokens per byte
+    (one channel), so a converter taking a byte yields a token pair."""
+    nc = d // 16
     byte, shift = C.fp4_code_map("v", d)
-    for g in range(d // 8):
+    for g in range(d // nc):
         for j in range(4):
             chunk = g * 4 + j
             t = np.arange(4 * j, 4 * j + 4)[:, None]
-            ch = np.arange(8 * g, 8 * g + 8)[None, :]
+            ch = np.arange(nc * g, nc * g + nc)[None, :]
             b = byte[t, ch]
-            assert np.all(b // 16 == chunk)
+            assert np.all(b // (2 * nc) == chunk)
             # one byte = one channel, two consecutive tokens (even token low)
-            for c in range(8):
+            for c in range(nc):
                 col = b[:, c]
                 assert col[0] == col[1] and col[2] == col[3] and col[0] + 1 == col[2]
+                assert col[0] % (2 * nc) == 2 * c
                 assert list(shift[t[:, 0], ch[0, c]]) == [0, 4, 0, 4]
 
 
-def test_fp4_put_codes_keeps_the_other_nibbles():
-    d = 128
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp4_put_codes_keeps_the_other_nibbles(d):
     for kv in ("k", "v"):
         pool = C.Pool.filled("fp4", 2, 1, d)
         rng = np.random.default_rng(3)
