@@ -34,11 +34,17 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "paged decode attention: achieved KV-read GB/s (% HBM peak) + seq-tokens/s"
+# the sources that decide the decode kernel's code and launch (the wave count is chosen in
+# pa_api.cpp): committed counter traffic is used only while their hash is unchanged
 KERNEL_SOURCES = ["paged_quantized_kv_reshape_amd/csrc/pa_decode.hip",
                   "paged_quantized_kv_reshape_amd/csrc/pa_tile.h",
                   "paged_quantized_kv_reshape_amd/csrc/pa_encode.h",
                   "paged_quantized_kv_reshape_amd/csrc/pa_fp4.h",
-                  "paged_quantized_kv_reshape_amd/csrc/pa_device.h"]
+                  "paged_quantized_kv_reshape_amd/csrc/pa_device.h",
+                  "paged_quantized_kv_reshape_amd/csrc/pa_api.cpp",
+                  "paged_quantized_kv_reshape_amd/csrc/pa_launch.h"]
+# decode output tolerance against the oracle: max |gpu - oracle| and relative L2 error
+ATOL, RTOL_L2 = 2e-3, 1e-2
 
 
 class HipTimer:
@@ -120,56 +126,119 @@ def counter_traffic(kernel: str, cfg: str, ps: int):
     return float(tb.group(1))
 
 
+def host_cores() -> dict:
+    """What the host offers this process: logical CPUs, the ones it may run on, and the
+    thread count of each BLAS / OpenMP pool NumPy would use."""
+    from threadpoolctl import threadpool_info
+    info = threadpool_info()
+    return {"cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+            "blas_threads": max([i.get("num_threads", 1) for i in info] or [1]),
+            "pools": sorted({f"{i.get('internal_api')}:{i.get('num_threads')}" for i in info})}
+
+
 def cpu_baseline(w, budget_s: float, decode_b_per_token: float):
     """The oracle (fp64 NumPy, unmodified) on a bounded sample of the same workload: the
     cache-write replay of a few whole sequences (every write call of setup and step,
-    restricted to their blocks) and their exact decode, one BLAS thread."""
+    restricted to their blocks) and their exact decode. Timed twice in this process, first
+    with every BLAS thread the host gives, then with one. Returns the record and the
+    oracle's outputs {seq: out [Hq, D]} of the sample, for the parity check."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import attention as A
     from oracle import cache as C
 
-    with threadpool_limits(limits=1):
-        ks = vs = None
-        if w.kv in ("fp8", "bf8"):  # inputs of the method (per-head scales), not timed
-            fmt = C.FP8_KINDS[w.kv][0]
-            ks = C.fp8_head_scale(w.k_rows, w.act, fmt)
-            vs = C.fp8_head_scale(w.v_rows, w.act, fmt)
+    ks = vs = None
+    if w.kv in ("fp8", "bf8"):  # inputs of the method (per-head scales), not timed
+        fmt = C.FP8_KINDS[w.kv][0]
+        ks = C.fp8_head_scale(w.k_rows, w.act, fmt)
+        vs = C.fp8_head_scale(w.v_rows, w.act, fmt)
+    calls = list(w.setup_calls) + [w.step_call]
+    blk_of_call = [c.slots // 16 for c in calls]
+
+    def run(seqs):
         pool = C.Pool.filled(w.kv, w.num_blocks, w.num_kv_heads, w.head_dim)
-        calls = list(w.setup_calls) + [w.step_call]
-        blk_of_call = [c.slots // 16 for c in calls]
-
-        def run(seqs):
-            blocks = set()
-            for s in seqs:
-                n = -(-int(w.context_lens[s]) // 16)
-                blocks.update(int(b) for b in w.block_tables[s, :n])
-            keep = np.asarray(sorted(blocks))
-            for c, blk in zip(calls, blk_of_call):
-                sel = np.isin(blk, keep)
-                if sel.any():
-                    C.cache_write(pool, w.k_rows[c.rows[sel]], w.v_rows[c.rows[sel]], w.act,
-                                  c.slots[sel], ks, vs)
-            A.paged_decode(w.q, w.act, pool, w.block_tables, w.context_lens, w.sm_scale, ks,
-                           vs, partition_size=w.partition_size, seqs=seqs)
-
-        order = list(range(w.num_seqs))
         t0 = time.perf_counter()
-        run(order[:1])
-        t1 = time.perf_counter() - t0
-        n = max(1, min(w.num_seqs - 1, int(budget_s / max(t1, 1e-3))))
-        sample = order[1:1 + n]
-        t0 = time.perf_counter()
-        run(sample)
-        dt = time.perf_counter() - t0
+        blocks = set()
+        for s in seqs:
+            n = -(-int(w.context_lens[s]) // 16)
+            blocks.update(int(b) for b in w.block_tables[s, :n])
+        keep = np.asarray(sorted(blocks))
+        for c, blk in zip(calls, blk_of_call):
+            sel = np.isin(blk, keep)
+            if sel.any():
+                C.cache_write(pool, w.k_rows[c.rows[sel]], w.v_rows[c.rows[sel]], w.act,
+                              c.slots[sel], ks, vs)
+        res = A.paged_decode(w.q, w.act, pool, w.block_tables, w.context_lens, w.sm_scale, ks,
+                             vs, partition_size=w.partition_size, seqs=seqs)
+        return time.perf_counter() - t0, res
+
+    cores = host_cores()
+    order = list(range(w.num_seqs))
+    t1, _ = run(order[:1])
+    n = max(1, min(w.num_seqs - 1, int(budget_s / max(t1, 1e-3))))
+    sample = order[1:1 + n]
+    dt_all, res = run(sample)
+    with threadpool_limits(limits=1):
+        dt_one, _ = run(sample)
     tokens = int(sum(int(w.context_lens[s]) for s in sample))
-    gbs = tokens * decode_b_per_token / dt / 1e9
-    return {"value": round(gbs, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds": round(dt, 2), "seq_tokens_per_s": round(tokens / dt, 1),
-            "sample": (f"{len(sample)} of {w.num_seqs} sequences ({tokens} KV tokens): replay of "
-                       f"every cache-write call into their blocks, then exact fp64 decode "
-                       f"(+ partitions) of the sequences; bytes counted as for the GPU step")}
+    outs = {}
+    for s in sample:
+        o, lse = res[s]
+        outs[s] = A.merge(o, lse)[0] if w.partition_size else o
+    gbs = lambda dt: round(tokens * decode_b_per_token / dt / 1e9, 6)
+    rec = {"value": gbs(dt_all), "unit": "GB/s", "cores": cores["blas_threads"],
+           "kind": "oracle", "seconds": round(dt_all, 2),
+           "seq_tokens_per_s": round(tokens / dt_all, 1),
+           "host": cores,
+           "single_thread": {"value": gbs(dt_one), "unit": "GB/s", "cores": 1,
+                             "seconds": round(dt_one, 2),
+                             "seq_tokens_per_s": round(tokens / dt_one, 1)},
+           "sample": (f"{len(sample)} of {w.num_seqs} sequences ({tokens} KV tokens): replay of "
+                      f"every cache-write call into their blocks, then exact fp64 decode "
+                      f"(+ partitions and merge) of the sequences; bytes counted as for the "
+                      f"GPU step; timed with all BLAS threads, then with one")}
+    return rec, outs
+
+
+def oracle_outputs(w, seqs) -> dict:
+    """The oracle's decode of the listed sequences (replay of their blocks, then exact
+    decode, merged when split), untimed."""
+    import numpy as np
+
+    from oracle import attention as A
+    from oracle import cache as C
+    ks = vs = None
+    if w.kv in ("fp8", "bf8"):
+        fmt = C.FP8_KINDS[w.kv][0]
+        ks = C.fp8_head_scale(w.k_rows, w.act, fmt)
+        vs = C.fp8_head_scale(w.v_rows, w.act, fmt)
+    pool = C.Pool.filled(w.kv, w.num_blocks, w.num_kv_heads, w.head_dim)
+    blocks = set()
+    for s in seqs:
+        blocks.update(int(b) for b in w.block_tables[s, :-(-int(w.context_lens[s]) // 16)])
+    keep = np.asarray(sorted(blocks))
+    for c in list(w.setup_calls) + [w.step_call]:
+        sel = np.isin(c.slots // 16, keep)
+        if sel.any():
+            C.cache_write(pool, w.k_rows[c.rows[sel]], w.v_rows[c.rows[sel]], w.act,
+                          c.slots[sel], ks, vs)
+    res = A.paged_decode(w.q, w.act, pool, w.block_tables, w.context_lens, w.sm_scale, ks, vs,
+                         partition_size=w.partition_size, seqs=seqs)
+    return {s: (A.merge(*res[s])[0] if w.partition_size else res[s][0]) for s in seqs}
+
+
+def parity_check(got, outs) -> dict:
+    """The bench's own output against the oracle's on the sampled sequences: elementwise
+    max |gpu - oracle| and relative L2 error, both within the decode tolerance."""
+    import numpy as np
+    g = np.stack([got[s] for s in outs]).astype(np.float64)
+    o = np.stack([outs[s] for s in outs])
+    max_abs = float(np.abs(g - o).max()) if g.size else 0.0
+    rel = float(np.linalg.norm(g - o) / max(np.linalg.norm(o), 1e-30))
+    ok = bool(np.isfinite(g).all() and max_abs <= ATOL and rel <= RTOL_L2)
+    return {"seqs": len(outs), "max_abs": max_abs, "rel_l2": rel, "atol": ATOL,
+            "rtol_l2": RTOL_L2, "ok": ok}
 
 
 def workload_of(args, config):
@@ -439,7 +508,8 @@ def main():
     ap.add_argument("--partition-size", type=int, default=None,
                     help="override the workload's split (0 = one pass per sequence)")
     ap.add_argument("--copies", type=int, default=3, help="pool copies rotated across steps")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle work per timed run (it runs twice: all threads, then one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
@@ -577,6 +647,15 @@ def main():
     t_dec_br = float(np.mean([timer.ms(e[1], e[2]) for e in ev])) * 1e-3
     t_merge = float(np.mean([timer.ms(e[2], e[3]) for e in ev])) * 1e-3
     t_dec = timer.ms(burst[0], burst[1]) * 1e-3 / K
+    # (4) the gather-only ceiling: the decode's launch and tile reads with no arithmetic,
+    # K launches back to back like (3)
+    probe = [timer.event(), timer.event()]
+    timer.record(probe[0], stream)
+    for i in range(K):
+        run.gather_probe(pool_of(i))
+    timer.record(probe[1], stream)
+    torch.cuda.synchronize()
+    t_probe = timer.ms(probe[0], probe[1]) * 1e-3 / K
     timer.close()
     if run.device_error():
         raise SystemExit(f"device error during timing: {run.device_error()}")
@@ -598,7 +677,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.act,
         "data": "synthetic",
         "config": {"workload": f"{args.config}: {DESCRIPTIONS[args.config]}"
                                + (f" (KV cache as {w.kv})" if args.kv else ""),
@@ -629,12 +708,27 @@ def main():
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes": kernel_bytes,
                      "traffic": traffic},
+        "ceiling": {"kernel": "k_gather_probe", "ms": round(t_probe * 1e3, 4),
+                    "gbs": round(kernel_bytes / t_probe / 1e9, 2),
+                    "pct_hbm_peak": round(100.0 * kernel_bytes / t_probe / 1e9 / HBM_PEAK_GBS, 2),
+                    "decode_frac_of_ceiling": round(t_probe / t_dec, 4),
+                    "what": "the decode's launch reading every attended K/V run through the "
+                            "block tables with its streaming 16-byte loads, no arithmetic; "
+                            "gbs counts the decode's algorithmic bytes"},
     }
+    print("[bench] checking the timed output against the oracle", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds,
-                                           dec["total"] / max(dec["tokens"], 1))
+        res["cpu_baseline"], outs = cpu_baseline(w, args.cpu_seconds,
+                                                 dec["total"] / max(dec["tokens"], 1))
+    else:  # no timing: the parity check still runs, on one sequence
+        outs = oracle_outputs(w, [w.num_seqs - 1])
+    res["parity"] = parity_check(out, outs)
     print(json.dumps(res), flush=True)
+    if not res["parity"]["ok"]:
+        print(f"bench: the timed output differs from the oracle: {res['parity']}",
+              file=sys.stderr, flush=True)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -31,7 +31,7 @@
  *   - All arrays are dense, row-major, in the shapes written below, 16-byte aligned.
  *   - Query head h reads kv head h / (num_q_heads / num_kv_heads) (grouped-query attention
  *     with contiguous groups); num_q_heads / num_kv_heads must be 1..16.
- *   - head_dim is 64 or 128; block_size is 16 (the block size the pages use: xonoai.com
+ *   - head_dim is 64 or 128 in every format; block_size is 16 (the block size the pages use: xonoai.com
  *     report, "Deconstructing the v0.7.2 Architecture", and its --block-size 16 flag).
  */
 #ifndef PA_H_
@@ -72,7 +72,8 @@ typedef enum {
   PA_ERR_ALIGN = -8,       /* a pointer is not 16-byte aligned                          */
   PA_ERR_MEMORY = -9,      /* a pointer is not memory this GPU can access               */
   PA_ERR_EXHAUSTED = -10,  /* the block allocator has fewer free blocks than requested  */
-  PA_ERR_STATE = -11       /* the block allocator was asked about a block not in use    */
+  PA_ERR_STATE = -11,      /* the block allocator was asked about a block not in use    */
+  PA_ERR_SCRATCH = -12     /* the call needs more than the library's static scratch      */
 } pa_status;
 
 #define PA_DEVERR_BAD_BLOCK 1        /* block table / copy pair id outside its pool      */
@@ -107,9 +108,11 @@ typedef enum {
  *                                   fetched in whole 128-byte lines:
  *                            [0, 8 D)       E2M1 codes, 4 bits each. K: token rows
  *                                           [16][D/2], even channel in the low nibble.
- *                                           V: 16-byte chunks, chunk (ch / 8) * 4 + t / 4
- *                                           holds channels 8 g .. 8 g + 7 of tokens
- *                                           4 j .. 4 j + 3; in it byte 2 (ch % 8) holds
+ *                                           V: chunks of NC = D / 16 channels of four
+ *                                           tokens (2 NC bytes: 16 at D = 128, 8 at
+ *                                           D = 64); chunk (ch / NC) * 4 + t / 4 holds
+ *                                           channels NC g .. NC g + NC - 1 of tokens
+ *                                           4 j .. 4 j + 3; in it byte 2 (ch % NC) holds
  *                                           tokens 4 j, 4 j + 1 and the next byte tokens
  *                                           4 j + 2, 4 j + 3 of channel ch, the even
  *                                           token in the low nibble (a decode lane reads
@@ -143,7 +146,7 @@ typedef struct pa_kv_pool {
   int32_t num_blocks;
   int32_t block_size;     /* must be 16 */
   int32_t num_kv_heads;
-  int32_t head_dim;       /* 64 or 128 (FP4: 128) */
+  int32_t head_dim;       /* 64 or 128 */
   int32_t reserved;
   void* k;
   void* v;
@@ -218,7 +221,7 @@ int pa_fp8_head_scales(const void* x, int32_t act, int32_t kv_dtype, int64_t num
  *   seq_records   [num_seqs, 2, num_kv_heads, 16] uint8 (written): K (index 0) and V (1)
  *                 sets in the block record format (count, ascending channel ids, 0xFF)
  * Same statistics as the per-block calibration: per-channel RMS over the rows, channels at
- * or above mean + 3.2 population sigma of the head_dim norms. head_dim 128. A sequence with
+ * or above mean + 3.2 population sigma of the head_dim norms. head_dim 64 or 128. A sequence with
  * no rows gets an empty set; one whose range is not inside [0, num_rows) too, flagged
  * PA_DEVERR_BAD_CONTEXT. Asynchronous on `stream`.
  */
@@ -388,10 +391,72 @@ int pa_prefill(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_h
                void* stream);
 
 /*
+ * Launch geometry for tuning and tests. Every entry point picks its own geometry; the _ex
+ * variants below take one of these (NULL, or a field 0, keeps the library's choice) and
+ * are otherwise identical to the entry point they extend. The library reads no
+ * environment variable and keeps no setting between calls.
+ *   decode_waves       waves per decode workgroup: 1, 2, 4 or 8 (a workgroup covers one
+ *                      partition of one (sequence, kv head); its waves take its blocks in
+ *                      turn and merge their states in LDS)
+ *   prefill_col_tiles  16-column MFMA tiles per pa_prefill wave: 2 or 3
+ *   reserved           must be 0
+ * Another value gives PA_ERR_SHAPE.
+ */
+typedef struct pa_launch_options {
+  int32_t decode_waves;
+  int32_t prefill_col_tiles;
+  int32_t reserved[6];
+} pa_launch_options;
+
+int pa_decode_ex(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                 const pa_kv_pool* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                 const int32_t* context_lens, float sm_scale, int32_t partition_size, float* out,
+                 float* part_out, float* part_lse, int32_t* dev_err,
+                 const pa_launch_options* opts, void* stream);
+int pa_append_decode_ex(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                        const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, float sm_scale, int32_t partition_size,
+                        float* out, float* part_out, float* part_lse, int32_t* dev_err,
+                        const pa_launch_options* opts, void* stream);
+int pa_prefill_ex(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                  int32_t num_queries, const int32_t* query_start, int32_t max_query_len,
+                  const pa_kv_pool* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, float sm_scale, float* out, int32_t* dev_err,
+                  const pa_launch_options* opts, void* stream);
+
+/*
+ * Gather-only ceiling of the decode's access pattern, for measurement: the launch
+ * pa_decode_ex would make for these arguments (same grid, waves and partitions), reading
+ * through the block tables every byte of every attended (block, kv head) run of K and V
+ * that the decode's tile loads touch (the whole run: codes, and for FP4 and per-token FP8
+ * pools the side data stored in it; not the FP4 outlier slots past the first, which only
+ * blocks with two or more outliers have), with the decode's 16-byte streaming loads and no
+ * arithmetic beyond an XOR that keeps the loads alive. Its time is what the decode's
+ * memory traffic alone costs on this GPU (the pages put the decode's limit on memory
+ * bandwidth: xonoai.com report on vLLM v0.7.2, "Deconstructing the v0.7.2 Architecture").
+ *   num_q_heads     no query is read; the group num_q_heads / num_kv_heads is checked as
+ *                   in pa_decode
+ *   sink            [1024] uint32, device memory: XORs of the loaded words (contents
+ *                   meaningless; need not be zeroed)
+ * Invalid block ids are skipped and flagged as in pa_decode. Asynchronous on `stream`.
+ */
+int pa_gather_probe(int32_t num_seqs, int32_t num_q_heads, const pa_kv_pool* pool,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t partition_size, uint32_t* sink,
+                    int32_t* dev_err, const pa_launch_options* opts, void* stream);
+
+/*
  * Log-sum-exp merge of pa_decode partitions: for each (s, h), over p < ceil(L_s / ps),
  * M = max lse_p, w_p = exp(lse_p - M), out = sum w_p o_p / sum w_p and, if lse_out is
- * not NULL, lse_out[s, h] = M + ln sum w_p. Shapes as in pa_decode; out [num_seqs,
- * num_q_heads, head_dim] fp32, lse_out [num_seqs, num_q_heads] fp32. Asynchronous.
+ * not NULL, lse_out[s, h] = M + ln sum w_p. The pages name split-KV decoding
+ * (Flash-Decoding, among the sources of dailyaiworld.com, "vLLM 0.7 Ships Unified KV
+ * Cache Compression") but not the recombination; this is the standard exact identity for
+ * softmax over a union of disjoint key sets, not a step the pages state. A partition whose
+ * lse is not finite weighs 0 and its row is not read into the sum; a sequence with
+ * L_s < 1 or L_s > max_partitions * partition_size (nothing its partitions can hold) gets
+ * a zero output and lse -inf. Shapes as in pa_decode; out [num_seqs, num_q_heads,
+ * head_dim] fp32, lse_out [num_seqs, num_q_heads] fp32. Asynchronous.
  */
 int pa_merge(const float* part_out, const float* part_lse, const int32_t* context_lens,
              int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_partitions,

@@ -21,6 +21,7 @@ ACT_DTYPES = {torch.float16: 0, torch.bfloat16: 1}
 BLOCK_SIZE = 16
 DEVERR_BITS = {1: "bad block id", 2: "bad slot", 4: "bad context length",
                8: "read of an uncalibrated FP4 block"}
+PROBE_SINK_WORDS = 1024  # pa_gather_probe's sink: uint32 [1024]
 
 
 class PAError(RuntimeError):
@@ -40,6 +41,21 @@ class pa_kv_pool(ctypes.Structure):
         ("k_out_val", ctypes.c_void_p), ("v_out_val", ctypes.c_void_p),
         ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
     ]
+
+
+class pa_launch_options(ctypes.Structure):
+    _fields_ = [("decode_waves", ctypes.c_int32), ("prefill_col_tiles", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 6)]
+
+
+def _opts(decode_waves=None, prefill_col_tiles=None):
+    """A pa_launch_options for the _ex entry points, or None (the library's choice)."""
+    if decode_waves is None and prefill_col_tiles is None:
+        return None
+    o = pa_launch_options()
+    o.decode_waves = int(decode_waves or 0)
+    o.prefill_col_tiles = int(prefill_col_tiles or 0)
+    return ctypes.byref(o)
 
 
 def fp4_tile_bytes(head_dim: int) -> int:
@@ -90,6 +106,14 @@ def lib():
             "pa_allocator_writable": (ctypes.c_int, [vp, i32, ctypes.POINTER(i32)]),
             "pa_allocator_refcount": (ctypes.c_int, [vp, i32]),
             "pa_allocator_num_free": (ctypes.c_int, [vp]),
+            "pa_decode_ex": (ctypes.c_int, [vp, i32, i32, i32, pool_p, vp, i32, vp, f32, i32, vp,
+                                            vp, vp, vp, vp, vp]),
+            "pa_append_decode_ex": (ctypes.c_int, [vp, i32, i32, i32, pool_p, vp, vp, vp, i32,
+                                                   vp, f32, i32, vp, vp, vp, vp, vp, vp]),
+            "pa_prefill_ex": (ctypes.c_int, [vp, i32, i32, i32, i32, vp, i32, pool_p, vp, i32,
+                                             vp, f32, vp, vp, vp, vp]),
+            "pa_gather_probe": (ctypes.c_int, [i32, i32, pool_p, vp, i32, vp, i32, vp, vp, vp,
+                                               vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -311,36 +335,44 @@ def max_partitions(max_blocks_per_seq: int, partition_size: int) -> int:
 
 
 def pa_decode(q, pool: KVPool, block_tables, context_lens, sm_scale, partition_size=0, out=None,
-              part_out=None, part_lse=None, dev_err=None):
+              part_out=None, part_lse=None, dev_err=None, waves=None):
     """q [S, Hq, D]; block_tables [S, MB] int32; context_lens [S] int32. With
-    partition_size = 0 fills out [S, Hq, D] fp32; otherwise part_out / part_lse."""
+    partition_size = 0 fills out [S, Hq, D] fp32; otherwise part_out / part_lse. waves
+    (1, 2, 4, 8) fixes the waves per workgroup (pa_decode_ex), else the library picks."""
     assert q.dtype in ACT_DTYPES and block_tables.dtype == torch.int32
     assert context_lens.dtype == torch.int32
     S, Hq, _ = q.shape
     s = pool.struct()
-    _check("pa_decode", lib().pa_decode(
-        _ptr(q), ACT_DTYPES[q.dtype], S, Hq, ctypes.byref(s), _ptr(block_tables),
-        block_tables.shape[1], _ptr(context_lens), float(sm_scale), partition_size, _ptr(out),
-        _ptr(part_out), _ptr(part_lse), _ptr(dev_err), _stream()))
+    args = (_ptr(q), ACT_DTYPES[q.dtype], S, Hq, ctypes.byref(s), _ptr(block_tables),
+            block_tables.shape[1], _ptr(context_lens), float(sm_scale), partition_size, _ptr(out),
+            _ptr(part_out), _ptr(part_lse), _ptr(dev_err))
+    if waves is None:
+        _check("pa_decode", lib().pa_decode(*args, _stream()))
+    else:
+        _check("pa_decode_ex", lib().pa_decode_ex(*args, _opts(waves), _stream()))
 
 
 def pa_append_decode(q, pool: KVPool, k_new, v_new, block_tables, context_lens, sm_scale,
-                     partition_size=0, out=None, part_out=None, part_lse=None, dev_err=None):
+                     partition_size=0, out=None, part_out=None, part_lse=None, dev_err=None,
+                     waves=None):
     """pa_decode after writing each sequence's new row k_new[s] / v_new[s] ([S, Hkv, D],
-    q's dtype) at its last position, in one launch (16-bit and FP8 pools)."""
+    q's dtype) at its last position, in one launch (every pool format)."""
     assert q.dtype in ACT_DTYPES and k_new.dtype == q.dtype and v_new.dtype == q.dtype
     assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
     assert k_new.is_contiguous() and v_new.is_contiguous()
     S, Hq, _ = q.shape
     s = pool.struct()
-    _check("pa_append_decode", lib().pa_append_decode(
-        _ptr(q), ACT_DTYPES[q.dtype], S, Hq, ctypes.byref(s), _ptr(k_new), _ptr(v_new),
-        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), float(sm_scale),
-        partition_size, _ptr(out), _ptr(part_out), _ptr(part_lse), _ptr(dev_err), _stream()))
+    args = (_ptr(q), ACT_DTYPES[q.dtype], S, Hq, ctypes.byref(s), _ptr(k_new), _ptr(v_new),
+            _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), float(sm_scale),
+            partition_size, _ptr(out), _ptr(part_out), _ptr(part_lse), _ptr(dev_err))
+    if waves is None:
+        _check("pa_append_decode", lib().pa_append_decode(*args, _stream()))
+    else:
+        _check("pa_append_decode_ex", lib().pa_append_decode_ex(*args, _opts(waves), _stream()))
 
 
 def pa_prefill(q, query_start, max_query_len, pool: KVPool, block_tables, context_lens,
-               sm_scale, out, dev_err=None):
+               sm_scale, out, dev_err=None, col_tiles=None):
     """q [T, Hq, D]; query_start [S + 1] int32 (sequence s owns rows query_start[s] ..
     query_start[s + 1] - 1, its last positions); fills out [T, Hq, D] fp32."""
     assert q.dtype in ACT_DTYPES and block_tables.dtype == torch.int32
@@ -350,10 +382,27 @@ def pa_prefill(q, query_start, max_query_len, pool: KVPool, block_tables, contex
     T, Hq, _ = q.shape
     assert out.shape[0] == T
     s = pool.struct()
-    _check("pa_prefill", lib().pa_prefill(
-        _ptr(q), ACT_DTYPES[q.dtype], S, Hq, T, _ptr(query_start), int(max_query_len),
-        ctypes.byref(s), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
-        float(sm_scale), _ptr(out), _ptr(dev_err), _stream()))
+    args = (_ptr(q), ACT_DTYPES[q.dtype], S, Hq, T, _ptr(query_start), int(max_query_len),
+            ctypes.byref(s), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+            float(sm_scale), _ptr(out), _ptr(dev_err))
+    if col_tiles is None:
+        _check("pa_prefill", lib().pa_prefill(*args, _stream()))
+    else:
+        _check("pa_prefill_ex", lib().pa_prefill_ex(*args, _opts(prefill_col_tiles=col_tiles),
+                                                    _stream()))
+
+
+def pa_gather_probe(pool: KVPool, num_q_heads, block_tables, context_lens, partition_size,
+                    sink, dev_err=None, waves=None):
+    """The decode's launch and tile reads with no arithmetic (a bandwidth ceiling); sink
+    [1024] uint32 device tensor."""
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    assert sink.dtype == torch.int32 and sink.numel() >= PROBE_SINK_WORDS
+    s = pool.struct()
+    _check("pa_gather_probe", lib().pa_gather_probe(
+        context_lens.shape[0], num_q_heads, ctypes.byref(s), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), partition_size, _ptr(sink), _ptr(dev_err),
+        _opts(waves), _stream()))
 
 
 def pa_merge(part_out, part_lse, context_lens, partition_size, out, lse_out=None):

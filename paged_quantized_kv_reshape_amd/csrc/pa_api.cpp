@@ -3,7 +3,6 @@
 // call has no effect on the device.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include "../../include/pa.h"
 #include "pa_launch.h"
@@ -26,7 +25,6 @@ int check_pool_arrays(const pa_kv_pool* p) {
   if (!p->k || !p->v) return PA_ERR_NULL;
   if (!aligned(p->k, 16) || !aligned(p->v, 16)) return PA_ERR_ALIGN;
   if (p->dtype == PA_KV_FP4_E2M1_OUTL) {
-    if (p->head_dim != 128) return PA_ERR_SHAPE;  // 4-bit format: head_dim 128 only
     if (!p->k_out_val || !p->v_out_val) return PA_ERR_NULL;
     if (!aligned(p->k_out_val, 8) || !aligned(p->v_out_val, 8)) return PA_ERR_ALIGN;
   }
@@ -81,10 +79,17 @@ int device_cus() {
   return n;
 }
 
-int env_int(const char* name, int fallback) {
-  const char* s = getenv(name);
-  if (!s || !*s) return fallback;
-  return atoi(s);
+// Launch options: NULL or zero fields keep the library's choice; anything else must be a
+// value the kernels are built for.
+int check_options(const pa_launch_options* o) {
+  if (!o) return PA_OK;
+  const int w = o->decode_waves;
+  if (w != 0 && w != 1 && w != 2 && w != 4 && w != 8) return PA_ERR_SHAPE;
+  if (o->prefill_col_tiles != 0 && o->prefill_col_tiles != 2 && o->prefill_col_tiles != 3)
+    return PA_ERR_SHAPE;
+  for (int i = 0; i < 6; ++i)
+    if (o->reserved[i] != 0) return PA_ERR_SHAPE;
+  return PA_OK;
 }
 
 }  // namespace
@@ -105,6 +110,8 @@ const char* pa_status_string(int status) {
     case PA_ERR_MEMORY: return "PA_ERR_MEMORY: a pointer is not memory this GPU can access";
     case PA_ERR_EXHAUSTED: return "PA_ERR_EXHAUSTED: not enough free blocks";
     case PA_ERR_STATE: return "PA_ERR_STATE: the block is not in use";
+    case PA_ERR_SCRATCH:
+      return "PA_ERR_SCRATCH: the call needs more device scratch than the library holds";
     default: return "unknown pa_status";
   }
 }
@@ -120,7 +127,6 @@ int pa_pool_layout(int32_t dtype, int32_t num_blocks, int32_t num_kv_heads, int3
   if (dtype < PA_KV_F16 || dtype > PA_KV_FP8_E5M2_TOKEN) return PA_ERR_DTYPE;
   if (num_blocks < 1 || num_kv_heads < 1 || (head_dim != 64 && head_dim != 128))
     return PA_ERR_SHAPE;
-  if (dtype == PA_KV_FP4_E2M1_OUTL && head_dim != 128) return PA_ERR_SHAPE;
   for (int i = 0; i < 4; ++i) bytes_out[i] = 0;
   const size_t bh = (size_t)num_blocks * num_kv_heads;
   const size_t rows = bh * PA_BLOCK_SIZE;
@@ -175,7 +181,7 @@ int pa_fp4_sequence_outliers(const void* k_rows, const void* v_rows, int32_t act
                              const int32_t* row_start, int32_t num_seqs, uint8_t* seq_records,
                              int32_t* dev_err, void* stream) {
   if (!act_ok(act)) return PA_ERR_DTYPE;
-  if (head_dim != 128 || num_rows < 0 || num_seqs < 0 || num_kv_heads < 1 ||
+  if ((head_dim != 64 && head_dim != 128) || num_rows < 0 || num_seqs < 0 || num_kv_heads < 1 ||
       num_kv_heads > kMaxGridYZ)
     return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
@@ -273,15 +279,15 @@ int pa_copy_blocks(const pa_kv_pool* src, const pa_kv_pool* dst, const int32_t* 
 
 namespace {
 
-// pa_decode and pa_append_decode: k_new / v_new NULL for the former
-int decode_call(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
-                const pa_kv_pool* pool, const void* k_new, const void* v_new,
-                const int32_t* block_tables, int32_t max_blocks_per_seq,
-                const int32_t* context_lens, float sm_scale, int32_t partition_size, float* out,
-                float* part_out, float* part_lse, int32_t* dev_err, void* stream) {
+// Checks shared by the decode entry points and the gather probe: the pool, the GQA group,
+// the table and partition sizes. Fills the launch arguments common to them.
+int decode_geometry(int32_t num_seqs, int32_t num_q_heads, const pa_kv_pool* pool,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t partition_size,
+                    const pa_launch_options* opts, pa::DecodeArgs& a) {
   int st = check_pool(pool);
   if (st != PA_OK) return st;
-  if (!act_ok(q_dtype) || !act_matches_pool(q_dtype, pool->dtype)) return PA_ERR_DTYPE;
+  if ((st = check_options(opts)) != PA_OK) return st;
   if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_q_heads < 1) return PA_ERR_SHAPE;
   if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_SHAPE;
   const int group = num_q_heads / pool->num_kv_heads;
@@ -289,28 +295,13 @@ int decode_call(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_
   if (max_blocks_per_seq < 1 || (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE > INT32_MAX)
     return PA_ERR_CONTEXT;
   if (partition_size < 0 || partition_size % PA_BLOCK_SIZE != 0) return PA_ERR_PARTITION;
-  if (num_seqs == 0) return PA_OK;
-  if (!q || !block_tables || !context_lens) return PA_ERR_NULL;
   const int64_t cap_tokens = (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE;
   const int max_part =
       partition_size > 0 ? (int)((cap_tokens + partition_size - 1) / partition_size) : 1;
   // the launch grid's x dimension counts (partition, kv head) pairs
   if ((int64_t)max_part * pool->num_kv_heads > INT32_MAX) return PA_ERR_SHAPE;
-  if (partition_size == 0) {
-    if (!out) return PA_ERR_NULL;
-    if (!aligned(out, 16)) return PA_ERR_ALIGN;
-  } else {
-    if (!part_out || !part_lse) return PA_ERR_NULL;
-    if (!aligned(part_out, 16) || !aligned(part_lse, 4)) return PA_ERR_ALIGN;
-  }
-  if (!aligned(q, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
-      !aligned(dev_err, 4) || !aligned(k_new, 16) || !aligned(v_new, 16))
-    return PA_ERR_ALIGN;
-
-  pa::DecodeArgs a{};
-  a.q = q;
-  a.k_new = k_new;
-  a.v_new = v_new;
+  if (num_seqs > 0 && (!block_tables || !context_lens)) return PA_ERR_NULL;
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4)) return PA_ERR_ALIGN;
   a.k = pool->k;
   a.v = pool->v;
   a.k_out_val = pool->k_out_val;
@@ -319,10 +310,6 @@ int decode_call(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_
   a.v_scale = pool->v_scale;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.out = out;
-  a.part_out = part_out;
-  a.part_lse = part_lse;
-  a.err = dev_err;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = pool->num_kv_heads;
@@ -332,65 +319,75 @@ int decode_call(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_
   a.partition_size = partition_size;
   a.max_partitions = max_part;
   a.cap = pa::outlier_capacity(pool->head_dim);
-  a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  return PA_OK;
+}
 
-  // Waves per workgroup. The decode streams K/V tiles from HBM. Measured on MI355X: with
-  // one kv head the gather of random 16-token tiles runs fastest with about 8 waves per
-  // compute unit in the grid, each walking a long run of blocks (more waves only open
-  // more DRAM rows at once); with several kv heads the workgroups of one block's heads
-  // run side by side and read neighbouring tiles, and about 8 waves per CU per kv head
-  // (up to 8 heads) keeps those reads together. So pick the smallest power of two
-  // W <= 8 that brings the grid to that many waves, without giving a wave fewer than two
-  // blocks of its partition.
-  const int64_t span = partition_size > 0 ? partition_size : cap_tokens;
+// Waves per decode workgroup. The decode streams K/V tiles from HBM. Measured on MI355X:
+// with one kv head the gather of random 16-token tiles runs fastest with about 8 waves per
+// compute unit in the grid, each walking a long run of blocks (more waves only open more
+// DRAM rows at once); with several kv heads the workgroups of one block's heads run side
+// by side and read neighbouring tiles, and about 8 waves per CU per kv head (up to 8
+// heads) keeps those reads together. So pick the smallest power of two W <= 8 that brings
+// the grid to that many waves, without giving a wave fewer than two blocks of its
+// partition. FP4 pools start from 2 waves: a 4-bit tile is half an FP8 one, so a one-wave
+// workgroup keeps too little in flight, and the FP4 kernel's wave merge reuses its own LDS,
+// so two waves cost no occupancy (c5: 107 us vs 113 us with one wave).
+int decode_waves(const pa::DecodeArgs& a, int32_t dtype, const pa_launch_options* opts) {
+  if (opts && opts->decode_waves) return opts->decode_waves;
+  const int64_t span = a.partition_size > 0 ? a.partition_size
+                                            : (int64_t)a.max_blocks * PA_BLOCK_SIZE;
   const int64_t blocks = (span + PA_BLOCK_SIZE - 1) / PA_BLOCK_SIZE;
-  const int64_t wgs = (int64_t)num_seqs * pool->num_kv_heads * max_part;
-  const int64_t heads = pool->num_kv_heads < 8 ? pool->num_kv_heads : 8;
+  const int64_t wgs = (int64_t)a.num_seqs * a.num_kv_heads * a.max_partitions;
+  const int64_t heads = a.num_kv_heads < 8 ? a.num_kv_heads : 8;
   const int64_t target_waves = 8 * heads * (int64_t)device_cus();
-  // FP4 pools start from 2 waves: a 4-bit tile is half an FP8 one, so a one-wave
-  // workgroup keeps too little in flight, and the FP4 kernel's wave merge reuses its own
-  // LDS, so two waves cost no occupancy (c5: 107 us vs 113 us with one wave).
-  int waves = pool->dtype == PA_KV_FP4_E2M1_OUTL && blocks >= 4 ? 2 : 1;
+  int waves = dtype == PA_KV_FP4_E2M1_OUTL && blocks >= 4 ? 2 : 1;
   while (waves < 8 && wgs * waves < target_waves && blocks >= 2 * waves) waves *= 2;
-  const int forced = env_int("PA_DECODE_WAVES", 0);
-  if (forced == 1 || forced == 2 || forced == 4 || forced == 8) waves = forced;
-  return pa::launch_decode(a, pool->dtype, q_dtype == PA_ACT_BF16, pool->head_dim, waves,
-                           (hipStream_t)stream);
+  return waves;
 }
 
-}  // namespace
-
-extern "C" {
-
-int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
-              const pa_kv_pool* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
-              const int32_t* context_lens, float sm_scale, int32_t partition_size, float* out,
-              float* part_out, float* part_lse, int32_t* dev_err, void* stream) {
-  return decode_call(q, q_dtype, num_seqs, num_q_heads, pool, nullptr, nullptr, block_tables,
-                     max_blocks_per_seq, context_lens, sm_scale, partition_size, out, part_out,
-                     part_lse, dev_err, stream);
+// pa_decode and pa_append_decode: k_new / v_new NULL for the former
+int decode_call(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                const int32_t* context_lens, float sm_scale, int32_t partition_size, float* out,
+                float* part_out, float* part_lse, int32_t* dev_err,
+                const pa_launch_options* opts, void* stream) {
+  pa::DecodeArgs a{};
+  int st = decode_geometry(num_seqs, num_q_heads, pool, block_tables, max_blocks_per_seq,
+                           context_lens, partition_size, opts, a);
+  if (st != PA_OK) return st;
+  if (!act_ok(q_dtype) || !act_matches_pool(q_dtype, pool->dtype)) return PA_ERR_DTYPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!q) return PA_ERR_NULL;
+  if (partition_size == 0) {
+    if (!out) return PA_ERR_NULL;
+    if (!aligned(out, 16)) return PA_ERR_ALIGN;
+  } else {
+    if (!part_out || !part_lse) return PA_ERR_NULL;
+    if (!aligned(part_out, 16) || !aligned(part_lse, 4)) return PA_ERR_ALIGN;
+  }
+  if (!aligned(q, 16) || !aligned(dev_err, 4) || !aligned(k_new, 16) || !aligned(v_new, 16))
+    return PA_ERR_ALIGN;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.out = out;
+  a.part_out = part_out;
+  a.part_lse = part_lse;
+  a.err = dev_err;
+  a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  return pa::launch_decode(a, pool->dtype, q_dtype == PA_ACT_BF16, pool->head_dim,
+                           decode_waves(a, pool->dtype, opts), (hipStream_t)stream);
 }
 
-int pa_append_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
-                     const pa_kv_pool* pool, const void* k_new, const void* v_new,
-                     const int32_t* block_tables, int32_t max_blocks_per_seq,
-                     const int32_t* context_lens, float sm_scale, int32_t partition_size,
-                     float* out, float* part_out, float* part_lse, int32_t* dev_err,
-                     void* stream) {
-  if (num_seqs > 0 && (!k_new || !v_new)) return PA_ERR_NULL;
-  return decode_call(q, q_dtype, num_seqs, num_q_heads, pool, k_new, v_new, block_tables,
-                     max_blocks_per_seq, context_lens, sm_scale, partition_size, out, part_out,
-                     part_lse, dev_err, stream);
-}
-
-int pa_prefill(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
-               int32_t num_queries, const int32_t* query_start, int32_t max_query_len,
-               const pa_kv_pool* pool,
-               const int32_t* block_tables, int32_t max_blocks_per_seq,
-               const int32_t* context_lens, float sm_scale, float* out, int32_t* dev_err,
-               void* stream) {
+int prefill_call(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                 int32_t num_queries, const int32_t* query_start, int32_t max_query_len,
+                 const pa_kv_pool* pool, const int32_t* block_tables,
+                 int32_t max_blocks_per_seq, const int32_t* context_lens, float sm_scale,
+                 float* out, int32_t* dev_err, const pa_launch_options* opts, void* stream) {
   int st = check_pool(pool);
   if (st != PA_OK) return st;
+  if ((st = check_options(opts)) != PA_OK) return st;
   if (!act_ok(q_dtype) || !act_matches_pool(q_dtype, pool->dtype)) return PA_ERR_DTYPE;
   if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_q_heads < 1) return PA_ERR_SHAPE;
   if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_SHAPE;
@@ -433,7 +430,90 @@ int pa_prefill(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_h
   a.cap = pa::outlier_capacity(pool->head_dim);
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
   return pa::launch_prefill(a, pool->dtype, q_dtype == PA_ACT_BF16, pool->head_dim,
-                            (hipStream_t)stream);
+                            opts ? opts->prefill_col_tiles : 0, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+              const pa_kv_pool* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, float sm_scale, int32_t partition_size, float* out,
+              float* part_out, float* part_lse, int32_t* dev_err, void* stream) {
+  return decode_call(q, q_dtype, num_seqs, num_q_heads, pool, nullptr, nullptr, block_tables,
+                     max_blocks_per_seq, context_lens, sm_scale, partition_size, out, part_out,
+                     part_lse, dev_err, nullptr, stream);
+}
+
+int pa_decode_ex(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                 const pa_kv_pool* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                 const int32_t* context_lens, float sm_scale, int32_t partition_size, float* out,
+                 float* part_out, float* part_lse, int32_t* dev_err,
+                 const pa_launch_options* opts, void* stream) {
+  return decode_call(q, q_dtype, num_seqs, num_q_heads, pool, nullptr, nullptr, block_tables,
+                     max_blocks_per_seq, context_lens, sm_scale, partition_size, out, part_out,
+                     part_lse, dev_err, opts, stream);
+}
+
+int pa_append_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                     const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, float sm_scale, int32_t partition_size,
+                     float* out, float* part_out, float* part_lse, int32_t* dev_err,
+                     void* stream) {
+  return pa_append_decode_ex(q, q_dtype, num_seqs, num_q_heads, pool, k_new, v_new,
+                             block_tables, max_blocks_per_seq, context_lens, sm_scale,
+                             partition_size, out, part_out, part_lse, dev_err, nullptr, stream);
+}
+
+int pa_append_decode_ex(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                        const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* context_lens, float sm_scale, int32_t partition_size,
+                        float* out, float* part_out, float* part_lse, int32_t* dev_err,
+                        const pa_launch_options* opts, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) return PA_ERR_NULL;
+  return decode_call(q, q_dtype, num_seqs, num_q_heads, pool, k_new, v_new, block_tables,
+                     max_blocks_per_seq, context_lens, sm_scale, partition_size, out, part_out,
+                     part_lse, dev_err, opts, stream);
+}
+
+int pa_prefill(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+               int32_t num_queries, const int32_t* query_start, int32_t max_query_len,
+               const pa_kv_pool* pool,
+               const int32_t* block_tables, int32_t max_blocks_per_seq,
+               const int32_t* context_lens, float sm_scale, float* out, int32_t* dev_err,
+               void* stream) {
+  return prefill_call(q, q_dtype, num_seqs, num_q_heads, num_queries, query_start,
+                      max_query_len, pool, block_tables, max_blocks_per_seq, context_lens,
+                      sm_scale, out, dev_err, nullptr, stream);
+}
+
+int pa_prefill_ex(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                  int32_t num_queries, const int32_t* query_start, int32_t max_query_len,
+                  const pa_kv_pool* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, float sm_scale, float* out, int32_t* dev_err,
+                  const pa_launch_options* opts, void* stream) {
+  return prefill_call(q, q_dtype, num_seqs, num_q_heads, num_queries, query_start,
+                      max_query_len, pool, block_tables, max_blocks_per_seq, context_lens,
+                      sm_scale, out, dev_err, opts, stream);
+}
+
+int pa_gather_probe(int32_t num_seqs, int32_t num_q_heads, const pa_kv_pool* pool,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t partition_size, uint32_t* sink,
+                    int32_t* dev_err, const pa_launch_options* opts, void* stream) {
+  pa::DecodeArgs a{};
+  int st = decode_geometry(num_seqs, num_q_heads, pool, block_tables, max_blocks_per_seq,
+                           context_lens, partition_size, opts, a);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return PA_OK;
+  if (!sink) return PA_ERR_NULL;
+  if (!aligned(sink, 4) || !aligned(dev_err, 4)) return PA_ERR_ALIGN;
+  a.err = dev_err;
+  return pa::launch_gather_probe(a, pool->dtype, pool->head_dim,
+                                 decode_waves(a, pool->dtype, opts), sink, (hipStream_t)stream);
 }
 
 int pa_merge(const float* part_out, const float* part_lse, const int32_t* context_lens,

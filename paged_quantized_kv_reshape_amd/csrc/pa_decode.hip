@@ -56,6 +56,21 @@ constexpr int fp4_qlds_floats() { return (D + 4) * GP; }
 constexpr int kIdsLds = 64;
 
 
+// Words 1 and 2 of an FP4 outlier record (channels 4 .. 11), wave-uniform. A record no
+// wave writes during the launch is read through the scalar cache (no vector-memory wait,
+// so a double-buffered tile's loads stay in flight). The record of the tile this wave
+// wrote itself in this launch (fresh) is read with a vector load: scalar loads assume
+// memory that is constant for the whole dispatch, and a fence does not order them.
+__device__ __forceinline__ uint2 record_words12(const uint8_t* rec, bool fresh) {
+  if (fresh) {
+    const uint2 r = *reinterpret_cast<const uint2*>(rec + 4);
+    return make_uint2((uint32_t)__builtin_amdgcn_readfirstlane((int)r.x),
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)r.y));
+  }
+  const uint4 r = load_uniform16(rec);
+  return make_uint2(r.y, r.z);
+}
+
 // pa_append_decode: the workgroup that reads sequence s's last position writes the
 // sequence's new row there first, for its kv head, exactly as the cache-write kernels
 // store it (16-bit copy, FP8 with the head's scale, FP8 with the row's own scale). K uses
@@ -174,6 +189,13 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     if (!split && p == 0) {
       for (int i = threadIdx.x; i < G * D; i += blockDim.x)
         a.out[((int64_t)s * Hq + kvh * G) * D + i] = 0.0f;
+    }
+    // split: every partition of the sequence reads as empty (lse -inf, zero output), so a
+    // merge over any number of them gives a zero output and lse -inf
+    if (split && (int)threadIdx.x < G) {
+      const int64_t row = ((int64_t)s * Hq + kvh * G + threadIdx.x) * a.max_partitions + p;
+      a.part_lse[row] = -INFINITY;
+      for (int i = 0; i < D; ++i) a.part_out[row * D + i] = 0.0f;
     }
     return;
   }
@@ -300,6 +322,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
       b_raw = __builtin_amdgcn_readlane(ids_a, x & 63);
     }
     T.jb = jb0 + wave + x * W;
+    T.fresh = APPEND && wrote && x == my_n - 1;
     T.ok = (unsigned)b_raw < (unsigned)a.num_blocks;
     err_bits |= T.ok ? 0 : PA_DEVERR_BAD_BLOCK;
     const int b = T.ok ? b_raw : 0;
@@ -311,13 +334,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     // lanes, stream (209 -> 195 us).
     load_words<G_::KW, kStreamK>(T.k, kpool + T.tile * G_::TILEB + k_lane_off);
     if constexpr (KV == KV_FP4) {
-      // one 16-byte chunk: channels 8 c .. 8 c + 7 of tokens 4 kg .. 4 kg + 3
-      uint32_t x[4];
-      load_words<4, true>(x, vpool + T.tile * G_::TILEB + (c * 4 + kg) * 16);
-      T.v[0][0] = x[0];
-      T.v[1][0] = x[1];
-      T.v[2][0] = x[2];
-      T.v[3][0] = x[3];
+      // one chunk: channels NT c .. NT c + NT - 1 of tokens 4 kg .. 4 kg + 3
+      fp4_v_chunk<D, true>(T, vpool + T.tile * G_::TILEB, c, kg);
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -383,9 +401,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
       uint32_t rw[3] = {(uint32_t)__builtin_amdgcn_readlane((int)T.r0, 0), 0u, 0u};
       int nk = (int)(rw[0] & 0xFFu);
       if (nk > 3 && nk != 0xFF) {  // more channels than the first word holds (rare)
-        const uint4 r = load_uniform16(kpool + T.tile * G_::TILEB + PA_FP4_RECORD_OFF(D));
-        rw[1] = r.y;
-        rw[2] = r.z;
+        const uint2 r = record_words12(kpool + T.tile * G_::TILEB + PA_FP4_RECORD_OFF(D), T.fresh);
+        rw[1] = r.x;
+        rw[2] = r.y;
       }
       if (nk == 0xFF) {
         err_bits |= T.ok ? PA_DEVERR_UNCALIBRATED : 0;
@@ -461,9 +479,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
       uint32_t rw[3] = {(uint32_t)__builtin_amdgcn_readlane((int)T.r0, 32), 0u, 0u};
       int nv = (int)(rw[0] & 0xFFu);
       if (nv > 3 && nv != 0xFF) {
-        const uint4 r = load_uniform16(vpool + T.tile * G_::TILEB + PA_FP4_RECORD_OFF(D));
-        rw[1] = r.y;
-        rw[2] = r.z;
+        const uint2 r = record_words12(vpool + T.tile * G_::TILEB + PA_FP4_RECORD_OFF(D), T.fresh);
+        rw[1] = r.x;
+        rw[2] = r.y;
       }
       if (nv == 0xFF) {
         err_bits |= T.ok ? PA_DEVERR_UNCALIBRATED : 0;
@@ -580,7 +598,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     const int src_lane = g + 16 * (d / DL);
     const int e = d % DL;
     for (int w = 0; w < W; ++w) {
-      const float f = __builtin_amdgcn_exp2f(m_lds[w * 16 + g] - M);  // 0 for idle waves
+      // 0 for a wave with nothing folded in (idle, or every block id bad): m = -inf, and
+      // -inf - -inf would be NaN when no wave has anything
+      const float mw = m_lds[w * 16 + g];
+      const float f = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
       Lsum += f * l_lds[w * 16 + g];
       const float4 x = *reinterpret_cast<const float4*>(acc_lds + ((int64_t)w * 64 + src_lane) * STRIDE + e);
       o.x += f * x.x;
@@ -694,6 +715,12 @@ int launch_decode(const DecodeArgs& a, int kv, bool qbf, int D, int waves, hipSt
       case KV_BF8T:
         return qbf ? launch_one<KV_BF8T, 64, true>(a, waves, st)
                    : launch_one<KV_BF8T, 64, false>(a, waves, st);
+      case KV_FP4:
+        if (a.group <= 8)
+          return qbf ? launch_one<KV_FP4, 64, true, 8>(a, waves, st)
+                     : launch_one<KV_FP4, 64, false, 8>(a, waves, st);
+        return qbf ? launch_one<KV_FP4, 64, true, 16>(a, waves, st)
+                   : launch_one<KV_FP4, 64, false, 16>(a, waves, st);
     }
   }
   return PA_ERR_DTYPE;

@@ -122,11 +122,13 @@ __device__ __forceinline__ void fp4_encode_row(const uint16_t* row, uint8_t* til
     if (!vside) {
       tile[off * (D / 2) + lane] = (uint8_t)(q0 | (q1 << 4));  // K: token rows
     } else {
-      // V: channels 2 lane and 2 lane + 1 sit in word lane % 4 of chunk
-      // (lane / 4) * 4 + off / 4, at bit 8 ((off % 4) / 2) + 4 (off % 2) and 16 above
+      // V: a chunk holds D / 16 channels of four tokens in D / 32 words, two channels per
+      // word; channels 2 lane and 2 lane + 1 sit in word lane % WPC of chunk
+      // (lane / WPC) * 4 + off / 4, at bit 8 ((off % 4) / 2) + 4 (off % 2) and 16 above
+      constexpr int WPC = D / 32;
       const int sh = 8 * ((off & 3) >> 1) + 4 * (off & 1);
       vb.word = reinterpret_cast<uint32_t*>(tile) +
-                (((lane >> 2) * 4 + (off >> 2)) * 4 + (lane & 3));
+                (((lane / WPC) * 4 + (off >> 2)) * WPC + (lane % WPC));
       vb.bits = (q0 << sh) | (q1 << (sh + 16));
       vb.mask = (0xFu << sh) | (0xFu << (sh + 16));
     }

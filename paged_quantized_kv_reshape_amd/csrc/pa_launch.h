@@ -54,8 +54,13 @@ struct DecodeArgs {
 
 int launch_decode(const DecodeArgs& a, int kv_dtype, bool q_bf16, int head_dim, int waves,
                   hipStream_t st);
-// multi-token queries (pa_prefill): the paired-block kernel, every pool format
-int launch_prefill(const DecodeArgs& a, int kv_dtype, bool q_bf16, int head_dim, hipStream_t st);
+// gather-only ceiling (pa_gather_probe): the decode's launch and tile reads, no math
+int launch_gather_probe(const DecodeArgs& a, int kv_dtype, int head_dim, int waves,
+                        uint32_t* sink, hipStream_t st);
+// multi-token queries (pa_prefill): the paired-block kernel, every pool format;
+// col_tiles 2 or 3 fixes the column tiles per wave (0: the format's default)
+int launch_prefill(const DecodeArgs& a, int kv_dtype, bool q_bf16, int head_dim, int col_tiles,
+                   hipStream_t st);
 
 // Whole-block copy: array j of the pool has vecs_per_block[j] 16-byte vectors per block.
 struct CopyArgs {

@@ -41,7 +41,8 @@ __global__ __launch_bounds__(64 * kMergeMaxWaves) void k_merge(
   const int64_t sh = blockIdx.x;  // s * Hq + h
   const int s = (int)(sh / Hq);
   const int L = cl[s];
-  const int np = L >= 1 ? min((L + ps - 1) / ps, P) : 0;
+  // a context the P partitions cannot hold (or none at all) has nothing valid to merge
+  const int np = L >= 1 && (int64_t)L <= (int64_t)P * ps ? (L + ps - 1) / ps : 0;
   vec_t* o = reinterpret_cast<vec_t*>(out + sh * D);
   if (np == 0) {
     if (wave == 0) {
@@ -56,7 +57,9 @@ __global__ __launch_bounds__(64 * kMergeMaxWaves) void k_merge(
   float wl = 0.0f;      // this lane's share of the weight sum
   vec_t acc = vec_t(0.0f);
   for (int b0 = wave * B; b0 < np; b0 += W * B) {
-    const float x = lane < B && b0 + lane < np ? lse[b0 + lane] : -INFINITY;
+    // a non-finite lse (nothing written there that a decode would write) weighs 0
+    float x = lane < B && b0 + lane < np ? lse[b0 + lane] : -INFINITY;
+    x = __builtin_isfinite(x) ? x : -INFINITY;
     vec_t r[B];
 #pragma unroll
     for (int j = 0; j < B; ++j) r[j] = rows[(int64_t)min(b0 + j, np - 1) * (D / CPL)];
@@ -71,8 +74,11 @@ __global__ __launch_bounds__(64 * kMergeMaxWaves) void k_merge(
     const float wx = x == -INFINITY ? 0.0f : __expf(x - m);
     wl += wx;
 #pragma unroll
-    for (int j = 0; j < B; ++j)
-      acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wx), j)) * r[j];
+    for (int j = 0; j < B; ++j) {
+      // a row of weight 0 is skipped, not multiplied: its values may be anything (NaN)
+      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wx), j));
+      if (wj != 0.0f) acc += wj * r[j];
+    }
   }
   const float wsum = wave_sum(wl);
   if (W == 1) {

@@ -26,8 +26,6 @@
 // the token scale and the K outliers' fp16 terms (q from the fragments already in LDS), P
 // takes the V token scale, and each V outlier's term goes straight into the accumulator
 // register of its channel (register indexing with a wave-uniform channel).
-#include <stdlib.h>
-
 #include <type_traits>
 
 #include "pa_device.h"
@@ -161,13 +159,9 @@ void k_prefill_mt(DecodeArgs a) {
     if constexpr (KV == KV_FP4) {
       const uint8_t* kt = kpool + T.tile * G_::TILEB;
       const uint8_t* vt = vpool + T.tile * G_::TILEB;
-      // V is stored by channel: one 16-byte chunk, channels 8 c .. 8 c + 7 of tokens
+      // V is stored by channel: one chunk, channels NT c .. NT c + NT - 1 of tokens
       // 4 kg .. 4 kg + 3
-      const uint4 x = *reinterpret_cast<const uint4*>(vt + (c * 4 + kg) * 16);
-      T.v[0][0] = x.x;
-      T.v[1][0] = x.y;
-      T.v[2][0] = x.z;
-      T.v[3][0] = x.w;
+      fp4_v_chunk<D, false>(T, vt, c, kg);
       // per-token scales, the first word of each outlier record (lanes 0-31 K's, 32-63
       // V's) and the first outlier slot, which a full block usually fills exactly
       T.sk = reinterpret_cast<const float4*>(kt + PA_FP4_SCALE_OFF(D))[kg];
@@ -495,21 +489,19 @@ int launch_d(const DecodeArgs& a, int kv, bool qbf, int nct, hipStream_t st) {
     case KV_BF8T:
       return qbf ? launch_kv<KV_BF8T, D, true>(a, nct, st) : launch_kv<KV_BF8T, D, false>(a, nct, st);
     case KV_FP4:
-      if constexpr (D == 128)
-        return qbf ? launch_kv<KV_FP4, D, true>(a, nct, st) : launch_kv<KV_FP4, D, false>(a, nct, st);
-      break;
+      return qbf ? launch_kv<KV_FP4, D, true>(a, nct, st) : launch_kv<KV_FP4, D, false>(a, nct, st);
   }
   return PA_ERR_DTYPE;
 }
 
 }  // namespace
 
-int launch_prefill(const DecodeArgs& a, int kv, bool qbf, int D, hipStream_t st) {
+int launch_prefill(const DecodeArgs& a, int kv, bool qbf, int D, int col_tiles,
+                   hipStream_t st) {
   // column tiles per wave: 3, or 2 for FP4 pools, whose tiles carry scales, records and
   // outlier slots (3 spill there: 258 vs 316 TFLOP/s on the long-context workload);
-  // PA_PREFILL_NCT=2 or 3 overrides, for tuning
-  const char* e = getenv("PA_PREFILL_NCT");
-  const int nct = e && *e ? atoi(e) : kv == KV_FP4 ? 2 : 3;
+  // col_tiles 2 or 3 overrides (pa_launch_options), for tuning
+  const int nct = col_tiles == 2 || col_tiles == 3 ? col_tiles : kv == KV_FP4 ? 2 : 3;
   return D == 128 ? launch_d<128>(a, kv, qbf, nct, st) : launch_d<64>(a, kv, qbf, nct, st);
 }
 

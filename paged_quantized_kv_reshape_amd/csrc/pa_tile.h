@@ -35,7 +35,9 @@ struct Geo {
                                : f8_tok(KV) ? PA_FP8T_TILE_BYTES(D)
                                             : kBlock * ROWB;
   static constexpr int KW = DL * EBITS / 32;       // K words per lane
-  static constexpr int VW = NT * EBITS / 32;       // V words per lane per token
+  // V words per lane per token; FP4 V is read by channel instead (fp4_v_chunk): T.v[w][0]
+  // holds word w of the lane's chunk
+  static constexpr int VW = KV == KV_FP4 ? 1 : NT * EBITS / 32;
   static constexpr int KLANEB = DL * EBITS / 8;    // K bytes per lane
   static constexpr int VLANEB = NT * EBITS / 8;    // V bytes per lane per token
 };
@@ -107,7 +109,21 @@ struct Tile {
   int64_t tile;   // b * Hkv + kv head
   int jb;         // logical block index in the sequence
   bool ok;        // block id in range
+  bool fresh = false;  // decode with append: the tile whose row this wave wrote in this launch
 };
+
+// FP4 V codes of one lane: chunk c * 4 + kg of the tile's first 8 D bytes holds channels
+// NT c .. NT c + NT - 1 of tokens 4 kg .. 4 kg + 3 (2 NT bytes: 16 at head_dim 128, 8 at 64),
+// loaded with one streaming or ordinary load into T.v[0..NT/2)[0].
+template <int D, bool NT_HINT>
+__device__ __forceinline__ void fp4_v_chunk(Tile<KV_FP4, D>& T, const uint8_t* tile, int c,
+                                            int kg) {
+  constexpr int W = D / 32;  // words per chunk
+  uint32_t x[W];
+  load_words<W, NT_HINT>(x, tile + (c * 4 + kg) * (4 * W));
+#pragma unroll
+  for (int w = 0; w < W; ++w) T.v[w][0] = x[w];
+}
 
 // 16-bit K fragment for step t: 8 values of channels D/4 kg + 8 t + (0..7).
 template <int KV, int D, bool QBF>

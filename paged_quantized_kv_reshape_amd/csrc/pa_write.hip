@@ -534,8 +534,8 @@ int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool
       }
     }
   } else {
-    // (the FP4 format exists for head_dim 128 only; heads index grid.y)
-    if (D != 128 || hkv > 65535) return PA_ERR_SHAPE;
+    // heads index grid.y
+    if ((D != 64 && D != 128) || hkv > 65535) return PA_ERR_SHAPE;
     Fp4Args a;
     a.side[0] = {(const uint16_t*)k_new, (uint8_t*)p.k, p.k_out_val};
     a.side[1] = {(const uint16_t*)v_new, (uint8_t*)p.v, p.v_out_val};
@@ -550,15 +550,18 @@ int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool
     a.seq_records = seq_records;
     a.num_seqs = num_seqs;
     const dim3 gt(grid1((int64_t)T * hkv, 256), 1, 2);
-    hipLaunchKernelGGL(k_fp4_mark<128>, gt, dim3(256), 0, st, a);
     const dim3 g((unsigned)((T + kRowsPerWg - 1) / kRowsPerWg), hkv, 2);
+    const bool d128 = D == 128;
+    hipLaunchKernelGGL(d128 ? k_fp4_mark<128> : k_fp4_mark<64>, gt, dim3(256), 0, st, a);
     if (seq_records) {
-      hipLaunchKernelGGL(k_fp4_adopt<128>, gt, dim3(256), 0, st, a);
+      hipLaunchKernelGGL(d128 ? k_fp4_adopt<128> : k_fp4_adopt<64>, gt, dim3(256), 0, st, a);
     } else {
-      auto cal = bf16 ? k_fp4_calibrate<true, 128> : k_fp4_calibrate<false, 128>;
+      auto cal = d128 ? (bf16 ? k_fp4_calibrate<true, 128> : k_fp4_calibrate<false, 128>)
+                      : (bf16 ? k_fp4_calibrate<true, 64> : k_fp4_calibrate<false, 64>);
       hipLaunchKernelGGL(cal, g, dim3(64 * kRowsPerWg), 0, st, a);
     }
-    auto enc = bf16 ? k_fp4_encode<true, 128> : k_fp4_encode<false, 128>;
+    auto enc = d128 ? (bf16 ? k_fp4_encode<true, 128> : k_fp4_encode<false, 128>)
+                    : (bf16 ? k_fp4_encode<true, 64> : k_fp4_encode<false, 64>);
     hipLaunchKernelGGL(enc, g, dim3(64 * kRowsPerWg), 0, st, a);
   }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
@@ -567,7 +570,7 @@ int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool
 int launch_fp4_seq_outliers(const void* k_rows, const void* v_rows, bool bf16, int64_t num_rows,
                            int32_t hkv, int32_t D, const int32_t* row_start, int32_t num_seqs,
                            uint8_t* records, int32_t* err, hipStream_t st) {
-  if (D != 128) return PA_ERR_SHAPE;
+  if (D != 64 && D != 128) return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;
   SeqOutlierArgs a;
   a.k_rows = (const uint16_t*)k_rows;
@@ -578,7 +581,8 @@ int launch_fp4_seq_outliers(const void* k_rows, const void* v_rows, bool bf16, i
   a.cap = outlier_capacity(D);
   a.records = records;
   a.err = err;
-  auto kern = bf16 ? k_fp4_seq_outliers<true, 128> : k_fp4_seq_outliers<false, 128>;
+  auto kern = D == 128 ? (bf16 ? k_fp4_seq_outliers<true, 128> : k_fp4_seq_outliers<false, 128>)
+                       : (bf16 ? k_fp4_seq_outliers<true, 64> : k_fp4_seq_outliers<false, 64>);
   hipLaunchKernelGGL(kern, dim3((unsigned)num_seqs, hkv, 2), dim3(256), 0, st, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
@@ -604,8 +608,9 @@ int launch_fp8_scales(const void* x, bool bf16, bool e5m2, int64_t rows, int32_t
 int launch_reset(const pa_kv_pool& p, const int32_t* ids, int32_t n, hipStream_t st) {
   if (n == 0) return PA_OK;
   const int64_t total = (int64_t)n * p.num_kv_heads;
-  if (p.head_dim != 128) return PA_ERR_SHAPE;
-  hipLaunchKernelGGL(k_reset_records<128>, dim3(grid1(total, 256)), dim3(256), 0, st,
+  if (p.head_dim != 64 && p.head_dim != 128) return PA_ERR_SHAPE;
+  hipLaunchKernelGGL(p.head_dim == 128 ? k_reset_records<128> : k_reset_records<64>,
+                     dim3(grid1(total, 256)), dim3(256), 0, st,
                      (uint8_t*)p.k, (uint8_t*)p.v, ids, n, p.num_kv_heads, p.num_blocks);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }

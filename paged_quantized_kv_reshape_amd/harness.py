@@ -28,10 +28,11 @@ class DeviceRun:
     SEQ_CHUNK = 512
 
     def __init__(self, w, device="cuda", partition_size=None, fill=0xA5, pool_copies=1,
-                 fp4_calibration="block"):
+                 fp4_calibration="block", waves=None):
         assert fp4_calibration in ("block", "sequence")
         assert fp4_calibration == "block" or w.kv == "fp4"
         self.w = w
+        self.waves = waves  # decode waves per workgroup (None: the library's choice)
         self.fp4_calibration = fp4_calibration
         self.device = device
         self.ps = w.partition_size if partition_size is None else partition_size
@@ -113,7 +114,7 @@ class DeviceRun:
         pool = pool or self.pool
         B.pa_decode(self.q, pool, self.block_tables, self.context_lens, self.w.sm_scale,
                     self.ps, out=self.out, part_out=self.part_out, part_lse=self.part_lse,
-                    dev_err=self.dev_err)
+                    dev_err=self.dev_err, waves=self.waves)
         if merge:
             self.merge()
 
@@ -140,7 +141,8 @@ class DeviceRun:
     def append_decode(self, pool=None, merge=True):
         B.pa_append_decode(self.q, pool or self.pool, self.step_k, self.step_v, self.block_tables,
                            self.context_lens, self.w.sm_scale, self.ps, out=self.out,
-                           part_out=self.part_out, part_lse=self.part_lse, dev_err=self.dev_err)
+                           part_out=self.part_out, part_lse=self.part_lse, dev_err=self.dev_err,
+                           waves=self.waves)
         if merge:
             self.merge()
 
@@ -148,6 +150,16 @@ class DeviceRun:
         """The same step in one launch (+ merge): each sequence's new row is written by the
         decode workgroup that reads it."""
         self.append_decode(pool)
+
+    def gather_probe(self, pool=None, sink=None):
+        """The decode's launch with its tile reads only (pa_gather_probe)."""
+        if sink is None:
+            if getattr(self, "probe_sink", None) is None:
+                self.probe_sink = torch.zeros(B.PROBE_SINK_WORDS, dtype=torch.int32,
+                                              device=self.device)
+            sink = self.probe_sink
+        B.pa_gather_probe(pool or self.pool, self.w.num_q_heads, self.block_tables,
+                          self.context_lens, self.ps, sink, self.dev_err, waves=self.waves)
 
     def device_error(self) -> int:
         return B.pa_read_device_error(self.dev_err)

@@ -14,7 +14,7 @@ from conftest import ROOT
 B = pytest.importorskip("paged_quantized_kv_reshape_amd.binding")
 
 PA_OK, NULL, SHAPE, DTYPE, BLOCK, CONTEXT, PART, LAUNCH, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7, -8
-MEMORY, EXHAUSTED, STATE = -9, -10, -11
+MEMORY, EXHAUSTED, STATE, SCRATCH = -9, -10, -11, -12
 FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
 
 
@@ -34,7 +34,7 @@ def test_library_exports_every_declared_entry_point():
 def test_status_strings():
     lib = B.lib()
     for code in (PA_OK, NULL, SHAPE, DTYPE, BLOCK, CONTEXT, PART, LAUNCH, ALIGN, MEMORY,
-                 EXHAUSTED, STATE):
+                 EXHAUSTED, STATE, SCRATCH):
         s = lib.pa_status_string(code).decode()
         assert s.startswith("PA_"), s
     assert "unknown" in lib.pa_status_string(-99).decode()
@@ -47,6 +47,8 @@ def test_status_strings():
     # FP4: per (block, head) 1024 code bytes + 64 scale bytes + 16 record bytes + 32 bytes of
     # the first outlier, padded to 1152; then 10 more outlier slots of 16 fp16 values
     ("fp4", 128, [10 * 3 * 1152] * 2 + [10 * 3 * 10 * 16 * 2] * 2),
+    # head_dim 64: 512 + 64 + 16 + 32 bytes padded to 640; 4 more outlier slots (capacity 5)
+    ("fp4", 64, [10 * 3 * 640] * 2 + [10 * 3 * 4 * 16 * 2] * 2),
     ("bf8", 128, [10 * 3 * 16 * 128] * 2 + [0] * 2),
     # per-token FP8: 16 x D code bytes + 16 fp32 scales per (block, head), padded to 128
     ("fp8t", 128, [10 * 3 * 2176] * 2 + [0] * 2),
@@ -63,7 +65,7 @@ def test_pool_layout_rejects():
     assert lib.pa_pool_layout(7, 10, 1, 128, out) == DTYPE
     assert lib.pa_pool_layout(0, 0, 1, 128, out) == SHAPE
     assert lib.pa_pool_layout(0, 10, 1, 96, out) == SHAPE
-    assert lib.pa_pool_layout(3, 10, 1, 64, out) == SHAPE  # FP4 needs head_dim 128
+    assert lib.pa_pool_layout(3, 10, 1, 96, out) == SHAPE
     assert lib.pa_pool_layout(0, 10, 1, 128, None) == NULL
     assert lib.pa_outlier_capacity(128) == 11 and lib.pa_outlier_capacity(64) == 5
     assert lib.pa_outlier_capacity(80) == SHAPE
@@ -91,7 +93,7 @@ def test_cache_write_rejects():
     assert _write(_pool(dtype=7)) == DTYPE
     assert _write(_pool(d=96)) == SHAPE
     assert _write(_pool(nb=0)) == SHAPE
-    assert _write(_pool(dtype=3, d=64)) == SHAPE
+    assert _write(_pool(dtype=3, d=96)) == SHAPE
     assert _write(_pool(dtype=0), act=1) == DTYPE      # fp16 pool, bf16 rows
     assert _write(_pool(dtype=1), act=0) == DTYPE      # bf16 pool, fp16 rows
     assert _write(_pool(), act=4) == DTYPE
@@ -230,7 +232,7 @@ def test_fp4_sequence_calls_reject():
         k.get("k", FAKE), k.get("v", FAKE), k.get("act", 1), k.get("rows", 10), k.get("hkv", 1),
         k.get("d", 128), k.get("rs", FAKE), k.get("S", 2), k.get("out", FAKE), k.get("err"), None)
     assert f(act=3) == DTYPE
-    assert f(d=64) == SHAPE and f(rows=-1) == SHAPE and f(S=-1) == SHAPE and f(hkv=0) == SHAPE
+    assert f(d=96) == SHAPE and f(rows=-1) == SHAPE and f(S=-1) == SHAPE and f(hkv=0) == SHAPE
     assert f(S=0) == PA_OK
     assert f(rs=None) == NULL and f(out=None) == NULL and f(k=None) == NULL
     assert f(out=FAKE + 4) == ALIGN and f(k=FAKE + 2) == ALIGN and f(err=FAKE + 1) == ALIGN
@@ -244,6 +246,57 @@ def test_fp4_sequence_calls_reject():
     assert w(ts=None) == NULL and w(recs=None) == NULL and w(slots=None) == NULL
     assert w(recs=FAKE + 4) == ALIGN and w(ts=FAKE + 2) == ALIGN
     assert w(pool=_pool(dtype=3, fp4=False)) == NULL
+
+
+def _opts(waves=0, tiles=0, reserved=0):
+    o = B.pa_launch_options()
+    o.decode_waves, o.prefill_col_tiles = waves, tiles
+    o.reserved[5] = reserved
+    return ctypes.byref(o)
+
+
+@pytest.mark.parametrize("opts,expect", [
+    (dict(waves=3), SHAPE), (dict(waves=16), SHAPE), (dict(waves=-1), SHAPE),
+    (dict(tiles=1), SHAPE), (dict(tiles=4), SHAPE), (dict(reserved=1), SHAPE),
+])
+def test_launch_options_reject(opts, expect):
+    """The _ex entry points check their launch options before anything else is launched;
+    valid options on an empty batch launch nothing."""
+    lib = B.lib()
+    pool = ctypes.byref(_pool())
+    d = lambda o, S=2: lib.pa_decode_ex(FAKE, 1, S, 8, pool, FAKE, 4, FAKE, 0.1, 0, FAKE, FAKE,
+                                        FAKE, None, o, None)
+    a = lambda o, S=2: lib.pa_append_decode_ex(FAKE, 1, S, 8, pool, FAKE, FAKE, FAKE, 4, FAKE,
+                                               0.1, 0, FAKE, FAKE, FAKE, None, o, None)
+    p = lambda o, S=2: lib.pa_prefill_ex(FAKE, 1, S, 8, 10, FAKE, 5, pool, FAKE, 4, FAKE, 0.1,
+                                         FAKE, None, o, None)
+    g = lambda o, S=2: lib.pa_gather_probe(S, 8, pool, FAKE, 4, FAKE, 0, FAKE, None, o, None)
+    for fn in (d, a, p, g):
+        assert fn(_opts(**opts)) == expect
+        assert fn(_opts(waves=8, tiles=2), S=0) == PA_OK
+        assert fn(None, S=0) == PA_OK
+
+
+def test_gather_probe_rejects():
+    lib = B.lib()
+    f = lambda pool=None, **k: lib.pa_gather_probe(
+        k.get("S", 2), k.get("Hq", 8), ctypes.byref(pool if pool is not None else _pool()),
+        k.get("bt", FAKE), k.get("MB", 4), k.get("cl", FAKE), k.get("ps", 0),
+        k.get("sink", FAKE), k.get("err"), None, None)
+    assert f(pool=_pool(bs=8)) == BLOCK and f(pool=_pool(dtype=9)) == DTYPE
+    assert f(pool=_pool(hkv=3)) == SHAPE and f(S=-1) == SHAPE and f(Hq=0) == SHAPE
+    assert f(MB=0) == CONTEXT and f(ps=24) == PART
+    assert f(bt=None) == NULL and f(cl=None) == NULL and f(sink=None) == NULL
+    assert f(sink=FAKE + 2) == ALIGN and f(err=FAKE + 1) == ALIGN
+    assert f(S=0) == PA_OK
+
+
+def test_library_reads_no_environment_knob():
+    """Launch geometry comes only from arguments: the library's text names no environment
+    variable it would read."""
+    data = open(B._LIB_PATH, "rb").read()
+    assert b"getenv" not in data
+    assert b"PA_DECODE_WAVES" not in data and b"PA_PREFILL_NCT" not in data
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):

@@ -6,7 +6,6 @@ or per-token scales, FP4 with outliers, including blocks the new row opens and c
 outputs within max-abs 2e-3 and relative L2 1e-2, single pass and split (with pa_merge),
 1 and 4 waves per workgroup; and bit for bit the output of pa_cache_write followed by
 pa_decode on the same inputs."""
-import os
 
 import numpy as np
 import pytest
@@ -34,17 +33,9 @@ CASES = {
     "fp4": ("c5", dict(num_seqs=4, lens=[300, 977, 33, 17])),
     "fp4-2kv": ("c5", dict(num_seqs=3, lens=[129, 50, 1], num_kv_heads=2, num_q_heads=16,
                            act="f16")),
+    "fp4-d64": ("c5", dict(num_seqs=4, lens=[300, 977, 33, 17], head_dim=64, num_kv_heads=2,
+                           num_q_heads=8)),
 }
-
-
-@pytest.fixture(autouse=True)
-def _waves_env():
-    old = os.environ.get("PA_DECODE_WAVES")
-    yield
-    if old is None:
-        os.environ.pop("PA_DECODE_WAVES", None)
-    else:
-        os.environ["PA_DECODE_WAVES"] = old
 
 
 @pytest.mark.parametrize("waves", [1, 4])
@@ -55,13 +46,12 @@ def test_append_decode_matches_oracle_and_separate_calls(case, ps, waves):
     from paged_quantized_kv_reshape_amd.harness import DeviceRun
     base, over = CASES[case]
     w = config(base, **over)
-    os.environ["PA_DECODE_WAVES"] = str(waves)
     sc = w.step_call
     assert len(sc.rows) == w.num_seqs  # one new token per sequence, at its last position
     last = w.seq_start + w.context_lens.astype(np.int64) - 1
     assert np.array_equal(sc.rows, last)
     _say(f"[append] {case} ({w.kv}) ps={ps} W={waves} lens={w.context_lens.tolist()}")
-    run = DeviceRun(w, partition_size=ps, pool_copies=2)
+    run = DeviceRun(w, partition_size=ps, pool_copies=2, waves=waves)
     for p in run.pools:
         run.setup_writes(p)
     # (1) the fused step on pool 0
@@ -74,7 +64,7 @@ def test_append_decode_matches_oracle_and_separate_calls(case, ps, waves):
         pl = torch.empty((S, Hq, P), dtype=torch.float32, device="cuda")
     pa_append_decode(run.q, run.pools[0], run.step_k, run.step_v, run.block_tables,
                      run.context_lens, w.sm_scale, ps, out=None if ps else out, part_out=po,
-                     part_lse=pl, dev_err=run.dev_err)
+                     part_lse=pl, dev_err=run.dev_err, waves=waves)
     if ps:
         pa_merge(po, pl, run.context_lens, ps, out)
     # (2) the separate calls on pool 1

@@ -9,7 +9,6 @@ That reaches every record word (count and channels 1-3, 4-7, 8-11) and the outli
 past the first one, in the cache write, the decode (single pass and split), the
 write-and-decode launch and multi-token attention. Pools bit-exact; outputs within max-abs
 2e-3 and relative L2 1e-2 of the oracle's exact attention on the same dequantized cache."""
-import os
 
 import numpy as np
 import pytest
@@ -26,8 +25,12 @@ torch = pytest.importorskip("torch")
 
 from test_parity_gpu import _say  # noqa: E402
 
-K_CHANNELS = [3, 17, 29, 40, 64, 77, 90, 101, 127]
-V_CHANNELS = [5, 33, 58, 71, 96, 120]
+# head_dim -> (K channels, V channels) scaled by 30; the count that a fraction `frac` of
+# the blocks must reach on both sides, and one some K blocks must reach. At head_dim 64
+# (capacity 5) a few channels already dominate sigma, so counts of 3 to 5 mix; blocks with
+# 4 or 5 still read the record's second word.
+PLANT = {128: ([3, 17, 29, 40, 64, 77, 90, 101, 127], [5, 33, 58, 71, 96, 120], 4, 0.9, 8),
+         64: ([3, 17, 29, 40], [5, 33, 58, 61], 3, 0.75, 4)}
 _cache = {}
 
 
@@ -42,41 +45,33 @@ def _plant(rows, channels, act, scale=30.0):
     _round_into(f, act, rows, np.empty(f.shape, np.uint32))
 
 
-def _workload(act):
+def _workload(act, d=128):
     """Three sequences; the 705-token one writes its last row into a fresh block."""
-    if act not in _cache:
-        w = config("c5", num_seqs=3, lens=[705, 333, 1500], act=act)
-        _plant(w.k_rows, K_CHANNELS, act)
-        _plant(w.v_rows, V_CHANNELS, act)
+    if (act, d) not in _cache:
+        kc, vc, most, frac, some = PLANT[d]
+        w = config("c5", num_seqs=3, lens=[705, 333, 1500], act=act, head_dim=d)
+        _plant(w.k_rows, kc, act)
+        _plant(w.v_rows, vc, act)
         pool, ks, vs, near = replay(w)
-        # the case is what it claims: blocks with 4+ outliers on both sides, 8+ on K
+        # the case is what it claims: most blocks hold `most`+ outliers on both sides, some
+        # hold 4+ (the record's second word), and some K blocks hold `some`
         counts = {kv: C.fp4_records(pool, kv)[..., 0] for kv in ("k", "v")}
         used = {kv: c[c != 0xFF] for kv, c in counts.items()}
-        assert (used["k"] >= 8).sum() > 0 and (used["k"] >= 4).mean() > 0.9
-        assert (used["v"] >= 4).mean() > 0.9
-        _cache[act] = (w, pool, ks, vs, near)
-    return _cache[act]
-
-
-@pytest.fixture(autouse=True)
-def _waves_env():
-    old = os.environ.get("PA_DECODE_WAVES")
-    yield
-    if old is None:
-        os.environ.pop("PA_DECODE_WAVES", None)
-    else:
-        os.environ["PA_DECODE_WAVES"] = old
+        for kv in ("k", "v"):
+            assert (used[kv] >= most).mean() > frac and (used[kv] >= 4).sum() > 0
+        assert (used["k"] >= some).sum() > 0
+        _cache[(act, d)] = (w, pool, ks, vs, near)
+    return _cache[(act, d)]
 
 
 @pytest.mark.parametrize("waves", [1, 2])
 @pytest.mark.parametrize("ps", [0, 64, 512])
-@pytest.mark.parametrize("act", ["bf16", "f16"])
-def test_many_outliers_write_and_decode(act, ps, waves):
+@pytest.mark.parametrize("act,d", [("bf16", 128), ("f16", 128), ("bf16", 64)])
+def test_many_outliers_write_and_decode(act, d, ps, waves):
     from paged_quantized_kv_reshape_amd.harness import DeviceRun
-    w, pool, ks, vs, near = _workload(act)
-    os.environ["PA_DECODE_WAVES"] = str(waves)
-    _say(f"[fp4 many outliers] {act} ps={ps} W={waves}")
-    run = DeviceRun(w, partition_size=ps)
+    w, pool, ks, vs, near = _workload(act, d)
+    _say(f"[fp4 many outliers] {act} D={d} ps={ps} W={waves}")
+    run = DeviceRun(w, partition_size=ps, waves=waves)
     run.prepare()
     run.decode()
     torch.cuda.synchronize()
@@ -87,14 +82,15 @@ def test_many_outliers_write_and_decode(act, ps, waves):
                  f"many outliers {act} ps={ps} W={waves}")
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("ps", [0, 512])
-def test_many_outliers_append_decode(ps):
+def test_many_outliers_append_decode(ps, d):
     """The step's row written by the decode launch itself (the fresh block of sequence 0
     is calibrated on that row): pool bit-exact, output bitwise equal to the separate
     write and decode."""
     from paged_quantized_kv_reshape_amd.harness import DeviceRun
-    w, pool, ks, vs, near = _workload("bf16")
-    _say(f"[fp4 many outliers append] ps={ps}")
+    w, pool, ks, vs, near = _workload("bf16", d)
+    _say(f"[fp4 many outliers append] D={d} ps={ps}")
     fused = DeviceRun(w, partition_size=ps)
     fused.setup_writes()
     fused.append_decode()
@@ -112,12 +108,12 @@ def test_many_outliers_append_decode(ps):
 
 
 @pytest.mark.parametrize("n", [1, 37, 333])
-@pytest.mark.parametrize("act", ["bf16", "f16"])
-def test_many_outliers_prefill(act, n):
+@pytest.mark.parametrize("act,d", [("bf16", 128), ("f16", 128), ("bf16", 64)])
+def test_many_outliers_prefill(act, d, n):
     from paged_quantized_kv_reshape_amd import pa_prefill
     from paged_quantized_kv_reshape_amd.harness import DeviceRun
-    w, pool, ks, vs, near = _workload(act)
-    _say(f"[fp4 many outliers prefill] {act} n={n}")
+    w, pool, ks, vs, near = _workload(act, d)
+    _say(f"[fp4 many outliers prefill] {act} D={d} n={n}")
     run = DeviceRun(w, partition_size=0)
     run.prepare()
     q_bits, qs = prefill_queries(w, n)

@@ -6,7 +6,6 @@ Writes bit-exact against the oracle (codes, per-token scales, untouched sentinel
 including every 16-bit activation pattern; decode (fused and split-KV) and multi-token
 attention within max-abs 2e-3 and relative L2 1e-2 of exact attention on the identical
 dequantized cache."""
-import os
 
 import numpy as np
 import pytest
@@ -30,16 +29,6 @@ SHAPES = {
 }
 
 _cache = {}
-
-
-@pytest.fixture(autouse=True)
-def _waves_env():
-    old = os.environ.get("PA_DECODE_WAVES")
-    yield
-    if old is None:
-        os.environ.pop("PA_DECODE_WAVES", None)
-    else:
-        os.environ["PA_DECODE_WAVES"] = old
 
 
 def _setup(kv, cfg):
@@ -77,7 +66,6 @@ def test_decode_matches_oracle(kv, cfg, ps, waves):
     from paged_quantized_kv_reshape_amd import max_partitions
     from paged_quantized_kv_reshape_amd.harness import DeviceRun
     w, run, pool, ks, vs = _setup(kv, cfg)
-    os.environ["PA_DECODE_WAVES"] = str(waves)
     _say(f"[decode] {kv}/{cfg} ps={ps} waves={waves}")
     r = DeviceRun.__new__(DeviceRun)
     r.__dict__.update(run.__dict__)
@@ -87,6 +75,7 @@ def test_decode_matches_oracle(kv, cfg, ps, waves):
         r.part_out = torch.empty((S, Hq, P, D), dtype=torch.float32, device="cuda")
         r.part_lse = torch.empty((S, Hq, P), dtype=torch.float32, device="cuda")
     r.ps = ps
+    r.waves = waves
     r.out = torch.full_like(run.out, float("nan"))
     r.lse = torch.full_like(run.lse, float("nan"))
     r.decode()

@@ -71,3 +71,37 @@ def test_merge_matches_oracle(D, P, ps, order):
             assert_close(got[s, h], want, what)
             assert np.abs(got[s, h] - want).max() < 1e-4, what
             assert abs(got_lse[s, h] - want_lse) < 1e-4 * max(1.0, abs(want_lse)), what
+
+
+def test_merge_ignores_nonfinite_partials_and_overlong_contexts():
+    """A partition whose lse is not finite (NaN, +inf or -inf) weighs 0 and its row, which
+    may hold anything (NaN here), is not read into the sum; a context that the partitions
+    cannot hold (L > P * ps) or an empty one gives a zero output and lse -inf."""
+    from paged_quantized_kv_reshape_amd import pa_merge
+    rng = np.random.default_rng(5)
+    S, Hq, P, D, ps = 4, 2, 40, 128, 64
+    o = rng.standard_normal((S, Hq, P, D)).astype(np.float32)
+    lse = (rng.standard_normal((S, Hq, P)) * 4.0).astype(np.float32)
+    lse[:, :, 3] = -np.inf
+    lse[:, :, 7] = np.nan
+    lse[:, :, 11] = np.inf
+    o[:, :, [3, 7, 11]] = np.nan
+    lens = np.array([P * ps, 17 * ps + 5, P * ps + 1, 0], dtype=np.int32)
+    dev = dict(device="cuda")
+    out = torch.full((S, Hq, D), float("nan"), dtype=torch.float32, **dev)
+    lse_out = torch.full((S, Hq), float("nan"), dtype=torch.float32, **dev)
+    pa_merge(torch.from_numpy(o).to(**dev), torch.from_numpy(lse).to(**dev),
+             torch.from_numpy(lens).to(**dev), ps, out, lse_out)
+    torch.cuda.synchronize()
+    got, got_lse = out.cpu().numpy(), lse_out.cpu().numpy()
+    assert np.isfinite(got).all()
+    for s in range(2):
+        n = -(-int(lens[s]) // ps)
+        for h in range(Hq):
+            keep = np.isfinite(lse[s, h, :n])
+            want, want_lse = A.merge(o[s, h, :n][keep].astype(np.float64),
+                                     lse[s, h, :n][keep].astype(np.float64))
+            assert_close(got[s, h], want, f"seq {s} head {h}")
+            assert abs(got_lse[s, h] - want_lse) < 1e-4 * max(1.0, abs(want_lse))
+    for s in (2, 3):
+        assert np.all(got[s] == 0.0) and np.all(np.isneginf(got_lse[s]))

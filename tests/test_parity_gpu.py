@@ -4,7 +4,6 @@ Cache writes (codes, scales, outlier records and values, untouched sentinel byte
 bit-exact; decode outputs within max-abs 2e-3 and relative L2 1e-2 of exact attention on
 the identical dequantized cache. Small cases check every output; the full-size workloads
 run in the launch configuration the bench times and are checked on sampled sequences."""
-import os
 import sys
 
 import numpy as np
@@ -47,16 +46,6 @@ def _setup(cfg):
     return _cache[cfg]
 
 
-@pytest.fixture(autouse=True)
-def _waves_env():
-    old = os.environ.get("PA_DECODE_WAVES")
-    yield
-    if old is None:
-        os.environ.pop("PA_DECODE_WAVES", None)
-    else:
-        os.environ["PA_DECODE_WAVES"] = old
-
-
 @pytest.mark.parametrize("cfg", list(SMALL))
 def test_cache_write_bit_exact(cfg):
     w, run, pool, ks, vs, near = _setup(cfg)
@@ -75,7 +64,6 @@ def test_cache_write_bit_exact(cfg):
 def test_decode_matches_oracle(cfg, ps, waves):
     from paged_quantized_kv_reshape_amd.harness import DeviceRun
     w, run, pool, ks, vs, _ = _setup(cfg)
-    os.environ["PA_DECODE_WAVES"] = str(waves)
     _say(f"[decode] {cfg} ps={ps} waves={waves}")
     r = DeviceRun.__new__(DeviceRun)
     r.__dict__.update(run.__dict__)
@@ -86,6 +74,7 @@ def test_decode_matches_oracle(cfg, ps, waves):
         r.part_out = torch.empty((S, Hq, P, D), dtype=torch.float32, device="cuda")
         r.part_lse = torch.empty((S, Hq, P), dtype=torch.float32, device="cuda")
     r.ps = ps
+    r.waves = waves
     r.out = torch.full_like(run.out, float("nan"))
     r.lse = torch.full_like(run.lse, float("nan"))
     r.decode()
@@ -267,10 +256,12 @@ def test_gqa_groups_not_powers_of_two(kv, hq, hkv, ps):
 @pytest.mark.parametrize("ps", [0, 128])
 @pytest.mark.parametrize("kv,act,d", [("fp8", "f16", 128), ("fp4", "f16", 128),
                                       ("fp8", "bf16", 64), ("fp8", "f16", 64),
-                                      ("f16", "f16", 128), ("bf16", "bf16", 64)])
+                                      ("f16", "f16", 128), ("bf16", "bf16", 64),
+                                      ("fp4", "bf16", 64), ("fp4", "f16", 64)])
 def test_activation_dtypes_and_head_dims(kv, act, d, ps):
     """fp16 activations with the quantized pools (their fp16 MFMA variants), head_dim 64
-    with FP8 and 16-bit pools, two kv heads: pools bit-exact, outputs within tolerance."""
+    with FP8, FP4 and 16-bit pools, two kv heads: pools bit-exact, outputs within
+    tolerance."""
     from paged_quantized_kv_reshape_amd.harness import DeviceRun
     base = "c5" if kv == "fp4" else "c4"
     w = config(base, num_seqs=3, lens=[300, 77, 16], num_q_heads=8, num_kv_heads=2,
@@ -294,12 +285,22 @@ def test_activation_dtypes_and_head_dims(kv, act, d, ps):
 
 @pytest.mark.parametrize("cfg", ["c2", "c3", "c4", "c5"])
 def test_full_size_sampled(cfg):
+    """Each full-size workload, sampled. Pool 0 gets the setup and step writes, then the
+    separate decode (pa_decode + pa_merge). Where the bench runs the step as one
+    pa_append_decode launch (one new token per sequence at its last position: c2, c4, c5),
+    that launch is checked too, in the bench's own configuration (the workload's partition
+    size, the library's wave count, then pa_merge): on pool 1, which holds the setup writes
+    only, so the launch itself writes (and for FP4 calibrates) the step's rows; and again
+    on pool 0, whose rows are already written, as every timed bench step after the first
+    finds them."""
     from paged_quantized_kv_reshape_amd.harness import DeviceRun
     w = config(cfg)
     _say(f"[full] {cfg}: S={w.num_seqs} tokens={w.tokens} blocks={w.num_blocks} ps={w.partition_size}")
-    run = DeviceRun(w)
-    run.prepare()
-    run.decode()
+    run = DeviceRun(w, pool_copies=2)
+    fused = run.can_append
+    run.setup_writes(run.pools[0])
+    run.step_write(run.pools[0])
+    run.decode(run.pools[0])
     torch.cuda.synchronize()
     assert run.device_error() == 0
     out = run.out.cpu().numpy()
@@ -311,18 +312,70 @@ def test_full_size_sampled(cfg):
     if ks is not None:
         assert np.array_equal(run.k_scale.cpu().numpy().view(np.uint32), ks.view(np.uint32))
         assert np.array_equal(run.v_scale.cpu().numpy().view(np.uint32), vs.view(np.uint32))
-    assert_pool_equal(run.pool.numpy(), pool, blocks=blocks, near=near)
+    assert_pool_equal(run.pools[0].numpy(), pool, blocks=blocks, near=near)
     ref = oracle_decode(w, pool, ks, vs, seqs)
     for s in seqs:
         assert_close(out[s], ref[s][0], f"{cfg} seq {s}")
     if w.kv == "fp4":
         # every full 16-token block calibrated by a prefill chunk flags exactly the
         # planted x20 channel (known a priori from the generator)
-        rec = run.pool.fp4_records("k").cpu().numpy()
+        rec = run.pools[0].fp4_records("k").cpu().numpy()
         s = seqs[0]
         full = w.block_tables[s, :(int(w.context_lens[s]) - 1) // 16]
         pk = int(w.planted_k[0]) % w.head_dim
         assert np.all(rec[full, 0, 0] == 1) and np.all(rec[full, 0, 1] == pk)
+    if not fused:
+        return
+    for label, pool_i, setup in (("fresh rows", 1, True), ("rows already written", 0, False)):
+        if setup:
+            run.setup_writes(run.pools[pool_i])
+        run.out.fill_(float("nan"))
+        run.append_decode(run.pools[pool_i])  # + pa_merge when split, as the bench step
+        torch.cuda.synchronize()
+        _say(f"[full fused] {cfg}: {label}")
+        assert run.device_error() == 0
+        got = run.out.cpu().numpy()
+        assert_pool_equal(run.pools[pool_i].numpy(), pool, blocks=blocks, near=near)
+        for s in seqs:
+            assert_close(got[s], ref[s][0], f"{cfg} fused ({label}) seq {s}")
+        # the fused launch reads what the separate write stored, with the same arithmetic
+        assert np.array_equal(got.view(np.uint32), out.view(np.uint32)), label
+
+
+def test_all_blocks_bad_gives_zero_output_and_a_flag():
+    """Sequences whose every block id is out of range, at 8 waves and ps > 0 (a merge
+    follows) and at ps = 0: flagged, and the output of those sequences is zero (every wave
+    of their workgroups has nothing to fold in), not NaN; the other sequences are unharmed.
+    The same for a context length past the block table in split mode."""
+    from paged_quantized_kv_reshape_amd.harness import DeviceRun
+    w = config("c4", num_seqs=4, lens=[16, 300, 1000, 77])
+    for ps in (0, 64):
+        run = DeviceRun(w, partition_size=ps, waves=8)
+        run.prepare()
+        run.decode()
+        torch.cuda.synchronize()
+        good = run.out.cpu().numpy().copy()
+        run.block_tables[0, 0] = w.num_blocks + 7       # one-block sequence, its only block
+        run.block_tables[1, :] = -5                      # every block of sequence 1
+        run.dev_err.zero_()
+        run.decode()
+        torch.cuda.synchronize()
+        assert run.device_error() & 1
+        got = run.out.cpu().numpy()
+        assert np.isfinite(got).all(), f"ps={ps}"
+        assert np.all(got[:2] == 0.0), f"ps={ps}"
+        assert np.array_equal(got[2:], good[2:]), f"ps={ps}"
+        if ps:
+            lse = run.lse.cpu().numpy()
+            assert np.all(np.isneginf(lse[:2])) and np.isfinite(lse[2:]).all()
+            # a context past the table (split): flagged, zero output, lse -inf
+            run.context_lens[3] = w.max_blocks_per_seq * 16 + 1
+            run.dev_err.zero_()
+            run.decode()
+            torch.cuda.synchronize()
+            assert run.device_error() & 4
+            assert np.all(run.out[3].cpu().numpy() == 0.0)
+            assert np.isneginf(run.lse[3].cpu().numpy()).all()
 
 
 # Scales of the FP8 sweep: reciprocals that are exact and inexact, a negative scale, a zero

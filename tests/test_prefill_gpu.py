@@ -101,7 +101,8 @@ def test_prefill_group_sizes(kv, hq):
 
 
 @pytest.mark.parametrize("kv,act,d", [("fp8", "f16", 128), ("fp4", "f16", 128),
-                                      ("fp8", "bf16", 64), ("f16", "f16", 64)])
+                                      ("fp8", "bf16", 64), ("f16", "f16", 64),
+                                      ("fp4", "bf16", 64), ("fp4", "f16", 64)])
 def test_prefill_dtypes_and_head_dims(kv, act, d):
     from paged_quantized_kv_reshape_amd.harness import DeviceRun
     base = "c5" if kv == "fp4" else "c4"
