@@ -62,10 +62,10 @@ constexpr int kIdsLds = 64;
 // wrote itself in this launch (fresh) is read with a vector load: scalar loads assume
 // memory that is constant for the whole dispatch, and a fence does not order them.
 __device__ __forceinline__ uint2 record_words12(const uint8_t* rec, bool fresh) {
-  if (fresh) {
-    const uint2 r = *reinterpret_cast<const uint2*>(rec + 4);
-    return make_uint2((uint32_t)__builtin_amdgcn_readfirstlane((int)r.x),
-                      (uint32_t)__builtin_amdgcn_readfirstlane((int)r.y));
+  if (fresh) {  // the record is 16-byte aligned
+    const uint4 r = *reinterpret_cast<const uint4*>(rec);
+    return make_uint2((uint32_t)__builtin_amdgcn_readfirstlane((int)r.y),
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)r.z));
   }
   const uint4 r = load_uniform16(rec);
   return make_uint2(r.y, r.z);
