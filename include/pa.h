@@ -426,17 +426,17 @@ int pa_prefill_ex(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_
                   const pa_launch_options* opts, void* stream);
 
 /*
- * Gather-only ceiling of the decode's access pattern, for measurement: the launch
- * pa_decode_ex would make for these arguments (same grid, waves and partitions), reading
- * through the block tables every byte of every attended (block, kv head) run of K and V
- * that the decode's tile loads touch (the whole run: codes, and for FP4 and per-token FP8
- * pools the side data stored in it; not the FP4 outlier slots past the first, which only
- * blocks with two or more outliers have), with the decode's 16-byte streaming loads and no
- * arithmetic beyond an XOR that keeps the loads alive. Its time is what the decode's
- * memory traffic alone costs on this GPU (the pages put the decode's limit on memory
- * bandwidth: xonoai.com report on vLLM v0.7.2, "Deconstructing the v0.7.2 Architecture").
- *   num_q_heads     no query is read; the group num_q_heads / num_kv_heads is checked as
- *                   in pa_decode
+ * Gather-only ceiling of the decode's access pattern, for measurement: the decode kernel
+ * pa_decode_ex would launch for these arguments (same grid, waves, partitions, block
+ * order) with its arithmetic compiled out. Every load the decode makes is kept - the
+ * block-table entries, each attended (block, kv head) tile of K and V with the same
+ * instructions and cache hints, the per-token scales, the 4-bit records and first outlier
+ * slots, but not the queries - and the loaded words are XORed together so the loads stay. Its time is what the
+ * decode's memory traffic alone costs on this GPU, the floor the decode's math must hide
+ * under (the pages put the decode's limit on memory bandwidth: xonoai.com report on vLLM
+ * v0.7.2, "Deconstructing the v0.7.2 Architecture").
+ *   num_q_heads     the query group num_q_heads / num_kv_heads is checked as in pa_decode;
+ *                   no query is read (0.1% of the decode's bytes at head_dim 128)
  *   sink            [1024] uint32, device memory: XORs of the loaded words (contents
  *                   meaningless; need not be zeroed)
  * Invalid block ids are skipped and flagged as in pa_decode. Asynchronous on `stream`.

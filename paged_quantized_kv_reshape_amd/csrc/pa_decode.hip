@@ -154,7 +154,10 @@ __device__ __forceinline__ void append_row_fp4(const DecodeArgs& a, int s, int k
 // (the next tile is loaded after the current one is consumed; the other waves of the
 // compute unit cover the latency), true double-buffers (the next tile's loads are issued
 // before the current tile's math, so each wave keeps a tile in flight while it computes).
-template <int KV, int D, bool QBF, int GP, bool DB, bool APPEND = false>
+// PROBE keeps every load of the decode (block ids, tiles, scales, records) and drops the
+// arithmetic: each tile's words are XORed into one word per wave, stored to a.sink; the
+// time of that launch is what the decode's memory traffic alone costs.
+template <int KV, int D, bool QBF, int GP, bool DB, bool APPEND = false, bool PROBE = false>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   using G_ = Geo<KV, D>;
   constexpr int KS = G_::KS, NT = G_::NT, DL = G_::DL;
@@ -186,6 +189,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   const bool split = a.partition_size > 0;
   if (L < 1 || L > cap_tokens) {
     if (threadIdx.x == 0 && p == 0 && kvh == 0 && a.err) atomicOr(a.err, PA_DEVERR_BAD_CONTEXT);
+    if (PROBE) return;  // the probe has no outputs
     if (!split && p == 0) {
       for (int i = threadIdx.x; i < G * D; i += blockDim.x)
         a.out[((int64_t)s * Hq + kvh * G) * D + i] = 0.0f;
@@ -236,7 +240,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 
   // ---- query fragments (B operand of S^T = K Q^T), zero for padded heads ----
   uint4 qf[KS];
-  {
+  if constexpr (PROBE) {  // no query is passed to the probe
+#pragma unroll
+    for (int t = 0; t < KS; ++t) qf[t] = make_uint4(0, 0, 0, 0);
+  } else {
     const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
                           (((int64_t)s * Hq + kvh * G + c) * D + DL * kg) * 2;
 #pragma unroll
@@ -369,11 +376,26 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   bool started = false;  // wave-uniform: a block has been folded into (m, l, acc)
 
+  uint32_t probe_x = 0u;  // PROBE: XOR of every loaded word
+
   // One block. kFull (a compile-time tag) says the block is in range and all 16 of its
   // tokens are inside the partition, which holds for every block but the last one of a
   // partition; that version carries no per-token masks.
   auto compute = [&](Tile<KV, D>& T, auto kFull) {
     constexpr bool FULL = decltype(kFull)::value;
+    if constexpr (PROBE) {
+#pragma unroll
+      for (int i = 0; i < G_::KW; ++i) probe_x ^= T.k[i];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int i = 0; i < G_::VW; ++i) probe_x ^= T.v[r][i];
+      if constexpr (tok_scaled(KV))
+        probe_x ^= __float_as_uint(T.sk.x + T.sk.y + T.sk.z + T.sk.w + T.sv.x + T.sv.y +
+                                   T.sv.z + T.sv.w);
+      if constexpr (KV == KV_FP4) probe_x ^= T.r0 ^ T.k_o0.x ^ T.k_o0.y ^ T.v_o0.x ^ T.v_o0.y;
+      return;
+    }
     const int tok0 = T.jb * kBlock + 4 * kg;
     bool valid[4];
 #pragma unroll
@@ -552,6 +574,14 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 
   // ---- epilogue ----
   if (err_bits != 0 && lane == 0 && a.err) atomicOr(a.err, err_bits);
+  if constexpr (PROBE) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) probe_x ^= (uint32_t)__shfl_xor((int)probe_x, o);
+    if (lane == 0 && probe_x != 0u)
+      atomicXor(a.sink + ((blockIdx.y * gridDim.x + blockIdx.x) * 8u + (unsigned)wave) % 1024u,
+                probe_x);
+    return;
+  }
   const float lt = group4_sum(l);
   const float vscale = head_scaled(KV) ? a.v_scale[kvh] : 1.0f;
   const int h = kvh * G + c;
@@ -625,18 +655,18 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 
 // 16-bit and FP8 pools: one tile in flight per wave, occupancy left to the register count
 // (5 waves per SIMD for FP8 at head_dim 128).
-template <int KV, int D, bool QBF, int GP, bool APPEND = false>
+template <int KV, int D, bool QBF, int GP, bool APPEND = false, bool PROBE = false>
 __global__ __launch_bounds__(512) void k_decode(DecodeArgs a) {
-  decode_body<KV, D, QBF, GP, false, APPEND>(a);
+  decode_body<KV, D, QBF, GP, false, APPEND, PROBE>(a);
 }
 
 // FP4 pools: a tile is half the bytes of an FP8 one, so one tile per wave leaves too little
 // in flight; the double-buffered loop, held to at least 4 waves per SIMD (128 registers),
 // keeps about twice as much.
-template <int D, bool QBF, int GP, bool APPEND = false>
+template <int D, bool QBF, int GP, bool APPEND = false, bool PROBE = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_fp4(
     DecodeArgs a) {
-  decode_body<KV_FP4, D, QBF, GP, true, APPEND>(a);
+  decode_body<KV_FP4, D, QBF, GP, true, APPEND, PROBE>(a);
 }
 
 template <int KV, int D, int GP>
@@ -651,7 +681,7 @@ static size_t decode_lds_bytes(int waves) {
 }
 
 template <int KV, int D, bool QBF, int GP = 16>
-static int launch_one(const DecodeArgs& a, int waves, hipStream_t st) {
+static int launch_one(const DecodeArgs& a, int waves, hipStream_t st, bool probe = false) {
   const int P = a.partition_size > 0 ? a.max_partitions : 1;
   // fewer waves per workgroup if their LDS would not fit the device's limit
   int dev = 0, max_lds = 65536;
@@ -662,6 +692,15 @@ static int launch_one(const DecodeArgs& a, int waves, hipStream_t st) {
   while (waves > 1 && decode_lds_bytes<KV, D, GP>(waves) > (size_t)max_lds) waves /= 2;
   const size_t lds = decode_lds_bytes<KV, D, GP>(waves);
   const dim3 grid((unsigned)((int64_t)P * a.num_kv_heads), (unsigned)a.num_seqs, 1);
+  if (probe) {
+    if constexpr (KV == KV_FP4)
+      hipLaunchKernelGGL((k_decode_fp4<D, QBF, GP, false, true>), grid, dim3(64 * waves), lds,
+                         st, a);
+    else
+      hipLaunchKernelGGL((k_decode<KV, D, QBF, GP, false, true>), grid, dim3(64 * waves), lds,
+                         st, a);
+    return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+  }
   if constexpr (KV == KV_FP4) {
     if (a.k_new)
       hipLaunchKernelGGL((k_decode_fp4<D, QBF, GP, true>), grid, dim3(64 * waves), lds, st, a);
@@ -721,6 +760,37 @@ int launch_decode(const DecodeArgs& a, int kv, bool qbf, int D, int waves, hipSt
                      : launch_one<KV_FP4, 64, false, 8>(a, waves, st);
         return qbf ? launch_one<KV_FP4, 64, true, 16>(a, waves, st)
                    : launch_one<KV_FP4, 64, false, 16>(a, waves, st);
+    }
+  }
+  return PA_ERR_DTYPE;
+}
+
+// The decode's launch with the arithmetic compiled out (decode_body's PROBE): same grid,
+// waves, partitions, block order and loads. The query dtype does not matter there.
+int launch_gather_probe(const DecodeArgs& a, int kv, int D, int waves, uint32_t* sink,
+                        hipStream_t st) {
+  DecodeArgs b = a;
+  b.sink = sink;
+  b.k_new = b.v_new = nullptr;
+  if (D == 128) {
+    switch (kv) {
+      case KV_F16: return launch_one<KV_F16, 128, false>(b, waves, st, true);
+      case KV_BF16: return launch_one<KV_BF16, 128, true>(b, waves, st, true);
+      case KV_FP8: return launch_one<KV_FP8, 128, true>(b, waves, st, true);
+      case KV_BF8: return launch_one<KV_BF8, 128, true>(b, waves, st, true);
+      case KV_FP8T: return launch_one<KV_FP8T, 128, true>(b, waves, st, true);
+      case KV_BF8T: return launch_one<KV_BF8T, 128, true>(b, waves, st, true);
+      case KV_FP4: return launch_one<KV_FP4, 128, true, 8>(b, waves, st, true);
+    }
+  } else {
+    switch (kv) {
+      case KV_F16: return launch_one<KV_F16, 64, false>(b, waves, st, true);
+      case KV_BF16: return launch_one<KV_BF16, 64, true>(b, waves, st, true);
+      case KV_FP8: return launch_one<KV_FP8, 64, true>(b, waves, st, true);
+      case KV_BF8: return launch_one<KV_BF8, 64, true>(b, waves, st, true);
+      case KV_FP8T: return launch_one<KV_FP8T, 64, true>(b, waves, st, true);
+      case KV_BF8T: return launch_one<KV_BF8T, 64, true>(b, waves, st, true);
+      case KV_FP4: return launch_one<KV_FP4, 64, true, 8>(b, waves, st, true);
     }
   }
   return PA_ERR_DTYPE;

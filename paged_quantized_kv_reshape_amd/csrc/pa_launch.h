@@ -45,6 +45,7 @@ struct DecodeArgs {
   // v_new + s * Hkv * D (activation dtype of q), written at position L_s - 1 first
   const void* k_new;
   const void* v_new;
+  uint32_t* sink;              // gather probe: [1024] XOR words
   const int32_t* query_start;  // multi-token queries: [S + 1] row offsets of q and out
   int32_t max_query_len, num_queries;
   int32_t num_seqs, num_q_heads, num_kv_heads, group, num_blocks, max_blocks, partition_size,
@@ -54,7 +55,7 @@ struct DecodeArgs {
 
 int launch_decode(const DecodeArgs& a, int kv_dtype, bool q_bf16, int head_dim, int waves,
                   hipStream_t st);
-// gather-only ceiling (pa_gather_probe): the decode's launch and tile reads, no math
+// gather-only ceiling (pa_gather_probe): the decode's launch and loads, no arithmetic
 int launch_gather_probe(const DecodeArgs& a, int kv_dtype, int head_dim, int waves,
                         uint32_t* sink, hipStream_t st);
 // multi-token queries (pa_prefill): the paired-block kernel, every pool format;
