@@ -462,6 +462,32 @@ int pa_merge(const float* part_out, const float* part_lse, const int32_t* contex
              int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_partitions,
              int32_t partition_size, float* out, float* lse_out, void* stream);
 
+/*
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. pa_decode with partition_size > 0
+ * followed by pa_merge, with the partials (part_out, part_lse) in a library-owned static
+ * device array of PA_STATIC_SCRATCH_BYTES instead of caller memory; the caller passes only
+ * inputs and outputs (out [num_seqs, num_q_heads, head_dim] fp32, lse_out [num_seqs,
+ * num_q_heads] fp32 or NULL, as pa_merge writes them). The call needs
+ * num_seqs * num_q_heads * P * (head_dim + 1) * 4 bytes of it, P = ceil(max_blocks_per_seq
+ * * 16 / partition_size); more gives PA_ERR_SCRATCH before anything is queued (32 MiB holds
+ * 32 sequences of up to 122,880 tokens with 8 query heads at head_dim 128 and 512-token
+ * partitions). It allocates nothing: each GPU holds its own copy of the array from the
+ * library's first call on that device until the process ends, and the call looks up its
+ * address on the current device. All calls on one GPU share that array, so calls that
+ * overlap in time on one GPU (other streams, other host threads) race and must be
+ * serialized by the caller; one call leaves its partials there until the next overwrites
+ * them, and every row a call's merge reads is written by its decode first. Same
+ * arguments, rules and results as pa_decode_ex (default launch) + pa_merge otherwise.
+ * Asynchronous on `stream`.
+ */
+#define PA_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+int pa_decode_split_static(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                           const pa_kv_pool* pool, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           float sm_scale, int32_t partition_size, float* out, float* lse_out,
+                           int32_t* dev_err, void* stream);
+
 /* Host-only: a static, human-readable name for a pa_status value. */
 const char* pa_status_string(int status);
 

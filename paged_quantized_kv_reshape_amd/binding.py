@@ -114,6 +114,8 @@ def lib():
                                              vp, f32, vp, vp, vp, vp]),
             "pa_gather_probe": (ctypes.c_int, [i32, i32, pool_p, vp, i32, vp, i32, vp, vp, vp,
                                                vp]),
+            "pa_decode_split_static": (ctypes.c_int, [vp, i32, i32, i32, pool_p, vp, i32, vp,
+                                                      f32, i32, vp, vp, vp, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -403,6 +405,20 @@ def pa_gather_probe(pool: KVPool, num_q_heads, block_tables, context_lens, parti
         context_lens.shape[0], num_q_heads, ctypes.byref(s), _ptr(block_tables),
         block_tables.shape[1], _ptr(context_lens), partition_size, _ptr(sink), _ptr(dev_err),
         _opts(waves), _stream()))
+
+
+def pa_decode_split_static(q, pool: KVPool, block_tables, context_lens, sm_scale,
+                           partition_size, out, lse_out=None, dev_err=None):
+    """Split decode + merge into out [S, Hq, D] (lse_out [S, Hq] optional), the partials
+    in the library's static device scratch: no allocation of any kind."""
+    assert q.dtype in ACT_DTYPES and block_tables.dtype == torch.int32
+    assert context_lens.dtype == torch.int32
+    S, Hq, _ = q.shape
+    s = pool.struct()
+    _check("pa_decode_split_static", lib().pa_decode_split_static(
+        _ptr(q), ACT_DTYPES[q.dtype], S, Hq, ctypes.byref(s), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), float(sm_scale), partition_size, _ptr(out),
+        _ptr(lse_out), _ptr(dev_err), _stream()))
 
 
 def pa_merge(part_out, part_lse, context_lens, partition_size, out, lse_out=None):

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpa.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["pa_api.cpp", "pa_alloc.cpp", "pa_write.hip", "pa_decode.hip", "pa_merge.hip",
-           "pa_blocks.hip", "pa_prefill.hip"]
+           "pa_blocks.hip", "pa_prefill.hip", "pa_static.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

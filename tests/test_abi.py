@@ -291,6 +291,25 @@ def test_gather_probe_rejects():
     assert f(S=0) == PA_OK
 
 
+def test_static_scratch_decode_rejects():
+    """pa_decode_split_static checks its sizes against the static scratch, and the merge's
+    output, before anything is queued."""
+    lib = B.lib()
+    f = lambda pool=None, **k: lib.pa_decode_split_static(
+        FAKE, 1, k.get("S", 2), k.get("Hq", 8),
+        None if pool == "null" else ctypes.byref(pool if pool is not None else _pool()),
+        FAKE, k.get("MB", 4), FAKE, 0.1, k.get("ps", 512), k.get("out", FAKE), k.get("lse"),
+        None, None)
+    assert f(pool="null") == NULL
+    assert f(ps=0) == PART and f(ps=24) == PART
+    assert f(MB=0) == CONTEXT and f(S=-1) == SHAPE and f(Hq=0) == SHAPE
+    assert f(pool=_pool(d=96)) == SHAPE
+    # 64 x 8 x 4096 partitions x 129 floats is about 1 GB, past the 32 MiB scratch
+    assert f(S=64, MB=4096, ps=16) == SCRATCH
+    assert f(S=0) == PA_OK
+    assert f(out=None) == NULL and f(out=FAKE + 4) == ALIGN and f(lse=FAKE + 2) == ALIGN
+
+
 def test_library_reads_no_environment_knob():
     """Launch geometry comes only from arguments: the library's text names no environment
     variable it would read."""
