@@ -43,6 +43,12 @@ KERNEL_SOURCES = ["paged_quantized_kv_reshape_amd/csrc/pa_decode.hip",
                   "paged_quantized_kv_reshape_amd/csrc/pa_device.h",
                   "paged_quantized_kv_reshape_amd/csrc/pa_api.cpp",
                   "paged_quantized_kv_reshape_amd/csrc/pa_launch.h"]
+# the sources that decide the multi-token kernel's code and launch
+PREFILL_SOURCES = ["paged_quantized_kv_reshape_amd/csrc/pa_prefill.hip",
+                   "paged_quantized_kv_reshape_amd/csrc/pa_tile.h",
+                   "paged_quantized_kv_reshape_amd/csrc/pa_device.h",
+                   "paged_quantized_kv_reshape_amd/csrc/pa_launch.h",
+                   "paged_quantized_kv_reshape_amd/csrc/pa_api.cpp"]
 # decode output tolerance against the oracle: max |gpu - oracle| and relative L2 error
 ATOL, RTOL_L2 = 2e-3, 1e-2
 
@@ -98,9 +104,10 @@ class HipTimer:
         self.events = []
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
+    """First 16 hex digits of the sha256 over the given sources (default: the decode's)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -459,6 +466,7 @@ def prefill_main(args, config, DESCRIPTIONS):
                      "achieved": round(tflops, 2),
                      "peak": 2500.0, "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4),
                      "traffic": None},
+        "kernel_source_sha256": kernel_source_hash(PREFILL_SOURCES),
     }
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_limits
@@ -708,13 +716,15 @@ def main():
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes": kernel_bytes,
                      "traffic": traffic},
-        "ceiling": {"kernel": "k_gather_probe", "ms": round(t_probe * 1e3, 4),
+        "ceiling": {"kernel": f"pa_gather_probe ({decode_kernel_name(w.kv)} with its "
+                              "arithmetic compiled out)", "ms": round(t_probe * 1e3, 4),
                     "gbs": round(kernel_bytes / t_probe / 1e9, 2),
                     "pct_hbm_peak": round(100.0 * kernel_bytes / t_probe / 1e9 / HBM_PEAK_GBS, 2),
                     "decode_frac_of_ceiling": round(t_probe / t_dec, 4),
                     "what": "the decode's launch reading every attended K/V run through the "
                             "block tables with its streaming 16-byte loads, no arithmetic; "
                             "gbs counts the decode's algorithmic bytes"},
+        "kernel_source_sha256": kernel_source_hash(),
     }
     print("[bench] checking the timed output against the oracle", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
