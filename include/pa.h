@@ -92,10 +92,13 @@ typedef enum {
  *                            ("FP8 (E4M3 and E5M2)", xonoai.com field report,
  *                            "Deconstructing the v0.7.2 Architecture").
  *   PA_KV_FP8_E4M3_TOKEN / _E5M2_TOKEN :
- *                            k, v   [num_blocks, num_kv_heads, PA_FP8T_TILE_BYTES(head_dim)]
- *                                   bytes, one run per (block, kv head): codes
- *                                   [16 tokens][head_dim], then at PA_FP8T_SCALE_OFF the 16
- *                                   per-token fp32 scales, padding to a multiple of 128.
+ *                            k  [num_blocks, num_kv_heads, PA_FP8T_TILE_BYTES(head_dim)]
+ *                               bytes, one run per (block, kv head): codes
+ *                               [16 tokens][head_dim], then at PA_FP8T_SCALE_OFF the 16
+ *                               per-token fp32 scales of K and at PA_FP8T_VSCALE_OFF the
+ *                               16 of V (together one whole 128-byte line);
+ *                            v  [num_blocks, num_kv_heads, PA_FP8T_VTILE_BYTES(head_dim)]
+ *                               bytes: the V codes [16 tokens][head_dim] only.
  *                            The scale of a token row is fp32(max |x| / 448) (E4M3) or
  *                            fp32(max |x| / 57344) (E5M2), set when the row is written:
  *                            quantization on the fly (dailyaiworld.com, "vLLM 0.7 Ships
@@ -137,9 +140,12 @@ typedef enum {
 #define PA_FP4_RECORD_OFF(head_dim) (8 * (head_dim) + 64)
 #define PA_FP4_SLOT0_OFF(head_dim) (8 * (head_dim) + 80)
 #define PA_FP4_TILE_BYTES(head_dim) ((8 * (head_dim) + 112 + 127) / 128 * 128)
-/* per-token-scaled FP8 run: token scales after the 16 x head_dim code bytes */
+/* per-token-scaled FP8 runs: K codes, K token scales, V token scales (k array); V codes
+ * (v array). Every run is a whole number of 128-byte lines with no padding. */
 #define PA_FP8T_SCALE_OFF(head_dim) (16 * (head_dim))
-#define PA_FP8T_TILE_BYTES(head_dim) ((16 * (head_dim) + 64 + 127) / 128 * 128)
+#define PA_FP8T_VSCALE_OFF(head_dim) (16 * (head_dim) + 64)
+#define PA_FP8T_TILE_BYTES(head_dim) (16 * (head_dim) + 128)
+#define PA_FP8T_VTILE_BYTES(head_dim) (16 * (head_dim))
 
 typedef struct pa_kv_pool {
   int32_t dtype;          /* pa_kv_dtype */

@@ -36,6 +36,11 @@ Readings where the pages are silent (each listed in the design notes):
 Pool layout (the boundary's layout, row-major, one array per field):
   f16 / bf16 : k, v          uint16 [NB, Hkv, 16, D]
   fp8        : k, v          uint8  [NB, Hkv, 16, D]        (+ per-head fp32 scales)
+  fp8t, bf8t : k             uint8  [NB, Hkv, 16 D + 128] one run per (block, head):
+                 [0, 16 D)         K codes [16 tokens][D]
+                 [16 D, 16 D + 64)  K per-token scales, fp32 [16]
+                 [16 D + 64, 16 D + 128)  V per-token scales, fp32 [16]
+               v             uint8  [NB, Hkv, 16 D]       V codes [16 tokens][D]
   fp4        : k, v          uint8  [NB, Hkv, TILE] one run of bytes per (block, head):
                  [0, 8 D)          codes [16 tokens][D/2], two per byte
                  [8 D, 8 D + 64)   per-token scales, fp32 [16]
@@ -105,8 +110,8 @@ class Pool:
         if kind in ("fp8", "bf8"):
             return {"k": ((nb, hkv, 16, d), np.uint8), "v": ((nb, hkv, 16, d), np.uint8)}
         if kind in ("fp8t", "bf8t"):
-            return {"k": ((nb, hkv, fp8t_run_bytes(d)), np.uint8),
-                    "v": ((nb, hkv, fp8t_run_bytes(d)), np.uint8)}
+            return {"k": ((nb, hkv, fp8t_run_bytes(d, "k")), np.uint8),
+                    "v": ((nb, hkv, fp8t_run_bytes(d, "v")), np.uint8)}
         if kind == "fp4":
             cap = outlier_capacity(d)
             out = {}
@@ -135,10 +140,11 @@ class Pool:
 # ----------------------------------------------------------------------------------
 
 
-def fp8t_run_bytes(head_dim: int) -> int:
+def fp8t_run_bytes(head_dim: int, kv: str = "k") -> int:
     """Bytes of one per-token-scaled FP8 (block, head) run: the 16 x D code bytes (token
-    rows), then the 16 fp32 token scales, rounded up to a multiple of 128 bytes."""
-    return -(-(16 * head_dim + 64) // 128) * 128
+    rows); the K run then holds the 16 fp32 token scales of K and the 16 of V (so every
+    run is a whole number of 128-byte lines)."""
+    return 16 * head_dim + (128 if kv == "k" else 0)
 
 
 def fp8t_codes(pool: Pool, kv: str) -> np.ndarray:
@@ -149,9 +155,11 @@ def fp8t_codes(pool: Pool, kv: str) -> np.ndarray:
 
 
 def fp8t_scales(pool: Pool, kv: str) -> np.ndarray:
-    """Per-token scales of a per-token-scaled FP8 pool, a view [NB, Hkv, 16] fp32."""
+    """Per-token scales of K or V in a per-token-scaled FP8 pool, a view [NB, Hkv, 16]
+    fp32 (both live in the K array's runs, K's first)."""
     d = pool.head_dim
-    return pool.arrays[kv][..., 16 * d:16 * d + 64].view(np.float32)
+    at = 16 * d + (0 if kv == "k" else 64)
+    return pool.arrays["k"][..., at:at + 64].view(np.float32)
 
 
 def fp4_tile_bytes(head_dim: int) -> int:

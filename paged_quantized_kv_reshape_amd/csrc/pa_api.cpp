@@ -137,7 +137,8 @@ int pa_pool_layout(int32_t dtype, int32_t num_blocks, int32_t num_kv_heads, int3
     case PA_KV_FP8_E5M2: bytes_out[0] = bytes_out[1] = rows * head_dim; break;
     case PA_KV_FP8_E4M3_TOKEN:
     case PA_KV_FP8_E5M2_TOKEN:
-      bytes_out[0] = bytes_out[1] = bh * (size_t)PA_FP8T_TILE_BYTES(head_dim);
+      bytes_out[0] = bh * (size_t)PA_FP8T_TILE_BYTES(head_dim);
+      bytes_out[1] = bh * (size_t)PA_FP8T_VTILE_BYTES(head_dim);
       break;
     default:
       bytes_out[0] = bytes_out[1] = bh * (size_t)PA_FP4_TILE_BYTES(head_dim);

@@ -86,8 +86,9 @@ __device__ __forceinline__ void append_row(const DecodeArgs& a, int s, int kvh, 
   const int c = t - (vside ? R : 0);
   const uint4* src = reinterpret_cast<const uint4*>(vside ? a.v_new : a.k_new) +
                      ((int64_t)s * a.num_kv_heads + kvh) * (D * 2 / 16);
+  const int64_t bh = (int64_t)b * a.num_kv_heads + kvh;
   uint8_t* tile = reinterpret_cast<uint8_t*>(const_cast<void*>(vside ? a.v : a.k)) +
-                  ((int64_t)b * a.num_kv_heads + kvh) * G_::TILEB;
+                  bh * (vside ? G_::VTILEB : G_::TILEB);
   if constexpr (KV == KV_F16 || KV == KV_BF16) {
     reinterpret_cast<uint4*>(tile + off * G_::ROWB)[c] = src[c];
   } else {
@@ -104,7 +105,11 @@ __device__ __forceinline__ void append_row(const DecodeArgs& a, int s, int kvh, 
 #pragma unroll
       for (int o = R / 2; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
       sc = mx / (E5 ? 57344.0f : 448.0f);
-      if (c == 0) reinterpret_cast<float*>(tile + PA_FP8T_SCALE_OFF(D))[off] = sc;
+      // both token scales live in the K run (K's, then V's)
+      if (c == 0)
+        reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(const_cast<void*>(a.k)) +
+                                 bh * G_::TILEB +
+                                 (vside ? PA_FP8T_VSCALE_OFF(D) : PA_FP8T_SCALE_OFF(D)))[off] = sc;
     } else {
       sc = vside ? a.v_scale[kvh] : a.k_scale[kvh];
     }
@@ -346,11 +351,11 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        load_words<G_::VW, true>(T.v[r], vpool + T.tile * G_::TILEB + v_lane_off + r * G_::ROWB);
+        load_words<G_::VW, true>(T.v[r], vpool + T.tile * G_::VTILEB + v_lane_off + r * G_::ROWB);
     }
     if constexpr (f8_tok(KV)) {  // per-token scales of tokens 4 kg .. 4 kg + 3
       T.sk = reinterpret_cast<const float4*>(kpool + T.tile * G_::TILEB + PA_FP8T_SCALE_OFF(D))[kg];
-      T.sv = reinterpret_cast<const float4*>(vpool + T.tile * G_::TILEB + PA_FP8T_SCALE_OFF(D))[kg];
+      T.sv = reinterpret_cast<const float4*>(kpool + T.tile * G_::TILEB + PA_FP8T_VSCALE_OFF(D))[kg];
     }
     if constexpr (KV == KV_FP4) {
       const uint8_t* kt = kpool + T.tile * G_::TILEB;

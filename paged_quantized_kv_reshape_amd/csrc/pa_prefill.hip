@@ -172,11 +172,11 @@ void k_prefill_mt(DecodeArgs a) {
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        load_words(T.v[r], vpool + T.tile * G_::TILEB + v_lane_off + r * G_::ROWB);
+        load_words(T.v[r], vpool + T.tile * G_::VTILEB + v_lane_off + r * G_::ROWB);
     }
     if constexpr (f8_tok(KV)) {
       T.sk = reinterpret_cast<const float4*>(kpool + T.tile * G_::TILEB + PA_FP8T_SCALE_OFF(D))[kg];
-      T.sv = reinterpret_cast<const float4*>(vpool + T.tile * G_::TILEB + PA_FP8T_SCALE_OFF(D))[kg];
+      T.sv = reinterpret_cast<const float4*>(kpool + T.tile * G_::TILEB + PA_FP8T_VSCALE_OFF(D))[kg];
     }
   };
   // the second block of a last, odd pair: no bytes, every token invalid

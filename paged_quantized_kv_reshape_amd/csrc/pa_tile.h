@@ -29,11 +29,14 @@ struct Geo {
   static constexpr int DL = D / 4;   // channels per lane in K fragments and outputs
   static constexpr int EBITS = is_f8(KV) ? 8 : KV == KV_FP4 ? 4 : 16;
   static constexpr int ROWB = D * EBITS / 8;       // bytes of one token row
-  // bytes between consecutive (block, head) tiles; an FP4 tile also holds its per-token
-  // scales, its outlier record and its first outlier slot after the codes
+  // bytes between consecutive (block, head) tiles of the k array (TILEB) and of the v
+  // array (VTILEB); an FP4 tile also holds its per-token scales, its outlier record and its
+  // first outlier slot after the codes; a per-token FP8 K tile holds the token scales of
+  // both K and V after its codes, and its V tile only codes
   static constexpr int TILEB = KV == KV_FP4   ? PA_FP4_TILE_BYTES(D)
                                : f8_tok(KV) ? PA_FP8T_TILE_BYTES(D)
                                             : kBlock * ROWB;
+  static constexpr int VTILEB = f8_tok(KV) ? PA_FP8T_VTILE_BYTES(D) : TILEB;
   static constexpr int KW = DL * EBITS / 32;       // K words per lane
   // V words per lane per token; FP4 V is read by channel instead (fp4_v_chunk): T.v[w][0]
   // holds word w of the lane's chunk

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void k_write_fp8_tok(const uint4* __restrict__
                                                        int32_t T, int32_t hkv, int64_t nslots,
                                                        int32_t* err) {
   constexpr int D = CH * 16;
-  constexpr int64_t TB = PA_FP8T_TILE_BYTES(D);
+  constexpr int64_t TB = PA_FP8T_TILE_BYTES(D), VTB = PA_FP8T_VTILE_BYTES(D);
   constexpr float FMAX = E5 ? 57344.0f : 448.0f;
   const uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x;
   const uint32_t per_tok = (uint32_t)hkv * CH;
@@ -134,13 +134,15 @@ __global__ __launch_bounds__(256) void k_write_fp8_tok(const uint4* __restrict__
   const float sk = mk / FMAX, sv = mv / FMAX;
   const bool fk = sk >= 0x1p-80f && sk <= 0x1p100f;
   const bool fv = sv >= 0x1p-80f && sv <= 0x1p100f;
-  const int64_t run = ((slot >> 4) * hkv + h) * TB;
+  const int64_t bh = (slot >> 4) * hkv + h;
   const int off = (int)(slot & 15);
-  *reinterpret_cast<uint4*>(k_pool + run + off * D + 16 * c) = fp8_encode16<BF16, E5>(k0, k1, sk, fk);
-  *reinterpret_cast<uint4*>(v_pool + run + off * D + 16 * c) = fp8_encode16<BF16, E5>(v0, v1, sv, fv);
-  if (c == 0) {
-    reinterpret_cast<float*>(k_pool + run + PA_FP8T_SCALE_OFF(D))[off] = sk;
-    reinterpret_cast<float*>(v_pool + run + PA_FP8T_SCALE_OFF(D))[off] = sv;
+  uint8_t* const krun = k_pool + bh * TB;
+  *reinterpret_cast<uint4*>(krun + off * D + 16 * c) = fp8_encode16<BF16, E5>(k0, k1, sk, fk);
+  *reinterpret_cast<uint4*>(v_pool + bh * VTB + off * D + 16 * c) =
+      fp8_encode16<BF16, E5>(v0, v1, sv, fv);
+  if (c == 0) {  // both token scales go to the K run
+    reinterpret_cast<float*>(krun + PA_FP8T_SCALE_OFF(D))[off] = sk;
+    reinterpret_cast<float*>(krun + PA_FP8T_VSCALE_OFF(D))[off] = sv;
   }
 }
 

@@ -51,8 +51,10 @@ def test_status_strings():
     ("fp4", 64, [10 * 3 * 640] * 2 + [10 * 3 * 4 * 16 * 2] * 2),
     ("bf8", 128, [10 * 3 * 16 * 128] * 2 + [0] * 2),
     # per-token FP8: 16 x D code bytes + 16 fp32 scales per (block, head), padded to 128
-    ("fp8t", 128, [10 * 3 * 2176] * 2 + [0] * 2),
-    ("bf8t", 64, [10 * 3 * 1152] * 2 + [0] * 2),
+    # per-token FP8: the K run holds the codes and the token scales of K and V (2048 + 128
+    # bytes at D = 128), the V run the codes only
+    ("fp8t", 128, [10 * 3 * 2176, 10 * 3 * 2048] + [0] * 2),
+    ("bf8t", 64, [10 * 3 * 1152, 10 * 3 * 1024] + [0] * 2),
 ])
 def test_pool_layout_sizes(kv, d, expect):
     assert B.pa_pool_layout(kv, 10, 3, d) == expect

@@ -311,11 +311,18 @@ def test_fp8_token_scale_pool_invariants(kind):
     step = np.max(np.diff(mags) / np.maximum(mags[1:], 1e-300))  # relative grid step bound
     s = sc[blk, :, off][..., None].astype(np.float64)
     assert np.all(np.abs(kd - xv) <= np.maximum(np.abs(xv) * step, s * mags[1]) + 1e-12)
-    # untouched rows: offsets other than the written ones, and block 0 / 3 entirely
+    # V rows are the K rows here, so V's token scales equal K's; both sets sit in the K run
+    # (K's at 16 D, V's at 16 D + 64) and the V run holds codes only
+    sv = C.fp8t_scales(pool, "v")
+    assert np.array_equal(sv[blk, :, off], sc[blk, :, off])
+    assert pool.arrays["k"].shape[-1] == 16 * d + 128 and pool.arrays["v"].shape[-1] == 16 * d
+    # untouched rows: offsets other than the written ones, and blocks 0 and 2 entirely
     raw = pool.arrays["k"]
     assert np.all(raw[[0, 2]] == 0xA5)
+    assert np.all(pool.arrays["v"][[0, 2]] == 0xA5)
     assert np.all(codes[1, :, [o for o in range(16) if o not in (3, 9)]] == 0xA5)
-    assert np.all(raw[3, :, 16 * d + 64:] == 0xA5)  # padding
+    assert np.all(raw[3, :, 16 * d + 32:16 * d + 64] == 0xA5)  # K scales of offsets 8..15
+    assert np.all(raw[3, :, 16 * d + 96:] == 0xA5)  # V scales of offsets 8..15
 
 
 def test_fp8_head_scale_e5m2_invariant():
