@@ -693,7 +693,9 @@ def main():
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": 16, "kv_tokens": dec["tokens"],
                    "partition_size": ps, "step_write_tokens": step_tokens,
-                   "step": ("pa_append_decode (write + decode, one launch)" if fused
+                   "step": ((f"pa_append_decode_n ({run.step_rows_per_seq} rows per sequence; "
+                             "write + decode, one launch)" if run.step_rows_per_seq > 1
+                             else "pa_append_decode (write + decode, one launch)") if fused
                             else "pa_cache_write + pa_decode") + (" + pa_merge" if ps else ""),
                    "pool_copies": args.copies}
                   | ({"fp4_calibration": args.fp4_calibration} if w.kv == "fp4" else {}),

@@ -425,6 +425,29 @@ int pa_append_decode_ex(const void* q, int32_t q_dtype, int32_t num_seqs, int32_
                         const int32_t* context_lens, float sm_scale, int32_t partition_size,
                         float* out, float* part_out, float* part_lse, int32_t* dev_err,
                         const pa_launch_options* opts, void* stream);
+/*
+ * pa_append_decode_ex with several new rows per sequence: k_new, v_new [num_seqs, new_tokens,
+ * num_kv_heads, head_dim] (q_dtype); row i of sequence s is stored at its position
+ * L_s - new_tokens + i, byte for byte as pa_cache_write stores it, by the wave that reads
+ * that position, and the sequence then attends over its L_s tokens exactly as pa_decode.
+ * For a step that appends a chunk of tokens to every sequence before attending (the
+ * workload with a 512-token write per step: 8 rows for each of 64 sequences), or the
+ * drafted tokens a verification step accepts (inferensys glossary "vLLM", speculative
+ * decoding entry), in one launch. new_tokens = 1 is pa_append_decode_ex.
+ *   new_tokens  1 .. max_blocks_per_seq * 16 (else PA_ERR_SHAPE); 16-bit and FP8 pools
+ *               (a 4-bit block takes its outlier set from the rows of its first write,
+ *               which a multi-row append would spread over several waves: an FP4 pool
+ *               accepts new_tokens = 1 only, else PA_ERR_DTYPE)
+ * A sequence with L_s < new_tokens is flagged (PA_DEVERR_BAD_CONTEXT), nothing of it is
+ * written and it reads as an invalid context (zero output; split: every partition empty).
+ * The new rows' blocks must not be read by another sequence of the batch.
+ */
+int pa_append_decode_n(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                       const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                       int32_t new_tokens, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens, float sm_scale,
+                       int32_t partition_size, float* out, float* part_out, float* part_lse,
+                       int32_t* dev_err, const pa_launch_options* opts, void* stream);
 int pa_prefill_ex(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
                   int32_t num_queries, const int32_t* query_start, int32_t max_query_len,
                   const pa_kv_pool* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -110,6 +110,8 @@ def lib():
                                             vp, vp, vp, vp, vp]),
             "pa_append_decode_ex": (ctypes.c_int, [vp, i32, i32, i32, pool_p, vp, vp, vp, i32,
                                                    vp, f32, i32, vp, vp, vp, vp, vp, vp]),
+            "pa_append_decode_n": (ctypes.c_int, [vp, i32, i32, i32, pool_p, vp, vp, i32, vp,
+                                                  i32, vp, f32, i32, vp, vp, vp, vp, vp, vp]),
             "pa_prefill_ex": (ctypes.c_int, [vp, i32, i32, i32, i32, vp, i32, pool_p, vp, i32,
                                              vp, f32, vp, vp, vp, vp]),
             "pa_gather_probe": (ctypes.c_int, [i32, i32, pool_p, vp, i32, vp, i32, vp, vp, vp,
@@ -371,6 +373,25 @@ def pa_append_decode(q, pool: KVPool, k_new, v_new, block_tables, context_lens, 
         _check("pa_append_decode", lib().pa_append_decode(*args, _stream()))
     else:
         _check("pa_append_decode_ex", lib().pa_append_decode_ex(*args, _opts(waves), _stream()))
+
+
+def pa_append_decode_n(q, pool: KVPool, k_new, v_new, block_tables, context_lens, sm_scale,
+                       partition_size=0, out=None, part_out=None, part_lse=None, dev_err=None,
+                       waves=None):
+    """pa_decode after writing each sequence's n new rows k_new[s, i] / v_new[s, i]
+    ([S, n, Hkv, D], q's dtype) at its positions L_s - n + i, in one launch (16-bit and FP8
+    pools; FP4 pools take n = 1)."""
+    assert q.dtype in ACT_DTYPES and k_new.dtype == q.dtype and v_new.dtype == q.dtype
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    assert k_new.is_contiguous() and v_new.is_contiguous() and k_new.dim() == 4
+    S, Hq, _ = q.shape
+    assert k_new.shape[0] == S and v_new.shape == k_new.shape
+    s = pool.struct()
+    _check("pa_append_decode_n", lib().pa_append_decode_n(
+        _ptr(q), ACT_DTYPES[q.dtype], S, Hq, ctypes.byref(s), _ptr(k_new), _ptr(v_new),
+        int(k_new.shape[1]), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        float(sm_scale), partition_size, _ptr(out), _ptr(part_out), _ptr(part_lse),
+        _ptr(dev_err), _opts(waves), _stream()))
 
 
 def pa_prefill(q, query_start, max_query_len, pool: KVPool, block_tables, context_lens,

@@ -346,9 +346,10 @@ int decode_waves(const pa::DecodeArgs& a, int32_t dtype, const pa_launch_options
   return waves;
 }
 
-// pa_decode and pa_append_decode: k_new / v_new NULL for the former
+// pa_decode and pa_append_decode[_n]: k_new / v_new NULL for the former; n_new new rows
+// per sequence for the latter
 int decode_call(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
-                const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                const pa_kv_pool* pool, const void* k_new, const void* v_new, int32_t n_new,
                 const int32_t* block_tables, int32_t max_blocks_per_seq,
                 const int32_t* context_lens, float sm_scale, int32_t partition_size, float* out,
                 float* part_out, float* part_lse, int32_t* dev_err,
@@ -369,9 +370,17 @@ int decode_call(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_
   }
   if (!aligned(q, 16) || !aligned(dev_err, 4) || !aligned(k_new, 16) || !aligned(v_new, 16))
     return PA_ERR_ALIGN;
+  if (k_new) {
+    if (n_new < 1 || (int64_t)n_new > (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE)
+      return PA_ERR_SHAPE;
+    // a 4-bit block takes its outlier set from the rows of its first write, which several
+    // new rows per sequence would spread over several waves
+    if (n_new > 1 && pool->dtype == PA_KV_FP4_E2M1_OUTL) return PA_ERR_DTYPE;
+  }
   a.q = q;
   a.k_new = k_new;
   a.v_new = v_new;
+  a.new_tokens = k_new ? n_new : 0;
   a.out = out;
   a.part_out = part_out;
   a.part_lse = part_lse;
@@ -442,7 +451,7 @@ int pa_decode(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_he
               const pa_kv_pool* pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
               const int32_t* context_lens, float sm_scale, int32_t partition_size, float* out,
               float* part_out, float* part_lse, int32_t* dev_err, void* stream) {
-  return decode_call(q, q_dtype, num_seqs, num_q_heads, pool, nullptr, nullptr, block_tables,
+  return decode_call(q, q_dtype, num_seqs, num_q_heads, pool, nullptr, nullptr, 0, block_tables,
                      max_blocks_per_seq, context_lens, sm_scale, partition_size, out, part_out,
                      part_lse, dev_err, nullptr, stream);
 }
@@ -452,7 +461,7 @@ int pa_decode_ex(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q
                  const int32_t* context_lens, float sm_scale, int32_t partition_size, float* out,
                  float* part_out, float* part_lse, int32_t* dev_err,
                  const pa_launch_options* opts, void* stream) {
-  return decode_call(q, q_dtype, num_seqs, num_q_heads, pool, nullptr, nullptr, block_tables,
+  return decode_call(q, q_dtype, num_seqs, num_q_heads, pool, nullptr, nullptr, 0, block_tables,
                      max_blocks_per_seq, context_lens, sm_scale, partition_size, out, part_out,
                      part_lse, dev_err, opts, stream);
 }
@@ -474,10 +483,22 @@ int pa_append_decode_ex(const void* q, int32_t q_dtype, int32_t num_seqs, int32_
                         const int32_t* context_lens, float sm_scale, int32_t partition_size,
                         float* out, float* part_out, float* part_lse, int32_t* dev_err,
                         const pa_launch_options* opts, void* stream) {
+  return pa_append_decode_n(q, q_dtype, num_seqs, num_q_heads, pool, k_new, v_new, 1,
+                            block_tables, max_blocks_per_seq, context_lens, sm_scale,
+                            partition_size, out, part_out, part_lse, dev_err, opts, stream);
+}
+
+int pa_append_decode_n(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
+                       const pa_kv_pool* pool, const void* k_new, const void* v_new,
+                       int32_t new_tokens, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens, float sm_scale,
+                       int32_t partition_size, float* out, float* part_out, float* part_lse,
+                       int32_t* dev_err, const pa_launch_options* opts, void* stream) {
   if (num_seqs > 0 && (!k_new || !v_new)) return PA_ERR_NULL;
-  return decode_call(q, q_dtype, num_seqs, num_q_heads, pool, k_new, v_new, block_tables,
-                     max_blocks_per_seq, context_lens, sm_scale, partition_size, out, part_out,
-                     part_lse, dev_err, opts, stream);
+  if (new_tokens < 1) return PA_ERR_SHAPE;
+  return decode_call(q, q_dtype, num_seqs, num_q_heads, pool, k_new, v_new, new_tokens,
+                     block_tables, max_blocks_per_seq, context_lens, sm_scale, partition_size,
+                     out, part_out, part_lse, dev_err, opts, stream);
 }
 
 int pa_prefill(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,

@@ -73,31 +73,52 @@ __device__ __forceinline__ uint2 record_words12(const uint8_t* rec, bool fresh) 
 
 // pa_append_decode: the workgroup that reads sequence s's last position writes the
 // sequence's new row there first, for its kv head, exactly as the cache-write kernels
-// store it (16-bit copy, FP8 with the head's scale, FP8 with the row's own scale). K uses
-// lanes [0, R) and V lanes [R, 2R) of one wave, R lanes per row.
-template <int KV, int D, bool QBF>
-__device__ __forceinline__ void append_row(const DecodeArgs& a, int s, int kvh, int b, int off) {
-  using G_ = Geo<KV, D>;
-  constexpr int R = is_f8(KV) ? D / 16 : D * 2 / 16;  // lanes per row
+// store it (16-bit copy, FP8 with the head's scale, FP8 with the row's own scale), by a
+// group of 2 R consecutive lanes (aligned to 2 R; t = the lane's place in the group): K on
+// places [0, R), V on [R, 2R). `row` indexes the new rows: k_new / v_new hold
+// [row][Hkv][D]. Loading (append_load) and storing (append_store) are separate steps, so
+// that a wave can have the loads of several rows in flight before it stores any.
+template <int KV, int D>
+constexpr int append_lanes() { return 2 * (is_f8(KV) ? D / 16 : D * 2 / 16); }
+struct NewRow {
+  uint4 lo, hi;  // the lane's 16 (FP8 pools: 2 x 8) input values of the row
+};
+template <int KV, int D>
+__device__ __forceinline__ NewRow append_load(const DecodeArgs& a, int row, int kvh, int t) {
+  constexpr int R = append_lanes<KV, D>() / 2;  // lanes per row and side
   static_assert(2 * R <= 64, "one wave writes the row");
-  const int t = threadIdx.x & 63;
-  if (t >= 2 * R) return;
   const bool vside = t >= R;
   const int c = t - (vside ? R : 0);
   const uint4* src = reinterpret_cast<const uint4*>(vside ? a.v_new : a.k_new) +
-                     ((int64_t)s * a.num_kv_heads + kvh) * (D * 2 / 16);
+                     ((int64_t)row * a.num_kv_heads + kvh) * (D * 2 / 16);
+  NewRow r;
+  if constexpr (KV == KV_F16 || KV == KV_BF16) {
+    r.lo = src[c];
+    r.hi = r.lo;
+  } else {
+    r.lo = src[2 * c];
+    r.hi = src[2 * c + 1];
+  }
+  return r;
+}
+template <int KV, int D, bool QBF>
+__device__ __forceinline__ void append_store(const DecodeArgs& a, const NewRow& r, int kvh,
+                                             int b, int off, int t) {
+  using G_ = Geo<KV, D>;
+  constexpr int R = append_lanes<KV, D>() / 2;
+  const bool vside = t >= R;
+  const int c = t - (vside ? R : 0);
   const int64_t bh = (int64_t)b * a.num_kv_heads + kvh;
   uint8_t* tile = reinterpret_cast<uint8_t*>(const_cast<void*>(vside ? a.v : a.k)) +
                   bh * (vside ? G_::VTILEB : G_::TILEB);
   if constexpr (KV == KV_F16 || KV == KV_BF16) {
-    reinterpret_cast<uint4*>(tile + off * G_::ROWB)[c] = src[c];
+    reinterpret_cast<uint4*>(tile + off * G_::ROWB)[c] = r.lo;
   } else {
     constexpr bool E5 = f8_e5(KV);
-    const uint4 lo = src[2 * c], hi = src[2 * c + 1];
     float sc;
     if constexpr (f8_tok(KV)) {
       // the row's absmax over its R threads (consecutive lanes, R divides 64)
-      const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      const uint32_t w[8] = {r.lo.x, r.lo.y, r.lo.z, r.lo.w, r.hi.x, r.hi.y, r.hi.z, r.hi.w};
       float mx = 0.0f;
 #pragma unroll
       for (int e = 0; e < 16; ++e)
@@ -114,7 +135,7 @@ __device__ __forceinline__ void append_row(const DecodeArgs& a, int s, int kvh, 
       sc = vside ? a.v_scale[kvh] : a.k_scale[kvh];
     }
     const bool fast = __builtin_fabsf(sc) >= 0x1p-80f && __builtin_fabsf(sc) <= 0x1p100f;
-    *reinterpret_cast<uint4*>(tile + off * D + 16 * c) = fp8_encode16<QBF, E5>(lo, hi, sc, fast);
+    *reinterpret_cast<uint4*>(tile + off * D + 16 * c) = fp8_encode16<QBF, E5>(r.lo, r.hi, sc, fast);
   }
 }
 
@@ -192,7 +213,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   const int L = a.context_lens[s];
   const int cap_tokens = a.max_blocks * kBlock;
   const bool split = a.partition_size > 0;
-  if (L < 1 || L > cap_tokens) {
+  if (L < 1 || L > cap_tokens || (APPEND && L < a.new_tokens)) {
     if (threadIdx.x == 0 && p == 0 && kvh == 0 && a.err) atomicOr(a.err, PA_DEVERR_BAD_CONTEXT);
     if (PROBE) return;  // the probe has no outputs
     if (!split && p == 0) {
@@ -208,38 +229,79 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     }
     return;
   }
-  // APPEND: whether this wave wrote the new row (and so fences before loading its tile)
-  bool wrote = false;
-  if constexpr (APPEND) {
-    // The wave that will read position L - 1 (the partition's blocks go round-robin to
-    // the workgroup's waves) writes the new row there first. No other wave or workgroup
-    // reads that (block, kv head) tile in this launch, and the block is the last of the
-    // partition, so it is this wave's last tile: a fence at workgroup scope just before
-    // that tile's loads is enough (its release waits for the stores to reach L2, its
-    // acquire orders the later loads after them), and by then the stores have long
-    // completed, so the wait costs nothing. The other waves do not wait. (A device-scope
-    // fence would also write back and invalidate the XCD's L2: measured, that cost the c4
-    // decode 60% of its speed.)
-    const int pos = L - 1;
-    const int start_blk = split ? p * (a.partition_size / kBlock) : 0;
-    const bool here = !split || p == pos / a.partition_size;  // uniform over the workgroup
-    if (here && wave == (pos / kBlock - start_blk) % W) {
-      const int32_t b = a.block_tables[(int64_t)s * a.max_blocks + pos / kBlock];
-      if ((unsigned)b < (unsigned)a.num_blocks) {
-        if constexpr (KV == KV_FP4)
-          append_row_fp4<D, QBF>(a, s, kvh, b, pos % kBlock);
-        else
-          append_row<KV, D, QBF>(a, s, kvh, b, pos % kBlock);
-      } else if (lane == 0 && a.err)
-        atomicOr(a.err, PA_DEVERR_BAD_BLOCK);
-      wrote = true;
-    }
-  }
   // the blocks this wave reads: its share of the partition, blocks w, w + W, ...
   const int start = split ? p * a.partition_size : 0;
   if (start >= L) return;  // empty partition: not written, the merge skips it
   const int end = split ? min(start + a.partition_size, L) : L;
   const int jb0 = start / kBlock;
+
+  // APPEND: whether this wave wrote new rows, and the first of its blocks that holds one
+  // (it fences before loading that tile); both wave-uniform
+  bool wrote = false;
+  int first_jb = 0;
+  if constexpr (APPEND) {
+    // The sequence's new rows go to positions L - n .. L - 1. The wave that will read a
+    // position (the partition's blocks go round-robin to the workgroup's waves) writes the
+    // new row there first. No other wave or workgroup reads those (block, kv head) tiles in
+    // this launch, and they are the last blocks of the sequence, so this wave's last
+    // tiles: a fence at workgroup scope just before the first of them is enough (its
+    // release waits for the stores to reach L2, its acquire orders the later loads after
+    // them), and by then the stores have long completed, so the wait costs nothing. The
+    // other waves do not wait. (A device-scope fence would also write back and invalidate
+    // the XCD's L2: measured, that cost the c4 decode 60% of its speed.)
+    const int n = a.new_tokens;
+    const int lo = max(L - n, start), hi = end;  // this partition's new positions
+    if (lo < hi) {
+      const int jb_lo = lo / kBlock, jb_hi = (hi - 1) / kBlock;
+      first_jb = jb_lo + ((wave - (jb_lo - jb0)) % W + W) % W;
+      wrote = first_jb <= jb_hi;
+    }
+  }
+  auto write_new_rows = [&] {
+    if constexpr (APPEND) {
+      if (!wrote) return;
+      const int n = a.new_tokens;
+      const int lo = max(L - n, start), hi = end;
+      if constexpr (KV == KV_FP4) {
+        // (one new row per sequence: position L - 1, the whole wave)
+        const int32_t b = a.block_tables[(int64_t)s * a.max_blocks + (L - 1) / kBlock];
+        if ((unsigned)b < (unsigned)a.num_blocks)
+          append_row_fp4<D, QBF>(a, s, kvh, b, (L - 1) % kBlock);
+        else if (lane == 0 && a.err)
+          atomicOr(a.err, PA_DEVERR_BAD_BLOCK);
+      } else {
+        // groups of 2 R lanes, one new row each, every row of this wave's blocks; two rows
+        // per group and trip, both loaded before either is stored
+        constexpr int LPR = append_lanes<KV, D>(), RPP = 64 / LPR;
+        const int g = lane / LPR, t = lane % LPR;
+        for (int p0 = lo; p0 < hi; p0 += 2 * RPP) {
+          int pos[2];
+          bool mine[2];
+          int32_t b[2];
+          NewRow r[2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            pos[k] = p0 + k * RPP + g;
+            mine[k] = pos[k] < hi && (pos[k] / kBlock - jb0) % W == wave;
+            if (mine[k]) {
+              b[k] = a.block_tables[(int64_t)s * a.max_blocks + pos[k] / kBlock];
+              r[k] = append_load<KV, D>(a, s * n + (pos[k] - (L - n)), kvh, t);
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            if (mine[k]) {
+              if ((unsigned)b[k] < (unsigned)a.num_blocks)
+                append_store<KV, D, QBF>(a, r[k], kvh, b[k], pos[k] % kBlock, t);
+              else if (t == 0 && a.err)
+                atomicOr(a.err, PA_DEVERR_BAD_BLOCK);
+            }
+          }
+        }
+      }
+    }
+  };
+  write_new_rows();
   const int nblk = (end + kBlock - 1) / kBlock - jb0;
   const int my_n = wave < nblk ? (nblk - wave + W - 1) / W : 0;
 
@@ -313,7 +375,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   int err_bits = 0;
   auto load_tile = [&](Tile<KV, D>& T, int x) {
     if constexpr (APPEND) {
-      if (wrote && x == my_n - 1) {  // the tile holding the row this wave wrote
+      if (wrote && jb0 + wave + x * W == first_jb) {  // the first tile holding a new row
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       }
@@ -334,7 +396,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
       b_raw = __builtin_amdgcn_readlane(ids_a, x & 63);
     }
     T.jb = jb0 + wave + x * W;
-    T.fresh = APPEND && wrote && x == my_n - 1;
+    T.fresh = APPEND && wrote && T.jb >= first_jb;
     T.ok = (unsigned)b_raw < (unsigned)a.num_blocks;
     err_bits |= T.ok ? 0 : PA_DEVERR_BAD_BLOCK;
     const int b = T.ok ? b_raw : 0;

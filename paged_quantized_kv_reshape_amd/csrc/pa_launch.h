@@ -41,10 +41,12 @@ struct DecodeArgs {
   float* part_out;  // [S, Hq, P, D] otherwise
   float* part_lse;  // [S, Hq, P]
   int32_t* err;
-  // decode with append (pa_append_decode): sequence s's new K/V row [Hkv, D] at k_new /
-  // v_new + s * Hkv * D (activation dtype of q), written at position L_s - 1 first
+  // decode with append (pa_append_decode[_n]): sequence s's new_tokens new K/V rows
+  // [new_tokens][Hkv][D] at k_new / v_new + s * new_tokens * Hkv * D (activation dtype of
+  // q), written at positions L_s - new_tokens .. L_s - 1 first
   const void* k_new;
   const void* v_new;
+  int32_t new_tokens;
   uint32_t* sink;              // gather probe: [1024] XOR words
   const int32_t* query_start;  // multi-token queries: [S + 1] row offsets of q and out
   int32_t max_query_len, num_queries;

@@ -129,20 +129,44 @@ class DeviceRun:
         self.decode(pool)
 
     @property
-    def can_append(self) -> bool:
-        """The step can run as one pa_append_decode launch: one new token per sequence, at
-        its last position (per-block FP4 calibration; the per-sequence mode writes through
-        its own entry point)."""
+    def step_rows_per_seq(self) -> int:
+        """n when the step writes the last n positions of every sequence, in sequence order
+        (then it can run as one pa_append_decode[_n] launch), else 0."""
         w = self.w
-        last = w.seq_start + w.context_lens.astype(np.int64) - 1
-        return (self.seq_records is None and len(w.step_call.rows) == w.num_seqs
-                and np.array_equal(w.step_call.rows, last))
+        S = w.num_seqs
+        if len(w.step_call.rows) % S:
+            return 0
+        n = len(w.step_call.rows) // S
+        L = w.context_lens.astype(np.int64)
+        if n == 0 or np.any(L < n):
+            return 0
+        want = (w.seq_start[:, None] + L[:, None] - n + np.arange(n)[None, :]).reshape(-1)
+        return n if np.array_equal(w.step_call.rows, want) else 0
+
+    @property
+    def can_append(self) -> bool:
+        """The step can run as one launch that writes and decodes: it writes the last n
+        positions of every sequence (n = 1 in a 4-bit pool, whose per-block calibration
+        takes a block's first-write rows; the per-sequence mode writes through its own entry
+        point)."""
+        n = self.step_rows_per_seq
+        return self.seq_records is None and (n == 1 or (n > 1 and self.w.kv != "fp4"))
 
     def append_decode(self, pool=None, merge=True):
-        B.pa_append_decode(self.q, pool or self.pool, self.step_k, self.step_v, self.block_tables,
-                           self.context_lens, self.w.sm_scale, self.ps, out=self.out,
-                           part_out=self.part_out, part_lse=self.part_lse, dev_err=self.dev_err,
-                           waves=self.waves)
+        n = self.step_rows_per_seq
+        if n == 1:
+            B.pa_append_decode(self.q, pool or self.pool, self.step_k, self.step_v,
+                               self.block_tables, self.context_lens, self.w.sm_scale, self.ps,
+                               out=self.out, part_out=self.part_out, part_lse=self.part_lse,
+                               dev_err=self.dev_err, waves=self.waves)
+        else:
+            S = self.w.num_seqs
+            B.pa_append_decode_n(self.q, pool or self.pool,
+                                 self.step_k.view(S, n, *self.step_k.shape[1:]),
+                                 self.step_v.view(S, n, *self.step_v.shape[1:]),
+                                 self.block_tables, self.context_lens, self.w.sm_scale, self.ps,
+                                 out=self.out, part_out=self.part_out, part_lse=self.part_lse,
+                                 dev_err=self.dev_err, waves=self.waves)
         if merge:
             self.merge()
 

@@ -155,6 +155,17 @@ def test_append_decode_rejects():
     assert f(S=0) == PA_OK
 
 
+def test_append_decode_n_rejects():
+    lib = B.lib()
+    f = lambda n, pool=None, S=2, MB=4: lib.pa_append_decode_n(
+        FAKE, 1, S, 8, ctypes.byref(pool if pool is not None else _pool()), FAKE, FAKE, n,
+        FAKE, MB, FAKE, 0.1, 0, FAKE, FAKE, FAKE, None, None, None)
+    assert f(0) == SHAPE and f(-3) == SHAPE
+    assert f(4 * 16 + 1) == SHAPE  # more new rows than the block table can hold
+    assert f(2, pool=_pool(dtype=3)) == DTYPE  # FP4 pools take one new row per sequence
+    assert f(8, S=0) == PA_OK
+
+
 def _prefill(pool=None, q=FAKE, qd=1, S=2, Hq=8, T=10, qs=FAKE, mq=5, bt=FAKE, MB=4,
              cl=FAKE, out=FAKE):
     pool = pool if pool is not None else _pool()

@@ -112,3 +112,92 @@ def test_append_decode_flags_a_bad_last_block():
     o = out.cpu().numpy()
     for s in (0, 2):
         assert_close(o[s], ref[s][0], f"bad block, seq {s}")
+
+
+# several new rows per sequence (pa_append_decode_n): the last n positions of every
+# sequence, written by the waves that read them; n = 8 is the 64-sequence FP8 workload's
+# 512-row step, 20 and 33 span two and three blocks (rows of one sequence then go to
+# different waves, and with ps = 64 to different partitions)
+NCASES = {
+    "fp8-n8": ("c3", dict(num_seqs=4, lens_range=(200, 900)), 8),
+    "fp8-n20": ("c3", dict(num_seqs=3, lens=[300, 77, 20]), 20),
+    "bf16-n33": ("c2", dict(num_seqs=3, lens=[300, 77, 33]), 33),
+    "fp8t-n5": ("c4", dict(num_seqs=3, lens=[300, 77, 17], kv="fp8t"), 5),
+    "bf8-d64-n16": ("c4", dict(num_seqs=3, lens=[300, 64, 16], kv="bf8", head_dim=64,
+                               num_kv_heads=2), 16),
+    "f16-n2": ("c1", {}, 2),
+}
+
+
+@pytest.mark.parametrize("waves", [1, 4])
+@pytest.mark.parametrize("ps", [0, 64])
+@pytest.mark.parametrize("case", list(NCASES))
+def test_append_decode_n_matches_oracle_and_separate_calls(case, ps, waves):
+    from paged_quantized_kv_reshape_amd import max_partitions, pa_append_decode_n, pa_merge
+    from paged_quantized_kv_reshape_amd.harness import DeviceRun
+    base, over, n = NCASES[case]
+    w = config(base, step_tokens=n, **over)
+    run = DeviceRun(w, partition_size=ps, pool_copies=2, waves=waves)
+    assert run.step_rows_per_seq == n  # the step writes the last n positions of each sequence
+    _say(f"[append n] {case} ({w.kv}) n={n} ps={ps} W={waves} lens={w.context_lens.tolist()}")
+    for p in run.pools:
+        run.setup_writes(p)
+    S, Hq, D = w.q.shape
+    out = torch.full((S, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    po = pl = None
+    if ps:
+        P = max_partitions(w.max_blocks_per_seq, ps)
+        po = torch.empty((S, Hq, P, D), dtype=torch.float32, device="cuda")
+        pl = torch.empty((S, Hq, P), dtype=torch.float32, device="cuda")
+    kn = run.step_k.view(S, n, *run.step_k.shape[1:])
+    vn = run.step_v.view(S, n, *run.step_v.shape[1:])
+    pa_append_decode_n(run.q, run.pools[0], kn, vn, run.block_tables, run.context_lens,
+                       w.sm_scale, ps, out=None if ps else out, part_out=po, part_lse=pl,
+                       dev_err=run.dev_err, waves=waves)
+    if ps:
+        pa_merge(po, pl, run.context_lens, ps, out)
+    run.step_write(run.pools[1])
+    run.decode(run.pools[1])
+    torch.cuda.synchronize()
+    assert run.device_error() == 0
+    pool, ks, vs, near = replay(w)
+    assert_pool_equal(run.pools[0].numpy(), pool, near=near)
+    got = out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), run.out.cpu().numpy().view(np.uint32))
+    ref = oracle_decode(w, pool, ks, vs, range(w.num_seqs))
+    assert_close(got, np.stack([ref[s][0] for s in range(w.num_seqs)]),
+                 f"append n {case} ps={ps} W={waves}")
+
+
+def test_append_decode_n_flags_a_context_shorter_than_its_new_rows():
+    """A sequence with fewer tokens than new rows: flagged as a bad context, nothing of it
+    written, a zero output; the other sequences as the separate calls give them."""
+    from paged_quantized_kv_reshape_amd import pa_append_decode_n
+    from paged_quantized_kv_reshape_amd.harness import DeviceRun
+    n = 8
+    w = config("c3", num_seqs=3, lens=[300, 77, 40], step_tokens=n)
+    run = DeviceRun(w, partition_size=0)
+    run.setup_writes()
+    before = {k: t.clone() for k, t in run.pool.bytes.items()}
+    cl = run.context_lens.clone()
+    cl[1] = n - 1  # sequence 1 now claims 7 tokens but gets 8 new rows
+    S = w.num_seqs
+    out = torch.full_like(run.out, float("nan"))
+    pa_append_decode_n(run.q, run.pool, run.step_k.view(S, n, *run.step_k.shape[1:]),
+                       run.step_v.view(S, n, *run.step_v.shape[1:]), run.block_tables, cl,
+                       w.sm_scale, 0, out=out, dev_err=run.dev_err)
+    torch.cuda.synchronize()
+    assert run.device_error() == 4  # PA_DEVERR_BAD_CONTEXT
+    o = out.cpu().numpy()
+    assert np.all(o[1] == 0.0)
+    # sequence 1's blocks are untouched; 0 and 2 got their rows and decode as the oracle
+    got = run.pool.numpy()
+    for name, t in before.items():
+        g = got[name].reshape(w.num_blocks, -1)
+        b0 = t.cpu().numpy().reshape(w.num_blocks, -1)
+        for b in w.block_tables[1, :-(-77 // 16)]:
+            assert np.array_equal(g[int(b)], b0[int(b)])
+    pool, ks, vs, _ = replay(w)
+    ref = oracle_decode(w, pool, ks, vs, [0, 2])
+    for s in (0, 2):
+        assert_close(o[s], ref[s][0], f"short context, seq {s}")
