@@ -192,6 +192,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   static_assert(!DB || KV == KV_FP4, "the double-buffered loop is the FP4 kernel's");
   static_assert(kQLds == (D + D / DL) * GP, "FP4 LDS layout");
   constexpr bool PVB = QBF || KV == KV_FP4;  // PV MFMA in bf16 (else fp16)
+  // FP4 with G <= 8 (GP = 8): MFMA columns 8..15 repeat heads 0..7 (the same q, hence the
+  // same logits, maxima and P); there the B operand of PV is P's low half, so one MFMA per
+  // 16 channels carries hi and lo, and the two column halves are added at the end
+  constexpr bool SPARE = KV == KV_FP4 && GP == 8 && !PROBE;
   constexpr bool kStreamK = KV != KV_F16 && KV != KV_BF16;  // non-temporal K tile loads
   extern __shared__ float smem[];
 
@@ -311,11 +315,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 #pragma unroll
     for (int t = 0; t < KS; ++t) qf[t] = make_uint4(0, 0, 0, 0);
   } else {
+    const int hc = SPARE ? (c & 7) : c;  // the head of MFMA column c
     const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
-                          (((int64_t)s * Hq + kvh * G + c) * D + DL * kg) * 2;
+                          (((int64_t)s * Hq + kvh * G + hc) * D + DL * kg) * 2;
 #pragma unroll
     for (int t = 0; t < KS; ++t)
-      qf[t] = c < G ? reinterpret_cast<const uint4*>(qrow)[t] : make_uint4(0, 0, 0, 0);
+      qf[t] = hc < G ? reinterpret_cast<const uint4*>(qrow)[t] : make_uint4(0, 0, 0, 0);
   }
   // FP4 only: q in fp32 for the K-outlier term, channel-major: head c of channel ch at
   // (ch + ch / DL) * GP + c. A column's heads are consecutive words (one read per outlier
@@ -595,15 +600,22 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
         part = group4_sum(part);
         // channel ch is entry ch % DL = NT r + n, in acc[n][r], of the lanes with
         // kg = ch / DL
-        add_entry<NT>(acc, ch % DL, kg == ch / DL ? part : 0.0f);
+        // (SPARE: the low-half columns 8..15 take no outlier term)
+        add_entry<NT>(acc, ch % DL, kg == ch / DL && (!SPARE || c < 8) ? part : 0.0f);
       }
     }
     uint2 vf[NT];
     v_fragments<KV, D, PVB>(T, vf);
+    if constexpr (SPARE) {
+      const uint2 pb = c < 8 ? ph : pl;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      acc[n] = mfma_k16(vf[n], ph, acc[n], PVB);
-      acc[n] = mfma_k16(vf[n], pl, acc[n], PVB);
+      for (int n = 0; n < NT; ++n) acc[n] = mfma_k16(vf[n], pb, acc[n], PVB);
+    } else {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        acc[n] = mfma_k16(vf[n], ph, acc[n], PVB);
+        acc[n] = mfma_k16(vf[n], pl, acc[n], PVB);
+      }
     }
   };
 
@@ -648,6 +660,16 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
       atomicXor(a.sink + ((blockIdx.y * gridDim.x + blockIdx.x) * 8u + (unsigned)wave) % 1024u,
                 probe_x);
     return;
+  }
+  if constexpr (SPARE) {
+    // column c < 8 adds column c + 8 (the same head's P-low products): rotate each 16-lane
+    // row by 8
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[n][r] += __int_as_float(__builtin_amdgcn_update_dpp(
+            0, __float_as_int(acc[n][r]), 0x128 /* row_ror:8 */, 0xF, 0xF, false));
   }
   const float lt = group4_sum(l);
   const float vscale = head_scaled(KV) ? a.v_scale[kvh] : 1.0f;
