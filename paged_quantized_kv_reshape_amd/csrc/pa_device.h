@@ -129,15 +129,24 @@ __device__ __forceinline__ float wave_sum(float x) {
 // halves) between two registers in the vector ALU; swapping a value with itself leaves
 // x_l in one result and x_(l^16) (resp. x_(l^32)) in the other, so combining the two
 // results is one butterfly step, with no trip through the LDS crossbar.
+// The maximum of two values a permlane swap returned. fmaxf would first quiet each
+// operand (a v_max of the value with itself), since the compiler cannot tell that the
+// swapped bits are already canonical floats; they are (each lane's own VALU result), so
+// one v_max_f32 gives fmaxf's answer.
+__device__ __forceinline__ float max_of_swapped(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float xor16_max(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_of_swapped(r[0], r[1]);
 }
 __device__ __forceinline__ float xor32_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_of_swapped(r[0], r[1]);
 }
 __device__ __forceinline__ float xor16_sum(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
