@@ -31,8 +31,8 @@
 //                 4 kg..4 kg+3); lane (c, kg) loads channels [NT c, NT (c+1)) of tokens
 //                 4 kg..4 kg+3 and transposes them in registers (v_perm) so one register
 //                 pair holds one channel of four tokens. P enters as a hi + lo pair of
-//                 16-bit values (about 16 significant bits), so PV loses nothing to
-//                 16-bit rounding of P. After the block loop lane (c, kg) holds head c's
+//                 16-bit values (about 16 significant bits in bf16, 22 in fp16), so PV
+//                 loses nothing to 16-bit rounding of P. After the block loop lane (c, kg) holds head c's
 //                 output channels [D/4 kg, D/4 (kg+1)).
 #include <stdlib.h>
 
@@ -191,7 +191,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   constexpr int kQLds = fp4_qlds_floats<D, GP>();
   static_assert(!DB || KV == KV_FP4, "the double-buffered loop is the FP4 kernel's");
   static_assert(kQLds == (D + D / DL) * GP, "FP4 LDS layout");
-  constexpr bool PVB = QBF || KV == KV_FP4;  // PV MFMA in bf16 (else fp16)
+  // PV MFMA in bf16 for bf16 pools and where P takes a token scale (p s_t may leave fp16's
+  // range), else in fp16: E4M3 and E5M2 codes are fp16 values, and P's hi + lo pair then
+  // carries 22 bits at fewer instructions
+  constexpr bool PVB = KV == KV_BF16 || tok_scaled(KV);
   // FP4 with G <= 8 (GP = 8): MFMA columns 8..15 repeat heads 0..7 (the same q, hence the
   // same logits, maxima and P); there the B operand of PV is P's low half, so one MFMA per
   // 16 channels carries hi and lo, and the two column halves are added at the end
@@ -560,9 +563,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) pv[r] = pr[r];
     }
-    const uint32_t h01 = pack2(pv[0], pv[1], PVB), h23 = pack2(pv[2], pv[3], PVB);
-    const uint32_t l01 = pack2(pv[0] - lo16_to_f32(h01, PVB), pv[1] - hi16_to_f32(h01, PVB), PVB);
-    const uint32_t l23 = pack2(pv[2] - lo16_to_f32(h23, PVB), pv[3] - hi16_to_f32(h23, PVB), PVB);
+    uint32_t h01, h23, l01, l23;
+    split2(pv[0], pv[1], PVB, h01, l01);
+    split2(pv[2], pv[3], PVB, h23, l23);
     const uint2 ph = make_uint2(h01, h23), pl = make_uint2(l01, l23);
 
     if constexpr (KV == KV_FP4) {

@@ -190,4 +190,28 @@ __device__ __forceinline__ float hi16_to_f32(uint32_t w, bool bf16) {
   return bf16 ? __uint_as_float(w & 0xFFFF0000u) : f16_bits_to_f32(w >> 16);
 }
 
+// x - h, h the fp16 value in the low (HI = false) or high half of w, in one v_fma_mix_f32
+// (the instruction reads the fp16 half itself; written out, the compiler converts the half
+// to fp32 first and subtracts after).
+template <bool HI>
+__device__ __forceinline__ float sub_f16_half(float x, uint32_t w) {
+  float r;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(x));
+  else
+    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(x));
+  return r;
+}
+
+// A pair of fp32 values as two 16-bit pairs, hi = (x, y) rounded and lo = their remainders
+// rounded: hi + lo carries about 16 significant bits in bf16 and 22 in fp16. (A remainder
+// x - hi is exact in fp32.)
+__device__ __forceinline__ void split2(float x, float y, bool bf16, uint32_t& hi, uint32_t& lo) {
+  hi = pack2(x, y, bf16);
+  if (bf16)
+    lo = pack2(x - lo16_to_f32(hi, true), y - hi16_to_f32(hi, true), true);
+  else
+    lo = pack2(sub_f16_half<false>(x, hi), sub_f16_half<true>(y, hi), false);
+}
+
 }  // namespace pa

@@ -21,7 +21,8 @@
 //                 running over the 32 tokens of the pair: k = 8 kg + i holds token
 //                 4 kg + i of A (i < 4) or 4 kg + i - 4 of B (i >= 4) - the order in which
 //                 the lane already holds both its probabilities and its V^T values. P
-//                 enters as a hi + lo pair of 16-bit values (about 16 significant bits).
+//                 enters as a hi + lo pair of 16-bit values (about 16 significant bits in bf16,
+//                 22 in fp16).
 // FP4 pools (dailyaiworld.com, same page, "Technical Breakdown", step 4): the logits take
 // the token scale and the K outliers' fp16 terms (q from the fragments already in LDS), P
 // takes the V token scale, and each V outlier's term goes straight into the accumulator
@@ -59,9 +60,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
 void k_prefill_mt(DecodeArgs a) {
   using G_ = Geo<KV, D>;
   constexpr int KS = G_::KS, NT = G_::NT, DL = G_::DL;
-  // PV MFMA type: the query's (FP8 codes are exact in both); FP4 in bf16, since p s_t (the
-  // V token scale folded into p) may leave fp16's range
-  constexpr bool PVB = QBF || KV == KV_FP4;
+  // PV MFMA type: bf16 for bf16 pools and where P takes the V token scale (FP4, per-token
+  // FP8: p s_t may leave fp16's range), else fp16 (E4M3 and E5M2 codes are fp16 values, and
+  // P's hi + lo pair then carries 22 bits at fewer instructions)
+  constexpr bool PVB = KV == KV_BF16 || tok_scaled(KV);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -399,9 +401,7 @@ void k_prefill_mt(DecodeArgs a) {
       uint32_t h[4], lo[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        h[i] = pack2(pv[2 * i], pv[2 * i + 1], PVB);
-        lo[i] = pack2(pv[2 * i] - lo16_to_f32(h[i], PVB), pv[2 * i + 1] - hi16_to_f32(h[i], PVB),
-                      PVB);
+        split2(pv[2 * i], pv[2 * i + 1], PVB, h[i], lo[i]);
       }
       ph[ct] = make_uint4(h[0], h[1], h[2], h[3]);
       pl[ct] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
