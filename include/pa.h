@@ -73,7 +73,8 @@ typedef enum {
   PA_ERR_MEMORY = -9,      /* a pointer is not memory this GPU can access               */
   PA_ERR_EXHAUSTED = -10,  /* the block allocator has fewer free blocks than requested  */
   PA_ERR_STATE = -11,      /* the block allocator was asked about a block not in use    */
-  PA_ERR_SCRATCH = -12     /* the call needs more than the library's static scratch      */
+  PA_ERR_SCRATCH = -12,    /* the call needs more than the library's static scratch      */
+  PA_ERR_SCALE = -13       /* sm_scale is not a positive finite number                   */
 } pa_status;
 
 #define PA_DEVERR_BAD_BLOCK 1        /* block table / copy pair id outside its pool      */
@@ -329,7 +330,9 @@ int pa_allocator_num_free(pa_block_allocator* a);
  *   block_tables  [num_seqs, max_blocks_per_seq] int32; entries past a sequence's last
  *                 block are never read
  *   context_lens  [num_seqs] int32, tokens to attend (including the token just written)
- *   sm_scale      softmax scale (1 / sqrt(head_dim) for the usual attention)
+ *   sm_scale      softmax scale (1 / sqrt(head_dim) for the usual attention); a positive
+ *                 finite number, else PA_ERR_SCALE (the kernels take each block's largest
+ *                 logit as sm_scale times its largest dot product)
  *   partition_size 0: one pass per sequence; writes out [num_seqs, num_q_heads, head_dim]
  *                 fp32. Otherwise a positive multiple of 16: partition p of a sequence
  *                 covers tokens [p * ps, min((p + 1) * ps, L)); each partition with

@@ -112,6 +112,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_STATE: return "PA_ERR_STATE: the block is not in use";
     case PA_ERR_SCRATCH:
       return "PA_ERR_SCRATCH: the call needs more device scratch than the library holds";
+    case PA_ERR_SCALE: return "PA_ERR_SCALE: sm_scale must be a positive finite number";
     default: return "unknown pa_status";
   }
 }
@@ -323,6 +324,10 @@ int decode_geometry(int32_t num_seqs, int32_t num_q_heads, const pa_kv_pool* poo
   return PA_OK;
 }
 
+// The softmax scale: positive (a block's largest logit is then the scale times its largest
+// dot product, which the multi-token kernel relies on) and finite; NaN fails both tests.
+bool scale_ok(float s) { return s > 0.0f && s <= 3.4028234663852886e38f; }
+
 // Waves per decode workgroup. The decode streams K/V tiles from HBM. Measured on MI355X:
 // with one kv head the gather of random 16-token tiles runs fastest with about 8 waves per
 // compute unit in the grid, each walking a long run of blocks (more waves only open more
@@ -359,6 +364,7 @@ int decode_call(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_
                            context_lens, partition_size, opts, a);
   if (st != PA_OK) return st;
   if (!act_ok(q_dtype) || !act_matches_pool(q_dtype, pool->dtype)) return PA_ERR_DTYPE;
+  if (!scale_ok(sm_scale)) return PA_ERR_SCALE;
   if (num_seqs == 0) return PA_OK;
   if (!q) return PA_ERR_NULL;
   if (partition_size == 0) {
@@ -399,6 +405,7 @@ int prefill_call(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q
   if (st != PA_OK) return st;
   if ((st = check_options(opts)) != PA_OK) return st;
   if (!act_ok(q_dtype) || !act_matches_pool(q_dtype, pool->dtype)) return PA_ERR_DTYPE;
+  if (!scale_ok(sm_scale)) return PA_ERR_SCALE;
   if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_q_heads < 1) return PA_ERR_SHAPE;
   if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_SHAPE;
   const int group = num_q_heads / pool->num_kv_heads;

@@ -300,7 +300,8 @@ void k_prefill_mt(DecodeArgs a) {
         add_entry<NT>(acc[ct], ch % DL, kg == ch / DL ? part : 0.0f);
       }
     };
-    // logits of tokens 4 kg .. 4 kg + 3 of one block for column tile ct, masked
+    // logits of tokens 4 kg .. 4 kg + 3 of one block for column tile ct, masked, before
+    // the scale cz (z = x cz, applied where p is formed: exp2(fma(x, cz, -m)))
     auto logits = [&](const Tile<KV, D>& T, const Rec& rk, const f32x4& sa, int ct, float* z) {
       const int tok0 = T.jb * kBlock + 4 * kg;
       float sk[4] = {1.0f, 1.0f, 1.0f, 1.0f};
@@ -317,7 +318,7 @@ void k_prefill_mt(DecodeArgs a) {
         const bool valid = FULL || (T.ok && tok0 + r < col_end[ct]);
         // (sk = 1 folds away; an fma with 1 and 0 would not, as it turns -0 into +0)
         const float x = KV == KV_FP4 ? __builtin_fmaf(sa[r], sk[r], ok[r]) : sa[r] * sk[r];
-        z[r] = valid ? x * cz : -INFINITY;
+        z[r] = valid ? x : -INFINITY;
       }
     };
     // logits of both blocks for every column tile; each K fragment feeds NCT MFMAs
@@ -342,23 +343,27 @@ void k_prefill_mt(DecodeArgs a) {
     v_fragments<KV, D, PVB>(TA, vfa);
     v_fragments<KV, D, PVB>(TB, vfb);
 
-    // masked logits and block maxima of every column tile, then one wave-uniform
-    // decision for a (rare, lazy) rescale of them all
-    float z[NCT][8], mb[NCT];
+    // masked logits and this lane's maxima of every column tile, then one wave-uniform
+    // decision for a (rare, lazy) rescale of them all. cz > 0, so the largest scaled
+    // logit is cz times the largest unscaled one; m is the same in a column's four lanes,
+    // so some column's block maximum passes m + kRescaleLog2 exactly when some lane's own
+    // logits do, and the maximum over the column's lanes is taken only then.
+    float z[NCT][8], xl[NCT];
     bool grow = false;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       logits(TA, rka, sacc[0][ct], ct, z[ct]);
       logits(TB, rkb, sacc[1][ct], ct, z[ct] + 4);
-      float x = fmaxf(fmaxf(fmaxf(z[ct][0], z[ct][1]), fmaxf(z[ct][2], z[ct][3])),
-                      fmaxf(fmaxf(z[ct][4], z[ct][5]), fmaxf(z[ct][6], z[ct][7])));
-      mb[ct] = group4_max(x);
-      grow = grow || mb[ct] > m[ct] + kRescaleLog2;
+      xl[ct] = fmaxf(fmaxf(fmaxf(z[ct][0], z[ct][1]), fmaxf(z[ct][2], z[ct][3])),
+                     fmaxf(fmaxf(z[ct][4], z[ct][5]), fmaxf(z[ct][6], z[ct][7])));
+      grow = grow || xl[ct] * cz > m[ct] + kRescaleLog2;
     }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const float mn = fmaxf(m[ct], mb[ct]);
+        const float xg = group4_max(xl[ct]);
+        const float mb = xg == -INFINITY ? -INFINITY : xg * cz;  // (-inf times cz = 0: NaN)
+        const float mn = fmaxf(m[ct], mb);
         if (started) {
           // (-inf - -inf for a column with nothing unmasked yet: its l and acc are 0 and
           // are left alone)
@@ -378,11 +383,10 @@ void k_prefill_mt(DecodeArgs a) {
       float pv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        // (masked logits are -inf: exp2(-inf - m) = 0 once m is finite; m is -inf only
-        // while every logit of the column so far is masked)
-        const float p = FULL ? __builtin_amdgcn_exp2f(z[ct][i] - m[ct])
-                             : (z[ct][i] == -INFINITY ? 0.0f
-                                                      : __builtin_amdgcn_exp2f(z[ct][i] - m[ct]));
+        // (masked logits are -inf and give p = 0; m is -inf only while every logit of the
+        // column so far is masked)
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(z[ct][i], cz, -m[ct]));
+        const float p = FULL ? e : (z[ct][i] == -INFINITY ? 0.0f : e);
         l[ct] += p;
         pv[i] = p;
       }

@@ -14,7 +14,7 @@ from conftest import ROOT
 B = pytest.importorskip("paged_quantized_kv_reshape_amd.binding")
 
 PA_OK, NULL, SHAPE, DTYPE, BLOCK, CONTEXT, PART, LAUNCH, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7, -8
-MEMORY, EXHAUSTED, STATE, SCRATCH = -9, -10, -11, -12
+MEMORY, EXHAUSTED, STATE, SCRATCH, SCALE = -9, -10, -11, -12, -13
 FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
 
 
@@ -34,7 +34,7 @@ def test_library_exports_every_declared_entry_point():
 def test_status_strings():
     lib = B.lib()
     for code in (PA_OK, NULL, SHAPE, DTYPE, BLOCK, CONTEXT, PART, LAUNCH, ALIGN, MEMORY,
-                 EXHAUSTED, STATE, SCRATCH):
+                 EXHAUSTED, STATE, SCRATCH, SCALE):
         s = lib.pa_status_string(code).decode()
         assert s.startswith("PA_"), s
     assert "unknown" in lib.pa_status_string(-99).decode()
@@ -167,9 +167,9 @@ def test_append_decode_n_rejects():
 
 
 def _prefill(pool=None, q=FAKE, qd=1, S=2, Hq=8, T=10, qs=FAKE, mq=5, bt=FAKE, MB=4,
-             cl=FAKE, out=FAKE):
+             cl=FAKE, out=FAKE, sc=0.1):
     pool = pool if pool is not None else _pool()
-    return B.lib().pa_prefill(q, qd, S, Hq, T, qs, mq, ctypes.byref(pool), bt, MB, cl, 0.1, out,
+    return B.lib().pa_prefill(q, qd, S, Hq, T, qs, mq, ctypes.byref(pool), bt, MB, cl, sc, out,
                               None, None)
 
 
@@ -186,6 +186,19 @@ def test_prefill_rejects():
     assert _prefill(bt=None) == NULL and _prefill(cl=None) == NULL
     assert _prefill(q=FAKE + 4) == ALIGN and _prefill(out=FAKE + 4) == ALIGN
     assert _prefill(S=0) == PA_OK  # nothing to launch
+
+
+@pytest.mark.parametrize("sc", [0.0, -0.0, -0.125, float("nan"), float("inf"), float("-inf")])
+def test_softmax_scale_must_be_positive_and_finite(sc):
+    lib = B.lib()
+    assert _prefill(sc=sc) == SCALE and _prefill(sc=sc, S=0) == SCALE
+    dec = lambda S: lib.pa_decode(FAKE, 1, S, 8, ctypes.byref(_pool()), FAKE, 4, FAKE, sc, 0,
+                                  FAKE, None, None, None, None)
+    assert dec(2) == SCALE and dec(0) == SCALE
+    assert lib.pa_append_decode_n(FAKE, 1, 2, 8, ctypes.byref(_pool()), FAKE, FAKE, 2, FAKE, 4,
+                                  FAKE, sc, 0, FAKE, FAKE, FAKE, None, None, None) == SCALE
+    # tiny and huge scales pass the check (and S = -1 then fails the next one)
+    assert _prefill(sc=1e-30, S=-1) == SHAPE and _prefill(sc=3e38, S=-1) == SHAPE
 
 
 def test_merge_and_scale_and_reset_reject():
