@@ -328,17 +328,36 @@ int decode_geometry(int32_t num_seqs, int32_t num_q_heads, const pa_kv_pool* poo
 // dot product, which the multi-token kernel relies on) and finite; NaN fails both tests.
 bool scale_ok(float s) { return s > 0.0f && s <= 3.4028234663852886e38f; }
 
-// Waves per decode workgroup. The decode streams K/V tiles from HBM. Measured on MI355X:
-// with one kv head the gather of random 16-token tiles runs fastest with about 8 waves per
-// compute unit in the grid, each walking a long run of blocks (more waves only open more
-// DRAM rows at once); with several kv heads the workgroups of one block's heads run side
-// by side and read neighbouring tiles, and about 8 waves per CU per kv head (up to 8
-// heads) keeps those reads together. So pick the smallest power of two W <= 8 that brings
-// the grid to that many waves, without giving a wave fewer than two blocks of its
-// partition. FP4 pools start from 2 waves: a 4-bit tile is half an FP8 one, so a one-wave
-// workgroup keeps too little in flight, and the FP4 kernel's wave merge reuses its own LDS,
-// so two waves cost no occupancy (c5: 107 us vs 113 us with one wave).
-int decode_waves(const pa::DecodeArgs& a, int32_t dtype, const pa_launch_options* opts) {
+// K + V bytes of one (block, kv head) tile of a pool format.
+size_t tile_pair_bytes(int32_t dtype, int32_t head_dim) {
+  switch (dtype) {
+    case PA_KV_F16:
+    case PA_KV_BF16: return (size_t)2 * PA_BLOCK_SIZE * head_dim * 2;
+    case PA_KV_FP8_E4M3:
+    case PA_KV_FP8_E5M2: return (size_t)2 * PA_BLOCK_SIZE * head_dim;
+    case PA_KV_FP4_E2M1_OUTL: return (size_t)2 * PA_FP4_TILE_BYTES(head_dim);
+    default: return (size_t)PA_FP8T_TILE_BYTES(head_dim) + PA_FP8T_VTILE_BYTES(head_dim);
+  }
+}
+
+// Waves per decode workgroup. The decode streams K/V tiles from HBM. Measured on MI355X,
+// two rules, the larger count wins (a power of two up to 8, doubled only while the
+// partition has at least two blocks per wave):
+//  * occupancy: with one kv head the gather of random 16-token tiles runs fastest with
+//    about 8 waves per compute unit in the grid (more waves only open more DRAM rows at
+//    once); with several kv heads the workgroups of one block's heads run side by side and
+//    read neighbouring tiles, and about 8 waves per CU per kv head (up to 8 heads) keeps
+//    those reads together. FP4 pools start from 2 waves: a 4-bit tile is half an FP8 one,
+//    so a one-wave workgroup keeps too little in flight, and the FP4 kernel's wave merge
+//    reuses its own LDS, so two waves cost no occupancy (c5: 107 us vs 113 us with one).
+//  * work per wave: about 48 KiB of K/V per wave of a partition. A workgroup's waves
+//    finish together and the last workgroups of a launch run with the GPU part idle, so
+//    a shorter wave shortens that tail, down to where its fixed costs (the query, the
+//    block ids, the wave merge) start to count. Sweeps of partition size and waves
+//    found the best at 6 bf16 (c2-shaped, 768-token partitions, 8 waves), 12 FP8 (c3,
+//    768, 4 waves) and 16 FP4 tiles (c5, 512, 2 waves) per wave: 48, 48 and 37 KiB.
+int decode_waves(const pa::DecodeArgs& a, int32_t dtype, int32_t head_dim,
+                 const pa_launch_options* opts) {
   if (opts && opts->decode_waves) return opts->decode_waves;
   const int64_t span = a.partition_size > 0 ? a.partition_size
                                             : (int64_t)a.max_blocks * PA_BLOCK_SIZE;
@@ -346,8 +365,11 @@ int decode_waves(const pa::DecodeArgs& a, int32_t dtype, const pa_launch_options
   const int64_t wgs = (int64_t)a.num_seqs * a.num_kv_heads * a.max_partitions;
   const int64_t heads = a.num_kv_heads < 8 ? a.num_kv_heads : 8;
   const int64_t target_waves = 8 * heads * (int64_t)device_cus();
+  const int64_t bytes = blocks * (int64_t)tile_pair_bytes(dtype, head_dim);
   int waves = dtype == PA_KV_FP4_E2M1_OUTL && blocks >= 4 ? 2 : 1;
-  while (waves < 8 && wgs * waves < target_waves && blocks >= 2 * waves) waves *= 2;
+  while (waves < 8 && blocks >= 2 * waves &&
+         (wgs * waves < target_waves || bytes > (int64_t)waves * (48 << 10)))
+    waves *= 2;
   return waves;
 }
 
@@ -393,7 +415,7 @@ int decode_call(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_
   a.err = dev_err;
   a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
   return pa::launch_decode(a, pool->dtype, q_dtype == PA_ACT_BF16, pool->head_dim,
-                           decode_waves(a, pool->dtype, opts), (hipStream_t)stream);
+                           decode_waves(a, pool->dtype, pool->head_dim, opts), (hipStream_t)stream);
 }
 
 int prefill_call(const void* q, int32_t q_dtype, int32_t num_seqs, int32_t num_q_heads,
@@ -542,7 +564,7 @@ int pa_gather_probe(int32_t num_seqs, int32_t num_q_heads, const pa_kv_pool* poo
   if (!aligned(sink, 4) || !aligned(dev_err, 4)) return PA_ERR_ALIGN;
   a.err = dev_err;
   return pa::launch_gather_probe(a, pool->dtype, pool->head_dim,
-                                 decode_waves(a, pool->dtype, opts), sink, (hipStream_t)stream);
+                                 decode_waves(a, pool->dtype, pool->head_dim, opts), sink, (hipStream_t)stream);
 }
 
 int pa_merge(const float* part_out, const float* part_lse, const int32_t* context_lens,

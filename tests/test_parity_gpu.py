@@ -287,8 +287,8 @@ def test_activation_dtypes_and_head_dims(kv, act, d, ps):
 def test_full_size_sampled(cfg):
     """Each full-size workload, sampled. Pool 0 gets the setup and step writes, then the
     separate decode (pa_decode + pa_merge). Where the bench runs the step as one
-    pa_append_decode launch (one new token per sequence at its last position: c2, c4, c5),
-    that launch is checked too, in the bench's own configuration (the workload's partition
+    pa_append_decode[_n] launch (the new tokens of every sequence at its last positions:
+    one in c2, c4, c5, eight in c3), that launch is checked too, in the bench's own configuration (the workload's partition
     size, the library's wave count, then pa_merge): on pool 1, which holds the setup writes
     only, so the launch itself writes (and for FP4 calibrates) the step's rows; and again
     on pool 0, whose rows are already written, as every timed bench step after the first

@@ -215,10 +215,10 @@ CONFIGS = {
     "c1": dict(seed=0, num_seqs=2, num_q_heads=4, num_kv_heads=1, head_dim=64, kv="f16",
                act="f16", lens=[37, 50], num_blocks=16),
     "c2": dict(seed=1, num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=128, kv="bf16",
-               act="bf16", lens_range=(1024, 8192), partition_size=1024),
+               act="bf16", lens_range=(1024, 8192), partition_size=768),
     "c3": dict(seed=2, num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=128, kv="fp8",
                act="bf16", lens_range=(1024, 8192), planted=True, step_tokens=8,
-               partition_size=512),
+               partition_size=768),
     "c4": dict(seed=3, num_seqs=256, num_q_heads=8, num_kv_heads=1, head_dim=128, kv="fp8",
                act="bf16", lens=[8192] * 256, planted=True, partition_size=0),
     "c5": dict(seed=4, num_seqs=32, num_q_heads=8, num_kv_heads=1, head_dim=128, kv="fp4",
