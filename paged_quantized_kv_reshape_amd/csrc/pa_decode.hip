@@ -308,9 +308,25 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
       }
     }
   };
-  write_new_rows();
   const int nblk = (end + kBlock - 1) / kBlock - jb0;
   const int my_n = wave < nblk ? (nblk - wave + W - 1) / W : 0;
+
+  // ---- block ids ----
+  // Single buffer: 64 of this wave's block ids per register, one register ahead, read
+  // with readlane. Double buffer: the same 64-id chunks staged in this wave's LDS slot
+  // and each id read one block ahead, so that no vector load of ids is pending when the
+  // next tile's loads are issued and no scalar load is pending during a block's math (a
+  // scalar load may complete out of order, so any wait on LDS would wait for it too).
+  // The first chunks are requested before anything else: the first tile's loads wait for
+  // them, and the new rows' writes and the query loads go out meanwhile.
+  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks + jb0 + wave;
+  auto load_ids = [&](int chunk) -> int {
+    const int x = chunk * 64 + lane;
+    return x < my_n ? bt[(int64_t)x * W] : 0;
+  };
+  int ids_a = load_ids(0), ids_b = load_ids(1), nid_v = 0;
+
+  write_new_rows();
 
   // ---- query fragments (B operand of S^T = K Q^T), zero for padded heads ----
   uint4 qf[KS];
@@ -329,46 +345,33 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   // (ch + ch / DL) * GP + c. A column's heads are consecutive words (one read per outlier
   // is conflict-free) and the pad of GP words after each DL channels puts the four lane
   // groups of a write on different banks.
+  // (staged after the first tile's loads are out: the barrier waits for wave 0's query)
   float* const q_lds = smem;
-  if constexpr (KV == KV_FP4) {
-    if (wave == 0) {
+  auto stage_q = [&] {
+    if constexpr (KV == KV_FP4) {
+      if (wave == 0) {
 #pragma unroll
-      for (int t = 0; t < KS; ++t) {
-        const uint32_t w[4] = {qf[t].x, qf[t].y, qf[t].z, qf[t].w};
+        for (int t = 0; t < KS; ++t) {
+          const uint32_t w[4] = {qf[t].x, qf[t].y, qf[t].z, qf[t].w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t b16 = (w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-          if (c < GP) q_lds[(DL * kg + 8 * t + e + kg) * GP + c] = act_to_f32<QBF>(b16);
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t b16 = (w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+            if (c < GP) q_lds[(DL * kg + 8 * t + e + kg) * GP + c] = act_to_f32<QBF>(b16);
+          }
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
-  }
+  };
 
   // ---- scale of the logits (base 2) ----
   float cz = a.sm_scale_log2;
   if constexpr (head_scaled(KV)) cz *= a.k_scale[kvh];
 
-  // ---- block ids ----
-  // Single buffer: 64 of this wave's block ids per register, one register ahead, read
-  // with readlane. Double buffer: the same 64-id chunks staged in this wave's LDS slot
-  // and each id read one block ahead, so that no vector load of ids is pending when the
-  // next tile's loads are issued and no scalar load is pending during a block's math (a
-  // scalar load may complete out of order, so any wait on LDS would wait for it too).
-  const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks + jb0 + wave;
-  auto load_ids = [&](int chunk) -> int {
-    const int x = chunk * 64 + lane;
-    return x < my_n ? bt[(int64_t)x * W] : 0;
-  };
-  int ids_a = 0, ids_b = 0, nid_v = 0;
   int* const ids_lds = reinterpret_cast<int*>(smem + kQLds) + wave * kIdsLds;
   if constexpr (DB) {
-    ids_lds[lane] = load_ids(0);
-    ids_b = load_ids(1);
+    ids_lds[lane] = ids_a;
     nid_v = ids_lds[0];
-  } else {
-    ids_a = load_ids(0);
-    ids_b = load_ids(1);
   }
 
   const uint8_t* kpool = reinterpret_cast<const uint8_t*>(a.k);
@@ -630,6 +633,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   if constexpr (DB) {
     Tile<KV, D> ta, tb;
     if (my_n > 0) load_tile(ta, 0);
+    stage_q();
     int i = 0;
     for (; i + 2 < my_n; i += 2) {
       load_tile(tb, i + 1);
@@ -647,6 +651,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
   } else {
     Tile<KV, D> tile;
     if (my_n > 0) load_tile(tile, 0);
+    stage_q();
     for (int i = 0; i + 1 < my_n; ++i) {
       if (tile.ok) compute(tile, std::true_type{});
       load_tile(tile, i + 1);
