@@ -86,7 +86,10 @@ typedef enum {
  * The paged KV pool (passed by host pointer; the arrays it points to are device memory).
  *
  *   PA_KV_F16 / PA_KV_BF16 : k, v   [num_blocks, num_kv_heads, 16, head_dim] 16-bit values
- *   PA_KV_FP8_E4M3 / _E5M2 : k, v   [num_blocks, num_kv_heads, 16, head_dim] uint8 codes
+ *   PA_KV_FP8_E4M3 / _E5M2 : k      [num_blocks, num_kv_heads, 16, head_dim] uint8 codes
+ *                            v      [num_blocks, num_kv_heads, 16 * head_dim] uint8 codes,
+ *                                   stored by channel: token t, channel ch of a (block,
+ *                                   kv head) run at byte PA_FP8_V_BYTE(t, ch, head_dim)
  *                            k_scale, v_scale [num_kv_heads] fp32 (inputs, read-only):
  *                            the stored value is code * scale (per layer and kv head;
  *                            see pa_fp8_head_scales). Both OCP FP8 formats are the pages'
@@ -99,7 +102,7 @@ typedef enum {
  *                               per-token fp32 scales of K and at PA_FP8T_VSCALE_OFF the
  *                               16 of V (together one whole 128-byte line);
  *                            v  [num_blocks, num_kv_heads, PA_FP8T_VTILE_BYTES(head_dim)]
- *                               bytes: the V codes [16 tokens][head_dim] only.
+ *                               bytes: the V codes only, by channel as above.
  *                            The scale of a token row is fp32(max |x| / 448) (E4M3) or
  *                            fp32(max |x| / 57344) (E5M2), set when the row is written:
  *                            quantization on the fly (dailyaiworld.com, "vLLM 0.7 Ships
@@ -141,6 +144,17 @@ typedef enum {
 #define PA_FP4_RECORD_OFF(head_dim) (8 * (head_dim) + 64)
 #define PA_FP4_SLOT0_OFF(head_dim) (8 * (head_dim) + 80)
 #define PA_FP4_TILE_BYTES(head_dim) ((8 * (head_dim) + 112 + 127) / 128 * 128)
+/* FP8 V code runs (both scale kinds) by channel: with nt = head_dim / 16, channel ch is
+ * channel j = ch % nt of group g = ch / nt. The run is head_dim / 64 pieces of 1024 bytes;
+ * piece j / 4 is 64 slots of 16 bytes, slot 16 (t / 4) + g holding channels j = 4 (j / 4)
+ * .. + 3 of group g for tokens 4 (t / 4) .. + 3, channel after channel, a channel's four
+ * token bytes side by side. One 16-byte slot is what one lane of the P.V product takes for
+ * its four keys, so a tile of V is loaded in whole lines with no byte shuffling. */
+#define PA_FP8_V_BYTE(t, ch, head_dim)                                                   \
+  ((((ch) % ((head_dim) / 16)) / 4) * 1024 +                                           \
+   (16 * ((t) / 4) + (ch) / ((head_dim) / 16)) * 16 + (((ch) % ((head_dim) / 16)) % 4) * 4 + \
+   (t) % 4)
+
 /* per-token-scaled FP8 runs: K codes, K token scales, V token scales (k array); V codes
  * (v array). Every run is a whole number of 128-byte lines with no padding. */
 #define PA_FP8T_SCALE_OFF(head_dim) (16 * (head_dim))

@@ -33,14 +33,17 @@ Readings where the pages are silent (each listed in the design notes):
     codes are E2M1(fp32(x / s_t)); outlier positions hold code +0; s_t = 0 gives +0 codes;
     two codes per byte, even channel in the low nibble; outliers are stored as fp16(x).
 
-Pool layout (the boundary's layout, row-major, one array per field):
-  f16 / bf16 : k, v          uint16 [NB, Hkv, 16, D]
-  fp8        : k, v          uint8  [NB, Hkv, 16, D]        (+ per-head fp32 scales)
+Pool layout (the boundary's layout, one array per field):
+  f16 / bf16 : k, v          uint16 [NB, Hkv, 16, D]        token rows
+  fp8, bf8   : k             uint8  [NB, Hkv, 16, D]        K codes, token rows
+               v             uint8  [NB, Hkv, 16, D]        V codes of a (block, head) by
+                                    channel in 16-byte slots, fp8_v_byte
+                                    (+ per-head fp32 scales)
   fp8t, bf8t : k             uint8  [NB, Hkv, 16 D + 128] one run per (block, head):
                  [0, 16 D)         K codes [16 tokens][D]
                  [16 D, 16 D + 64)  K per-token scales, fp32 [16]
                  [16 D + 64, 16 D + 128)  V per-token scales, fp32 [16]
-               v             uint8  [NB, Hkv, 16 D]       V codes [16 tokens][D]
+               v             uint8  [NB, Hkv, 16 D]       V codes by channel, fp8_v_byte
   fp4        : k, v          uint8  [NB, Hkv, TILE] one run of bytes per (block, head):
                  [0, 8 D)          codes [16 tokens][D/2], two per byte
                  [8 D, 8 D + 64)   per-token scales, fp32 [16]
@@ -148,10 +151,67 @@ def fp8t_run_bytes(head_dim: int, kv: str = "k") -> int:
 
 
 def fp8t_codes(pool: Pool, kv: str) -> np.ndarray:
-    """Codes of a per-token-scaled FP8 pool, a view [NB, Hkv, 16, D] uint8."""
+    """K codes of a per-token-scaled FP8 pool, a view [NB, Hkv, 16, D] uint8 (token rows;
+    V runs store their codes by channel, see fp8_v_byte)."""
+    assert kv == "k", "V codes are stored by channel: fp8_get_codes"
     d = pool.head_dim
     a = pool.arrays[kv]
     return a[..., :16 * d].reshape(a.shape[0], a.shape[1], 16, d)
+
+
+def fp8_v_byte(t, ch, d):
+    """Byte offset of token t (0..15), channel ch in the V code run of one (block, kv head)
+    of an FP8 pool (E4M3 or E5M2, head or token scales). With nt = d / 16, channel ch is
+    channel j = ch % nt of group g = ch // nt, and token t is token r = t % 4 of four
+    q = t // 4. The run is d / 64 pieces of 1024 bytes; piece j // 4 holds 64 slots of 16
+    bytes, slot 16 q + g holding channels 4 (j // 4) .. 4 (j // 4) + 3 of group g for the
+    four tokens of four q, channel after channel, a channel's four token bytes side by
+    side."""
+    nt = d // 16
+    g, j = ch // nt, ch % nt
+    return (j // 4) * 1024 + (16 * (t // 4) + g) * 16 + (j % 4) * 4 + t % 4
+
+
+def _fp8_v_offsets(d):
+    t = np.arange(16)[:, None]
+    ch = np.arange(d)[None, :]
+    return fp8_v_byte(t, ch, d)  # [16, d]
+
+
+def _fp8_runs(pool: Pool, kv: str) -> np.ndarray:
+    """[NB, Hkv, 16 D] view of the code bytes of an FP8 pool's K or V runs."""
+    a = pool.arrays[kv]
+    d = pool.head_dim
+    return a.reshape(a.shape[0], a.shape[1], -1)[..., :16 * d]
+
+
+def fp8_put_codes(pool: Pool, kv: str, blk, off, codes) -> None:
+    """Store code rows codes [n, Hkv, D] of tokens (blk[i], off[i]): K runs by token row,
+    V runs by channel (fp8_v_byte)."""
+    blk = np.asarray(blk, dtype=np.int64)
+    off = np.asarray(off, dtype=np.int64)
+    d = pool.head_dim
+    runs = _fp8_runs(pool, kv)
+    if kv == "k":
+        pos = off[:, None] * d + np.arange(d)[None, :]  # [n, d]
+    else:
+        pos = _fp8_v_offsets(d)[off]  # [n, d]
+    h = np.arange(pool.num_kv_heads)
+    runs[blk[:, None, None], h[None, :, None], pos[:, None, :]] = codes
+
+
+def fp8_get_codes(pool: Pool, kv: str, blk, off) -> np.ndarray:
+    """Code rows [n, Hkv, D] of tokens (blk[i], off[i]), the inverse of fp8_put_codes."""
+    blk = np.asarray(blk, dtype=np.int64)
+    off = np.asarray(off, dtype=np.int64)
+    d = pool.head_dim
+    runs = _fp8_runs(pool, kv)
+    if kv == "k":
+        pos = off[:, None] * d + np.arange(d)[None, :]
+    else:
+        pos = _fp8_v_offsets(d)[off]
+    h = np.arange(pool.num_kv_heads)
+    return runs[blk[:, None, None], h[None, :, None], pos[:, None, :]]
 
 
 def fp8t_scales(pool: Pool, kv: str) -> np.ndarray:
@@ -387,10 +447,8 @@ def cache_write(pool: Pool, k_rows, v_rows, act: str, slots, k_scale=None, v_sca
                 s = fp8_token_scale(x, fmt)[..., None]  # [n, Hkv, 1]
             q = f32_quotient(x, s)
             codes = fp8_encode(np.where(s == 0.0, 0.0, q), fmt)
-            if where == "head":
-                A[name][blk, :, off, :] = codes
-            else:
-                fp8t_codes(pool, name)[blk, :, off, :] = codes
+            fp8_put_codes(pool, name, blk, off, codes)
+            if where == "token":
                 fp8t_scales(pool, name)[blk, :, off] = s[..., 0].astype(np.float32)
         return
     if pool.kind == "fp4":
@@ -459,10 +517,9 @@ def dequant_slot_rows(pool: Pool, blk, off, k_scale=None, v_scale=None):
             fmt, where = FP8_KINDS[pool.kind]
             if where == "head":
                 s = np.asarray(sc, dtype=np.float32).astype(np.float64)[None, :, None]
-                out.append(fp8_decode(A[name][blk, :, off, :], fmt) * s)
             else:
                 s = fp8t_scales(pool, name)[blk, :, off].astype(np.float64)[..., None]
-                out.append(fp8_decode(fp8t_codes(pool, name)[blk, :, off, :], fmt) * s)
+            out.append(fp8_decode(fp8_get_codes(pool, name, blk, off), fmt) * s)
         elif pool.kind == "fp4":
             codes = fp4_get_codes(pool, name)[blk, :, off, :]  # [n, Hkv, D]
             n, hkv = codes.shape[:2]
@@ -499,6 +556,7 @@ __all__ = [
     "fp4_scales", "fp4_records", "fp4_slot0",
     "fp4_outlier_values",
     "FP8_KINDS", "fp8t_run_bytes", "fp8t_codes", "fp8t_scales", "fp8_token_scale",
+    "fp8_v_byte", "fp8_put_codes", "fp8_get_codes",
     "fp8_head_scale", "fp4_calibrate", "fp4_calibration_margin", "fp4_encode_row",
     "cache_write", "dequant_slot_rows", "gather_sequence", "f32_round",
 ]

@@ -29,11 +29,12 @@
 //   O^T += V^T P^T MFMA 16x16x16 per 16 output channels (rows = channels, k = tokens):
 //                 the probabilities are already in the B-operand layout (head c, tokens
 //                 4 kg..4 kg+3); lane (c, kg) loads channels [NT c, NT (c+1)) of tokens
-//                 4 kg..4 kg+3 and transposes them in registers (v_perm) so one register
-//                 pair holds one channel of four tokens. P enters as a hi + lo pair of
-//                 16-bit values (about 16 significant bits in bf16, 22 in fp16), so PV
-//                 loses nothing to 16-bit rounding of P. After the block loop lane (c, kg) holds head c's
-//                 output channels [D/4 kg, D/4 (kg+1)).
+//                 4 kg..4 kg+3 (8- and 4-bit runs store that chunk by channel; 16-bit
+//                 token rows are transposed in registers with v_perm) so one register pair
+//                 holds one channel of four tokens. P enters as a hi + lo pair of 16-bit
+//                 values (about 16 significant bits in bf16, 22 in fp16), so PV loses
+//                 nothing to 16-bit rounding of P. After the block loop lane (c, kg) holds
+//                 head c's output channels [D/4 kg, D/4 (kg+1)).
 #include <stdlib.h>
 
 #include <type_traits>
@@ -135,7 +136,11 @@ __device__ __forceinline__ void append_store(const DecodeArgs& a, const NewRow& 
       sc = vside ? a.v_scale[kvh] : a.k_scale[kvh];
     }
     const bool fast = __builtin_fabsf(sc) >= 0x1p-80f && __builtin_fabsf(sc) <= 0x1p100f;
-    *reinterpret_cast<uint4*>(tile + off * D + 16 * c) = fp8_encode16<QBF, E5>(r.lo, r.hi, sc, fast);
+    const uint4 codes = fp8_encode16<QBF, E5>(r.lo, r.hi, sc, fast);
+    if (vside)
+      f8_v_store16<D>(tile, off, c, codes);  // V runs are stored by channel
+    else
+      *reinterpret_cast<uint4*>(tile + off * D + 16 * c) = codes;
   }
 }
 
@@ -421,6 +426,8 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     if constexpr (KV == KV_FP4) {
       // one chunk: channels NT c .. NT c + NT - 1 of tokens 4 kg .. 4 kg + 3
       fp4_v_chunk<D, true>(T, vpool + T.tile * G_::TILEB, c, kg);
+    } else if constexpr (is_f8(KV)) {
+      f8_v_chunk<KV, D, true>(T, vpool + T.tile * G_::VTILEB, c, kg);  // the same chunk
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -480,7 +487,15 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a) {
     for (int r = 0; r < 4; ++r) valid[r] = FULL || (T.ok && (tok0 + r < end));
     // V bytes of tokens past the context are arbitrary: zeroed, as a NaN code times p = 0
     // would still be NaN (E2M1 has no NaN code)
-    if constexpr (!FULL && KV != KV_FP4) {
+    if constexpr (!FULL && is_f8(KV)) {  // byte r of every word is token 4 kg + r
+      const uint32_t keep = (valid[0] ? 0xFFu : 0u) | (valid[1] ? 0xFF00u : 0u) |
+                            (valid[2] ? 0xFF0000u : 0u) | (valid[3] ? 0xFF000000u : 0u);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int i = 0; i < G_::VW; ++i) T.v[r][i] &= keep;
+      }
+    } else if constexpr (!FULL && KV != KV_FP4) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
 #pragma unroll

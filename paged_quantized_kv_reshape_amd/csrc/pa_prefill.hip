@@ -171,6 +171,8 @@ void k_prefill_mt(DecodeArgs a) {
       T.r0 = *reinterpret_cast<const uint32_t*>((lane < 32 ? kt : vt) + PA_FP4_RECORD_OFF(D));
       T.k_o0 = reinterpret_cast<const uint2*>(kt + PA_FP4_SLOT0_OFF(D))[kg];
       T.v_o0 = reinterpret_cast<const uint2*>(vt + PA_FP4_SLOT0_OFF(D))[kg];
+    } else if constexpr (is_f8(KV)) {
+      f8_v_chunk<KV, D, false>(T, vpool + T.tile * G_::VTILEB, c, kg);  // stored by channel
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -216,11 +218,22 @@ void k_prefill_mt(DecodeArgs a) {
       // is still NaN): zeroed, with the wave's bound, which holds for every column (E2M1
       // has no NaN code, so FP4 codes need no zeroing)
       auto mask_v = [&](Tile<KV, D>& T) {
+        if constexpr (is_f8(KV)) {  // byte r of every word is token 4 kg + r
+          uint32_t keep = 0u;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool keep = T.ok && T.jb * kBlock + 4 * kg + r < end;
+          for (int r = 0; r < 4; ++r)
+            keep |= T.ok && T.jb * kBlock + 4 * kg + r < end ? 0xFFu << (8 * r) : 0u;
 #pragma unroll
-          for (int i = 0; i < G_::VW; ++i) T.v[r][i] = keep ? T.v[r][i] : 0u;
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < G_::VW; ++i) T.v[r][i] &= keep;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool keep = T.ok && T.jb * kBlock + 4 * kg + r < end;
+#pragma unroll
+            for (int i = 0; i < G_::VW; ++i) T.v[r][i] = keep ? T.v[r][i] : 0u;
+          }
         }
       };
       mask_v(TA);

@@ -5,8 +5,10 @@
 // Lane l of a wave (c = l % 16, kg = l / 16) holds, of a 16-token block:
 //   K  token c's channels [D/4 kg, D/4 (kg + 1)) - the A operand of S^T = K Q^T, one
 //      16x16x32 MFMA per 32 channels (k_fragment);
-//   V  tokens 4 kg .. 4 kg + 3 of channels NT c .. NT c + NT - 1 - after an in-register
-//      transpose, the A operand of O^T += V^T P^T (v_fragments).
+//   V  tokens 4 kg .. 4 kg + 3 of channels NT c .. NT c + NT - 1 - the A operand of
+//      O^T += V^T P^T (v_fragments). 4- and 8-bit V runs store those values by channel (a
+//      channel's four tokens together), in the order the lanes load them; 16-bit V runs
+//      store token rows, transposed in registers.
 #pragma once
 
 #include "../../include/pa.h"
@@ -104,7 +106,8 @@ template <int KV, int D>
 struct Tile {
   using G_ = Geo<KV, D>;
   uint32_t k[G_::KW];
-  uint32_t v[4][G_::VW];  // token rows 4 kg .. 4 kg + 3 (FP4: words of one channel chunk)
+  uint32_t v[4][G_::VW];  // 16-bit: token rows 4 kg .. 4 kg + 3; 8- and 4-bit: the words
+                          // of the lane's channel chunk, in order (v[w / VW][w % VW])
   float4 sk, sv;  // FP4 per-token scales of tokens 4 kg .. 4 kg + 3
   uint32_t r0;    // FP4: first word of the K (lanes 0-31) and V (lanes 32-63) records
   uint2 k_o0, v_o0;  // FP4 outlier slot 0 of tokens 4 kg .. 4 kg + 3 (fp16), fetched with
@@ -126,6 +129,43 @@ __device__ __forceinline__ void fp4_v_chunk(Tile<KV_FP4, D>& T, const uint8_t* t
   load_words<W, NT_HINT>(x, tile + (c * 4 + kg) * (4 * W));
 #pragma unroll
   for (int w = 0; w < W; ++w) T.v[w][0] = x[w];
+}
+
+// FP8 V runs (every 8-bit format) are stored by channel, in the order the lanes read them:
+// with NT = D / 16, lane (c, kg) needs channels NT c .. NT c + NT - 1 of tokens
+// 4 kg .. 4 kg + 3, a 32-bit word per channel (its four token bytes). Those NT words are
+// D / 64 pieces of 4 words; piece p of every lane forms 1024 bytes at p * 1024, lane
+// l = 16 kg + c at 16 l. So each 16-byte load instruction of the wave reads 1024
+// contiguous bytes, whole cache lines (a chunk per lane read in two pieces 16 bytes apart
+// would touch every line of the run twice, and the streaming hint can evict a line
+// between the two). Token t, channel ch: (j / 4) * 1024 + (16 (t / 4) + ch / NT) * 16 +
+// (j % 4) * 4 + t % 4, j = ch % NT. Word w of the lane's channels goes to
+// T.v[w / VW][w % VW].
+template <int KV, int D, bool NT_HINT>
+__device__ __forceinline__ void f8_v_chunk(Tile<KV, D>& T, const uint8_t* run, int c, int kg) {
+  constexpr int NT = D / 16, VW = Geo<KV, D>::VW;
+  static_assert(4 * VW == NT && NT % 4 == 0, "a lane's pieces fill the tile's V words");
+  const uint8_t* at = run + 16u * (16u * (uint32_t)kg + (uint32_t)c);
+#pragma unroll
+  for (int p = 0; p < NT / 4; ++p) {
+    uint32_t x[4];
+    load_words<4, NT_HINT>(x, at + 1024 * p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) T.v[(4 * p + i) / VW][(4 * p + i) % VW] = x[i];
+  }
+}
+// Store the 16 codes of channels 16 j .. 16 j + 15 of token t (byte e of `codes` is channel
+// 16 j + e) into an FP8 V run: one byte per channel.
+template <int D>
+__device__ __forceinline__ void f8_v_store16(uint8_t* run, int t, int j, const uint4& codes) {
+  constexpr int NT = D / 16;
+  const uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int ch = 16 * j + e, g = ch / NT, jj = ch % NT;
+    run[(jj / 4) * 1024 + (16 * (t / 4) + g) * 16 + (jj % 4) * 4 + t % 4] =
+        (uint8_t)(w[e >> 2] >> ((e & 3) * 8));
+  }
 }
 
 // 16-bit K fragment for step t: 8 values of channels D/4 kg + 8 t + (0..7).
@@ -177,62 +217,16 @@ __device__ __forceinline__ void v_fragments(const Tile<KV, D>& T, uint2 (&vf)[Ge
       vf[2 * i + 1].y = __builtin_amdgcn_perm(pairs[3][i], pairs[2][i], 0x07060302u);
     }
   } else {
-    // FP8: 4x4 byte transposes, then one conversion per token pair.
+    // FP8: the lane's chunk holds channel NT c + n of its four tokens in word n; one
+    // conversion per token pair
 #pragma unroll
-    for (int wi = 0; wi < Geo<KV, D>::VW; ++wi) {
-      const uint32_t x0 = T.v[0][wi], x1 = T.v[1][wi], x2 = T.v[2][wi], x3 = T.v[3][wi];
-      const uint32_t u0 = __builtin_amdgcn_perm(x1, x0, 0x05010400u);  // x0b0 x1b0 x0b1 x1b1
-      const uint32_t u1 = __builtin_amdgcn_perm(x1, x0, 0x07030602u);  // x0b2 x1b2 x0b3 x1b3
-      const uint32_t w0 = __builtin_amdgcn_perm(x3, x2, 0x05010400u);
-      const uint32_t w1 = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
-      const uint32_t t[4] = {
-          __builtin_amdgcn_perm(w0, u0, 0x05040100u),  // channel 0 of tokens 0..3
-          __builtin_amdgcn_perm(w0, u0, 0x07060302u),  // channel 1
-          __builtin_amdgcn_perm(w1, u1, 0x05040100u),  // channel 2
-          __builtin_amdgcn_perm(w1, u1, 0x07060302u)}; // channel 3
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        vf[4 * wi + c].x = cvt_fp8x2<PVB, 0, f8_e5(KV)>(t[c]);
-        vf[4 * wi + c].y = cvt_fp8x2<PVB, 1, f8_e5(KV)>(t[c]);
-      }
+    for (int n = 0; n < NT; ++n) {
+      const uint32_t w = T.v[n / Geo<KV, D>::VW][n % Geo<KV, D>::VW];
+      vf[n].x = cvt_fp8x2<PVB, 0, f8_e5(KV)>(w);
+      vf[n].y = cvt_fp8x2<PVB, 1, f8_e5(KV)>(w);
     }
   }
 }
-
-
-
-// V^T fragments of one channel group, for kernels that consume V a group at a time:
-// group g of a 16-bit tile gives vf[j] = v_fragments' vf[2 g + j] (j < 2), of an FP8 tile
-// vf[j] = vf[4 g + j] (j < 4). kVGroup is the group size.
-template <int KV>
-constexpr int kVGroup = is_f8(KV) ? 4 : 2;
-template <int KV, int D, bool PVB, int GI>
-__device__ __forceinline__ void v_fragments_group(const Tile<KV, D>& T, uint2 (&vf)[kVGroup<KV>]) {
-  static_assert(KV != KV_FP4, "FP4 V fragments come from channel chunks");
-  if constexpr (KV == KV_F16 || KV == KV_BF16) {
-    const uint32_t p0 = T.v[0][GI], p1 = T.v[1][GI], p2 = T.v[2][GI], p3 = T.v[3][GI];
-    vf[0].x = __builtin_amdgcn_perm(p1, p0, 0x05040100u);
-    vf[0].y = __builtin_amdgcn_perm(p3, p2, 0x05040100u);
-    vf[1].x = __builtin_amdgcn_perm(p1, p0, 0x07060302u);
-    vf[1].y = __builtin_amdgcn_perm(p3, p2, 0x07060302u);
-  } else {
-    const uint32_t x0 = T.v[0][GI], x1 = T.v[1][GI], x2 = T.v[2][GI], x3 = T.v[3][GI];
-    const uint32_t u0 = __builtin_amdgcn_perm(x1, x0, 0x05010400u);
-    const uint32_t u1 = __builtin_amdgcn_perm(x1, x0, 0x07030602u);
-    const uint32_t w0 = __builtin_amdgcn_perm(x3, x2, 0x05010400u);
-    const uint32_t w1 = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
-    const uint32_t t[4] = {__builtin_amdgcn_perm(w0, u0, 0x05040100u),
-                           __builtin_amdgcn_perm(w0, u0, 0x07060302u),
-                           __builtin_amdgcn_perm(w1, u1, 0x05040100u),
-                           __builtin_amdgcn_perm(w1, u1, 0x07060302u)};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      vf[c].x = cvt_fp8x2<PVB, 0, f8_e5(KV)>(t[c]);
-      vf[c].y = cvt_fp8x2<PVB, 1, f8_e5(KV)>(t[c]);
-    }
-  }
-}
-
 
 // acc[n][r] += x for the entry e = NT r + n (wave-uniform) of a lane's output channels
 // (channel DL kg + NT r + n of the lane's column, DL = 4 NT). The accumulators are viewed as

@@ -8,12 +8,15 @@
 // Unified KV Cache Compression", "Technical Breakdown: Dynamic Quantization with Outlier
 // Retention", steps 1-3).
 //
-// Pool tile of (block, kv head): 16 token rows, row-major, so one token's row is one
-// contiguous run of head_dim values (head_dim / 2 bytes for FP4).
+// Pool tile of (block, kv head): K in 16 token rows, row-major, so one token's row is one
+// contiguous run of head_dim values (head_dim / 2 bytes for FP4); 16-bit V likewise, FP8
+// and FP4 V codes by channel (a channel's codes for consecutive tokens together, the order
+// the P.V product takes them).
 #include "pa_device.h"
 #include "pa_encode.h"
 #include "pa_fp4.h"
 #include "pa_launch.h"
+#include "pa_tile.h"
 
 namespace pa {
 
@@ -23,9 +26,10 @@ __device__ __forceinline__ void flag(int32_t* err, int32_t bit) {
 
 // ---------------------------------------------------------------------------------
 // 16-bit copy and FP8: one thread per 16-byte input chunk (copy) or per 16 values (FP8)
-// of a (token, head) row; consecutive threads walk chunk, then head, then token, so a
-// workgroup reads whole token rows. CH = threads per (token, head) row, a power of two.
-// The launcher keeps T * Hkv * CH below 2^31, so the index math is 32-bit.
+// of a (token, head) row - of four rows for FP8; consecutive threads walk chunk, then head,
+// then token, so a workgroup reads whole token rows. CH = threads per (token, head) row, a
+// power of two. The launcher keeps the thread count below 2^31, so the index math is
+// 32-bit.
 // ---------------------------------------------------------------------------------
 template <int CH>
 __device__ __forceinline__ bool row_chunk(int32_t T, int32_t hkv, const int64_t* __restrict__ slots,
@@ -64,85 +68,144 @@ __global__ __launch_bounds__(256) void k_write_copy(const uint4* __restrict__ k_
   v_pool[dst] = v_new[src];
 }
 
-template <bool BF16, int CH, bool E5>
+// FP8 (head or token scales). A V run is stored by channel (a channel's codes for four
+// tokens share a word, see f8_v_chunk), so the rows of a call that land in four aligned
+// slots 4 q .. 4 q + 3 of one block in order - a prefill chunk's rows do - are written
+// together: whole 16-byte V slots (four channels of the four tokens) and their four K rows.
+// Any other row is written alone, its V codes byte by byte.
+//   One thread per 16 values (chunk c of CH) of a head over a window of four rows
+// 4 f .. 4 f + 3; consecutive threads walk chunk, then head, then window. The thread writes
+// the four that starts in its window, if any (it may reach three rows past the window),
+// and every other row of the window that no four covers. At most one four starts within
+// any four rows, so each row is written once.
+//   Token scales (TOK): a row's scale is fp32(max |x| / M) (M = 448 or 57344), reduced over
+// its CH threads (consecutive lanes of one wave: CH divides 64, every (head, window) starts
+// on a multiple of CH, and a group's lanes branch alike); both scales go to the K run.
+template <bool BF16, int CH, bool E5, bool TOK>
 __global__ __launch_bounds__(256) void k_write_fp8(const uint4* __restrict__ k_new,
                                                    const uint4* __restrict__ v_new,
-                                                   uint4* __restrict__ k_pool,
-                                                   uint4* __restrict__ v_pool,
+                                                   uint8_t* __restrict__ k_pool,
+                                                   uint8_t* __restrict__ v_pool,
                                                    const float* __restrict__ k_scale,
                                                    const float* __restrict__ v_scale,
                                                    const int64_t* __restrict__ slots,
                                                    int32_t T, int32_t hkv, int64_t nslots,
                                                    int32_t* err) {
-  int64_t src, dst;  // in 16-value chunks
-  int h;
-  if (!row_chunk<CH>(T, hkv, slots, nslots, err, src, dst, h)) return;
-  const float sk = k_scale[h], sv = v_scale[h];
-  const bool fk = __builtin_fabsf(sk) >= 0x1p-80f && __builtin_fabsf(sk) <= 0x1p100f;
-  const bool fv = __builtin_fabsf(sv) >= 0x1p-80f && __builtin_fabsf(sv) <= 0x1p100f;
-  const uint4 k0 = k_new[2 * src], k1 = k_new[2 * src + 1];
-  const uint4 v0 = v_new[2 * src], v1 = v_new[2 * src + 1];
-  k_pool[dst] = fp8_encode16<BF16, E5>(k0, k1, sk, fk);
-  v_pool[dst] = fp8_encode16<BF16, E5>(v0, v1, sv, fv);
-}
-
-// Per-token-scaled FP8: the row's scale is fp32(max |x| / M) (M = 448 or 57344), computed
-// here by the row's CH threads (consecutive lanes of one wave: CH divides 64 and every row
-// starts on a multiple of CH), then the codes as above; the run holds the 16 code rows and
-// then the 16 scales.
-template <bool BF16, int CH, bool E5>
-__global__ __launch_bounds__(256) void k_write_fp8_tok(const uint4* __restrict__ k_new,
-                                                       const uint4* __restrict__ v_new,
-                                                       uint8_t* __restrict__ k_pool,
-                                                       uint8_t* __restrict__ v_pool,
-                                                       const int64_t* __restrict__ slots,
-                                                       int32_t T, int32_t hkv, int64_t nslots,
-                                                       int32_t* err) {
-  constexpr int D = CH * 16;
-  constexpr int64_t TB = PA_FP8T_TILE_BYTES(D), VTB = PA_FP8T_VTILE_BYTES(D);
+  constexpr int D = CH * 16, NT = D / 16;
+  constexpr int64_t TB = TOK ? PA_FP8T_TILE_BYTES(D) : 16 * D;
+  constexpr int64_t VTB = TOK ? PA_FP8T_VTILE_BYTES(D) : 16 * D;
   constexpr float FMAX = E5 ? 57344.0f : 448.0f;
   const uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x;
-  const uint32_t per_tok = (uint32_t)hkv * CH;
-  const uint32_t i = idx / per_tok;
-  const uint32_t rem = idx - i * per_tok;
+  const uint32_t per_win = (uint32_t)hkv * CH;
+  const uint32_t f = idx / per_win;
+  const uint32_t rem = idx - f * per_win;
   const int c = (int)(rem & (CH - 1));
   const int h = (int)(rem / CH);
-  if (i >= (uint32_t)T) return;  // (a whole row's lanes leave together)
-  const int64_t slot = slots[i];
-  if (slot < 0) return;
-  if (slot >= nslots) {
-    if (c == 0) flag(err, PA_DEVERR_BAD_SLOT);
-    return;
-  }
-  const int64_t src = ((int64_t)i * hkv + h) * CH + c;
-  const uint4 k0 = k_new[2 * src], k1 = k_new[2 * src + 1];
-  const uint4 v0 = v_new[2 * src], v1 = v_new[2 * src + 1];
-  auto absmax16 = [](const uint4 a, const uint4 b) {
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    float m = 0.0f;
+  const int64_t i0 = 4 * (int64_t)f;
+  if (i0 >= T) return;  // (a whole (head, window)'s lanes leave together)
+  // slots of rows i0 - 3 .. i0 + 6 (-1 outside the call)
+  int64_t sl[10];
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-      m = fmaxf(m, __builtin_fabsf(act_to_f32<BF16>((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu)));
-    return m;
+  for (int k = 0; k < 10; ++k) {
+    const int64_t i = i0 - 3 + k;
+    sl[k] = i >= 0 && i < T ? slots[i] : -1;
+  }
+  auto four_at = [&](int k) {  // rows i0 - 3 + k .. + 3 fill an aligned four in order
+    return sl[k] >= 0 && (sl[k] & 3) == 0 && sl[k] + 3 < nslots && sl[k + 1] == sl[k] + 1 &&
+           sl[k + 2] == sl[k] + 2 && sl[k + 3] == sl[k] + 3;
   };
-  float mk = absmax16(k0, k1), mv = absmax16(v0, v1);
+  int lo = 3;  // window rows before lo are covered by a four that starts before the window
 #pragma unroll
-  for (int o = CH / 2; o >= 1; o >>= 1) {
-    mk = fmaxf(mk, __shfl_xor(mk, o));
-    mv = fmaxf(mv, __shfl_xor(mv, o));
+  for (int k = 0; k < 3; ++k)
+    if (four_at(k)) lo = k + 4;
+  int mine = 7;  // the four that starts in the window, 7 for none
+#pragma unroll
+  for (int k = 6; k >= 3; --k)
+    if (k >= lo && four_at(k)) mine = k;
+
+  auto scale_of = [&](const uint4 a, const uint4 b, const float* hs) {
+    if constexpr (TOK) {
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        m = fmaxf(m, __builtin_fabsf(act_to_f32<BF16>((w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu)));
+#pragma unroll
+      for (int o = CH / 2; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      return m / FMAX;
+    } else {
+      return hs[h];
+    }
+  };
+  auto finite = [](float x) {
+    return __builtin_fabsf(x) >= 0x1p-80f && __builtin_fabsf(x) <= 0x1p100f;
+  };
+
+  // rows of the window that no four covers, one by one
+  for (int k = lo; k < mine && k < 7; ++k) {
+    const int64_t slot = sl[k];
+    if (slot < 0) continue;  // (also past the end of the call)
+    if (slot >= nslots) {
+      if (c == 0) flag(err, PA_DEVERR_BAD_SLOT);
+      continue;
+    }
+    const int64_t src = ((i0 - 3 + k) * hkv + h) * CH + c;
+    const uint4 k0 = k_new[2 * src], k1 = k_new[2 * src + 1];
+    const uint4 v0 = v_new[2 * src], v1 = v_new[2 * src + 1];
+    const float sk = scale_of(k0, k1, k_scale), sv = scale_of(v0, v1, v_scale);
+    const int64_t bh = (slot >> 4) * hkv + h;
+    const int off = (int)(slot & 15);
+    uint8_t* const krun = k_pool + bh * TB;
+    *reinterpret_cast<uint4*>(krun + off * D + 16 * c) =
+        fp8_encode16<BF16, E5>(k0, k1, sk, finite(sk));
+    f8_v_store16<D>(v_pool + bh * VTB, off, c, fp8_encode16<BF16, E5>(v0, v1, sv, finite(sv)));
+    if (TOK && c == 0) {
+      reinterpret_cast<float*>(krun + PA_FP8T_SCALE_OFF(D))[off] = sk;
+      reinterpret_cast<float*>(krun + PA_FP8T_VSCALE_OFF(D))[off] = sv;
+    }
   }
-  const float sk = mk / FMAX, sv = mv / FMAX;
-  const bool fk = sk >= 0x1p-80f && sk <= 0x1p100f;
-  const bool fv = sv >= 0x1p-80f && sv <= 0x1p100f;
-  const int64_t bh = (slot >> 4) * hkv + h;
-  const int off = (int)(slot & 15);
+  if (mine == 7) return;
+
+  // the four rows i0 - 3 + mine .. + 3 into slots s .. s + 3 of one block
+  const int64_t s = sl[mine];
+  const int64_t bh = (s >> 4) * hkv + h;
+  const int off0 = (int)(s & 15);
   uint8_t* const krun = k_pool + bh * TB;
-  *reinterpret_cast<uint4*>(krun + off * D + 16 * c) = fp8_encode16<BF16, E5>(k0, k1, sk, fk);
-  *reinterpret_cast<uint4*>(v_pool + bh * VTB + off * D + 16 * c) =
-      fp8_encode16<BF16, E5>(v0, v1, sv, fv);
-  if (c == 0) {  // both token scales go to the K run
-    reinterpret_cast<float*>(krun + PA_FP8T_SCALE_OFF(D))[off] = sk;
-    reinterpret_cast<float*>(krun + PA_FP8T_VSCALE_OFF(D))[off] = sv;
+  uint8_t* const vrun = v_pool + bh * VTB;
+  uint32_t w[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t src = ((i0 - 3 + mine + r) * hkv + h) * CH + c;
+    const uint4 k0 = k_new[2 * src], k1 = k_new[2 * src + 1];
+    const uint4 v0 = v_new[2 * src], v1 = v_new[2 * src + 1];
+    const float sk = scale_of(k0, k1, k_scale), sv = scale_of(v0, v1, v_scale);
+    *reinterpret_cast<uint4*>(krun + (off0 + r) * D + 16 * c) =
+        fp8_encode16<BF16, E5>(k0, k1, sk, finite(sk));
+    const uint4 vc = fp8_encode16<BF16, E5>(v0, v1, sv, finite(sv));
+    w[r][0] = vc.x;
+    w[r][1] = vc.y;
+    w[r][2] = vc.z;
+    w[r][3] = vc.w;
+    if (TOK && c == 0) {
+      reinterpret_cast<float*>(krun + PA_FP8T_SCALE_OFF(D))[off0 + r] = sk;
+      reinterpret_cast<float*>(krun + PA_FP8T_VSCALE_OFF(D))[off0 + r] = sv;
+    }
+  }
+  // V slot i of the chunk: channels 16 c + 4 i .. + 3 of the four tokens, a channel's four
+  // token bytes to a word - a 4 x 4 byte transpose of word i of the four rows' codes
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x0 = w[0][i], x1 = w[1][i], x2 = w[2][i], x3 = w[3][i];
+    const uint32_t u0 = __builtin_amdgcn_perm(x1, x0, 0x05010400u);  // x0b0 x1b0 x0b1 x1b1
+    const uint32_t u1 = __builtin_amdgcn_perm(x1, x0, 0x07030602u);  // x0b2 x1b2 x0b3 x1b3
+    const uint32_t y0 = __builtin_amdgcn_perm(x3, x2, 0x05010400u);
+    const uint32_t y1 = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
+    const uint4 slot16 = make_uint4(__builtin_amdgcn_perm(y0, u0, 0x05040100u),
+                                    __builtin_amdgcn_perm(y0, u0, 0x07060302u),
+                                    __builtin_amdgcn_perm(y1, u1, 0x05040100u),
+                                    __builtin_amdgcn_perm(y1, u1, 0x07060302u));
+    const int ch = 16 * c + 4 * i, g = ch / NT, jj = ch % NT;
+    *reinterpret_cast<uint4*>(vrun + (jj / 4) * 1024 + (16 * (off0 / 4) + g) * 16) = slot16;
   }
 }
 
@@ -499,40 +562,38 @@ int launch_write(const pa_kv_pool& p, const void* k_new, const void* v_new, bool
     const bool fp8 = p.dtype != PA_KV_F16 && p.dtype != PA_KV_BF16;
     const bool e5 = p.dtype == PA_KV_FP8_E5M2 || p.dtype == PA_KV_FP8_E5M2_TOKEN;
     const bool tok = p.dtype == PA_KV_FP8_E4M3_TOKEN || p.dtype == PA_KV_FP8_E5M2_TOKEN;
-    // threads per (token, head) row: 16-byte chunks of the copy, 16 values for FP8
+    // threads per (token, head) row: 16-byte chunks of the copy, 16 values for FP8 (whose
+    // threads take a window of four rows)
     const int ch = fp8 ? D / 16 : D * 2 / 16;
     const int64_t per_tok = (int64_t)hkv * ch;
     const int64_t row_u4 = (int64_t)hkv * D * 2 / 16;  // one input token row in 16 B units
-    const int64_t max_tok = ((int64_t)1 << 31) / per_tok;
+    const int64_t max_tok = (((int64_t)1 << 31) / per_tok) & ~(int64_t)3;
     for (int64_t t0 = 0; t0 < T; t0 += max_tok) {
       const int32_t n = (int32_t)(T - t0 < max_tok ? T - t0 : max_tok);
       const uint4* kn = (const uint4*)k_new + t0 * row_u4;
       const uint4* vn = (const uint4*)v_new + t0 * row_u4;
-      const dim3 g(grid1((int64_t)n * per_tok, 256));
       if (!fp8) {
+        const dim3 g(grid1((int64_t)n * per_tok, 256));
         auto kern = D == 128 ? k_write_copy<16> : k_write_copy<8>;
         hipLaunchKernelGGL(kern, g, dim3(256), 0, st, kn, vn, (uint4*)p.k, (uint4*)p.v,
                            slots + t0, n, hkv, nslots, err);
-      } else if (tok) {
-        // kernel table: [bf16][D == 128][e5]
-        void (*const tab[2][2][2])(const uint4*, const uint4*, uint8_t*, uint8_t*,
-                                   const int64_t*, int32_t, int32_t, int64_t, int32_t*) = {
-            {{k_write_fp8_tok<false, 4, false>, k_write_fp8_tok<false, 4, true>},
-             {k_write_fp8_tok<false, 8, false>, k_write_fp8_tok<false, 8, true>}},
-            {{k_write_fp8_tok<true, 4, false>, k_write_fp8_tok<true, 4, true>},
-             {k_write_fp8_tok<true, 8, false>, k_write_fp8_tok<true, 8, true>}}};
-        hipLaunchKernelGGL(tab[bf16][D == 128][e5], g, dim3(256), 0, st, kn, vn,
-                           (uint8_t*)p.k, (uint8_t*)p.v, slots + t0, n, hkv, nslots, err);
       } else {
-        void (*const tab[2][2][2])(const uint4*, const uint4*, uint4*, uint4*, const float*,
-                                   const float*, const int64_t*, int32_t, int32_t, int64_t,
-                                   int32_t*) = {
-            {{k_write_fp8<false, 4, false>, k_write_fp8<false, 4, true>},
-             {k_write_fp8<false, 8, false>, k_write_fp8<false, 8, true>}},
-            {{k_write_fp8<true, 4, false>, k_write_fp8<true, 4, true>},
-             {k_write_fp8<true, 8, false>, k_write_fp8<true, 8, true>}}};
-        hipLaunchKernelGGL(tab[bf16][D == 128][e5], g, dim3(256), 0, st, kn, vn, (uint4*)p.k,
-                           (uint4*)p.v, p.k_scale, p.v_scale, slots + t0, n, hkv, nslots, err);
+        const dim3 g(grid1((((int64_t)n + 3) / 4) * per_tok, 256));
+        // kernel table: [token scales][bf16][D == 128][e5]
+        void (*const tab[2][2][2][2])(const uint4*, const uint4*, uint8_t*, uint8_t*,
+                                      const float*, const float*, const int64_t*, int32_t,
+                                      int32_t, int64_t, int32_t*) = {
+            {{{k_write_fp8<false, 4, false, false>, k_write_fp8<false, 4, true, false>},
+              {k_write_fp8<false, 8, false, false>, k_write_fp8<false, 8, true, false>}},
+             {{k_write_fp8<true, 4, false, false>, k_write_fp8<true, 4, true, false>},
+              {k_write_fp8<true, 8, false, false>, k_write_fp8<true, 8, true, false>}}},
+            {{{k_write_fp8<false, 4, false, true>, k_write_fp8<false, 4, true, true>},
+              {k_write_fp8<false, 8, false, true>, k_write_fp8<false, 8, true, true>}},
+             {{k_write_fp8<true, 4, false, true>, k_write_fp8<true, 4, true, true>},
+              {k_write_fp8<true, 8, false, true>, k_write_fp8<true, 8, true, true>}}}};
+        hipLaunchKernelGGL(tab[tok][bf16][D == 128][e5], g, dim3(256), 0, st, kn, vn,
+                           (uint8_t*)p.k, (uint8_t*)p.v, p.k_scale, p.v_scale, slots + t0, n,
+                           hkv, nslots, err);
       }
     }
   } else {

@@ -336,3 +336,61 @@ def test_fp8_head_scale_e5m2_invariant():
         if np.abs(xv[:, h]).max() == np.abs(F.f16_decode(x)[:, h]).max():
             j = np.unravel_index(np.argmax(np.abs(xv[:, h])), xv[:, h].shape)
             assert int(pool.arrays["k"][1, h, j[0], j[1]]) & 0x7F == 0x7B
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_v_run_layout_by_channel(d):
+    """FP8 V runs hold their codes by channel, in 16-byte slots (piece, token four, channel
+    group): the byte order, written out as nested loops, equals fp8_v_byte; it is a
+    permutation of the run; and writing rows then reading them back gives the rows."""
+    nt = d // 16
+    want = np.empty((16, d), dtype=np.int64)
+    pos = 0
+    for piece in range(nt // 4):
+        for q in range(4):
+            for g in range(16):
+                for jj in range(4):
+                    for r in range(4):
+                        want[4 * q + r, nt * g + 4 * piece + jj] = pos
+                        pos += 1
+    got = C.fp8_v_byte(np.arange(16)[:, None], np.arange(d)[None, :], d)
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.sort(got.ravel()), np.arange(16 * d))
+    rng = np.random.default_rng(7)
+    for kind in ("fp8", "fp8t"):
+        pool = C.Pool.filled(kind, 3, 2, d)
+        blk = np.array([2, 0, 2, 1])
+        off = np.array([5, 15, 0, 7])
+        rows = rng.integers(0, 256, (4, 2, d), dtype=np.uint8)
+        C.fp8_put_codes(pool, "v", blk, off, rows)
+        assert np.array_equal(C.fp8_get_codes(pool, "v", blk, off), rows)
+        run = pool.arrays["v"].reshape(3, 2, -1)
+        assert run[2, 1, C.fp8_v_byte(5, d - 1, d)] == rows[0, 1, d - 1]
+        # the K run keeps token rows
+        C.fp8_put_codes(pool, "k", blk, off, rows)
+        krun = pool.arrays["k"].reshape(3, 2, -1)
+        assert np.array_equal(krun[0, 1, 15 * d:16 * d], rows[1, 1])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_header_fp8_v_byte_macro_matches_oracle(d, tmp_path):
+    """The public header's PA_FP8_V_BYTE, compiled with the host C compiler, gives the
+    oracle's byte offset for every (token, channel) of a run."""
+    import os
+    import shutil
+    import subprocess
+    from conftest import ROOT
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    src = tmp_path / "v.c"
+    src.write_text('#include <stdio.h>\n#include "pa.h"\nint main(void) {\n'
+                   f'  for (int t = 0; t < 16; ++t) for (int c = 0; c < {d}; ++c)\n'
+                   f'    printf("%d\\n", PA_FP8_V_BYTE(t, c, {d}));\n  return 0;\n}}\n')
+    exe = tmp_path / "v"
+    subprocess.run([cc, "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    got = np.array(out.split(), dtype=np.int64).reshape(16, d)
+    want = C.fp8_v_byte(np.arange(16)[:, None], np.arange(d)[None, :], d)
+    assert np.array_equal(got, want)
