@@ -236,3 +236,74 @@ def test_write_every_input(fmt_kind, act, d):
         mant_only = ((codes & 0x7F) != 0) & ((codes & (0x78 if fmt_kind == "fp8t" else 0x7C)) == 0)
         assert mant_only.sum() > 100
     assert_pool_equal(pool.numpy(), opool)
+
+
+@pytest.mark.parametrize("fmt_kind", ["fp8", "bf8", "fp8t", "bf8t"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_write_slot_patterns(fmt_kind, d):
+    """The FP8 write stores four rows that land in an aligned four of slots (4 q .. 4 q + 3
+    of one block, in order) together and every other row alone. Runs that start at any row
+    and any offset, runs broken by a skipped (-1) or out-of-range slot, a four that ends at
+    the call's last row and scattered single rows must all match the oracle bit for bit;
+    the out-of-range slots are flagged and write nothing."""
+    from oracle import cache as C
+    from paged_quantized_kv_reshape_amd import KVPool, pa_cache_write
+    rng = np.random.default_rng(11 + d)
+    nb, hkv = 24, 2
+    nslots = nb * 16
+    blocks = [int(b) for b in rng.permutation(nb)]
+    slots = []
+
+    def run(b, off, n):
+        slots.extend(blocks[b] * 16 + off + j for j in range(n))
+
+    def at_row(r):  # skipped rows until the next row is r mod 4
+        while len(slots) % 4 != r:
+            slots.append(-1)
+
+    at_row(1)
+    run(0, 0, 16)                            # a whole block: four aligned fours
+    run(1, 2, 5)                             # offsets 2 .. 6: the four 4 .. 7 cut short
+    at_row(0)
+    run(2, 4, 8)                             # two aligned fours
+    slots.append(nslots + 5)                 # out of range
+    run(3, 0, 3)
+    slots.append(-1)                         # a four broken by a skipped row
+    at_row(2)
+    run(3, 4, 4)                             # an aligned four
+    run(4, 1, 4)                             # offsets 1 .. 4: no aligned four
+    run(5, 0, 2)
+    slots.append(nslots + 40)                # a four broken by an out-of-range slot
+    run(5, 3, 1)
+    singles = [blocks[b] * 16 + int(o) for b in range(10, 20) for o in rng.permutation(16)[:3]]
+    slots.extend(int(x) for x in rng.permutation(singles))
+    at_row(3)
+    run(6, 8, 4)                             # the last four rows: an aligned four
+    T = len(slots)
+    assert T % 4 != 0
+    slots = np.asarray(slots, dtype=np.int64)
+    live = slots[(slots >= 0) & (slots < nslots)]
+    assert len(np.unique(live)) == len(live)
+
+    x = (rng.standard_normal((2, T, hkv, d)) * 3.0).astype(np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    bits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)  # bf16, nearest even
+    k_rows, v_rows = bits[0], bits[1]
+    ks_np = vs_np = None
+    ks = vs = None
+    if fmt_kind in ("fp8", "bf8"):
+        ks_np = np.asarray([0.011, 0.023], dtype=np.float32)
+        vs_np = np.asarray([0.017, 0.009], dtype=np.float32)
+        ks, vs = torch.from_numpy(ks_np).cuda(), torch.from_numpy(vs_np).cuda()
+    opool = C.Pool.filled(fmt_kind, nb, hkv, d)
+    C.cache_write(opool, k_rows, v_rows, "bf16", np.where(slots < nslots, slots, -1),
+                  k_scale=ks_np, v_scale=vs_np)
+    pool = KVPool(fmt_kind, nb, hkv, d, fill=0xA5, k_scale=ks, v_scale=vs)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kt = torch.from_numpy(k_rows.view(np.int16)).cuda().view(torch.bfloat16)
+    vt = torch.from_numpy(v_rows.view(np.int16)).cuda().view(torch.bfloat16)
+    _say(f"[slot patterns] kv={fmt_kind} d={d} T={T}")
+    pa_cache_write(pool, kt, vt, torch.from_numpy(slots).cuda(), err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 2  # PA_DEVERR_BAD_SLOT
+    assert_pool_equal(pool.numpy(), opool)
