@@ -77,7 +77,8 @@ typedef enum {
   PA_ERR_SCALE = -13       /* sm_scale is not a positive finite number                   */
 } pa_status;
 
-#define PA_DEVERR_BAD_BLOCK 1        /* block table / copy pair id outside its pool      */
+#define PA_DEVERR_BAD_BLOCK 1        /* block table / copy pair id outside its pool: the
+                                        attention calls skip that block's keys and values */
 #define PA_DEVERR_BAD_SLOT 2         /* slot_mapping entry outside [0, num_blocks * 16)   */
 #define PA_DEVERR_BAD_CONTEXT 4      /* context_lens entry outside [1, MB * 16]           */
 #define PA_DEVERR_UNCALIBRATED 8     /* decode read an FP4 block whose record is unset    */

@@ -447,7 +447,9 @@ void k_prefill_mt(DecodeArgs a) {
   };
   load_pair(0);
   int pi = 0;
-  for (; pi + 1 < npair && 2 * pi + 2 <= nfull; ++pi) {
+  // (a pair with a bad block id takes the masked body, which skips that block, as the
+  // decode does; so do the pairs after it - only when ids are bad)
+  for (; pi + 1 < npair && 2 * pi + 2 <= nfull && ta.ok && tb.ok; ++pi) {
     compute(ta, tb, std::true_type{});
     load_pair(pi + 1);
   }

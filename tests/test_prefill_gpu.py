@@ -131,3 +131,36 @@ def test_prefill_bad_query_count_is_flagged_and_zeroed():
         assert np.all(np.isfinite(got))
     finally:
         run.dev_err.zero_()  # the prepared run is shared with other test modules
+
+
+@pytest.mark.parametrize("cfg", ["c4", "c5"])
+def test_prefill_bad_block_is_flagged_and_skipped(cfg):
+    """A block id outside the pool among a sequence's early blocks (read by every query,
+    in the unmasked pairs) is flagged and skipped, as the decode skips it: that sequence's
+    outputs equal exact attention over its other keys, the other sequences' are unchanged."""
+    from oracle.attention import decode_dense, gather_sequence
+    from oracle.formats import act_decode
+    w, run, pool, ks, vs, near = _setup(cfg)
+    n, bad = 16, 1  # block 1 (tokens 16 .. 31) of sequence 0
+    q, qs = prefill_queries(w, n)
+    L0 = int(w.context_lens[0])
+    assert L0 - n >= 2 * 16 * 2  # the block lies in pairs before every query's position
+    clean = _run_prefill(w, run, q, qs)
+    assert run.device_error() == 0
+    bt = run.block_tables.clone()
+    try:
+        run.block_tables[0, bad] = w.num_blocks + 7
+        got = _run_prefill(w, run, q, qs)
+        e = run.device_error()
+    finally:
+        run.block_tables.copy_(bt)
+    assert e & 1
+    assert np.array_equal(got[n:], clean[n:])
+    k_seq, v_seq = gather_sequence(pool, w.block_tables[0], L0, ks, vs)
+    qv = act_decode(q, w.act)
+    want = np.zeros((n, w.num_q_heads, w.head_dim))
+    for i in range(n):
+        keep = np.arange(L0 - n + i + 1)
+        keep = keep[(keep // 16) != bad]
+        want[i], _ = decode_dense(qv[i], k_seq[keep], v_seq[keep], float(w.sm_scale))
+    assert_close(got[:n], want, f"{cfg} bad block")
