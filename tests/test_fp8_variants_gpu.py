@@ -307,3 +307,34 @@ def test_write_slot_patterns(fmt_kind, d):
     torch.cuda.synchronize()
     assert int(err.item()) == 2  # PA_DEVERR_BAD_SLOT
     assert_pool_equal(pool.numpy(), opool)
+
+
+@pytest.mark.parametrize("fmt_kind", ["fp8", "fp8t"])
+@pytest.mark.parametrize("T,first", [(1, 0), (2, 14), (3, 4), (4, 4), (5, 8), (5, 3)])
+def test_write_short_calls(fmt_kind, T, first):
+    """Calls of a few rows (less than a window of four, one four, one past it) into
+    consecutive slots from `first` of one block: bit for bit against the oracle."""
+    from oracle import cache as C
+    from paged_quantized_kv_reshape_amd import KVPool, pa_cache_write
+    rng = np.random.default_rng(100 * T + first)
+    nb, hkv, d = 3, 2, 128
+    slots = (16 + first + np.arange(T)).astype(np.int64)  # block 1; may run into block 2
+    x = (rng.standard_normal((2, T, hkv, d)) * 2.0).astype(np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    bits = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    ks_np = vs_np = ks = vs = None
+    if fmt_kind == "fp8":
+        ks_np = np.asarray([0.01, 0.02], dtype=np.float32)
+        vs_np = np.asarray([0.03, 0.015], dtype=np.float32)
+        ks, vs = torch.from_numpy(ks_np).cuda(), torch.from_numpy(vs_np).cuda()
+    opool = C.Pool.filled(fmt_kind, nb, hkv, d)
+    C.cache_write(opool, bits[0], bits[1], "bf16", slots, k_scale=ks_np, v_scale=vs_np)
+    pool = KVPool(fmt_kind, nb, hkv, d, fill=0xA5, k_scale=ks, v_scale=vs)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kt = torch.from_numpy(bits[0].view(np.int16)).cuda().view(torch.bfloat16)
+    vt = torch.from_numpy(bits[1].view(np.int16)).cuda().view(torch.bfloat16)
+    _say(f"[short write] kv={fmt_kind} T={T} first={first}")
+    pa_cache_write(pool, kt, vt, torch.from_numpy(slots).cuda(), err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert_pool_equal(pool.numpy(), opool)
