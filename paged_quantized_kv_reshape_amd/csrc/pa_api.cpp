@@ -349,13 +349,15 @@ size_t tile_pair_bytes(int32_t dtype, int32_t head_dim) {
 //    read neighbouring tiles, and about 8 waves per CU per kv head (up to 8 heads) keeps
 //    those reads together. FP4 pools start from 2 waves: a 4-bit tile is half an FP8 one,
 //    so a one-wave workgroup keeps too little in flight, and the FP4 kernel's wave merge
-//    reuses its own LDS, so two waves cost no occupancy (c5: 107 us vs 113 us with one).
+//    reuses its own LDS, so two waves cost no occupancy (FP4, 32 x 64k-120k tokens: 107 us
+//    vs 113 us with one).
 //  * work per wave: about 48 KiB of K/V per wave of a partition. A workgroup's waves
 //    finish together and the last workgroups of a launch run with the GPU part idle, so
 //    a shorter wave shortens that tail, down to where its fixed costs (the query, the
 //    block ids, the wave merge) start to count. Sweeps of partition size and waves
-//    found the best at 6 bf16 (c2-shaped, 768-token partitions, 8 waves), 12 FP8 (c3,
-//    768, 4 waves) and 16 FP4 tiles (c5, 512, 2 waves) per wave: 48, 48 and 37 KiB.
+//    found the best at 6 bf16 (64 x 1k-8k tokens, 8 kv heads, 768-token partitions, 8
+//    waves), 12 FP8 (the same shapes, 768, 4 waves) and 16 FP4 tiles (32 x 64k-120k tokens,
+//    512, 2 waves) per wave: 48, 48 and 37 KiB.
 int decode_waves(const pa::DecodeArgs& a, int32_t dtype, int32_t head_dim,
                  const pa_launch_options* opts) {
   if (opts && opts->decode_waves) return opts->decode_waves;
