@@ -133,7 +133,7 @@ def test_prefill_bad_query_count_is_flagged_and_zeroed():
         run.dev_err.zero_()  # the prepared run is shared with other test modules
 
 
-@pytest.mark.parametrize("cfg", ["c4", "c5"])
+@pytest.mark.parametrize("cfg", ["c2", "c4", "c5"])
 def test_prefill_bad_block_is_flagged_and_skipped(cfg):
     """A block id outside the pool among a sequence's early blocks (read by every query,
     in the unmasked pairs) is flagged and skipped, as the decode skips it: that sequence's
